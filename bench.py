@@ -1,0 +1,172 @@
+"""Throughput of the full-T Wan 2.2 VAE-decoder ResidualBlock on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one ``wanvae_resblock_forward`` over the whole clip (norm1, conv A,
+norm2, conv B with the residual add), with x, weights, workspace and y already
+resident in HBM.  The default workload is the latent-resolution block:
+bf16, 384 -> 384 channels, x = [1, 21, 90, 160, 384], seeded synthetic values.
+The run prints one JSON line:
+
+* value: frames per second (T * K / elapsed) over K timed steps;
+* roofline: the conv kernel's achieved TFLOP/s (algorithmic FLOPs per launch,
+  2 * P * C_out * 27 * C_in plus 2 * P * C_out * C_in for a 1x1x1 shortcut,
+  divided by its average launch time from hipEvents the library records
+  around each launch on the timed stream) against the 2.5 PFLOP/s dense bf16
+  MFMA peak;
+* norm: the fused RMS_norm + SiLU kernel's achieved GB/s (2 * P * C * 2 bytes
+  per launch) against the 8 TB/s HBM peak;
+* cpu_baseline: the CPU oracle timed on this host on a bounded sample (the
+  whole block over the clip's first frame(s); causal, so those frames are
+  exactly the clip's first output frames), scaled to frames per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ResidualBlock frames/sec + conv TFLOP/s (% bf16 MFMA peak), full-T, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def conv_flops(w):
+    """Algorithmic FLOPs of conv A and conv B (+ the fused 1x1x1 shortcut)."""
+    P = w.positions
+    fa = 2.0 * P * w.cout * 27 * w.cin
+    fb = 2.0 * P * w.cout * 27 * w.cout
+    if w.cin != w.cout:
+        fb += 2.0 * P * w.cout * w.cin
+    return fa, fb
+
+
+def norm_bytes(w, esize):
+    P = w.positions
+    return 2.0 * P * w.cin * esize, 2.0 * P * w.cout * esize
+
+
+def cpu_baseline(w, p, x_dev, frames):
+    import numpy as np
+
+    import oracle
+    ob = oracle.Block(p["gamma1"], p["beta1"], p["wa"], p["ba"], p["gamma2"], p["beta2"],
+                      p["wb"], p["bb"], p.get("ws"), p.get("bs"))
+    xs = x_dev[:, :frames].float().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.resblock_full(ob, np.ascontiguousarray(xs))
+    dt = time.perf_counter() - t0
+    return {"value": frames / dt, "unit": "frames/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"whole block (fp64 accumulation) over frames 0..{frames - 1} of "
+                      f"[{w.n},{w.t},{w.h},{w.w},{w.cin}] -> {w.cout}: {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--cpu-frames", type=int, default=1,
+                    help="frames of the clip the CPU oracle baseline computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the ResidualBlock path here is single-GPU "
+              "(the multi-GPU H-split with halo exchange is designed, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_convolution_amd as wv
+    from causal_convolution_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dt = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
+    esize = 2 if w.dtype == wl.BF16 else 4
+    torch.cuda.set_device(0)
+    p = wl.make_params(w, seed=0)
+    blk = wv.ResBlock.from_host(p, dt)
+    x = wl.make_x_device(w, seed=0)
+    y = torch.empty((w.n, w.t, w.h, w.w, w.cout), dtype=dt, device="cuda")
+    ws = blk.workspace(w.n, w.t, w.h, w.w)
+    stream = torch.cuda.current_stream()
+    print(f"[bench] {w.desc}; steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        blk.forward(x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+
+    wv.timing_reset()
+    wv.timing_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        blk.forward(x, out=y, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wv.timing_enable(False)
+    total_ms = e0.elapsed_time(e1)
+    conv_kind = wv.KERNEL_CONV_BF16 if w.dtype == wl.BF16 else wv.KERNEL_CONV_F32
+    n_conv, conv_ms = wv.timing_read(conv_kind)
+    n_norm, norm_ms = wv.timing_read(wv.KERNEL_NORM)
+    wv.timing_reset()
+    print(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    fa, fb = conv_flops(w)
+    conv_avg_ms = conv_ms / n_conv
+    conv_flop_per_launch = (fa + fb) / 2.0
+    conv_tflops = conv_flop_per_launch / (conv_avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == wl.BF16 else PEAK_F32_TFLOPS
+    nb1, nb2 = norm_bytes(w, esize)
+    norm_avg_ms = norm_ms / n_norm
+    norm_gbs = (nb1 + nb2) / 2.0 / (norm_avg_ms * 1e-3) / 1e9
+
+    ms_per_step = total_ms / args.steps
+    out = {
+        "metric": METRIC,
+        "value": w.t * args.steps / (total_ms * 1e-3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) input, random-init weights)",
+        "config": {"workload": f"ResidualBlock {w.cin}->{w.cout} "
+                               f"{'identity' if w.cin == w.cout else '1x1x1'} shortcut, "
+                               f"x [{w.n},{w.t},{w.h},{w.w},{w.cin}] {w.dtype}, full-T",
+                   "frames": w.t, "positions": w.positions, "parallelism": "1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": conv_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": conv_tflops / peak, "traffic": None,
+                     "kernel": "conv3d_bf16_kernel (conv A and conv B launches)",
+                     "flop_per_launch": conv_flop_per_launch, "avg_launch_ms": conv_avg_ms,
+                     "launches": n_conv},
+        "norm": {"bound": "hbm", "achieved": norm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": norm_gbs / PEAK_HBM_GBS, "bytes_per_launch": (nb1 + nb2) / 2.0,
+                 "avg_launch_ms": norm_avg_ms, "launches": n_norm},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline on {args.cpu_frames} frame(s) ...", file=sys.stderr,
+              flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, p, x, args.cpu_frames)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,274 @@
+"""Wan 2.2 VAE-decoder ResidualBlock on MI355X: Python binding of libwanvae.so.
+
+Argument marshalling only: every entry point takes torch tensors that live on
+the GPU, checks their dtype / shape / contiguity, and passes raw device
+pointers plus torch's current HIP stream to the C ABI declared in
+``include/wanvae.h``.  All computation happens in the library's HIP kernels;
+there is no other implementation and no fallback: if ``libwanvae.so`` is not
+built, importing the binding's functions raises.
+
+Layouts are channels-last: activations ``[n, t, h, w, C]``, 3x3x3 conv
+weights ``[C_out, 3, 3, 3, C_in]``, shortcut weight ``[C_out, C_in]``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libwanvae.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(7)
+F32, BF16 = 0, 1
+KERNEL_NORM, KERNEL_CONV_BF16, KERNEL_CONV_F32, KERNEL_ROLL = range(4)
+EPS = 1e-12
+
+
+class WanVaeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"wanvae status {status}: {msg}")
+        self.status = status
+
+
+class Dims(C.Structure):
+    _fields_ = [("n", C.c_int64), ("t", C.c_int64), ("h", C.c_int64), ("w", C.c_int64)]
+
+
+class ResblockParamsC(C.Structure):
+    _fields_ = [
+        ("in_dim", C.c_int32), ("out_dim", C.c_int32), ("dtype", C.c_int32), ("eps", C.c_float),
+        ("gamma1", C.c_void_p), ("beta1", C.c_void_p), ("w_a", C.c_void_p), ("b_a", C.c_void_p),
+        ("gamma2", C.c_void_p), ("beta2", C.c_void_p), ("w_b", C.c_void_p), ("b_b", C.c_void_p),
+        ("w_sc", C.c_void_p), ("b_sc", C.c_void_p),
+    ]
+
+
+EXPORTS = {
+    "wanvae_rmsnorm_silu": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p,
+                                      C.c_void_p, C.c_float, C.c_int32, C.c_void_p]),
+    "wanvae_causal_conv3d": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                       C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32,
+                                       C.c_void_p]),
+    "wanvae_resblock_workspace_size": (C.c_int, [C.POINTER(ResblockParamsC), C.POINTER(Dims),
+                                                 C.POINTER(C.c_size_t)]),
+    "wanvae_resblock_forward": (C.c_int, [C.POINTER(ResblockParamsC), C.c_void_p, C.c_void_p,
+                                          C.POINTER(Dims), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wanvae_resblock_stream_step": (C.c_int, [C.POINTER(ResblockParamsC), C.c_void_p, C.c_void_p,
+                                              C.POINTER(Dims), C.c_void_p, C.c_void_p,
+                                              C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wanvae_last_error": (C.c_char_p, []),
+    "wanvae_timing_enable": (C.c_int, [C.c_int]),
+    "wanvae_timing_reset": (C.c_int, []),
+    "wanvae_timing_read": (C.c_int, [C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libwanvae.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m causal_convolution_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().wanvae_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise WanVaeError(status, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+# --------------------------------------------------------------------------- single ops
+def rmsnorm_silu(x, gamma, beta=None, eps: float = EPS, out=None, stream=None):
+    """y = silu(RMS_norm over the last axis of x) (``wanvae_rmsnorm_silu``)."""
+    torch = _torch()
+    Cc = x.shape[-1]
+    _dev(x, "x")
+    _dev(gamma, "gamma", torch.float32, (Cc,))
+    _dev(beta, "beta", torch.float32, (Cc,))
+    y = torch.empty_like(x) if out is None else out
+    _dev(y, "out", x.dtype, x.shape)
+    rows = x.numel() // Cc if Cc else 0
+    _check(lib().wanvae_rmsnorm_silu(_ptr(x), _ptr(y), rows, Cc, _ptr(gamma), _ptr(beta),
+                                     float(eps), _dtype_code(x), _stream(stream)))
+    return y
+
+
+def causal_conv3d(x, w, bias=None, cache=None, out=None, stream=None):
+    """Causal 3x3x3 conv (``wanvae_causal_conv3d``): x [n,t,h,w,Cin],
+    w [Cout,3,3,3,Cin], cache [n,2,h,w,Cin] or None -> [n,t,h,w,Cout]."""
+    torch = _torch()
+    n, t, h, wd, cin = x.shape
+    cout = w.shape[0]
+    _dev(x, "x")
+    _dev(w, "w", x.dtype, (cout, 3, 3, 3, cin))
+    _dev(bias, "bias", torch.float32, (cout,))
+    _dev(cache, "cache", x.dtype, (n, 2, h, wd, cin))
+    y = torch.empty((n, t, h, wd, cout), dtype=x.dtype, device=x.device) if out is None else out
+    _dev(y, "out", x.dtype, (n, t, h, wd, cout))
+    d = Dims(n, t, h, wd)
+    _check(lib().wanvae_causal_conv3d(_ptr(x), _ptr(cache), _ptr(w), _ptr(bias), _ptr(y),
+                                      C.byref(d), cin, cout, _dtype_code(x), _stream(stream)))
+    return y
+
+
+# --------------------------------------------------------------------------- block
+class ResBlock:
+    """Device-resident parameters of one ResidualBlock.
+
+    ``from_host`` takes float32 numpy arrays with conv weights in the pages'
+    order [C_out, C_in, kD, kH, kW] and stores them channels-last
+    ([C_out, 3, 3, 3, C_in]) in the block's dtype, once, at setup.
+    """
+
+    def __init__(self, in_dim, out_dim, dtype, gamma1, beta1, w_a, b_a, gamma2, beta2, w_b, b_b,
+                 w_sc=None, b_sc=None, eps: float = EPS):
+        torch = _torch()
+        self.in_dim, self.out_dim, self.eps = int(in_dim), int(out_dim), float(eps)
+        self.dtype = dtype
+        self.tensors = dict(gamma1=gamma1, beta1=beta1, w_a=w_a, b_a=b_a, gamma2=gamma2,
+                            beta2=beta2, w_b=w_b, b_b=b_b, w_sc=w_sc, b_sc=b_sc)
+        ci, co = self.in_dim, self.out_dim
+        shapes = dict(gamma1=(ci,), beta1=(ci,), b_a=(co,), gamma2=(co,), beta2=(co,), b_b=(co,),
+                      b_sc=(co,))
+        for k, shp in shapes.items():
+            _dev(self.tensors[k], k, torch.float32, shp)
+        _dev(w_a, "w_a", dtype, (co, 3, 3, 3, ci))
+        _dev(w_b, "w_b", dtype, (co, 3, 3, 3, co))
+        _dev(w_sc, "w_sc", dtype, (co, ci))
+        self.c = ResblockParamsC(ci, co, BF16 if dtype == torch.bfloat16 else F32, self.eps,
+                                 *[None if self.tensors[k] is None else self.tensors[k].data_ptr()
+                                   for k in ("gamma1", "beta1", "w_a", "b_a", "gamma2", "beta2",
+                                             "w_b", "b_b", "w_sc", "b_sc")])
+
+    @classmethod
+    def from_host(cls, p: dict, dtype, device="cuda", eps: float = EPS):
+        import numpy as np
+        torch = _torch()
+
+        def f32(a):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+        def wt(a, conv3):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(np.transpose(a, (0, 2, 3, 4, 1)) if conv3 else a, np.float32)
+            return torch.from_numpy(a).to(device=device, dtype=dtype).contiguous()
+
+        ci, co = p["wa"].shape[1], p["wa"].shape[0]
+        return cls(ci, co, dtype, f32(p["gamma1"]), f32(p["beta1"]), wt(p["wa"], True), f32(p["ba"]),
+                   f32(p["gamma2"]), f32(p["beta2"]), wt(p["wb"], True), f32(p["bb"]),
+                   wt(p.get("ws"), False), f32(p.get("bs")), eps)
+
+    def workspace_size(self, n, t, h, w) -> int:
+        d = Dims(n, t, h, w)
+        b = C.c_size_t(0)
+        _check(lib().wanvae_resblock_workspace_size(C.byref(self.c), C.byref(d), C.byref(b)))
+        return b.value
+
+    def workspace(self, n, t, h, w, device="cuda"):
+        torch = _torch()
+        return torch.empty(max(self.workspace_size(n, t, h, w), 1), dtype=torch.uint8, device=device)
+
+    def forward(self, x, out=None, workspace=None, stream=None):
+        """Full-T block (``wanvae_resblock_forward``): x [n,t,h,w,in_dim] -> y."""
+        torch = _torch()
+        n, t, h, w, ci = x.shape
+        _dev(x, "x", self.dtype, (n, t, h, w, self.in_dim))
+        y = torch.empty((n, t, h, w, self.out_dim), dtype=x.dtype, device=x.device) if out is None else out
+        _dev(y, "out", self.dtype, (n, t, h, w, self.out_dim))
+        ws = self.workspace(n, t, h, w, x.device) if workspace is None else workspace
+        d = Dims(n, t, h, w)
+        _check(lib().wanvae_resblock_forward(C.byref(self.c), _ptr(x), _ptr(y), C.byref(d),
+                                             _ptr(ws), ws.numel() * ws.element_size(),
+                                             _stream(stream)))
+        return y
+
+    def new_caches(self, n, h, w, device="cuda"):
+        """Zero caches for a fresh stream: ([n,2,h,w,in_dim], [n,2,h,w,out_dim])."""
+        torch = _torch()
+        return (torch.zeros((n, 2, h, w, self.in_dim), dtype=self.dtype, device=device),
+                torch.zeros((n, 2, h, w, self.out_dim), dtype=self.dtype, device=device))
+
+    def stream_step(self, x_chunk, cache_a, cache_b, out=None, workspace=None, stream=None):
+        """One streaming step (``wanvae_resblock_stream_step``); caches update in place."""
+        torch = _torch()
+        n, t, h, w, ci = x_chunk.shape
+        _dev(x_chunk, "x_chunk", self.dtype, (n, t, h, w, self.in_dim))
+        _dev(cache_a, "cache_a", self.dtype, (n, 2, h, w, self.in_dim))
+        _dev(cache_b, "cache_b", self.dtype, (n, 2, h, w, self.out_dim))
+        y = torch.empty((n, t, h, w, self.out_dim), dtype=x_chunk.dtype,
+                        device=x_chunk.device) if out is None else out
+        _dev(y, "out", self.dtype, (n, t, h, w, self.out_dim))
+        ws = self.workspace(n, t, h, w, x_chunk.device) if workspace is None else workspace
+        d = Dims(n, t, h, w)
+        _check(lib().wanvae_resblock_stream_step(C.byref(self.c), _ptr(x_chunk), _ptr(y),
+                                                 C.byref(d), _ptr(cache_a), _ptr(cache_b),
+                                                 _ptr(ws), ws.numel() * ws.element_size(),
+                                                 _stream(stream)))
+        return y
+
+
+# --------------------------------------------------------------------------- timing
+def timing_enable(on: bool = True):
+    _check(lib().wanvae_timing_enable(1 if on else 0))
+
+
+def timing_reset():
+    _check(lib().wanvae_timing_reset())
+
+
+def timing_read(kind: int):
+    """(launches, total_ms) of one kernel kind since the last reset."""
+    n = C.c_int64(0)
+    ms = C.c_double(0.0)
+    _check(lib().wanvae_timing_read(kind, C.byref(n), C.byref(ms)))
+    return n.value, ms.value

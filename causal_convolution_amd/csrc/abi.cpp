@@ -1,0 +1,420 @@
+// C ABI of libwanvae.so: argument validation, workspace planning, dispatch
+// to the HIP kernels, per-kernel timing.  Every check runs on the host before
+// the first launch of a call; see include/wanvae.h for the contract.
+#include "wanvae.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+#define WV_CHECK(cond, code, ...)              \
+    do {                                       \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+an) and [b, b+bn) intersect (empty ranges never do)
+bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+size_t esize(int32_t dt) { return dt == WANVAE_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t dt) { return dt == WANVAE_F32 || dt == WANVAE_BF16; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// number of positions n*t*h*w, with overflow / sign checks
+int positions(const wanvae_dims *d, int64_t *P) {
+    WV_CHECK(d != nullptr, WANVAE_ERR_NULL, "dims is NULL");
+    WV_CHECK(d->n >= 0 && d->t >= 0 && d->h >= 0 && d->w >= 0, WANVAE_ERR_SHAPE,
+             "negative extent [%lld,%lld,%lld,%lld]", (long long)d->n, (long long)d->t,
+             (long long)d->h, (long long)d->w);
+    WV_CHECK(d->h <= (1 << 30) && d->w <= (1 << 30), WANVAE_ERR_SHAPE, "h or w too large");
+    int64_t p1, p2, p3;
+    WV_CHECK(mul_ok(d->n, d->t, &p1) && mul_ok(p1, d->h, &p2) && mul_ok(p2, d->w, &p3) &&
+                 p3 <= (INT64_MAX >> 12),
+             WANVAE_ERR_SHAPE, "tensor extent overflows");
+    *P = p3;
+    return WANVAE_OK;
+}
+
+// ------------------------------------------------------------------ timing
+struct TimingRec {
+    int kind;
+    hipEvent_t start, stop;
+};
+std::mutex g_tm_mu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs one launch, bracketed by timing events when timing is enabled.
+template <typename F>
+int timed_launch(int kind, hipStream_t s, const char *what, F &&launch) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_tm_mu);
+        if (g_timing) {
+            e0 = take_event();
+            e1 = take_event();
+        }
+    }
+    bool timed = e0 && e1 && hipEventRecord(e0, s) == hipSuccess;
+    const hipError_t err = launch();
+    timed = timed && hipEventRecord(e1, s) == hipSuccess;
+    if (e0 || e1) {
+        std::lock_guard<std::mutex> lk(g_tm_mu);
+        if (timed) {
+            g_recs.push_back({kind, e0, e1});
+        } else {
+            if (e0) g_pool.push_back(e0);
+            if (e1) g_pool.push_back(e1);
+        }
+    }
+    if (err != hipSuccess)
+        return fail(WANVAE_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(err));
+    return WANVAE_OK;
+}
+
+// ------------------------------------------------------------------ validated launchers
+int run_norm(const void *x, void *y, int64_t rows, int C, const float *g, const float *b,
+             float eps, int32_t dt, hipStream_t s) {
+    if (rows == 0) return WANVAE_OK;
+    return timed_launch(WANVAE_KERNEL_NORM, s, "rmsnorm_silu", [&] {
+        return dt == WANVAE_BF16 ? wanvae::launch_rmsnorm_silu_bf16(x, y, rows, C, g, b, eps, s)
+                                 : wanvae::launch_rmsnorm_silu_f32(x, y, rows, C, g, b, eps, s);
+    });
+}
+
+int run_conv(const wanvae::ConvLaunch &c, int32_t dt, hipStream_t s) {
+    if (c.n * c.t * c.h * c.w_ == 0) return WANVAE_OK;
+    if (dt == WANVAE_BF16)
+        return timed_launch(WANVAE_KERNEL_CONV_BF16, s, "conv3d_bf16",
+                            [&] { return wanvae::launch_conv3d_bf16(c, s); });
+    return timed_launch(WANVAE_KERNEL_CONV_F32, s, "conv3d_f32",
+                        [&] { return wanvae::launch_conv3d_f32(c, s); });
+}
+
+int check_conv_channels(int32_t cin, int32_t cout, int32_t dt) {
+    if (dt == WANVAE_BF16) {
+        WV_CHECK(wanvae::conv3d_bf16_supported(cin, cout), WANVAE_ERR_SHAPE,
+                 "bf16 conv needs cin, cout multiples of 32 in [32, 1024] (got %d, %d)", cin,
+                 cout);
+    } else {
+        WV_CHECK(cin >= 1 && cin <= 1024 && cout >= 1 && cout <= 1024, WANVAE_ERR_SHAPE,
+                 "fp32 conv needs cin, cout in [1, 1024] (got %d, %d)", cin, cout);
+    }
+    return WANVAE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_params(const wanvae_resblock_params *p) {
+    WV_CHECK(p != nullptr, WANVAE_ERR_NULL, "params is NULL");
+    WV_CHECK(valid_dtype(p->dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", p->dtype);
+    WV_CHECK(wanvae::rmsnorm_silu_supported(p->in_dim) && wanvae::rmsnorm_silu_supported(p->out_dim),
+             WANVAE_ERR_SHAPE, "in_dim and out_dim must be multiples of 32 in [32, 1024] (got %d, %d)",
+             p->in_dim, p->out_dim);
+    if (int r = check_conv_channels(p->in_dim, p->out_dim, p->dtype)) return r;
+    WV_CHECK(std::isfinite(p->eps) && p->eps >= 0.0f, WANVAE_ERR_SHAPE, "eps must be finite and >= 0");
+    WV_CHECK(p->gamma1 && p->w_a && p->gamma2 && p->w_b, WANVAE_ERR_NULL,
+             "gamma1, w_a, gamma2 and w_b are required");
+    WV_CHECK(p->w_sc != nullptr || p->in_dim == p->out_dim, WANVAE_ERR_SHAPE,
+             "identity shortcut (w_sc NULL) needs in_dim == out_dim (got %d, %d)", p->in_dim,
+             p->out_dim);
+    const void *ptrs[] = {p->gamma1, p->beta1, p->w_a, p->b_a, p->gamma2,
+                          p->beta2,  p->w_b,   p->b_b, p->w_sc, p->b_sc};
+    for (const void *q : ptrs)
+        WV_CHECK(aligned16(q), WANVAE_ERR_SHAPE, "parameter pointers must be 16-byte aligned");
+    return WANVAE_OK;
+}
+
+struct Plan {
+    int64_t P = 0;
+    size_t x_bytes = 0, y_bytes = 0, n1_off = 0, n1_bytes = 0, a_off = 0, a_bytes = 0, total = 0;
+};
+
+int plan_block(const wanvae_resblock_params *p, const wanvae_dims *d, Plan *pl) {
+    if (int r = check_params(p)) return r;
+    if (int r = positions(d, &pl->P)) return r;
+    const size_t es = esize(p->dtype);
+    pl->x_bytes = (size_t)pl->P * p->in_dim * es;
+    pl->y_bytes = (size_t)pl->P * p->out_dim * es;
+    pl->n1_off = 0;
+    pl->n1_bytes = pl->x_bytes;
+    pl->a_off = round_up(pl->n1_bytes);
+    pl->a_bytes = pl->y_bytes;
+    pl->total = pl->a_off + round_up(pl->a_bytes);
+    return WANVAE_OK;
+}
+
+int check_block_buffers(const wanvae_resblock_params *p, const Plan &pl, const void *x,
+                        const void *y, void *ws, size_t ws_bytes) {
+    WV_CHECK(x && y, WANVAE_ERR_NULL, "x and y are required");
+    WV_CHECK(aligned16(x) && aligned16(y), WANVAE_ERR_SHAPE, "x and y must be 16-byte aligned");
+    WV_CHECK(!overlaps(x, pl.x_bytes, y, pl.y_bytes), WANVAE_ERR_ALIAS, "y overlaps x");
+    WV_CHECK(ws != nullptr, WANVAE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", pl.total);
+    WV_CHECK(ws_bytes >= pl.total, WANVAE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed",
+             ws_bytes, pl.total);
+    WV_CHECK(aligned16(ws), WANVAE_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    WV_CHECK(!overlaps(ws, pl.total, x, pl.x_bytes) && !overlaps(ws, pl.total, y, pl.y_bytes),
+             WANVAE_ERR_ALIAS, "workspace overlaps x or y");
+    (void)p;
+    return WANVAE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *wanvae_last_error(void) { return g_error.c_str(); }
+
+int wanvae_rmsnorm_silu(const void *x, void *y, int64_t rows, int32_t C, const float *gamma,
+                        const float *beta, float eps, int32_t dtype, void *stream) {
+    g_error.clear();
+    WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
+    WV_CHECK(wanvae::rmsnorm_silu_supported(C), WANVAE_ERR_SHAPE,
+             "C must be a multiple of 32 in [32, 1024] (got %d)", C);
+    WV_CHECK(rows >= 0 && rows <= (INT64_MAX >> 12), WANVAE_ERR_SHAPE, "bad row count %lld",
+             (long long)rows);
+    WV_CHECK(std::isfinite(eps) && eps >= 0.0f, WANVAE_ERR_SHAPE, "eps must be finite and >= 0");
+    if (rows == 0) return WANVAE_OK;
+    WV_CHECK(x && y && gamma, WANVAE_ERR_NULL, "x, y and gamma are required");
+    WV_CHECK(aligned16(x) && aligned16(y) && aligned16(gamma) && aligned16(beta), WANVAE_ERR_SHAPE,
+             "pointers must be 16-byte aligned");
+    const size_t bytes = (size_t)rows * C * esize(dtype);
+    WV_CHECK(x == y || !overlaps(x, bytes, y, bytes), WANVAE_ERR_ALIAS,
+             "y partially overlaps x (only y == x is allowed)");
+    return run_norm(x, y, rows, C, gamma, beta, eps, dtype, static_cast<hipStream_t>(stream));
+}
+
+int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const float *bias,
+                         void *y, const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
+                         void *stream) {
+    g_error.clear();
+    WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
+    int64_t P = 0;
+    if (int r = positions(d, &P)) return r;
+    if (int r = check_conv_channels(cin, cout, dtype)) return r;
+    if (P == 0) return WANVAE_OK;
+    WV_CHECK(x && w && y, WANVAE_ERR_NULL, "x, w and y are required");
+    WV_CHECK(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(cache) && aligned16(bias),
+             WANVAE_ERR_SHAPE, "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype);
+    const size_t xb = (size_t)P * cin * es, yb = (size_t)P * cout * es;
+    const size_t cb = (size_t)d->n * 2 * d->h * d->w * cin * es;
+    const size_t wb = (size_t)cout * 27 * cin * es;
+    WV_CHECK(!overlaps(y, yb, x, xb) && !overlaps(y, yb, cache, cb) && !overlaps(y, yb, w, wb),
+             WANVAE_ERR_ALIAS, "y overlaps x, cache or w");
+    wanvae::ConvLaunch c;
+    c.x = x;
+    c.cache = cache;
+    c.w = w;
+    c.bias = bias;
+    c.y = y;
+    c.n = d->n;
+    c.t = d->t;
+    c.h = d->h;
+    c.w_ = d->w;
+    c.cin = cin;
+    c.cout = cout;
+    return run_conv(c, dtype, static_cast<hipStream_t>(stream));
+}
+
+int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, const wanvae_dims *d,
+                                   size_t *bytes) {
+    g_error.clear();
+    WV_CHECK(bytes != nullptr, WANVAE_ERR_NULL, "bytes is NULL");
+    Plan pl;
+    if (int r = plan_block(p, d, &pl)) return r;
+    *bytes = pl.total;
+    return WANVAE_OK;
+}
+
+int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void *y,
+                            const wanvae_dims *d, void *workspace, size_t ws_bytes, void *stream) {
+    g_error.clear();
+    Plan pl;
+    if (int r = plan_block(p, d, &pl)) return r;
+    if (pl.P == 0) return WANVAE_OK;
+    if (int r = check_block_buffers(p, pl, x, y, workspace, ws_bytes)) return r;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *n1 = ws + pl.n1_off;
+    void *a = ws + pl.a_off;
+
+    if (int r = run_norm(x, n1, pl.P, p->in_dim, p->gamma1, p->beta1, p->eps, p->dtype, s)) return r;
+    wanvae::ConvLaunch ca;
+    ca.x = n1;
+    ca.w = p->w_a;
+    ca.bias = p->b_a;
+    ca.y = a;
+    ca.n = d->n;
+    ca.t = d->t;
+    ca.h = d->h;
+    ca.w_ = d->w;
+    ca.cin = p->in_dim;
+    ca.cout = p->out_dim;
+    if (int r = run_conv(ca, p->dtype, s)) return r;
+    if (int r = run_norm(a, a, pl.P, p->out_dim, p->gamma2, p->beta2, p->eps, p->dtype, s)) return r;
+    wanvae::ConvLaunch cb = ca;
+    cb.x = a;
+    cb.w = p->w_b;
+    cb.bias = p->b_b;
+    cb.res = x;
+    cb.wsc = p->w_sc;
+    cb.bsc = p->b_sc;
+    cb.cres = p->in_dim;
+    cb.y = y;
+    cb.cin = p->out_dim;
+    return run_conv(cb, p->dtype, s);
+}
+
+int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_chunk,
+                                void *y_chunk, const wanvae_dims *d, void *cache_a, void *cache_b,
+                                void *workspace, size_t ws_bytes, void *stream) {
+    g_error.clear();
+    Plan pl;
+    if (int r = plan_block(p, d, &pl)) return r;
+    if (pl.P == 0) return WANVAE_OK;
+    if (int r = check_block_buffers(p, pl, x_chunk, y_chunk, workspace, ws_bytes)) return r;
+    WV_CHECK(cache_a && cache_b, WANVAE_ERR_NULL, "cache_a and cache_b are required");
+    WV_CHECK(aligned16(cache_a) && aligned16(cache_b), WANVAE_ERR_SHAPE,
+             "caches must be 16-byte aligned");
+    const size_t es = esize(p->dtype);
+    const size_t slab_a = (size_t)d->h * d->w * p->in_dim * es;
+    const size_t slab_b = (size_t)d->h * d->w * p->out_dim * es;
+    const size_t ca_bytes = (size_t)d->n * 2 * slab_a, cb_bytes = (size_t)d->n * 2 * slab_b;
+    WV_CHECK(!overlaps(cache_a, ca_bytes, cache_b, cb_bytes) &&
+                 !overlaps(cache_a, ca_bytes, x_chunk, pl.x_bytes) &&
+                 !overlaps(cache_a, ca_bytes, y_chunk, pl.y_bytes) &&
+                 !overlaps(cache_b, cb_bytes, x_chunk, pl.x_bytes) &&
+                 !overlaps(cache_b, cb_bytes, y_chunk, pl.y_bytes) &&
+                 !overlaps(cache_a, ca_bytes, workspace, pl.total) &&
+                 !overlaps(cache_b, cb_bytes, workspace, pl.total),
+             WANVAE_ERR_ALIAS, "caches overlap each other, x, y or the workspace");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *n1 = ws + pl.n1_off;
+    void *a = ws + pl.a_off;
+
+    if (int r = run_norm(x_chunk, n1, pl.P, p->in_dim, p->gamma1, p->beta1, p->eps, p->dtype, s))
+        return r;
+    wanvae::ConvLaunch ca;
+    ca.x = n1;
+    ca.cache = cache_a;
+    ca.w = p->w_a;
+    ca.bias = p->b_a;
+    ca.y = a;
+    ca.n = d->n;
+    ca.t = d->t;
+    ca.h = d->h;
+    ca.w_ = d->w;
+    ca.cin = p->in_dim;
+    ca.cout = p->out_dim;
+    if (int r = run_conv(ca, p->dtype, s)) return r;
+    if (int r = timed_launch(WANVAE_KERNEL_ROLL, s, "roll_cache", [&] {
+            return wanvae::launch_roll_cache(cache_a, n1, d->n, d->t, (int64_t)slab_a, s);
+        }))
+        return r;
+    if (int r = run_norm(a, a, pl.P, p->out_dim, p->gamma2, p->beta2, p->eps, p->dtype, s)) return r;
+    wanvae::ConvLaunch cb = ca;
+    cb.x = a;
+    cb.cache = cache_b;
+    cb.w = p->w_b;
+    cb.bias = p->b_b;
+    cb.res = x_chunk;
+    cb.wsc = p->w_sc;
+    cb.bsc = p->b_sc;
+    cb.cres = p->in_dim;
+    cb.y = y_chunk;
+    cb.cin = p->out_dim;
+    if (int r = run_conv(cb, p->dtype, s)) return r;
+    return timed_launch(WANVAE_KERNEL_ROLL, s, "roll_cache", [&] {
+        return wanvae::launch_roll_cache(cache_b, a, d->n, d->t, (int64_t)slab_b, s);
+    });
+}
+
+int wanvae_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_tm_mu);
+    g_timing = on != 0;
+    return WANVAE_OK;
+}
+
+int wanvae_timing_reset(void) {
+    std::lock_guard<std::mutex> lk(g_tm_mu);
+    for (auto &r : g_recs) {
+        g_pool.push_back(r.start);
+        g_pool.push_back(r.stop);
+    }
+    g_recs.clear();
+    return WANVAE_OK;
+}
+
+int wanvae_timing_read(int32_t kind, int64_t *launches, double *total_ms) {
+    g_error.clear();
+    WV_CHECK(launches && total_ms, WANVAE_ERR_NULL, "launches and total_ms are required");
+    WV_CHECK(kind >= 0 && kind < WANVAE_KERNEL_KINDS, WANVAE_ERR_SHAPE, "unknown kernel kind %d",
+             kind);
+    std::lock_guard<std::mutex> lk(g_tm_mu);
+    int64_t n = 0;
+    double ms = 0.0;
+    for (auto &r : g_recs) {
+        if (r.kind != kind) continue;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+        float f = 0.0f;
+        e = hipEventElapsedTime(&f, r.start, r.stop);
+        if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+        ms += f;
+        ++n;
+    }
+    *launches = n;
+    *total_ms = ms;
+    return WANVAE_OK;
+}
+
+}  // extern "C"

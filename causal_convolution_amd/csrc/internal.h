@@ -1,0 +1,49 @@
+// Internal launch interface between the C-ABI layer (abi.cpp) and the HIP
+// kernels.  Every launcher assumes its arguments were validated by abi.cpp:
+// shapes supported, pointers non-null where required and 16-byte aligned.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace wanvae {
+
+// One causal 3x3x3 conv launch.  Activations channels-last.  The optional
+// residual source `res` ([n][t][h][w][cres]) is added in the epilogue: as is
+// (identity shortcut, cres == cout) when `wsc` is null, or through the 1x1x1
+// shortcut weight `wsc` ([cout][cres]) plus `bsc` otherwise.
+struct ConvLaunch {
+    const void *x = nullptr;      // conv input [n][t][h][w][cin]
+    const void *cache = nullptr;  // frames -2, -1: [n][2][h][w][cin], or null
+    const void *w = nullptr;      // [cout][3][3][3][cin]
+    const float *bias = nullptr;  // [cout] or null
+    const void *res = nullptr;    // residual / shortcut input, or null
+    const void *wsc = nullptr;    // [cout][cres] or null
+    const float *bsc = nullptr;   // [cout] or null
+    void *y = nullptr;            // [n][t][h][w][cout]
+    int64_t n = 0, t = 0, h = 0, w_ = 0;
+    int cin = 0, cout = 0, cres = 0;
+};
+
+// Fused RMS_norm + SiLU over rows of C channels (C % 32 == 0, 32..1024).
+bool rmsnorm_silu_supported(int C);
+hipError_t launch_rmsnorm_silu_bf16(const void *x, void *y, int64_t rows, int C,
+                                    const float *gamma, const float *beta, float eps,
+                                    hipStream_t s);
+hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, const float *gamma,
+                                   const float *beta, float eps, hipStream_t s);
+
+// bf16 implicit-GEMM conv on MFMA: cin, cout (and cres) multiples of 32.
+bool conv3d_bf16_supported(int cin, int cout);
+hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
+
+// fp32 direct conv, any channel counts.
+hipError_t launch_conv3d_f32(const ConvLaunch &a, hipStream_t s);
+
+// cache[nb][0..1] <- last two frames of [cache[nb], chunk[nb]] for each batch
+// item; a frame is `slab_bytes` bytes (a multiple of 4).
+hipError_t launch_roll_cache(void *cache, const void *chunk, int64_t nbatch, int64_t tc,
+                             int64_t slab_bytes, hipStream_t s);
+
+}  // namespace wanvae

@@ -1,0 +1,197 @@
+/*
+ * wanvae.h — C ABI of the Wan 2.2 VAE-decoder ResidualBlock library
+ * (libwanvae.so, hand-written HIP kernels for MI355X / gfx950).
+ *
+ * The block is the decoder's residual unit as described on "Sharding of WAN
+ * 2.2 VAE" (Channel sharding: residual = RMS_norm, SiLU, CausalConv3d k3,
+ * RMS_norm, SiLU, CausalConv3d k3; shortcut = CausalConv3d k1, or Identity
+ * when in_dim == out_dim; output = residual + shortcut), run over all frames
+ * at once ("Closing the gap: Wan 2.2 14B VAE decoder", gap #1 / section 1,
+ * full-T) or frame-chunk by frame-chunk with a feat_cache ("Sharding of WAN
+ * 2.2 VAE", Why depth sharding is not beneficial).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers to dense tensors.  Activations are
+ *    channels-last [n][t][h][w][C] (C innermost), the NDHWC layout of
+ *    "Closing the gap", gap #6; nothing is permuted inside the library.
+ *  - 3x3x3 conv weights are [C_out][3][3][3][C_in] = [C_out][kt][kh][kw][C_in]:
+ *    the pages' [C_out, C_in, kD, kH, kW] ("Sharding of WAN 2.2 VAE",
+ *    Available Sharding Dimensions) with C_in moved innermost.  The 1x1x1
+ *    shortcut weight is [C_out][C_in].
+ *  - dtype (wanvae_dtype) applies to activations and conv weights.  Norm
+ *    scales/shifts and all biases are fp32 [C].  Arithmetic is fp32 (norm
+ *    statistics, conv accumulation, bias and residual adds); bf16 outputs are
+ *    rounded once, to nearest even.
+ *  - Alignment: every pointer must be 16-byte aligned (torch allocations
+ *    are); a misaligned pointer returns WANVAE_ERR_SHAPE.
+ *  - Ownership: the caller allocates and owns every buffer (tensors, weights,
+ *    caches, workspace).  The library allocates no device memory and keeps no
+ *    pointer after a call returns.
+ *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  All
+ *    work is enqueued on it; no call synchronizes the device or the stream
+ *    (except wanvae_timing_read, which waits for its own events).
+ *  - Errors: every entry point validates all arguments on the host before it
+ *    enqueues anything and returns a wanvae_status.  On an error nothing has
+ *    been enqueued, except WANVAE_ERR_HIP, which reports a launch failure
+ *    (earlier launches of the same call may already be enqueued).
+ *    wanvae_last_error() describes the most recent failure of this thread.
+ *  - Threads: entry points may be called from several host threads; calls
+ *    that share output buffers must be ordered by the caller.
+ */
+#ifndef WANVAE_H
+#define WANVAE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define WANVAE_API __attribute__((visibility("default")))
+#else
+#define WANVAE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WANVAE_OK = 0,
+    WANVAE_ERR_NULL = 1,      /* a required pointer is NULL                      */
+    WANVAE_ERR_SHAPE = 2,     /* negative extent, unsupported channel count, ... */
+    WANVAE_ERR_DTYPE = 3,     /* unknown dtype                                   */
+    WANVAE_ERR_ALIAS = 4,     /* an output overlaps an input it must not overlap */
+    WANVAE_ERR_WORKSPACE = 5, /* workspace missing or smaller than required      */
+    WANVAE_ERR_HIP = 6        /* a HIP launch or runtime call failed             */
+} wanvae_status;
+
+typedef enum { WANVAE_F32 = 0, WANVAE_BF16 = 1 } wanvae_dtype;
+
+/* Activation extent: a tensor is [n][t][h][w][C].  Any extent may be 0
+ * (an empty tensor: the call does nothing and returns WANVAE_OK). */
+typedef struct {
+    int64_t n, t, h, w;
+} wanvae_dims;
+
+/* Parameters of one ResidualBlock.  All pointers are device pointers. */
+typedef struct {
+    int32_t in_dim, out_dim;  /* channel counts of x and y                          */
+    int32_t dtype;            /* wanvae_dtype of activations and conv weights        */
+    float eps;                /* clamp of the channel L2 norm (1e-12 in the decoder) */
+    const float *gamma1;      /* [in_dim]  norm1 scale                                */
+    const float *beta1;       /* [in_dim]  norm1 shift, or NULL for 0                 */
+    const void *w_a;          /* [out_dim][3][3][3][in_dim]  conv A weight            */
+    const float *b_a;         /* [out_dim] conv A bias, or NULL                        */
+    const float *gamma2;      /* [out_dim] norm2 scale                                */
+    const float *beta2;       /* [out_dim] norm2 shift, or NULL                        */
+    const void *w_b;          /* [out_dim][3][3][3][out_dim] conv B weight            */
+    const float *b_b;         /* [out_dim] conv B bias, or NULL                        */
+    const void *w_sc;         /* [out_dim][in_dim] 1x1x1 shortcut weight, or NULL for
+                                 the identity shortcut (requires in_dim == out_dim)   */
+    const float *b_sc;        /* [out_dim] shortcut bias, or NULL                      */
+} wanvae_resblock_params;
+
+/*
+ * Fused channel RMS_norm + SiLU over `rows` independent C-vectors:
+ *   d = max(sqrt(sum_c x_c^2), eps)
+ *   y_c = silu(x_c / d * sqrt(C) * gamma_c + beta_c),  silu(u) = u / (1 + exp(-u))
+ * The norm is the F.normalize chain of "Closing the gap", section 4 (RMSNorm
+ * not fused: abs, pow 2, sum over channels, sqrt, clamp(eps), divide, scale
+ * by sqrt(D)*gamma), with beta added after the scale; SiLU is fused into the
+ * same pass as tt-metal's fused norm kernel does (same section).
+ *   x, y   : [rows][C] of dtype.  y == x (in place) is allowed; any other
+ *            overlap returns WANVAE_ERR_ALIAS.
+ *   C      : a multiple of 32 in [32, 1024].
+ *   gamma  : [C] fp32; beta: [C] fp32 or NULL.
+ */
+WANVAE_API int wanvae_rmsnorm_silu(const void *x, void *y, int64_t rows, int32_t C, const float *gamma,
+                        const float *beta, float eps, int32_t dtype, void *stream);
+
+/*
+ * Causal 3x3x3 convolution, stride 1, with bias:
+ *   y[n,t,h,w,co] = bias[co] + sum_{kt,kh,kw,ci} w[co,kt,kh,kw,ci] *
+ *                   Z[n, t+kt-2, h+kh-1, w+kw-1, ci]
+ * ("Sharding of WAN 2.2 VAE", Available Sharding Dimensions, for the conv and
+ * its weight; causal in time, zero pad of one pixel in H and W: "Closing the
+ * gap", section 2, the padding mask and causal-T-pad).  Z is x inside the
+ * tensor and 0 outside it in H and W.  Frames -2 and -1 are cache[:,0] and
+ * cache[:,1] when a cache is given (the feat_cache of "Sharding of WAN 2.2
+ * VAE", Why depth sharding is not beneficial), else 0 (causal zero pad).
+ *   x     : [d.n][d.t][d.h][d.w][cin] of dtype.
+ *   cache : [d.n][2][d.h][d.w][cin] of dtype, or NULL.  Only read.
+ *   w     : [cout][3][3][3][cin] of dtype.   bias: [cout] fp32 or NULL.
+ *   y     : [d.n][d.t][d.h][d.w][cout] of dtype; must not overlap x, cache, w.
+ *   Channels: bf16 needs cin and cout multiples of 32 and <= 1024 (bf16 MFMA
+ *   implicit GEMM); fp32 accepts 1..1024 (direct fp32 kernel).
+ */
+WANVAE_API int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const float *bias,
+                         void *y, const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
+                         void *stream);
+
+/*
+ * Workspace bytes that wanvae_resblock_forward / wanvae_resblock_stream_step
+ * need for extent *d (for the stream step, d->t is the chunk length):
+ * the conv A input (n1, [P][in_dim]) and the conv A output, normalised in
+ * place into the conv B input ([P][out_dim]), P = n*t*h*w, each 256-byte
+ * aligned.  Validates p and d as the forward call does.
+ */
+WANVAE_API int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, const wanvae_dims *d,
+                                   size_t *bytes);
+
+/*
+ * Whole ResidualBlock over every frame in one pass (full-T, no cache):
+ *   n1 = rmsnorm_silu(x; gamma1, beta1); a = conv3d(n1; w_a, b_a)
+ *   n2 = rmsnorm_silu(a; gamma2, beta2)
+ *   y  = conv3d(n2; w_b, b_b) + shortcut(x)
+ * shortcut(x) = x for the identity, else w_sc . x + b_sc per position; the
+ * shortcut reads the block's original input ("Sharding of WAN 2.2 VAE",
+ * Channel sharding and the op-sequence diagram; "Closing the gap", gap #6:
+ * the 1x1x1 conv is a matmul).  Conv B's accumulator, its bias and the
+ * shortcut are summed in fp32 and rounded once.
+ *   x : [d.n][d.t][d.h][d.w][in_dim];  y : [..][out_dim]; y must not overlap x.
+ *   workspace: device buffer of at least wanvae_resblock_workspace_size bytes.
+ * Four kernel launches on `stream`: norm1, conv A, norm2 (in place), conv B
+ * with the shortcut and residual add in its epilogue.
+ */
+WANVAE_API int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void *y,
+                            const wanvae_dims *d, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One streaming step over a chunk of d->t >= 1 frames with the feat_cache
+ * ("Sharding of WAN 2.2 VAE", Why depth sharding is not beneficial: one frame
+ * at a time with a cache of the last frames of every CausalConv3d's input;
+ * "Closing the gap", section 1: the per-frame decode loop carrying feat_cache).
+ *   cache_a : [d.n][2][d.h][d.w][in_dim]  conv A input frames -2, -1 (in/out)
+ *   cache_b : [d.n][2][d.h][d.w][out_dim] conv B input frames -2, -1 (in/out)
+ * Each conv reads its cache as the two frames before the chunk; afterwards
+ * the cache holds the last two frames of [cache, this chunk's conv input].
+ * A fresh stream starts from zero-filled caches (zero is the causal pad), so
+ * running a clip chunk by chunk gives the full-T result.  Caches must not
+ * overlap each other, x, y or the workspace.
+ */
+WANVAE_API int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_chunk,
+                                void *y_chunk, const wanvae_dims *d, void *cache_a, void *cache_b,
+                                void *workspace, size_t ws_bytes, void *stream);
+
+/* Text of this thread's most recent error (library-owned, valid until the
+ * thread's next call into the library).  "" when there was none. */
+WANVAE_API const char *wanvae_last_error(void);
+
+/*
+ * Per-kernel timing, for measurement.  While enabled, every kernel the
+ * library launches is bracketed by a pair of hipEvents recorded on the same
+ * stream.  wanvae_timing_read waits for the recorded events and returns, for
+ * one kernel kind, the number of launches and their summed duration in ms.
+ * Kinds: 0 = fused RMS_norm+SiLU, 1 = bf16 MFMA conv, 2 = fp32 conv,
+ * 3 = cache roll.  wanvae_timing_reset forgets all records.  Timing state is
+ * process-wide; enable it only while one thread drives the library.
+ */
+enum { WANVAE_KERNEL_NORM = 0, WANVAE_KERNEL_CONV_BF16 = 1, WANVAE_KERNEL_CONV_F32 = 2,
+       WANVAE_KERNEL_ROLL = 3, WANVAE_KERNEL_KINDS = 4 };
+WANVAE_API int wanvae_timing_enable(int on);
+WANVAE_API int wanvae_timing_reset(void);
+WANVAE_API int wanvae_timing_read(int32_t kind, int64_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WANVAE_H */

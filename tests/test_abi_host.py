@@ -1,0 +1,145 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+that include/wanvae.h declares, and rejects invalid arguments before it
+touches the GPU (argument validation runs on the host before any launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import causal_convolution_amd as wv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wanvae.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"WANVAE_API\s+[\w\s\*]+?\b(wanvae_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("wanvae_rmsnorm_silu", "wanvae_causal_conv3d", "wanvae_resblock_forward",
+              "wanvae_resblock_stream_step", "wanvae_resblock_workspace_size", "wanvae_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_function():
+    L = wv.lib()
+    for f in declared_functions():
+        assert hasattr(L, f), f
+    assert set(declared_functions()) == set(wv.EXPORTS)
+
+
+def _dims(n=1, t=2, h=3, w=4):
+    return wv.Dims(n, t, h, w)
+
+
+def test_norm_validation():
+    L = wv.lib()
+    p = C.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    assert L.wanvae_rmsnorm_silu(p, p, 10, 33, p, None, 1e-12, wv.BF16, None) == wv.ERR_SHAPE
+    assert "multiple of 32" in wv.last_error()
+    assert L.wanvae_rmsnorm_silu(p, p, 10, 2048, p, None, 1e-12, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_rmsnorm_silu(p, p, 10, 64, p, None, 1e-12, 9, None) == wv.ERR_DTYPE
+    assert L.wanvae_rmsnorm_silu(None, p, 10, 64, p, None, 1e-12, wv.BF16, None) == wv.ERR_NULL
+    assert L.wanvae_rmsnorm_silu(p, p, 10, 64, None, None, 1e-12, wv.BF16, None) == wv.ERR_NULL
+    assert L.wanvae_rmsnorm_silu(p, p, -1, 64, p, None, 1e-12, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_rmsnorm_silu(p, p, 10, 64, p, None, float("nan"), wv.BF16, None) == wv.ERR_SHAPE
+    # partial overlap is an alias error (y == x is allowed)
+    q = C.c_void_p((1 << 20) + 64)
+    assert L.wanvae_rmsnorm_silu(p, q, 10, 64, p, None, 1e-12, wv.BF16, None) == wv.ERR_ALIAS
+    # misaligned pointer
+    m = C.c_void_p((1 << 20) + 2)
+    assert L.wanvae_rmsnorm_silu(m, m, 10, 64, p, None, 1e-12, wv.BF16, None) == wv.ERR_SHAPE
+    # empty input: nothing to do, no pointer needed
+    assert L.wanvae_rmsnorm_silu(None, None, 0, 64, None, None, 1e-12, wv.BF16, None) == wv.OK
+    assert wv.last_error() == ""
+
+
+def test_conv_validation():
+    L = wv.lib()
+    p = C.c_void_p(1 << 24)
+    d = _dims()
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(d), 48, 64, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(d), 64, 2048, wv.F32, None) == wv.ERR_SHAPE
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, None, 64, 64, wv.BF16, None) == wv.ERR_NULL
+    assert L.wanvae_causal_conv3d(None, None, p, None, p, C.byref(d), 64, 64, wv.BF16, None) == wv.ERR_NULL
+    neg = _dims(1, -1, 3, 4)
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(neg), 64, 64, wv.BF16, None) == wv.ERR_SHAPE
+    huge = _dims(1 << 40, 1 << 40, 4, 4)
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(huge), 64, 64, wv.BF16, None) == wv.ERR_SHAPE
+    # y == x is not allowed for the conv
+    assert L.wanvae_causal_conv3d(p, None, C.c_void_p(1 << 30), None, p, C.byref(d), 64, 64, wv.BF16,
+                                  None) == wv.ERR_ALIAS
+    empty = _dims(1, 0, 3, 4)
+    assert L.wanvae_causal_conv3d(None, None, None, None, None, C.byref(empty), 64, 64, wv.BF16,
+                                  None) == wv.OK
+
+
+def _params(cin=384, cout=192, dtype=wv.BF16, shortcut=True):
+    a = 1 << 24
+    vals = [a + i * (1 << 20) for i in range(10)]
+    p = wv.ResblockParamsC(cin, cout, dtype, 1e-12, *vals)
+    if not shortcut:
+        p.w_sc = None
+        p.b_sc = None
+    return p
+
+
+def test_workspace_size():
+    L = wv.lib()
+    b = C.c_size_t(0)
+    d = wv.Dims(1, 41, 180, 320)
+    p = _params()
+    assert L.wanvae_resblock_workspace_size(C.byref(p), C.byref(d), C.byref(b)) == wv.OK
+    P = 41 * 180 * 320
+    assert b.value >= P * (384 + 192) * 2 and b.value < P * (384 + 192) * 2 + 1024
+    assert b.value % 256 == 0
+    # identity shortcut with in != out is rejected
+    p2 = _params(shortcut=False)
+    assert L.wanvae_resblock_workspace_size(C.byref(p2), C.byref(d), C.byref(b)) == wv.ERR_SHAPE
+    assert "identity" in wv.last_error()
+    p3 = _params(cin=100)
+    assert L.wanvae_resblock_workspace_size(C.byref(p3), C.byref(d), C.byref(b)) == wv.ERR_SHAPE
+    p4 = _params()
+    p4.gamma1 = None
+    assert L.wanvae_resblock_workspace_size(C.byref(p4), C.byref(d), C.byref(b)) == wv.ERR_NULL
+    assert L.wanvae_resblock_workspace_size(None, C.byref(d), C.byref(b)) == wv.ERR_NULL
+
+
+def test_forward_and_stream_validation():
+    L = wv.lib()
+    p = _params()
+    d = wv.Dims(1, 2, 8, 32)
+    x, y, ws = C.c_void_p(1 << 34), C.c_void_p(1 << 35), C.c_void_p(1 << 36)
+    need = C.c_size_t(0)
+    assert L.wanvae_resblock_workspace_size(C.byref(p), C.byref(d), C.byref(need)) == wv.OK
+    assert L.wanvae_resblock_forward(C.byref(p), x, y, C.byref(d), ws, need.value - 1,
+                                     None) == wv.ERR_WORKSPACE
+    assert L.wanvae_resblock_forward(C.byref(p), x, y, C.byref(d), None, need.value,
+                                     None) == wv.ERR_WORKSPACE
+    assert L.wanvae_resblock_forward(C.byref(p), x, x, C.byref(d), ws, need.value,
+                                     None) == wv.ERR_ALIAS
+    assert L.wanvae_resblock_forward(C.byref(p), x, y, C.byref(d), x, need.value,
+                                     None) == wv.ERR_ALIAS
+    assert L.wanvae_resblock_forward(C.byref(p), None, y, C.byref(d), ws, need.value,
+                                     None) == wv.ERR_NULL
+    ca, cb = C.c_void_p(1 << 37), C.c_void_p(1 << 38)
+    assert L.wanvae_resblock_stream_step(C.byref(p), x, y, C.byref(d), None, cb, ws, need.value,
+                                         None) == wv.ERR_NULL
+    assert L.wanvae_resblock_stream_step(C.byref(p), x, y, C.byref(d), ca, ca, ws, need.value,
+                                         None) == wv.ERR_ALIAS
+    assert L.wanvae_resblock_stream_step(C.byref(p), x, y, C.byref(d), ca, x, ws, need.value,
+                                         None) == wv.ERR_ALIAS
+    empty = wv.Dims(1, 0, 8, 32)
+    assert L.wanvae_resblock_forward(C.byref(p), None, None, C.byref(empty), None, 0, None) == wv.OK
+
+
+def test_timing_kind_validation():
+    L = wv.lib()
+    n, ms = C.c_int64(0), C.c_double(0)
+    assert L.wanvae_timing_read(99, C.byref(n), C.byref(ms)) == wv.ERR_SHAPE
+    assert L.wanvae_timing_read(0, None, C.byref(ms)) == wv.ERR_NULL

@@ -1,0 +1,264 @@
+"""GPU parity: every entry point of libwanvae.so against the CPU oracle.
+
+Inputs are seeded; bf16 tensors are compared on the exact bf16 values the
+device holds (widened to float32 for the oracle).  Bars (max|diff| /
+max|ref|): 1e-5 for fp32 paths, 2e-2 for bf16-in / fp32-accumulate paths.
+
+Small shapes are compared element by element over the whole output; they
+span several workgroup tiles (8 rows x 32 columns x up to 192 channels) and
+have ragged tails in H, W and the row count.  The five full-size workloads
+run in the launch configuration the benchmark times and are compared on
+sampled output boxes (corners, edge midpoints, first and last frames,
+random interior), each computed by the oracle from its receptive field.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from causal_convolution_amd import workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return gu.require_gpu()
+
+
+@pytest.fixture(scope="module")
+def wv(torch):
+    import causal_convolution_amd as m
+    return m
+
+
+def rnd(rng, shape, scale=1.0, dt=wl.F32):
+    a = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return wl.round_bf16(a) if dt == wl.BF16 else a
+
+
+def tol(dt):
+    return gu.TOL_BF16 if dt == wl.BF16 else gu.TOL_F32
+
+
+# --------------------------------------------------------------------------- norm
+@pytest.mark.parametrize("dt", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("C", [32, 64, 96, 192, 384, 1024])
+@pytest.mark.parametrize("rows", [1, 17, 70001])
+def test_rmsnorm_silu(torch, wv, dt, C, rows):
+    rng = np.random.default_rng(C * 1000 + rows)
+    x = rnd(rng, (rows, C), 2.0, dt)
+    g = rng.uniform(0.5, 1.5, C).astype(np.float32)
+    b = rnd(rng, (C,), 0.3)
+    ref = oracle.norm_silu(x, g, b)
+    xd = gu.to_dev(x, dt)
+    y = wv.rmsnorm_silu(xd, gu.to_dev(g, wl.F32), gu.to_dev(b, wl.F32))
+    err = gu.rel_err(gu.to_host(y), ref)
+    gu.report(f"norm {dt} C={C} rows={rows}", err, tol(dt))
+    assert err <= tol(dt)
+    # in place, and beta = NULL
+    ref0 = oracle.norm_silu(x, g, None)
+    wv.rmsnorm_silu(xd, gu.to_dev(g, wl.F32), None, out=xd)
+    assert gu.rel_err(gu.to_host(xd), ref0) <= tol(dt)
+
+
+def test_rmsnorm_silu_zero_rows_and_vectors(torch, wv):
+    C = 96
+    g = gu.to_dev(np.ones(C, np.float32), wl.F32)
+    b_h = np.linspace(-2, 2, C).astype(np.float32)
+    x = torch.zeros((5, C), dtype=torch.bfloat16, device="cuda")
+    y = wv.rmsnorm_silu(x, g, gu.to_dev(b_h, wl.F32))
+    ref = oracle.norm_silu(np.zeros((5, C), np.float32), np.ones(C, np.float32), b_h)
+    assert gu.rel_err(gu.to_host(y), ref) <= gu.TOL_BF16
+    e = torch.zeros((0, C), dtype=torch.bfloat16, device="cuda")
+    assert wv.rmsnorm_silu(e, g, None).shape == (0, C)
+
+
+# --------------------------------------------------------------------------- conv
+CONV_SHAPES = [
+    # N, T, H, W, Cin, Cout
+    (1, 3, 19, 70, 64, 96),      # ragged H (19 = 2*8+3) and W (70 = 2*32+6)
+    (2, 4, 9, 33, 96, 192),      # batch 2, W one past a tile
+    (1, 5, 8, 32, 384, 384),     # exact tiles, 2 channel blocks
+    (1, 3, 17, 40, 192, 128),
+    (1, 2, 5, 7, 32, 32),        # smaller than one tile
+    (1, 1, 1, 1, 32, 64),        # one position, one frame
+    (1, 4, 3, 35, 1024, 1024),   # widest channel count
+    (1, 3, 6, 36, 160, 224),     # channel counts with odd multiples of 32
+]
+
+
+@pytest.mark.parametrize("shape", CONV_SHAPES)
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_causal_conv3d_bf16(torch, wv, shape, with_cache):
+    N, T, H, W, Cin, Cout = shape
+    rng = np.random.default_rng(sum(shape) + with_cache)
+    x = rnd(rng, (N, T, H, W, Cin), 1.0, wl.BF16)
+    w = rnd(rng, (Cout, Cin, 3, 3, 3), 1 / math.sqrt(27 * Cin), wl.BF16)
+    b = rnd(rng, (Cout,), 0.1)
+    cache = rnd(rng, (N, 2, H, W, Cin), 1.0, wl.BF16) if with_cache else None
+    ref = oracle.causal_conv3d(x, w, b, cache)
+    y = wv.causal_conv3d(gu.to_dev(x, wl.BF16), gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.BF16),
+                         gu.to_dev(b, wl.F32),
+                         None if cache is None else gu.to_dev(cache, wl.BF16))
+    err = gu.rel_err(gu.to_host(y), ref)
+    gu.report(f"conv bf16 {shape} cache={with_cache}", err, gu.TOL_BF16, f"pcc={gu.pcc(gu.to_host(y), ref):.6f}")
+    assert err <= gu.TOL_BF16
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 16, 16, 64, 64), (2, 3, 5, 7, 3, 5), (1, 2, 9, 4, 33, 1)])
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_causal_conv3d_f32(torch, wv, shape, with_cache):
+    N, T, H, W, Cin, Cout = shape
+    rng = np.random.default_rng(sum(shape) + 7 * with_cache)
+    x = rnd(rng, (N, T, H, W, Cin))
+    w = rnd(rng, (Cout, Cin, 3, 3, 3), 1 / math.sqrt(27 * Cin))
+    b = rnd(rng, (Cout,), 0.1)
+    cache = rnd(rng, (N, 2, H, W, Cin)) if with_cache else None
+    ref = oracle.causal_conv3d(x, w, b, cache)
+    y = wv.causal_conv3d(gu.to_dev(x, wl.F32), gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.F32),
+                         gu.to_dev(b, wl.F32), None if cache is None else gu.to_dev(cache, wl.F32))
+    err = gu.rel_err(gu.to_host(y), ref)
+    gu.report(f"conv f32 {shape} cache={with_cache}", err, gu.TOL_F32)
+    assert err <= gu.TOL_F32
+
+
+def test_causal_conv3d_no_bias_and_empty(torch, wv):
+    rng = np.random.default_rng(3)
+    x = rnd(rng, (1, 2, 8, 32, 64), 1.0, wl.BF16)
+    w = rnd(rng, (32, 64, 3, 3, 3), 0.05, wl.BF16)
+    y = wv.causal_conv3d(gu.to_dev(x, wl.BF16), gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.BF16))
+    assert gu.rel_err(gu.to_host(y), oracle.causal_conv3d(x, w)) <= gu.TOL_BF16
+    e = torch.zeros((1, 0, 8, 32, 64), dtype=torch.bfloat16, device="cuda")
+    assert wv.causal_conv3d(e, gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.BF16)).shape == (1, 0, 8, 32, 32)
+
+
+# --------------------------------------------------------------------------- block, small
+SMALL_BLOCKS = [
+    wl.custom("id96", wl.BF16, 1, 4, 19, 70, 96, 96),
+    wl.custom("sc384_192", wl.BF16, 1, 3, 12, 40, 384, 192),
+    wl.custom("id192_b2", wl.BF16, 2, 3, 9, 33, 192, 192),
+    wl.custom("sc64_128", wl.BF16, 1, 5, 8, 64, 64, 128),
+    wl.custom("f32_sc", wl.F32, 1, 3, 6, 10, 64, 32),
+]
+
+
+def _block(wv, w, seed=0):
+    p = wl.make_params(w, seed)
+    return p, wv.ResBlock.from_host(p, gu.tdtype(w.dtype))
+
+
+def test_block_c1_full(torch, wv):
+    w = wl.WORKLOADS["c1"]
+    p, blk = _block(wv, w)
+    x = wl.make_x_host(w)
+    ref = oracle.resblock_full(gu.oracle_block(p), x)
+    y = blk.forward(gu.to_dev(x, w.dtype))
+    err = gu.rel_err(gu.to_host(y), ref)
+    gu.report("block c1 fp32 full", err, gu.TOL_F32)
+    assert err <= gu.TOL_F32
+
+
+@pytest.mark.parametrize("w", SMALL_BLOCKS, ids=lambda w: w.name)
+def test_block_small_full_and_stream(torch, wv, w):
+    p, blk = _block(wv, w, seed=5)
+    x = wl.make_x_host(w, seed=5)
+    ref = oracle.resblock_full(gu.oracle_block(p), x)
+    xd = gu.to_dev(x, w.dtype)
+    y = blk.forward(xd)
+    err = gu.rel_err(gu.to_host(y), ref)
+    gu.report(f"block {w.name} full", err, tol(w.dtype), f"pcc={gu.pcc(gu.to_host(y), ref):.6f}")
+    assert err <= tol(w.dtype)
+    for ts in (1, 2):
+        ca, cb = blk.new_caches(w.n, w.h, w.w)
+        ys = [blk.stream_step(xd[:, t0:t0 + ts].contiguous(), ca, cb) for t0 in range(0, w.t, ts)]
+        ys = torch.cat(ys, dim=1)
+        e2 = gu.rel_err(gu.to_host(ys), ref)
+        same = bool(torch.equal(ys, y))
+        gu.report(f"block {w.name} stream t_step={ts}", e2, tol(w.dtype), f"bitwise==full: {same}")
+        assert e2 <= tol(w.dtype)
+
+
+# --------------------------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_block_full_size_sampled(torch, wv, name):
+    w = wl.WORKLOADS[name]
+    print(f"[full-size] {name}: {w.desc}", flush=True)
+    p, blk = _block(wv, w)
+    x = wl.make_x_device(w)
+    y = blk.forward(x)
+    torch.cuda.synchronize()
+    boxes = gu.sample_boxes(w.t, w.h, w.w, n_random=8 if w.cin <= 192 else 4)
+    err, r = gu.window_compare(gu.oracle_block(p), x, y, boxes)
+    gu.report(f"block {name} full-size, {len(boxes)} boxes", err, tol(w.dtype), f"pcc={r:.6f}")
+    assert err <= tol(w.dtype)
+    del x, y, blk
+    torch.cuda.empty_cache()
+
+
+def test_c5_stream_equals_full_t(torch, wv):
+    w = wl.WORKLOADS["c5"]
+    p, blk = _block(wv, w)
+    x = wl.make_x_device(w)
+    y = blk.forward(x)
+    ca, cb = blk.new_caches(w.n, w.h, w.w)
+    ws = blk.workspace(w.n, 1, w.h, w.w)
+    ys = torch.empty_like(y)
+    for t in range(w.t):
+        blk.stream_step(x[:, t:t + 1], ca, cb, out=ys[:, t:t + 1], workspace=ws)
+    torch.cuda.synchronize()
+    diff = (ys.float() - y.float()).abs().max().item()
+    scale = y.float().abs().max().item()
+    same = bool(torch.equal(ys, y))
+    gu.report("c5 stream (41 x T=1) vs full-T", diff / scale, gu.TOL_BF16, f"bitwise: {same}")
+    assert diff / scale <= gu.TOL_BF16
+    # and the streamed output against the oracle on sampled boxes
+    boxes = gu.sample_boxes(w.t, w.h, w.w, n_random=2)
+    err, _ = gu.window_compare(gu.oracle_block(p), x, ys, boxes)
+    assert err <= gu.TOL_BF16
+    del x, y, ys
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- robustness
+def test_deterministic_and_workspace_independent(torch, wv):
+    w = wl.custom("det", wl.BF16, 1, 5, 20, 64, 192, 96)
+    p, blk = _block(wv, w, seed=9)
+    xd = gu.to_dev(wl.make_x_host(w, seed=9), w.dtype)
+    ws = blk.workspace(w.n, w.t, w.h, w.w)
+    y1 = blk.forward(xd, workspace=ws)
+    ws.view(torch.int16).fill_(-1)          # 0xffff bf16 = NaN everywhere
+    y2 = blk.forward(xd, workspace=ws)
+    assert torch.equal(y1, y2)
+
+
+def test_output_guard_bands(torch, wv):
+    w = wl.custom("guard", wl.BF16, 1, 3, 10, 40, 96, 96)
+    p, blk = _block(wv, w, seed=11)
+    xd = gu.to_dev(wl.make_x_host(w, seed=11), w.dtype)
+    n = w.positions * w.cout
+    g = 4096
+    buf = torch.full((n + 2 * g,), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = buf[g:g + n].view(w.n, w.t, w.h, w.w, w.cout)
+    blk.forward(xd, out=y)
+    torch.cuda.synchronize()
+    assert bool((buf[:g] == 7.0).all()) and bool((buf[g + n:] == 7.0).all())
+    assert torch.equal(y, blk.forward(xd))
+
+
+def test_timing_counts_launches(torch, wv):
+    w = wl.custom("timing", wl.BF16, 1, 2, 8, 32, 96, 96)
+    p, blk = _block(wv, w)
+    xd = gu.to_dev(wl.make_x_host(w), w.dtype)
+    wv.timing_reset()
+    wv.timing_enable(True)
+    blk.forward(xd)
+    blk.forward(xd)
+    wv.timing_enable(False)
+    n_norm, ms_norm = wv.timing_read(wv.KERNEL_NORM)
+    n_conv, ms_conv = wv.timing_read(wv.KERNEL_CONV_BF16)
+    wv.timing_reset()
+    assert n_norm == 4 and n_conv == 4
+    assert ms_norm > 0 and ms_conv > 0
