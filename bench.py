@@ -74,7 +74,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--cpu-frames", type=int, default=1,
+    ap.add_argument("--cpu-frames", type=int, default=4,
                     help="frames of the clip the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

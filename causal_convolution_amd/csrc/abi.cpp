@@ -137,6 +137,16 @@ int run_conv(const wanvae::ConvLaunch &c, int32_t dt, hipStream_t s) {
                         [&] { return wanvae::launch_conv3d_f32(c, s); });
 }
 
+// The bf16 conv addresses one frame slab (h*w*C elements) with 32-bit byte
+// offsets: a slab must stay below 2 GiB.
+int check_conv_slab(const wanvae_dims *d, int32_t c, int32_t dt) {
+    if (dt != WANVAE_BF16) return WANVAE_OK;
+    WV_CHECK((double)d->h * (double)d->w * c * 2.0 < 2147483648.0, WANVAE_ERR_SHAPE,
+             "a frame of h*w*C = %lld*%lld*%d bf16 values exceeds 2 GiB", (long long)d->h,
+             (long long)d->w, c);
+    return WANVAE_OK;
+}
+
 int check_conv_channels(int32_t cin, int32_t cout, int32_t dt) {
     if (dt == WANVAE_BF16) {
         WV_CHECK(wanvae::conv3d_bf16_supported(cin, cout), WANVAE_ERR_SHAPE,
@@ -180,6 +190,8 @@ struct Plan {
 int plan_block(const wanvae_resblock_params *p, const wanvae_dims *d, Plan *pl) {
     if (int r = check_params(p)) return r;
     if (int r = positions(d, &pl->P)) return r;
+    if (int r = check_conv_slab(d, p->in_dim > p->out_dim ? p->in_dim : p->out_dim, p->dtype))
+        return r;
     const size_t es = esize(p->dtype);
     pl->x_bytes = (size_t)pl->P * p->in_dim * es;
     pl->y_bytes = (size_t)pl->P * p->out_dim * es;
@@ -239,6 +251,7 @@ int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const 
     int64_t P = 0;
     if (int r = positions(d, &P)) return r;
     if (int r = check_conv_channels(cin, cout, dtype)) return r;
+    if (int r = check_conv_slab(d, cin > cout ? cin : cout, dtype)) return r;
     if (P == 0) return WANVAE_OK;
     WV_CHECK(x && w && y, WANVAE_ERR_NULL, "x, w and y are required");
     WV_CHECK(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(cache) && aligned16(bias),

@@ -22,13 +22,15 @@
 //   A tile (LDS): HB rows x 34 columns (32 + the 1-pixel W halo) x 32 channels
 //                 of input frame t+kt-2, rows shifted by kh-1; pad positions are
 //                 written as zeros, so the padding costs no branches in the MFMA
-//                 loop and the 3 kw taps reuse the same tile.
+//                 loop and the 3 kw taps reuse the same tile.  Tiles are fetched
+//                 with raw buffer loads over one frame slab: a pad position gets an
+//                 out-of-range offset and the hardware returns zeros for it.
 //   B tile (LDS): NB channels x 3 taps (kw) x 32 channels of the weights.
 // Stages are double-buffered through registers: the global loads of stage
 // s+1 are issued before the MFMAs of stage s and written to the other LDS
 // buffer after them, one barrier per stage.  LDS rows are padded from 64 to
-// 80 bytes so the 16-byte per-lane operand reads of 8 (or 16) consecutive
-// lanes fall in distinct banks.
+// 80 bytes so the 16-byte per-lane operand reads and writes of 8 (or 16)
+// consecutive lanes, which touch consecutive rows, fall in distinct banks.
 //
 // Causal pad: for a frame t < 2 without a cache, the stages whose source
 // frame is before 0 would only add exact zeros and are skipped (uniform per
@@ -42,9 +44,11 @@
 // x at the output positions and its B tile the shortcut weight.
 //
 // Workgroup order: tiles are numbered output-channel-block slowest, then
-// (batch, frame), then row block, then column block, and the dispatch index is
+// batch, row block, column block, and frame fastest, and the dispatch index is
 // remapped so that each of the 8 XCDs walks a contiguous range of tiles: the
-// XCD's L2 then serves one weight slice and neighbouring input rows.
+// workgroups resident on one XCD then share one weight slice and the input
+// frames t-2..t of one spatial block through that XCD's L2.
+#include "bf16.h"
 #include "internal.h"
 
 namespace wanvae {
@@ -52,6 +56,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource word 3 for raw (unformatted, stride 0) buffers on gfx9-family
+// GPUs; loads past num_records return zero.
+constexpr int kBufFlags = 0x00020000;
 
 constexpr int kKC = 32;           // input channels per stage
 constexpr int kPS = kKC + 8;      // LDS position stride in bf16 elements (80 bytes)
@@ -75,12 +84,7 @@ struct Args {
     int tiles_w, tiles_h;
 };
 
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-    __bf16 b = static_cast<__bf16>(f);  // round to nearest even
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
-}
 
-__device__ inline float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 template <int WM, int WN, int FM, int FN>
 struct Tile {
@@ -90,10 +94,10 @@ struct Tile {
     static constexpr int A_POS = HB * kAW;                  // positions in the A tile
     static constexpr int A_ELEMS = A_POS * kPS;             // bf16 elements per A buffer
     static constexpr int B_ELEMS = 3 * NB * kPS;            // bf16 elements per B buffer
-    static constexpr int A_CHUNKS = A_POS * (kKC / 8);      // 16-byte chunks per stage
-    static constexpr int B_CHUNKS = 3 * NB * (kKC / 8);
-    static constexpr int A_PER_T = (A_CHUNKS + kThreads - 1) / kThreads;
-    static constexpr int B_PER_T = (B_CHUNKS + kThreads - 1) / kThreads;
+    static constexpr int UPR = kThreads / 4;                // units loaded per round
+    static constexpr int A_PER_T = (A_POS + UPR - 1) / UPR;  // load rounds per stage
+    static constexpr int B_PER_T = (3 * NB + UPR - 1) / UPR;
+    static_assert(kThreads % 32 == 0, "chunk mapping needs whole 32-lane groups");
     static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * 2;
     static_assert(LDS_BYTES <= 160 * 1024, "tile does not fit the 160 KB LDS");
 };
@@ -121,33 +125,75 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     const int64_t xcd = bid % kXCD, loc = bid / kXCD;
     int64_t tile = xcd < rmd ? xcd * (q + 1) + loc : rmd * (q + 1) + (xcd - rmd) * q + loc;
 
+    // frame fastest: consecutive tiles are the same spatial block in consecutive
+    // frames, so the input frames t-2..t of neighbouring workgroups overlap in L2
+    const int64_t tq = tile % a.T;
+    tile /= a.T;
     const int wt = (int)(tile % a.tiles_w);
     tile /= a.tiles_w;
     const int ht = (int)(tile % a.tiles_h);
     tile /= a.tiles_h;
-    const int64_t nt_idx = tile % (a.N * a.T);
-    const int ntile = (int)(tile / (a.N * a.T));
-    const int64_t tq = nt_idx % a.T;
-    const int64_t nq = nt_idx / a.T;
+    const int64_t nq = tile % a.N;
+    const int ntile = (int)(tile / a.N);
     const int h0 = ht * HB;
     const int w0 = wt * kWB;
     const int n0 = ntile * NB;
     const int H = (int)a.H, W = (int)a.W;
+    const int64_t HW = (int64_t)H * W;
 
     // ---- stage list: conv stages (kt from kt_begin, kh, channel slice), then shortcut stages
     const int ck = a.cin / kKC;
     const int kt_begin = (a.cache != nullptr || tq >= 2) ? 0 : (int)(2 - tq);
     const int s_conv = (3 - kt_begin) * 3 * ck;
     const int s_total = s_conv + (EPI == EPI_SHORTCUT ? a.cres / kKC : 0);
-    const int64_t HW = (int64_t)H * W;
 
-    uint4 ra[TL::A_PER_T];
-    uint4 rb[TL::B_PER_T];
+    // ---- per-thread load descriptors, fixed for the whole K loop.
+    // A tile unit = one position (r, c) of the HB x 34 halo tile; B tile unit =
+    // one (kw tap, output channel) row.  Each unit holds 4 sixteen-byte quarters
+    // of the 32-channel slice.  Chunk j = tid + i * NT maps to unit
+    // 8 * (j >> 5) + (j & 7) and quarter (j >> 3) & 3: the 8 lanes of each LDS
+    // access group write 8 different units with the same quarter, which the
+    // 80-byte unit stride spreads over distinct banks, and one wavefront
+    // instruction still covers 16 whole units (64 contiguous bytes each) in HBM.
+    const int qd = (tid >> 3) & 3;
+    const int u0 = 8 * (tid >> 5) + (tid & 7);
+    constexpr int UPR = NT / 4;  // units advanced per round
+    int a_pix[TL::A_PER_T];      // input pixel index (h0 + r) * W + (w0 + c - 1)
+    int a_row[TL::A_PER_T];      // input row h0 + r, or a large negative value if unused
+#pragma unroll
+    for (int i = 0; i < TL::A_PER_T; ++i) {
+        const int u = u0 + i * UPR;
+        const int r = u / kAW, c = u % kAW;
+        const int ww = w0 + c - 1;
+        const bool ok = u < TL::A_POS && ww >= 0 && ww < W;
+        a_pix[i] = (h0 + r) * W + ww;
+        a_row[i] = ok ? h0 + r : -(1 << 29);
+    }
+    constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer: the load returns zeros
+    const uint32_t wrow2 = (uint32_t)(27 * a.cin * 2), tap2 = (uint32_t)(a.cin * 2);
+    uint32_t b_off[TL::B_PER_T];   // weight byte offset of the unit (stage part excluded)
+    uint32_t b_sc[EPI == EPI_SHORTCUT ? TL::B_PER_T : 1];
+#pragma unroll
+    for (int i = 0; i < TL::B_PER_T; ++i) {
+        const int u = u0 + i * UPR;
+        const int tap = u / NB, nl = u % NB;
+        b_off[i] = u < 3 * NB ? (uint32_t)(n0 + nl) * wrow2 + (uint32_t)tap * tap2 + qd * 16 : kOOB;
+        if constexpr (EPI == EPI_SHORTCUT)
+            b_sc[i] = u < NB ? (uint32_t)((n0 + nl) * a.cres * 2 + qd * 16) : kOOB;
+    }
+    const int lds_a0 = u0 * kPS + qd * 8;
+    const int lds_b0 = u0 * kPS + qd * 8;
 
+    u32x4 ra[TL::A_PER_T];
+    u32x4 rb[TL::B_PER_T];
+
+    // Buffer loads: a pad position (outside H or W) or an unused chunk gets an
+    // out-of-range offset, for which the hardware returns zeros, so the loads
+    // are branch-free.
     auto load_stage = [&](int s) {
         const uint16_t *abase;
-        int cstride, dh, ntaps, wrow, tapstride;
-        const uint16_t *wbase;
+        uint32_t aslab, cs2;
+        int dh;
         if (s < s_conv) {
             const int kt = kt_begin + s / (3 * ck);
             const int kh = (s / ck) % 3;
@@ -156,67 +202,51 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
             abase = ts >= 0 ? a.x + ((nq * a.T + ts) * HW) * a.cin
                             : a.cache + ((nq * 2 + (ts + 2)) * HW) * a.cin;
             abase += cc * kKC;
-            cstride = a.cin;
+            aslab = (uint32_t)(HW * a.cin * 2 - cc * kKC * 2);
+            cs2 = (uint32_t)a.cin * 2;
             dh = kh - 1;
-            ntaps = 3;
-            wrow = 27 * a.cin;
-            tapstride = a.cin;
-            wbase = a.w + ((int64_t)n0 * 27 + kt * 9 + kh * 3) * a.cin + cc * kKC;
+            const uint32_t woff = (uint32_t)(((kt * 9 + kh * 3) * a.cin + cc * kKC) * 2);
+            const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)a.w, (short)0, (int)((int64_t)a.cout * 27 * a.cin * 2), kBufFlags);
+#pragma unroll
+            for (int i = 0; i < TL::B_PER_T; ++i)
+                rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[i] + woff, 0, 0);
         } else {
             const int cc = s - s_conv;
             abase = a.res + ((nq * a.T + tq) * HW) * a.cres + cc * kKC;
-            cstride = a.cres;
+            aslab = (uint32_t)(HW * a.cres * 2 - cc * kKC * 2);
+            cs2 = (uint32_t)a.cres * 2;
             dh = 0;
-            ntaps = 1;
-            wrow = a.cres;
-            tapstride = 0;
-            wbase = a.wsc + (int64_t)n0 * a.cres + cc * kKC;
+            if constexpr (EPI == EPI_SHORTCUT) {
+                const uint32_t woff = (uint32_t)(cc * kKC * 2);
+                const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)a.wsc, (short)0, (int)((int64_t)a.cout * a.cres * 2), kBufFlags);
+#pragma unroll
+                for (int i = 0; i < TL::B_PER_T; ++i)
+                    rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, b_sc[i] + woff, 0, 0);
+            }
         }
+        const __amdgpu_buffer_rsrc_t ar =
+            __builtin_amdgcn_make_buffer_rsrc((void *)abase, (short)0, (int)aslab, kBufFlags);
+        const int dpix = dh * W;
 #pragma unroll
         for (int i = 0; i < TL::A_PER_T; ++i) {
-            const int idx = tid + i * NT;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (idx < TL::A_CHUNKS) {
-                const int pos = idx >> 2, qd = idx & 3;
-                const int r = pos / kAW, c = pos % kAW;
-                const int hh = h0 + r + dh, ww = w0 + c - 1;
-                if (hh >= 0 && hh < H && ww >= 0 && ww < W)
-                    v = *reinterpret_cast<const uint4 *>(abase + ((int64_t)hh * W + ww) * cstride +
-                                                         qd * 8);
-            }
-            ra[i] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < TL::B_PER_T; ++i) {
-            const int idx = tid + i * NT;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (idx < ntaps * NB * 4) {
-                const int tap = idx / (NB * 4), rem = idx % (NB * 4);
-                const int nl = rem >> 2, qd = rem & 3;
-                v = *reinterpret_cast<const uint4 *>(wbase + (int64_t)nl * wrow + tap * tapstride +
-                                                     qd * 8);
-            }
-            rb[i] = v;
+            const int hh = a_row[i] + dh;
+            const bool ok = hh >= 0 && hh < H;
+            const uint32_t off = ok ? (uint32_t)(a_pix[i] + dpix) * cs2 + qd * 16 : kOOB;
+            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
         }
     };
 
     auto store_stage = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < TL::A_PER_T; ++i) {
-            const int idx = tid + i * NT;
-            if (idx < TL::A_CHUNKS) {
-                const int pos = idx >> 2, qd = idx & 3;
-                *reinterpret_cast<uint4 *>(&smA[buf][pos * kPS + qd * 8]) = ra[i];
-            }
-        }
+        for (int i = 0; i < TL::A_PER_T; ++i)
+            if ((i + 1) * UPR <= TL::A_POS || u0 + i * UPR < TL::A_POS)
+                *reinterpret_cast<u32x4 *>(&smA[buf][lds_a0 + i * UPR * kPS]) = ra[i];
 #pragma unroll
-        for (int i = 0; i < TL::B_PER_T; ++i) {
-            const int idx = tid + i * NT;
-            if (idx < TL::B_CHUNKS) {
-                const int tn = idx >> 2, qd = idx & 3;  // tn = tap * NB + nl
-                *reinterpret_cast<uint4 *>(&smB[buf][tn * kPS + qd * 8]) = rb[i];
-            }
-        }
+        for (int i = 0; i < TL::B_PER_T; ++i)
+            if ((i + 1) * UPR <= 3 * NB || u0 + i * UPR < 3 * NB)
+                *reinterpret_cast<u32x4 *>(&smB[buf][lds_b0 + i * UPR * kPS]) = rb[i];
     };
 
     floatx16 acc[FM][FN];
@@ -230,34 +260,44 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     const int l32 = lane & 31;
     const int lhi = lane >> 5;
 
-    auto compute = [&](int buf, int ntaps) {
-        for (int kw = 0; kw < ntaps; ++kw) {
-            const int coloff = ntaps == 1 ? 1 : kw;
+    // One stage of MFMAs: NTAPS kw taps x 2 sixteen-channel k-steps.  The
+    // operand fragments of the next k-step are read from LDS while the MFMAs of
+    // the current one run.
+    auto compute = [&]<int NTAPS>(int buf) {
+        constexpr int NSTEP = NTAPS * (kKC / 16);
+        bf16x8 fx[2][FM], fw[2][FN];
+        auto ldfrag = [&](int step, int slot) {
+            const int kw = step / (kKC / 16), ks = step % (kKC / 16);
+            const int coloff = NTAPS == 1 ? 1 : kw;
+            const int qd = ks * 2 + lhi;
 #pragma unroll
-            for (int ks = 0; ks < kKC / 16; ++ks) {
-                const int qd = ks * 2 + lhi;
-                bf16x8 bx[FM], bw[FN];
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    const int row = wm * FM + fm;
-                    const uint4 v = *reinterpret_cast<const uint4 *>(
-                        &smA[buf][(row * kAW + l32 + coloff) * kPS + qd * 8]);
-                    bx[fm] = __builtin_bit_cast(bf16x8, v);
-                }
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    const int nl = wn * FN * 32 + fn * 32 + l32;
-                    const uint4 v =
-                        *reinterpret_cast<const uint4 *>(&smB[buf][(kw * NB + nl) * kPS + qd * 8]);
-                    bw[fn] = __builtin_bit_cast(bf16x8, v);
-                }
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[fn], bx[fm],
-                                                                              acc[fm][fn], 0, 0, 0);
+            for (int fm = 0; fm < FM; ++fm) {
+                const int row = wm * FM + fm;
+                fx[slot][fm] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(
+                                &smA[buf][(row * kAW + l32 + coloff) * kPS + qd * 8]));
             }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int nl = wn * FN * 32 + fn * 32 + l32;
+                fw[slot][fn] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(&smB[buf][(kw * NB + nl) * kPS + qd * 8]));
+            }
+        };
+        ldfrag(0, 0);
+#pragma unroll
+        for (int step = 0; step < NSTEP; ++step) {
+            // the reads of step + 1 are issued before, and complete under, the
+            // MFMAs of this step (sched_barrier keeps the compiler from sinking them)
+            if (step + 1 < NSTEP) ldfrag(step + 1, (step + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        fw[step & 1][fn], fx[step & 1][fm], acc[fm][fn], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -267,10 +307,14 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     for (int s = 0; s < s_total; ++s) {
         const bool more = s + 1 < s_total;
         if (more) load_stage(s + 1);
-        if (s < s_conv)
-            compute(s & 1, 3);
-        else
-            compute(s & 1, 1);
+        if constexpr (EPI == EPI_SHORTCUT) {
+            if (s < s_conv)
+                compute.template operator()<3>(s & 1);
+            else
+                compute.template operator()<1>(s & 1);
+        } else {
+            compute.template operator()<3>(s & 1);
+        }
         if (more) store_stage((s + 1) & 1);
         __syncthreads();
     }
@@ -316,7 +360,7 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     }
 }
 
-template <int WM, int WN, int FM, int FN>
+template <int WM, int WN, int FM, int FN, int EPI>
 hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     using TL = Tile<WM, WN, FM, FN>;
     Args a;
@@ -340,14 +384,15 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     const int64_t tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (c.cout / TL::NB);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)tiles), block(TL::kThreads);
-    if (!c.res)
-        conv3d_bf16_kernel<WM, WN, FM, FN, EPI_BIAS><<<grid, block, 0, s>>>(a);
-    else if (!c.wsc)
-        conv3d_bf16_kernel<WM, WN, FM, FN, EPI_IDENTITY><<<grid, block, 0, s>>>(a);
-    else
-        conv3d_bf16_kernel<WM, WN, FM, FN, EPI_SHORTCUT><<<grid, block, 0, s>>>(a);
+    conv3d_bf16_kernel<WM, WN, FM, FN, EPI><<<dim3((unsigned)tiles), dim3(TL::kThreads), 0, s>>>(a);
     return hipGetLastError();
+}
+
+// bias-only or identity-residual epilogue, chosen at run time
+template <int WM, int WN, int FM, int FN>
+hipError_t launch_plain(const ConvLaunch &c, hipStream_t s) {
+    return c.res ? launch_cfg<WM, WN, FM, FN, EPI_IDENTITY>(c, s)
+                 : launch_cfg<WM, WN, FM, FN, EPI_BIAS>(c, s);
 }
 
 }  // namespace
@@ -357,14 +402,21 @@ bool conv3d_bf16_supported(int cin, int cout) {
            cout % 32 == 0;
 }
 
-// Tile choice per output-channel count: the widest channel block that divides
-// C_out, 8 output rows x 32 columns per workgroup.
+// Tile choice, measured on MI355X over the decoder's channel counts (latent
+// 384, mid 192, output 96): 8-wave workgroups (2 waves per SIMD) beat 4-wave
+// ones at every shape.  The fused 1x1x1 shortcut variant keeps 4-wave tiles,
+// whose register budget holds its second operand stream without spilling.
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
-    if (c.cout % 192 == 0) return launch_cfg<2, 2, 4, 3>(c, s);   // NB = 192, 4 waves
-    if (c.cout % 128 == 0) return launch_cfg<2, 2, 4, 2>(c, s);   // NB = 128, 4 waves
-    if (c.cout % 96 == 0) return launch_cfg<4, 1, 2, 3>(c, s);    // NB = 96, 4 waves
-    if (c.cout % 64 == 0) return launch_cfg<4, 1, 2, 2>(c, s);    // NB = 64
-    return launch_cfg<4, 1, 2, 1>(c, s);                          // NB = 32
+    if (c.res != nullptr && c.wsc != nullptr) {
+        if (c.cout % 96 == 0) return launch_cfg<4, 1, 2, 3, EPI_SHORTCUT>(c, s);  // 8 rows x 96 ch
+        if (c.cout % 64 == 0) return launch_cfg<4, 1, 2, 2, EPI_SHORTCUT>(c, s);  // 8 rows x 64 ch
+        return launch_cfg<4, 1, 2, 1, EPI_SHORTCUT>(c, s);                        // 8 rows x 32 ch
+    }
+    if (c.cout % 128 == 0) return launch_plain<4, 2, 4, 2>(c, s);   // 16 rows x 128 ch
+    if (c.cout % 192 == 0) return launch_plain<4, 2, 2, 3>(c, s);   // 8 rows x 192 ch
+    if (c.cout % 96 == 0) return launch_plain<8, 1, 2, 3>(c, s);    // 16 rows x 96 ch
+    if (c.cout % 64 == 0) return launch_plain<4, 1, 2, 2>(c, s);    // 8 rows x 64 ch
+    return launch_plain<4, 1, 2, 1>(c, s);                          // 8 rows x 32 ch
 }
 
 }  // namespace wanvae

@@ -15,6 +15,7 @@
 // loop; each lane keeps U rows in flight to cover HBM latency.  y may equal x
 // (in place): each element is read and then written by the same lane.  x is read once
 // and y written once: 2 * rows * C * sizeof(T) bytes of HBM traffic.
+#include "bf16.h"
 #include "internal.h"
 
 namespace wanvae {
@@ -24,12 +25,7 @@ constexpr int kLanesPerRow = 16;
 constexpr int kThreads = 256;
 constexpr int kRowsPerPass = kThreads / kLanesPerRow;  // 16 rows per block per pass
 
-__device__ inline float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-    __bf16 b = static_cast<__bf16>(f);  // round to nearest even
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
-}
 
 // Load NDW dwords from a pointer aligned to VW dwords.
 template <int NDW, int VW>
@@ -96,6 +92,16 @@ template <int E> struct Row<uint16_t, E> {  // bf16 bits
     }
 };
 
+// E consecutive fp32 values (16-byte aligned when E is a multiple of 4, 8-byte when even).
+template <int E>
+__device__ inline void load_params(const float *__restrict__ p, float (&v)[E]) {
+    constexpr int VW = E % 4 == 0 ? 4 : (E % 2 == 0 ? 2 : 1);
+    uint32_t d[E];
+    load_dwords<E, VW>(reinterpret_cast<const uint32_t *>(p), d);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = __uint_as_float(d[e]);
+}
+
 __device__ inline float silu(float u) {
     // u / (1 + exp(-u)); exp(-u) = inf for very negative u gives -0
     return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
@@ -114,11 +120,16 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
     const int lane = threadIdx.x % kLanesPerRow;
     const int slot = threadIdx.x / kLanesPerRow;
 
+    // gamma * sqrt(C) and beta for this lane's E channels, loaded once
     float g[E], b[E];
+    load_params<E>(gamma + lane * E, g);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        g[e] = gamma[lane * E + e] * sqrt_c;
-        b[e] = beta ? beta[lane * E + e] : 0.0f;
+    for (int e = 0; e < E; ++e) g[e] *= sqrt_c;
+    if (beta) {
+        load_params<E>(beta + lane * E, b);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) b[e] = 0.0f;
     }
 
     const uint32_t *xs = reinterpret_cast<const uint32_t *>(x);
@@ -163,10 +174,14 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
 template <typename T, int E>
 hipError_t launch_e(const void *x, void *y, int64_t rows, int C, const float *gamma,
                     const float *beta, float eps, hipStream_t s) {
-    constexpr int U = E <= 8 ? 4 : (E <= 16 ? 2 : 1);
+    // rows in flight per lane: at least ~96 bytes of loads outstanding per lane
+    constexpr int ROW_BYTES = E * (int)sizeof(T);
+    constexpr int U = ROW_BYTES >= 96 ? 1 : (96 + ROW_BYTES - 1) / ROW_BYTES > 8 ? 8
+                                                 : (96 + ROW_BYTES - 1) / ROW_BYTES;
     const int64_t per_block = (int64_t)kRowsPerPass * U;
     int64_t blocks = (rows + per_block - 1) / per_block;
-    if (blocks > 8192) blocks = 8192;
+    // a resident grid (8 blocks of 256 threads per CU on 256 CUs) that strides over the rows
+    if (blocks > 2048) blocks = 2048;
     if (blocks < 1) blocks = 1;
     rmsnorm_silu_kernel<T, E, U><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
         static_cast<const T *>(x), static_cast<T *>(y), rows, gamma, beta, eps,
