@@ -11,43 +11,60 @@
 // GEMM view: M = output channels (MFMA A operand = weights), N = output
 // positions (MFMA B operand = input), K = 27 taps x C_in (+ C_res for the
 // fused 1x1x1 shortcut).  Both operands are K-contiguous in HBM (weights
-// [co][tap][ci], activations [pos][ci]), which is exactly the per-lane layout
-// the MFMA wants, so no operand is transposed anywhere.
+// [co][tap][ci], activations [pos][ci]), which is the per-lane operand layout
+// of the MFMA, so nothing is transposed.
 //
-// Tiling (one workgroup): one frame t, HB output rows x 32 output columns, NB
-// output channels.  Waves are arranged WM (rows) x WN (channels); each wave
-// holds FM x FN 32x32 accumulator tiles.
+// Workgroup tile: one frame t, HB = WM*FM output rows x 32 output columns x
+// NB = WN*FN*32 output channels; wave (wm, wn) owns FM rows x FN channel blocks
+// (FM*FN 32x32 fp32 accumulators).
 //
-// K loop in stages.  One stage = (kt, kh, 32-channel slice):
-//   A tile (LDS): HB rows x 34 columns (32 + the 1-pixel W halo) x 32 channels
-//                 of input frame t+kt-2, rows shifted by kh-1; pad positions are
-//                 written as zeros, so the padding costs no branches in the MFMA
-//                 loop and the 3 kw taps reuse the same tile.  Tiles are fetched
-//                 with raw buffer loads over one frame slab: a pad position gets an
-//                 out-of-range offset and the hardware returns zeros for it.
-//   B tile (LDS): NB channels x 3 taps (kw) x 32 channels of the weights.
-// Stages are double-buffered through registers: the global loads of stage
-// s+1 are issued before the MFMAs of stage s and written to the other LDS
-// buffer after them, one barrier per stage.  LDS rows are padded from 64 to
-// 80 bytes so the 16-byte per-lane operand reads and writes of 8 (or 16)
-// consecutive lanes, which touch consecutive rows, fall in distinct banks.
+// K loop in stages of (kt, 16 input channels):
+//   A tile (LDS): HB+2 input rows (the H halo) x 34 columns (the W halo) x 16
+//     channels of frame t+kt-2.  Every (kh, kw) tap of the stage reads it.
+//   B tile (LDS): the 9 (kh, kw) taps x NB channels x 16 input channels.
+// A wave walks its FM+2 input rows once per stage ("row-stationary"): for each
+// row it reads the three kw-shifted operand fragments from LDS and feeds them
+// to every (kh, output row) pair that uses that input row, with all 9*FN weight
+// fragments held in registers for the stage.  Per MFMA that is about
+// (3(FM+2) + 9 FN) / (9 FM FN) KB of LDS reads, against one fragment pair per
+// MFMA when every tap re-reads its operands.
 //
-// Causal pad: for a frame t < 2 without a cache, the stages whose source
-// frame is before 0 would only add exact zeros and are skipped (uniform per
-// workgroup).  With a cache they read the cached frames instead.
+// Loads go straight from L2 to LDS (buffer_load ... lds): each wavefront
+// instruction fills one 1 KB block of the stage buffer, lane l writing bytes
+// 16l..16l+15, so no VGPRs stage the data and no LDS-write instructions run.
+// They are raw buffer loads over one frame slab: an input position outside
+// the image gets an out-of-range offset and the hardware writes zeros, so
+// padding costs no branch.  Because the tile already holds the H and W halo,
+// every per-lane load offset is fixed for the whole K loop; a stage only moves
+// the buffer base (frame and channel slice).  Stages rotate through a ring of
+// NBUF LDS buffers: stage s+NBUF-1 is requested while stage s computes, its
+// load instructions interleaved with stage s's MFMA groups (issuing them in a
+// burst stalls the wave on the LDS-DMA queue while the MFMA pipe runs dry),
+// and a stage waits once (vmcnt) and meets one barrier before its MFMAs.
+//
+// LDS layout: 32-byte units (16 bf16 channels of one position or one weight
+// row), the two 16-byte halves swapped when bit 3 of the unit index is set.
+// 16 lanes reading one half of 16 consecutive units then hit 16 distinct
+// 16-byte bank groups (gfx950 serves 16 lanes x 16 bytes per LDS cycle).  A
+// tile rows are padded to 40 units so a lane's swizzle bit for (row, kw) is a
+// compile-time function of the row parity.
+//
+// Causal pad: without a cache, the stages of a frame before 0 only add exact
+// zeros and are skipped (uniform per workgroup); with a cache they read it.
 //
 // Epilogue: each lane owns one output position and 4 consecutive output
 // channels per accumulator quad; bias, then the identity residual or the
-// 1x1x1 shortcut bias, are added in fp32 and the result is rounded once to
-// bf16 and written as 8-byte stores.  The 1x1x1 shortcut GEMM itself runs as
-// extra K stages (C_res / 32 of them) of the same accumulators: its A tile is
-// x at the output positions and its B tile the shortcut weight.
+// shortcut bias, are added in fp32 and the result is rounded once to bf16
+// (8-byte stores).  The 1x1x1 shortcut GEMM runs as C_res/16 extra stages of
+// the same accumulators: A tile = x at the output positions, B tile = w_sc.
 //
 // Workgroup order: tiles are numbered output-channel-block slowest, then
 // batch, row block, column block, and frame fastest, and the dispatch index is
 // remapped so that each of the 8 XCDs walks a contiguous range of tiles: the
 // workgroups resident on one XCD then share one weight slice and the input
 // frames t-2..t of one spatial block through that XCD's L2.
+#include <utility>
+
 #include "bf16.h"
 #include "internal.h"
 
@@ -61,12 +78,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Buffer resource word 3 for raw (unformatted, stride 0) buffers on gfx9-family
 // GPUs; loads past num_records return zero.
 constexpr int kBufFlags = 0x00020000;
+constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer: the load returns zeros
 
-constexpr int kKC = 32;           // input channels per stage
-constexpr int kPS = kKC + 8;      // LDS position stride in bf16 elements (80 bytes)
-constexpr int kWB = 32;           // output columns per tile (one MFMA N block)
-constexpr int kAW = kWB + 2;      // A tile columns including the W halo
-constexpr int kXCD = 8;           // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kKC = 16;          // input channels per stage = one MFMA k-step
+constexpr int kUnit = 32;        // bytes per LDS unit (16 bf16)
+constexpr int kWB = 32;          // output columns per tile (one MFMA N block)
+constexpr int kAW = kWB + 2;     // A tile columns including the W halo
+constexpr int kAS = 40;          // A tile row stride in units (34 used)
+constexpr int kXCD = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 enum Epilogue { EPI_BIAS = 0, EPI_IDENTITY = 1, EPI_SHORTCUT = 2 };
 
@@ -84,23 +103,52 @@ struct Args {
     int tiles_w, tiles_h;
 };
 
-
-
 template <int WM, int WN, int FM, int FN>
 struct Tile {
     static constexpr int kThreads = WM * WN * 64;
-    static constexpr int HB = WM * FM;                      // output rows
-    static constexpr int NB = WN * FN * 32;                 // output channels
-    static constexpr int A_POS = HB * kAW;                  // positions in the A tile
-    static constexpr int A_ELEMS = A_POS * kPS;             // bf16 elements per A buffer
-    static constexpr int B_ELEMS = 3 * NB * kPS;            // bf16 elements per B buffer
-    static constexpr int UPR = kThreads / 4;                // units loaded per round
-    static constexpr int A_PER_T = (A_POS + UPR - 1) / UPR;  // load rounds per stage
-    static constexpr int B_PER_T = (3 * NB + UPR - 1) / UPR;
-    static_assert(kThreads % 32 == 0, "chunk mapping needs whole 32-lane groups");
-    static constexpr int LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * 2;
-    static_assert(LDS_BYTES <= 160 * 1024, "tile does not fit the 160 KB LDS");
+    static constexpr int NWAVE = WM * WN;
+    static constexpr int HB = WM * FM;                       // output rows
+    static constexpr int NB = WN * FN * 32;                  // output channels
+    static constexpr int AR = HB + 2;                        // A tile rows (H halo)
+    static constexpr int A_BLOCKS = (AR * kAS + 31) / 32;    // 1 KB blocks = 32 units
+    static constexpr int B_BLOCKS = 9 * NB / 32;
+    static constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;       // load instructions per stage
+    static constexpr int LPW = (BLOCKS + NWAVE - 1) / NWAVE; // per wave (at most)
+    static constexpr int LMIN = BLOCKS / NWAVE;              // per wave (at least)
+    static constexpr int STAGE_BYTES = BLOCKS * 1024;
+    static constexpr int NBUF = 3 * STAGE_BYTES <= 160 * 1024 ? 3 : 2;  // LDS ring depth
+    static_assert(NBUF * STAGE_BYTES <= 160 * 1024, "tile does not fit the 160 KB LDS");
+    static_assert(LMIN < 64, "vmcnt holds at most 63 outstanding loads");
 };
+
+// byte offset of half `h` (0/1) of LDS unit `u`
+__device__ __host__ constexpr int lds_off(int u, int h) { return u * kUnit + ((h ^ ((u >> 3) & 1)) << 4); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (stride 0, num_records bytes) for a wave-uniform base.
+__device__ inline i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)), (int)bytes, kBufFlags};
+}
+
+// One wavefront-wide 16-byte-per-lane load from a buffer straight into LDS:
+// lane l's 16 bytes at byte offset voff land at LDS byte address
+// lds_addr + 16 * l (lds_addr wave-uniform).  Written as inline assembly so the
+// compiler does not wait for these loads before unrelated LDS reads; the
+// kernel orders them itself with explicit vmcnt waits and barriers.  M0 is set
+// inside the same statement, immediately before its only use.
+__device__ inline void lds_dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+__device__ inline uint32_t lds_address(const unsigned char *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
 
 template <int WM, int WN, int FM, int FN, int EPI>
 __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
@@ -109,12 +157,15 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     constexpr int HB = TL::HB;
     constexpr int NB = TL::NB;
 
-    __shared__ __attribute__((aligned(16))) uint16_t smA[2][TL::A_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t smB[2][TL::B_ELEMS];
+    // the ring's buffers are separate LDS objects, so a buffer being filled by
+    // DMA is never confused with the one being read
+    __shared__ __attribute__((aligned(1024))) unsigned char sm0[TL::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sm1[TL::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sm2[TL::NBUF == 3 ? TL::STAGE_BYTES : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
 
@@ -141,112 +192,86 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     const int H = (int)a.H, W = (int)a.W;
     const int64_t HW = (int64_t)H * W;
 
-    // ---- stage list: conv stages (kt from kt_begin, kh, channel slice), then shortcut stages
+    // ---- stage list: conv stages (kt from kt_begin, channel slice), then shortcut stages
     const int ck = a.cin / kKC;
     const int kt_begin = (a.cache != nullptr || tq >= 2) ? 0 : (int)(2 - tq);
-    const int s_conv = (3 - kt_begin) * 3 * ck;
+    const int s_conv = (3 - kt_begin) * ck;
     const int s_total = s_conv + (EPI == EPI_SHORTCUT ? a.cres / kKC : 0);
 
-    // ---- per-thread load descriptors, fixed for the whole K loop.
-    // A tile unit = one position (r, c) of the HB x 34 halo tile; B tile unit =
-    // one (kw tap, output channel) row.  Each unit holds 4 sixteen-byte quarters
-    // of the 32-channel slice.  Chunk j = tid + i * NT maps to unit
-    // 8 * (j >> 5) + (j & 7) and quarter (j >> 3) & 3: the 8 lanes of each LDS
-    // access group write 8 different units with the same quarter, which the
-    // 80-byte unit stride spreads over distinct banks, and one wavefront
-    // instruction still covers 16 whole units (64 contiguous bytes each) in HBM.
-    const int qd = (tid >> 3) & 3;
-    const int u0 = 8 * (tid >> 5) + (tid & 7);
-    constexpr int UPR = NT / 4;  // units advanced per round
-    int a_pix[TL::A_PER_T];      // input pixel index (h0 + r) * W + (w0 + c - 1)
-    int a_row[TL::A_PER_T];      // input row h0 + r, or a large negative value if unused
-#pragma unroll
-    for (int i = 0; i < TL::A_PER_T; ++i) {
-        const int u = u0 + i * UPR;
-        const int r = u / kAW, c = u % kAW;
-        const int ww = w0 + c - 1;
-        const bool ok = u < TL::A_POS && ww >= 0 && ww < W;
-        a_pix[i] = (h0 + r) * W + ww;
-        a_row[i] = ok ? h0 + r : -(1 << 29);
-    }
-    constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer: the load returns zeros
+    // ---- per-lane load offsets, fixed for the whole K loop.  Load k of this
+    // wave fills stage block b = wave + k * NWAVE; lane l writes half
+    // (l & 1) ^ swizzle(u) of unit u = 32 * b' + l / 2 (b' relative to the A or
+    // B region), so the lane fetches that half of that unit.
+    const uint32_t cs2 = (uint32_t)a.cin * 2;
     const uint32_t wrow2 = (uint32_t)(27 * a.cin * 2), tap2 = (uint32_t)(a.cin * 2);
-    uint32_t b_off[TL::B_PER_T];   // weight byte offset of the unit (stage part excluded)
-    uint32_t b_sc[EPI == EPI_SHORTCUT ? TL::B_PER_T : 1];
+    uint32_t l_off[TL::LPW];                                  // conv stages
+    uint32_t l_sc[EPI == EPI_SHORTCUT ? TL::LPW : 1];         // shortcut stages
 #pragma unroll
-    for (int i = 0; i < TL::B_PER_T; ++i) {
-        const int u = u0 + i * UPR;
-        const int tap = u / NB, nl = u % NB;
-        b_off[i] = u < 3 * NB ? (uint32_t)(n0 + nl) * wrow2 + (uint32_t)tap * tap2 + qd * 16 : kOOB;
-        if constexpr (EPI == EPI_SHORTCUT)
-            b_sc[i] = u < NB ? (uint32_t)((n0 + nl) * a.cres * 2 + qd * 16) : kOOB;
+    for (int k = 0; k < TL::LPW; ++k) {
+        const int b = wave + k * TL::NWAVE;
+        uint32_t off = kOOB, osc = kOOB;
+        if (b < TL::A_BLOCKS) {
+            const int u = b * 32 + (lane >> 1);
+            const int hf = (lane & 1) ^ ((u >> 3) & 1);
+            const int r = u / kAS, c = u % kAS;
+            const int hh = h0 - 1 + r, ww = w0 - 1 + c;
+            const bool inside = r < TL::AR && c < kAW && hh >= 0 && hh < H && ww >= 0 && ww < W;
+            if (inside) off = (uint32_t)(hh * W + ww) * cs2 + hf * 16;
+            if (EPI == EPI_SHORTCUT && inside && r >= 1 && r <= HB && c >= 1 && c <= kWB)
+                osc = (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + hf * 16;
+        } else if (b < TL::BLOCKS) {
+            const int u = (b - TL::A_BLOCKS) * 32 + (lane >> 1);
+            const int hf = (lane & 1) ^ ((u >> 3) & 1);
+            const int tap = u / NB, nl = u % NB;
+            off = (uint32_t)(n0 + nl) * wrow2 + (uint32_t)tap * tap2 + hf * 16;
+            if (EPI == EPI_SHORTCUT && tap == 0) osc = (uint32_t)((n0 + nl) * a.cres * 2) + hf * 16;
+        }
+        l_off[k] = off;
+        if constexpr (EPI == EPI_SHORTCUT) l_sc[k] = osc;
     }
-    const int lds_a0 = u0 * kPS + qd * 8;
-    const int lds_b0 = u0 * kPS + qd * 8;
 
-    u32x4 ra[TL::A_PER_T];
-    u32x4 rb[TL::B_PER_T];
-
-    // Buffer loads: a pad position (outside H or W) or an unused chunk gets an
-    // out-of-range offset, for which the hardware returns zeros, so the loads
-    // are branch-free.
-    auto load_stage = [&](int s) {
-        const uint16_t *abase;
-        uint32_t aslab, cs2;
-        int dh;
-        if (s < s_conv) {
-            const int kt = kt_begin + s / (3 * ck);
-            const int kh = (s / ck) % 3;
+    // A stage request: the two buffer resources and the LDS base of its buffer.
+    struct Req {
+        i32x4 ar, br;
+        uint32_t base;
+        bool sc, live;
+    };
+    auto make_req = [&](int s, unsigned char *dst) {
+        Req r;
+        r.live = s < s_total;
+        r.sc = s >= s_conv;
+        r.base = lds_address(dst);
+        if (!r.sc) {
+            const int kt = kt_begin + s / ck;
             const int cc = s % ck;
             const int64_t ts = tq + kt - 2;
-            abase = ts >= 0 ? a.x + ((nq * a.T + ts) * HW) * a.cin
-                            : a.cache + ((nq * 2 + (ts + 2)) * HW) * a.cin;
-            abase += cc * kKC;
-            aslab = (uint32_t)(HW * a.cin * 2 - cc * kKC * 2);
-            cs2 = (uint32_t)a.cin * 2;
-            dh = kh - 1;
-            const uint32_t woff = (uint32_t)(((kt * 9 + kh * 3) * a.cin + cc * kKC) * 2);
-            const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)a.w, (short)0, (int)((int64_t)a.cout * 27 * a.cin * 2), kBufFlags);
-#pragma unroll
-            for (int i = 0; i < TL::B_PER_T; ++i)
-                rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[i] + woff, 0, 0);
+            const uint16_t *abase = (ts >= 0 ? a.x + ((nq * a.T + ts) * HW) * a.cin
+                                             : a.cache + ((nq * 2 + (ts + 2)) * HW) * a.cin) +
+                                    cc * kKC;
+            r.ar = buffer_rsrc(abase, (uint32_t)(HW * a.cin * 2 - cc * kKC * 2));
+            const int wskip = (kt * 9) * a.cin + cc * kKC;   // elements before this stage's slice
+            r.br = buffer_rsrc(a.w + wskip, (uint32_t)((int64_t)a.cout * 27 * a.cin * 2 - wskip * 2));
         } else {
             const int cc = s - s_conv;
-            abase = a.res + ((nq * a.T + tq) * HW) * a.cres + cc * kKC;
-            aslab = (uint32_t)(HW * a.cres * 2 - cc * kKC * 2);
-            cs2 = (uint32_t)a.cres * 2;
-            dh = 0;
-            if constexpr (EPI == EPI_SHORTCUT) {
-                const uint32_t woff = (uint32_t)(cc * kKC * 2);
-                const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)a.wsc, (short)0, (int)((int64_t)a.cout * a.cres * 2), kBufFlags);
+            r.ar = buffer_rsrc(a.res + ((nq * a.T + tq) * HW) * a.cres + cc * kKC,
+                               (uint32_t)(HW * a.cres * 2 - cc * kKC * 2));
+            r.br = buffer_rsrc(a.wsc + cc * kKC, (uint32_t)((int64_t)a.cout * a.cres * 2 - cc * kKC * 2));
+        }
+        return r;
+    };
+    // Issue this wave's loads k in [K0, K1) of request r (asynchronous; completion via vmcnt).
+    auto issue_part = [&]<int K0, int K1>(const Req &r) {
+        if (!r.live) return;
 #pragma unroll
-                for (int i = 0; i < TL::B_PER_T; ++i)
-                    rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, b_sc[i] + woff, 0, 0);
+        for (int k = K0; k < K1; ++k) {
+            const int b = wave + k * TL::NWAVE;
+            if (b < TL::BLOCKS) {
+                uint32_t off = l_off[k];
+                if constexpr (EPI == EPI_SHORTCUT)
+                    if (r.sc) off = l_sc[k];
+                lds_dma16(b < TL::A_BLOCKS ? r.ar : r.br, r.base + b * 1024, off);
             }
         }
-        const __amdgpu_buffer_rsrc_t ar =
-            __builtin_amdgcn_make_buffer_rsrc((void *)abase, (short)0, (int)aslab, kBufFlags);
-        const int dpix = dh * W;
-#pragma unroll
-        for (int i = 0; i < TL::A_PER_T; ++i) {
-            const int hh = a_row[i] + dh;
-            const bool ok = hh >= 0 && hh < H;
-            const uint32_t off = ok ? (uint32_t)(a_pix[i] + dpix) * cs2 + qd * 16 : kOOB;
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
-        }
-    };
-
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < TL::A_PER_T; ++i)
-            if ((i + 1) * UPR <= TL::A_POS || u0 + i * UPR < TL::A_POS)
-                *reinterpret_cast<u32x4 *>(&smA[buf][lds_a0 + i * UPR * kPS]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < TL::B_PER_T; ++i)
-            if ((i + 1) * UPR <= 3 * NB || u0 + i * UPR < 3 * NB)
-                *reinterpret_cast<u32x4 *>(&smB[buf][lds_b0 + i * UPR * kPS]) = rb[i];
     };
 
     floatx16 acc[FM][FN];
@@ -258,68 +283,146 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int l32 = lane & 31;
-    const int lhi = lane >> 5;
+    const int g = lane >> 5;   // k-group: which 8-channel half of the 16-channel unit
+    // B fragment (tap, fn): unit tap*NB + wn*FN*32 + fn*32 + l32; NB and 32 are
+    // multiples of 16, so its swizzle bit is bit 3 of l32
+    const int b_rd0 = lds_off(wn * FN * 32 + l32, g);
+    // A fragment (row wm*FM + qr, column l32 + kw): the swizzle bit is bit 3 of
+    // (row * 40 + l32 + kw) = parity(row) ^ bit 3 of (l32 + kw); a_rd[par] serves
+    // the rows qr with qr & 1 == par, whose parity is par ^ parity(wm * FM)
+    int a_rd[2][3];
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int u = l32 + kw;
+            const int row_par = par ^ ((wm * FM) & 1);
+            a_rd[par][kw] = (wm * FM) * kAS * kUnit + u * kUnit + ((g ^ ((u >> 3) & 1) ^ row_par) << 4);
+        }
 
-    // One stage of MFMAs: NTAPS kw taps x 2 sixteen-channel k-steps.  The
-    // operand fragments of the next k-step are read from LDS while the MFMAs of
-    // the current one run.
-    auto compute = [&]<int NTAPS>(int buf) {
-        constexpr int NSTEP = NTAPS * (kKC / 16);
-        bf16x8 fx[2][FM], fw[2][FN];
-        auto ldfrag = [&](int step, int slot) {
-            const int kw = step / (kKC / 16), ks = step % (kKC / 16);
-            const int coloff = NTAPS == 1 ? 1 : kw;
-            const int qd = ks * 2 + lhi;
+    auto ldA = [&](const unsigned char *buf, int qr, int kw) {
+        const int off = a_rd[qr & 1][kw] + qr * kAS * kUnit;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
+    };
+    auto ldB = [&](const unsigned char *buf, int tap, int fn) {
+        const int off = TL::A_BLOCKS * 1024 + b_rd0 + (tap * NB + fn * 32) * kUnit;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
+    };
+
+    // The LPW loads of a stage request are spread over the FM+2 row groups of
+    // a conv stage (a burst of LDS-DMA issues would stall the wave and leave
+    // the MFMA pipe idle): row group qr issues loads [DMA_LO(qr), DMA_LO(qr+1)).
+    constexpr int NROW = FM + 2;
+#define WANVAE_DMA_LO(qr) (((qr) * TL::LPW) / NROW)
+
+    // One conv stage: 9 taps x FM rows x FN channel blocks of MFMAs, with the
+    // loads of request `next` issued in between.
+    auto compute_conv = [&](const unsigned char *buf, const Req &next) {
+        // LDS reads complete in order, so they are issued in the order of first
+        // use: input row 0 and the kh = 0 weights, then the kh = 1 weights and
+        // row 1 (used from row group 1 on), then the kh = 2 weights (row group 2).
+        bf16x8 fw[9][FN];
+        bf16x8 fx[2][3];
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int row = wm * FM + fm;
-                fx[slot][fm] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(
-                                &smA[buf][(row * kAW + l32 + coloff) * kPS + qd * 8]));
-            }
+        for (int kw = 0; kw < 3; ++kw) fx[0][kw] = ldA(buf, 0, kw);
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int nl = wn * FN * 32 + fn * 32 + l32;
-                fw[slot][fn] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(&smB[buf][(kw * NB + nl) * kPS + qd * 8]));
-            }
-        };
-        ldfrag(0, 0);
+        for (int tap = 0; tap < 3; ++tap)
 #pragma unroll
-        for (int step = 0; step < NSTEP; ++step) {
-            // the reads of step + 1 are issued before, and complete under, the
-            // MFMAs of this step (sched_barrier keeps the compiler from sinking them)
-            if (step + 1 < NSTEP) ldfrag(step + 1, (step + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = ldB(buf, tap, fn);
+        [&]<int... QR>(std::integer_sequence<int, QR...>) {
+            (
+                [&] {
+                    constexpr int qr = QR;
+                    // weights of tap row kh = qr + 1 are first needed by row group qr + 1
+                    if constexpr (qr + 1 < 3) {
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+                        for (int tap = 3 * (qr + 1); tap < 3 * (qr + 2); ++tap)
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        fw[step & 1][fn], fx[step & 1][fm], acc[fm][fn], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                            for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = ldB(buf, tap, fn);
+                    }
+                    // input row qr feeds output rows fm = qr - kh; the next row is read meanwhile
+                    if constexpr (qr + 1 < NROW) {
+#pragma unroll
+                        for (int kw = 0; kw < 3; ++kw) fx[(qr + 1) & 1][kw] = ldA(buf, qr + 1, kw);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                        for (int kh = 0; kh < 3; ++kh) {
+                            const int fm = qr - kh;
+                            if (fm < 0 || fm >= FM) continue;
+#pragma unroll
+                            for (int fn = 0; fn < FN; ++fn)
+                                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    fw[kh * 3 + kw][fn], fx[qr & 1][kw], acc[fm][fn], 0, 0, 0);
+                        }
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_part.template operator()<WANVAE_DMA_LO(qr), WANVAE_DMA_LO(qr + 1)>(next);
+                    __builtin_amdgcn_sched_barrier(0);
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, NROW>{});
+    };
+
+    // One shortcut stage: the centre position of each output row, w_sc as the only tap.
+    auto compute_shortcut = [&](const unsigned char *buf, const Req &next) {
+        issue_part.template operator()<0, TL::LPW>(next);
+        bf16x8 fw[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) fw[fn] = ldB(buf, 0, fn);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const bf16x8 fx = ldA(buf, fm + 1, 1);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fn], fx, acc[fm][fn], 0, 0, 0);
         }
     };
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int s = 0; s < s_total; ++s) {
-        const bool more = s + 1 < s_total;
-        if (more) load_stage(s + 1);
-        if constexpr (EPI == EPI_SHORTCUT) {
-            if (s < s_conv)
-                compute.template operator()<3>(s & 1);
-            else
-                compute.template operator()<1>(s & 1);
-        } else {
-            compute.template operator()<3>(s & 1);
+    // ---- K loop over the LDS ring: stages 0..NBUF-2 are in flight before the
+    // first MFMA; stage s waits for its own loads (leaving the next stage's
+    // outstanding), meets the barrier that also frees buffer (s-1) % NBUF, then
+    // requests stage s+NBUF-1 into that buffer and runs its MFMAs.
+    constexpr int NBUF = TL::NBUF;
+    unsigned char *ring[3] = {sm0, sm1, NBUF == 3 ? sm2 : sm0};
+    // s_waitcnt immediates for "vmcnt <= LMIN" and "vmcnt = 0", other counters
+    // left alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+    constexpr int kWaitOne = (TL::LMIN & 15) | ((TL::LMIN >> 4) << 14) | (7 << 4) | (15 << 8);
+    constexpr int kWaitAll = (7 << 4) | (15 << 8);
+#pragma unroll
+    for (int p = 0; p < NBUF - 1; ++p) issue_part.template operator()<0, TL::LPW>(make_req(p, ring[p]));
+    for (int s0 = 0; s0 < s_total; s0 += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+            const int s = s0 + j;
+            if (s < s_total) {
+                if (NBUF == 3 && s + 1 < s_total)
+                    __builtin_amdgcn_s_waitcnt(kWaitOne);
+                else
+                    __builtin_amdgcn_s_waitcnt(kWaitAll);
+                // A plain barrier, not __syncthreads(): its release fence would wait
+                // for every outstanding load, including the prefetched next stage.
+                // This wave's stage-s data has landed (vmcnt above), and every LDS
+                // read of the buffer refilled below was consumed by an MFMA of the
+                // previous stage, i.e. completed (lgkmcnt), before this point.
+                __builtin_amdgcn_s_barrier();
+                // stage s + NBUF - 1 refills buffer (s - 1) % NBUF, freed by the barrier
+                const Req next = make_req(s + NBUF - 1, ring[(j + NBUF - 1) % NBUF]);
+                if constexpr (EPI == EPI_SHORTCUT) {
+                    if (s < s_conv)
+                        compute_conv(ring[j], next);
+                    else
+                        compute_shortcut(ring[j], next);
+                } else {
+                    compute_conv(ring[j], next);
+                }
+            }
         }
-        if (more) store_stage((s + 1) & 1);
-        __syncthreads();
     }
+#undef WANVAE_DMA_LO
 
-    // ---- epilogue: lane owns position (row, w0 + l32) and channels 8g + 4*lhi + [0,4)
+    // ---- epilogue: lane owns position (row, w0 + l32) and channels 8j + 4g + [0,4)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int hh = h0 + wm * FM + fm;
@@ -329,11 +432,11 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int co = n0 + wn * FN * 32 + fn * 32 + 8 * g + 4 * lhi;
+            for (int j = 0; j < 4; ++j) {
+                const int co = n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * g + e];
+                for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * j + e];
                 if (a.bias) {
                     const float4 bv = *reinterpret_cast<const float4 *>(a.bias + co);
                     v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
@@ -402,21 +505,19 @@ bool conv3d_bf16_supported(int cin, int cout) {
            cout % 32 == 0;
 }
 
-// Tile choice, measured on MI355X over the decoder's channel counts (latent
-// 384, mid 192, output 96): 8-wave workgroups (2 waves per SIMD) beat 4-wave
-// ones at every shape.  The fused 1x1x1 shortcut variant keeps 4-wave tiles,
-// whose register budget holds its second operand stream without spilling.
+// Tile choice per output-channel count: 4 waves (one per SIMD) with the
+// accumulators in AGPRs, 16 output rows x 32 columns per workgroup, and the
+// widest channel block (96, 64 or 32) that divides C_out and compiles without
+// register spills; the fused-shortcut variant holds a second set of load
+// offsets and uses at most 64 channels.
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
     if (c.res != nullptr && c.wsc != nullptr) {
-        if (c.cout % 96 == 0) return launch_cfg<4, 1, 2, 3, EPI_SHORTCUT>(c, s);  // 8 rows x 96 ch
-        if (c.cout % 64 == 0) return launch_cfg<4, 1, 2, 2, EPI_SHORTCUT>(c, s);  // 8 rows x 64 ch
-        return launch_cfg<4, 1, 2, 1, EPI_SHORTCUT>(c, s);                        // 8 rows x 32 ch
+        if (c.cout % 64 == 0) return launch_cfg<4, 1, 4, 2, EPI_SHORTCUT>(c, s);
+        return launch_cfg<4, 1, 4, 1, EPI_SHORTCUT>(c, s);
     }
-    if (c.cout % 128 == 0) return launch_plain<4, 2, 4, 2>(c, s);   // 16 rows x 128 ch
-    if (c.cout % 192 == 0) return launch_plain<4, 2, 2, 3>(c, s);   // 8 rows x 192 ch
-    if (c.cout % 96 == 0) return launch_plain<8, 1, 2, 3>(c, s);    // 16 rows x 96 ch
-    if (c.cout % 64 == 0) return launch_plain<4, 1, 2, 2>(c, s);    // 8 rows x 64 ch
-    return launch_plain<4, 1, 2, 1>(c, s);                          // 8 rows x 32 ch
+    if (c.cout % 96 == 0) return launch_plain<4, 1, 4, 3>(c, s);    // 16 rows x 96 ch
+    if (c.cout % 64 == 0) return launch_plain<4, 1, 4, 2>(c, s);    // 16 rows x 64 ch
+    return launch_plain<4, 1, 4, 1>(c, s);                          // 16 rows x 32 ch
 }
 
 }  // namespace wanvae
