@@ -29,18 +29,19 @@
 // (3(FM+2) + 9 FN) / (9 FM FN) KB of LDS reads, against one fragment pair per
 // MFMA when every tap re-reads its operands.
 //
-// Loads go straight from L2 to LDS (buffer_load ... lds): each wavefront
-// instruction fills one 1 KB block of the stage buffer, lane l writing bytes
-// 16l..16l+15, so no VGPRs stage the data and no LDS-write instructions run.
+// A workgroup has WM*WN MFMA waves and one load wave.  The load wave moves
+// every byte of the tile from L2 straight to LDS (buffer_load ... lds): each of
+// its instructions fills one 1 KB block of a stage buffer, lane l writing
+// bytes 16l..16l+15, so no VGPRs stage the data and no LDS-write instructions
+// run.  Issuing these loads stalls the issuing wave on the LDS-DMA queue; with
+// a wave of its own for them, the MFMA waves never wait on the memory pipe.
 // They are raw buffer loads over one frame slab: an input position outside
 // the image gets an out-of-range offset and the hardware writes zeros, so
 // padding costs no branch.  Because the tile already holds the H and W halo,
 // every per-lane load offset is fixed for the whole K loop; a stage only moves
 // the buffer base (frame and channel slice).  Stages rotate through a ring of
-// NBUF LDS buffers: stage s+NBUF-1 is requested while stage s computes, its
-// load instructions interleaved with stage s's MFMA groups (issuing them in a
-// burst stalls the wave on the LDS-DMA queue while the MFMA pipe runs dry),
-// and a stage waits once (vmcnt) and meets one barrier before its MFMAs.
+// NBUF LDS buffers: stage s+NBUF-1 is requested while stage s computes; per
+// stage the load wave waits once (vmcnt) and all waves meet one barrier.
 //
 // LDS layout: 32-byte units (16 bf16 channels of one position or one weight
 // row), the two 16-byte halves swapped when bit 3 of the unit index is set.
@@ -63,8 +64,6 @@
 // remapped so that each of the 8 XCDs walks a contiguous range of tiles: the
 // workgroups resident on one XCD then share one weight slice and the input
 // frames t-2..t of one spatial block through that XCD's L2.
-#include <utility>
-
 #include "bf16.h"
 #include "internal.h"
 
@@ -105,20 +104,18 @@ struct Args {
 
 template <int WM, int WN, int FM, int FN>
 struct Tile {
-    static constexpr int kThreads = WM * WN * 64;
-    static constexpr int NWAVE = WM * WN;
+    static constexpr int NWAVE = WM * WN;                    // MFMA waves
+    static constexpr int kThreads = (NWAVE + 1) * 64;        // + one load wave
     static constexpr int HB = WM * FM;                       // output rows
     static constexpr int NB = WN * FN * 32;                  // output channels
     static constexpr int AR = HB + 2;                        // A tile rows (H halo)
     static constexpr int A_BLOCKS = (AR * kAS + 31) / 32;    // 1 KB blocks = 32 units
     static constexpr int B_BLOCKS = 9 * NB / 32;
     static constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;       // load instructions per stage
-    static constexpr int LPW = (BLOCKS + NWAVE - 1) / NWAVE; // per wave (at most)
-    static constexpr int LMIN = BLOCKS / NWAVE;              // per wave (at least)
     static constexpr int STAGE_BYTES = BLOCKS * 1024;
     static constexpr int NBUF = 3 * STAGE_BYTES <= 160 * 1024 ? 3 : 2;  // LDS ring depth
     static_assert(NBUF * STAGE_BYTES <= 160 * 1024, "tile does not fit the 160 KB LDS");
-    static_assert(LMIN < 64, "vmcnt holds at most 63 outstanding loads");
+    static_assert(BLOCKS < 64, "vmcnt holds at most 63 outstanding loads");
 };
 
 // byte offset of half `h` (0/1) of LDS unit `u`
@@ -151,21 +148,17 @@ __device__ inline uint32_t lds_address(const unsigned char *p) {
 }
 
 template <int WM, int WN, int FM, int FN, int EPI>
-__global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
+__global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) {
     using TL = Tile<WM, WN, FM, FN>;
     constexpr int NT = TL::kThreads;
     constexpr int HB = TL::HB;
     constexpr int NB = TL::NB;
 
-    // the ring's buffers are separate LDS objects, so a buffer being filled by
-    // DMA is never confused with the one being read
-    __shared__ __attribute__((aligned(1024))) unsigned char sm0[TL::STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sm1[TL::STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sm2[TL::NBUF == 3 ? TL::STAGE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[TL::NBUF * TL::STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // NWAVE = the load wave
     const int wm = wave % WM;
     const int wn = wave / WM;
 
@@ -198,82 +191,95 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     const int s_conv = (3 - kt_begin) * ck;
     const int s_total = s_conv + (EPI == EPI_SHORTCUT ? a.cres / kKC : 0);
 
-    // ---- per-lane load offsets, fixed for the whole K loop.  Load k of this
-    // wave fills stage block b = wave + k * NWAVE; lane l writes half
-    // (l & 1) ^ swizzle(u) of unit u = 32 * b' + l / 2 (b' relative to the A or
-    // B region), so the lane fetches that half of that unit.
-    const uint32_t cs2 = (uint32_t)a.cin * 2;
-    const uint32_t wrow2 = (uint32_t)(27 * a.cin * 2), tap2 = (uint32_t)(a.cin * 2);
-    uint32_t l_off[TL::LPW];                                  // conv stages
-    uint32_t l_sc[EPI == EPI_SHORTCUT ? TL::LPW : 1];         // shortcut stages
-#pragma unroll
-    for (int k = 0; k < TL::LPW; ++k) {
-        const int b = wave + k * TL::NWAVE;
-        uint32_t off = kOOB, osc = kOOB;
-        if (b < TL::A_BLOCKS) {
-            const int u = b * 32 + (lane >> 1);
-            const int hf = (lane & 1) ^ ((u >> 3) & 1);
-            const int r = u / kAS, c = u % kAS;
-            const int hh = h0 - 1 + r, ww = w0 - 1 + c;
-            const bool inside = r < TL::AR && c < kAW && hh >= 0 && hh < H && ww >= 0 && ww < W;
-            if (inside) off = (uint32_t)(hh * W + ww) * cs2 + hf * 16;
-            if (EPI == EPI_SHORTCUT && inside && r >= 1 && r <= HB && c >= 1 && c <= kWB)
-                osc = (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + hf * 16;
-        } else if (b < TL::BLOCKS) {
+    constexpr int NBUF = TL::NBUF;
+    const uint32_t smem_base = lds_address(smem);
+
+    if (wave == TL::NWAVE) {
+        // ================= load wave: all global -> LDS traffic of the tile
+        // Block b of a stage: lane l writes half (l & 1) ^ swizzle(u) of unit
+        // u = 32 * b' + l / 2 (b' relative to the A or B region), so the lane
+        // fetches that half of that unit.  Offsets are fixed for the K loop; a
+        // stage only moves the buffer base (frame and channel slice).
+        const uint32_t cs2 = (uint32_t)a.cin * 2;
+        const uint32_t wrow2 = (uint32_t)(27 * a.cin * 2), tap2 = (uint32_t)(a.cin * 2);
+        // byte offset of block b's piece for a conv stage (sc = false) or a
+        // shortcut stage (sc = true: x at the output positions, w_sc as one tap)
+        auto block_off = [&](int b, bool sc) -> uint32_t {
+            if (b < TL::A_BLOCKS) {
+                const int u = b * 32 + (lane >> 1);
+                const int hf = (lane & 1) ^ ((u >> 3) & 1);
+                const int r = u / kAS, c = u % kAS;
+                const int hh = h0 - 1 + r, ww = w0 - 1 + c;
+                const bool inside = r < TL::AR && c < kAW && hh >= 0 && hh < H && ww >= 0 && ww < W;
+                if (!sc) return inside ? (uint32_t)(hh * W + ww) * cs2 + hf * 16 : kOOB;
+                return inside && r >= 1 && r <= HB && c >= 1 && c <= kWB
+                           ? (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + hf * 16
+                           : kOOB;
+            }
             const int u = (b - TL::A_BLOCKS) * 32 + (lane >> 1);
             const int hf = (lane & 1) ^ ((u >> 3) & 1);
             const int tap = u / NB, nl = u % NB;
-            off = (uint32_t)(n0 + nl) * wrow2 + (uint32_t)tap * tap2 + hf * 16;
-            if (EPI == EPI_SHORTCUT && tap == 0) osc = (uint32_t)((n0 + nl) * a.cres * 2) + hf * 16;
+            if (!sc) return (uint32_t)(n0 + nl) * wrow2 + (uint32_t)tap * tap2 + hf * 16;
+            return tap == 0 ? (uint32_t)((n0 + nl) * a.cres * 2) + hf * 16 : kOOB;
+        };
+        uint32_t l_off[TL::BLOCKS];   // conv-stage offsets, kept for the whole K loop
+#pragma unroll
+        for (int b = 0; b < TL::BLOCKS; ++b) l_off[b] = block_off(b, false);
+
+        // request stage s into ring buffer s % NBUF (asynchronous; completion via vmcnt)
+        auto issue = [&](int s) {
+            i32x4 ar, br;
+            const bool sc = s >= s_conv;
+            if (!sc) {
+                const int kt = kt_begin + s / ck;
+                const int cc = s % ck;
+                const int64_t ts = tq + kt - 2;
+                const uint16_t *abase = (ts >= 0 ? a.x + ((nq * a.T + ts) * HW) * a.cin
+                                                 : a.cache + ((nq * 2 + (ts + 2)) * HW) * a.cin) +
+                                        cc * kKC;
+                ar = buffer_rsrc(abase, (uint32_t)(HW * a.cin * 2 - cc * kKC * 2));
+                const int wskip = (kt * 9) * a.cin + cc * kKC;   // elements before this slice
+                br = buffer_rsrc(a.w + wskip, (uint32_t)((int64_t)a.cout * 27 * a.cin * 2 - wskip * 2));
+            } else {
+                const int cc = s - s_conv;
+                ar = buffer_rsrc(a.res + ((nq * a.T + tq) * HW) * a.cres + cc * kKC,
+                                 (uint32_t)(HW * a.cres * 2 - cc * kKC * 2));
+                br = buffer_rsrc(a.wsc + cc * kKC,
+                                 (uint32_t)((int64_t)a.cout * a.cres * 2 - cc * kKC * 2));
+            }
+            const uint32_t base = smem_base + (uint32_t)(s % NBUF) * TL::STAGE_BYTES;
+#pragma unroll
+            for (int b = 0; b < TL::BLOCKS; ++b) {
+                uint32_t off = l_off[b];
+                if constexpr (EPI == EPI_SHORTCUT)
+                    if (sc) off = block_off(b, true);
+                lds_dma16(b < TL::A_BLOCKS ? ar : br, base + b * 1024, off);
+            }
+        };
+
+        // s_waitcnt immediates for "vmcnt <= BLOCKS" (one stage may stay in
+        // flight) and "vmcnt = 0"; other counters left alone (gfx9 encoding:
+        // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+        constexpr int kWaitOne = (TL::BLOCKS & 15) | ((TL::BLOCKS >> 4) << 14) | (7 << 4) | (15 << 8);
+        constexpr int kWaitAll = (7 << 4) | (15 << 8);
+        for (int p = 0; p < NBUF - 1 && p < s_total; ++p) issue(p);
+        for (int s = 0; s < s_total; ++s) {
+            // stage s has landed in LDS once at most the next stage is outstanding
+            if (NBUF == 3 && s + 1 < s_total)
+                __builtin_amdgcn_s_waitcnt(kWaitOne);
+            else
+                __builtin_amdgcn_s_waitcnt(kWaitAll);
+            // A plain barrier, not __syncthreads(): its release fence would wait
+            // for every outstanding load, including the prefetched stage.
+            __builtin_amdgcn_s_barrier();
+            // the barrier also means every MFMA wave has finished stage s - 1, so
+            // its buffer ((s + NBUF - 1) % NBUF) can be refilled
+            if (s + NBUF - 1 < s_total) issue(s + NBUF - 1);
         }
-        l_off[k] = off;
-        if constexpr (EPI == EPI_SHORTCUT) l_sc[k] = osc;
+        return;
     }
 
-    // A stage request: the two buffer resources and the LDS base of its buffer.
-    struct Req {
-        i32x4 ar, br;
-        uint32_t base;
-        bool sc, live;
-    };
-    auto make_req = [&](int s, unsigned char *dst) {
-        Req r;
-        r.live = s < s_total;
-        r.sc = s >= s_conv;
-        r.base = lds_address(dst);
-        if (!r.sc) {
-            const int kt = kt_begin + s / ck;
-            const int cc = s % ck;
-            const int64_t ts = tq + kt - 2;
-            const uint16_t *abase = (ts >= 0 ? a.x + ((nq * a.T + ts) * HW) * a.cin
-                                             : a.cache + ((nq * 2 + (ts + 2)) * HW) * a.cin) +
-                                    cc * kKC;
-            r.ar = buffer_rsrc(abase, (uint32_t)(HW * a.cin * 2 - cc * kKC * 2));
-            const int wskip = (kt * 9) * a.cin + cc * kKC;   // elements before this stage's slice
-            r.br = buffer_rsrc(a.w + wskip, (uint32_t)((int64_t)a.cout * 27 * a.cin * 2 - wskip * 2));
-        } else {
-            const int cc = s - s_conv;
-            r.ar = buffer_rsrc(a.res + ((nq * a.T + tq) * HW) * a.cres + cc * kKC,
-                               (uint32_t)(HW * a.cres * 2 - cc * kKC * 2));
-            r.br = buffer_rsrc(a.wsc + cc * kKC, (uint32_t)((int64_t)a.cout * a.cres * 2 - cc * kKC * 2));
-        }
-        return r;
-    };
-    // Issue this wave's loads k in [K0, K1) of request r (asynchronous; completion via vmcnt).
-    auto issue_part = [&]<int K0, int K1>(const Req &r) {
-        if (!r.live) return;
-#pragma unroll
-        for (int k = K0; k < K1; ++k) {
-            const int b = wave + k * TL::NWAVE;
-            if (b < TL::BLOCKS) {
-                uint32_t off = l_off[k];
-                if constexpr (EPI == EPI_SHORTCUT)
-                    if (r.sc) off = l_sc[k];
-                lds_dma16(b < TL::A_BLOCKS ? r.ar : r.br, r.base + b * 1024, off);
-            }
-        }
-    };
-
+    // ================= MFMA waves
     floatx16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
     const int g = lane >> 5;   // k-group: which 8-channel half of the 16-channel unit
     // B fragment (tap, fn): unit tap*NB + wn*FN*32 + fn*32 + l32; NB and 32 are
     // multiples of 16, so its swizzle bit is bit 3 of l32
-    const int b_rd0 = lds_off(wn * FN * 32 + l32, g);
+    const int b_rd0 = TL::A_BLOCKS * 1024 + lds_off(wn * FN * 32 + l32, g);
     // A fragment (row wm*FM + qr, column l32 + kw): the swizzle bit is bit 3 of
     // (row * 40 + l32 + kw) = parity(row) ^ bit 3 of (l32 + kw); a_rd[par] serves
     // the rows qr with qr & 1 == par, whose parity is par ^ parity(wm * FM)
@@ -305,22 +311,16 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
     };
     auto ldB = [&](const unsigned char *buf, int tap, int fn) {
-        const int off = TL::A_BLOCKS * 1024 + b_rd0 + (tap * NB + fn * 32) * kUnit;
+        const int off = b_rd0 + (tap * NB + fn * 32) * kUnit;
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
     };
 
-    // The LPW loads of a stage request are spread over the FM+2 row groups of
-    // a conv stage (a burst of LDS-DMA issues would stall the wave and leave
-    // the MFMA pipe idle): row group qr issues loads [DMA_LO(qr), DMA_LO(qr+1)).
     constexpr int NROW = FM + 2;
-#define WANVAE_DMA_LO(qr) (((qr) * TL::LPW) / NROW)
-
-    // One conv stage: 9 taps x FM rows x FN channel blocks of MFMAs, with the
-    // loads of request `next` issued in between.
-    auto compute_conv = [&](const unsigned char *buf, const Req &next) {
-        // LDS reads complete in order, so they are issued in the order of first
-        // use: input row 0 and the kh = 0 weights, then the kh = 1 weights and
-        // row 1 (used from row group 1 on), then the kh = 2 weights (row group 2).
+    // One conv stage: 9 taps x FM rows x FN channel blocks of MFMAs.  LDS
+    // reads complete in order, so they are issued in the order of first use:
+    // input row 0 and the kh = 0 weights, then the kh = 1 weights and row 1
+    // (used from row group 1 on), then the kh = 2 weights (row group 2).
+    auto compute_conv = [&](const unsigned char *buf) {
         bf16x8 fw[9][FN];
         bf16x8 fx[2][3];
 #pragma unroll
@@ -329,45 +329,37 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
         for (int tap = 0; tap < 3; ++tap)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = ldB(buf, tap, fn);
-        [&]<int... QR>(std::integer_sequence<int, QR...>) {
-            (
-                [&] {
-                    constexpr int qr = QR;
-                    // weights of tap row kh = qr + 1 are first needed by row group qr + 1
-                    if constexpr (qr + 1 < 3) {
 #pragma unroll
-                        for (int tap = 3 * (qr + 1); tap < 3 * (qr + 2); ++tap)
+        for (int qr = 0; qr < NROW; ++qr) {
+            if (qr + 1 < 3) {
 #pragma unroll
-                            for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = ldB(buf, tap, fn);
-                    }
-                    // input row qr feeds output rows fm = qr - kh; the next row is read meanwhile
-                    if constexpr (qr + 1 < NROW) {
+                for (int tap = 3 * (qr + 1); tap < 3 * (qr + 2); ++tap)
 #pragma unroll
-                        for (int kw = 0; kw < 3; ++kw) fx[(qr + 1) & 1][kw] = ldA(buf, qr + 1, kw);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = ldB(buf, tap, fn);
+            }
+            // input row qr feeds output rows fm = qr - kh; the next row is read meanwhile
+            if (qr + 1 < NROW) {
 #pragma unroll
-                    for (int kw = 0; kw < 3; ++kw)
+                for (int kw = 0; kw < 3; ++kw) fx[(qr + 1) & 1][kw] = ldA(buf, qr + 1, kw);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int kh = 0; kh < 3; ++kh) {
-                            const int fm = qr - kh;
-                            if (fm < 0 || fm >= FM) continue;
+            for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
-                            for (int fn = 0; fn < FN; ++fn)
-                                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                    fw[kh * 3 + kw][fn], fx[qr & 1][kw], acc[fm][fn], 0, 0, 0);
-                        }
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_part.template operator()<WANVAE_DMA_LO(qr), WANVAE_DMA_LO(qr + 1)>(next);
-                    __builtin_amdgcn_sched_barrier(0);
-                }(),
-                ...);
-        }(std::make_integer_sequence<int, NROW>{});
+                for (int kh = 0; kh < 3; ++kh) {
+                    const int fm = qr - kh;
+                    if (fm < 0 || fm >= FM) continue;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fw[kh * 3 + kw][fn], fx[qr & 1][kw], acc[fm][fn], 0, 0, 0);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // One shortcut stage: the centre position of each output row, w_sc as the only tap.
-    auto compute_shortcut = [&](const unsigned char *buf, const Req &next) {
-        issue_part.template operator()<0, TL::LPW>(next);
+    auto compute_shortcut = [&](const unsigned char *buf) {
         bf16x8 fw[FN];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) fw[fn] = ldB(buf, 0, fn);
@@ -380,47 +372,17 @@ __global__ __launch_bounds__(WM *WN * 64) void conv3d_bf16_kernel(Args a) {
         }
     };
 
-    // ---- K loop over the LDS ring: stages 0..NBUF-2 are in flight before the
-    // first MFMA; stage s waits for its own loads (leaving the next stage's
-    // outstanding), meets the barrier that also frees buffer (s-1) % NBUF, then
-    // requests stage s+NBUF-1 into that buffer and runs its MFMAs.
-    constexpr int NBUF = TL::NBUF;
-    unsigned char *ring[3] = {sm0, sm1, NBUF == 3 ? sm2 : sm0};
-    // s_waitcnt immediates for "vmcnt <= LMIN" and "vmcnt = 0", other counters
-    // left alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-    constexpr int kWaitOne = (TL::LMIN & 15) | ((TL::LMIN >> 4) << 14) | (7 << 4) | (15 << 8);
-    constexpr int kWaitAll = (7 << 4) | (15 << 8);
-#pragma unroll
-    for (int p = 0; p < NBUF - 1; ++p) issue_part.template operator()<0, TL::LPW>(make_req(p, ring[p]));
-    for (int s0 = 0; s0 < s_total; s0 += NBUF) {
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-            const int s = s0 + j;
-            if (s < s_total) {
-                if (NBUF == 3 && s + 1 < s_total)
-                    __builtin_amdgcn_s_waitcnt(kWaitOne);
-                else
-                    __builtin_amdgcn_s_waitcnt(kWaitAll);
-                // A plain barrier, not __syncthreads(): its release fence would wait
-                // for every outstanding load, including the prefetched next stage.
-                // This wave's stage-s data has landed (vmcnt above), and every LDS
-                // read of the buffer refilled below was consumed by an MFMA of the
-                // previous stage, i.e. completed (lgkmcnt), before this point.
-                __builtin_amdgcn_s_barrier();
-                // stage s + NBUF - 1 refills buffer (s - 1) % NBUF, freed by the barrier
-                const Req next = make_req(s + NBUF - 1, ring[(j + NBUF - 1) % NBUF]);
-                if constexpr (EPI == EPI_SHORTCUT) {
-                    if (s < s_conv)
-                        compute_conv(ring[j], next);
-                    else
-                        compute_shortcut(ring[j], next);
-                } else {
-                    compute_conv(ring[j], next);
-                }
-            }
+    // one barrier per stage, matching the load wave's: after it, stage s is in LDS
+    for (int s = 0; s < s_conv; ++s) {
+        __builtin_amdgcn_s_barrier();
+        compute_conv(smem + (s % NBUF) * TL::STAGE_BYTES);
+    }
+    if constexpr (EPI == EPI_SHORTCUT) {
+        for (int s = s_conv; s < s_total; ++s) {
+            __builtin_amdgcn_s_barrier();
+            compute_shortcut(smem + (s % NBUF) * TL::STAGE_BYTES);
         }
     }
-#undef WANVAE_DMA_LO
 
     // ---- epilogue: lane owns position (row, w0 + l32) and channels 8j + 4g + [0,4)
 #pragma unroll
@@ -505,19 +467,20 @@ bool conv3d_bf16_supported(int cin, int cout) {
            cout % 32 == 0;
 }
 
-// Tile choice per output-channel count: 4 waves (one per SIMD) with the
-// accumulators in AGPRs, 16 output rows x 32 columns per workgroup, and the
-// widest channel block (96, 64 or 32) that divides C_out and compiles without
-// register spills; the fused-shortcut variant holds a second set of load
-// offsets and uses at most 64 channels.
+// Tile choice per output-channel count (measured on the workload shapes):
+// 16 output rows x 32 columns per workgroup as a 2 x 2 grid of MFMA waves,
+// each wave 8 rows x 32 columns x 32 channels (128 accumulators), plus the
+// load wave; a 2 x 3 grid (96 channels) when C_out is a multiple of 96 but
+// not of 64; 16 rows x 32 channels from four 4-row waves otherwise.
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
     if (c.res != nullptr && c.wsc != nullptr) {
-        if (c.cout % 64 == 0) return launch_cfg<4, 1, 4, 2, EPI_SHORTCUT>(c, s);
+        if (c.cout % 64 == 0) return launch_cfg<2, 2, 8, 1, EPI_SHORTCUT>(c, s);
+        if (c.cout % 96 == 0) return launch_cfg<2, 3, 8, 1, EPI_SHORTCUT>(c, s);
         return launch_cfg<4, 1, 4, 1, EPI_SHORTCUT>(c, s);
     }
-    if (c.cout % 96 == 0) return launch_plain<4, 1, 4, 3>(c, s);    // 16 rows x 96 ch
-    if (c.cout % 64 == 0) return launch_plain<4, 1, 4, 2>(c, s);    // 16 rows x 64 ch
-    return launch_plain<4, 1, 4, 1>(c, s);                          // 16 rows x 32 ch
+    if (c.cout % 64 == 0) return launch_plain<2, 2, 8, 1>(c, s);
+    if (c.cout % 96 == 0) return launch_plain<2, 3, 8, 1>(c, s);
+    return launch_plain<4, 1, 4, 1>(c, s);
 }
 
 }  // namespace wanvae
