@@ -7,8 +7,10 @@ pointers plus torch's current HIP stream to the C ABI declared in
 there is no other implementation and no fallback: if ``libwanvae.so`` is not
 built, importing the binding's functions raises.
 
-Layouts are channels-last: activations ``[n, t, h, w, C]``, 3x3x3 conv
-weights ``[C_out, 3, 3, 3, C_in]``, shortcut weight ``[C_out, C_in]``.
+Layouts: activations are channels-last ``[n, t, h, w, C]``; 3x3x3 conv
+weights enter in the PyTorch Conv3d layout ``[C_out, C_in, 3, 3, 3]`` and are
+packed once on the GPU (``pack_conv3d_weights``) into the order the conv
+kernels stream; the shortcut weight is ``[C_out, C_in]``.
 """
 from __future__ import annotations
 
@@ -46,6 +48,8 @@ class ResblockParamsC(C.Structure):
 EXPORTS = {
     "wanvae_rmsnorm_silu": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p,
                                       C.c_void_p, C.c_float, C.c_int32, C.c_void_p]),
+    "wanvae_pack_conv3d_weights": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                             C.c_void_p]),
     "wanvae_causal_conv3d": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32,
                                        C.c_void_p]),
@@ -142,20 +146,54 @@ def rmsnorm_silu(x, gamma, beta=None, eps: float = EPS, out=None, stream=None):
     return y
 
 
+class PackedWeight:
+    """A 3x3x3 conv weight packed by ``wanvae_pack_conv3d_weights``: ``data`` is
+    a flat device tensor of 27 * cin * cout elements."""
+
+    def __init__(self, data, cin: int, cout: int):
+        self.data, self.cin, self.cout = data, int(cin), int(cout)
+
+    @property
+    def dtype(self):
+        return self.data.dtype
+
+
+def pack_conv3d_weights(w, stream=None) -> PackedWeight:
+    """Pack a conv weight [C_out, C_in, 3, 3, 3] (PyTorch Conv3d layout, on the
+    GPU, bf16 or fp32) for the conv kernels (``wanvae_pack_conv3d_weights``)."""
+    torch = _torch()
+    if w.dim() != 5 or tuple(w.shape[2:]) != (3, 3, 3):
+        raise ValueError(f"w must be [C_out, C_in, 3, 3, 3], got {tuple(w.shape)}")
+    _dev(w, "w")
+    cout, cin = int(w.shape[0]), int(w.shape[1])
+    out = torch.empty(w.numel(), dtype=w.dtype, device=w.device)
+    _check(lib().wanvae_pack_conv3d_weights(_ptr(w), _ptr(out), cin, cout, _dtype_code(w),
+                                            _stream(stream)))
+    return PackedWeight(out, cin, cout)
+
+
+def _packed(w, name, dtype, cin, cout):
+    if not isinstance(w, PackedWeight):
+        raise TypeError(f"{name} must be a PackedWeight (see pack_conv3d_weights)")
+    if (w.cin, w.cout) != (cin, cout):
+        raise ValueError(f"{name} is {w.cin}->{w.cout}, expected {cin}->{cout}")
+    _dev(w.data, name, dtype, (27 * cin * cout,))
+
+
 def causal_conv3d(x, w, bias=None, cache=None, out=None, stream=None):
-    """Causal 3x3x3 conv (``wanvae_causal_conv3d``): x [n,t,h,w,Cin],
-    w [Cout,3,3,3,Cin], cache [n,2,h,w,Cin] or None -> [n,t,h,w,Cout]."""
+    """Causal 3x3x3 conv (``wanvae_causal_conv3d``): x [n,t,h,w,Cin], w a
+    PackedWeight (Cin -> Cout), cache [n,2,h,w,Cin] or None -> [n,t,h,w,Cout]."""
     torch = _torch()
     n, t, h, wd, cin = x.shape
-    cout = w.shape[0]
+    cout = w.cout
     _dev(x, "x")
-    _dev(w, "w", x.dtype, (cout, 3, 3, 3, cin))
+    _packed(w, "w", x.dtype, cin, cout)
     _dev(bias, "bias", torch.float32, (cout,))
     _dev(cache, "cache", x.dtype, (n, 2, h, wd, cin))
     y = torch.empty((n, t, h, wd, cout), dtype=x.dtype, device=x.device) if out is None else out
     _dev(y, "out", x.dtype, (n, t, h, wd, cout))
     d = Dims(n, t, h, wd)
-    _check(lib().wanvae_causal_conv3d(_ptr(x), _ptr(cache), _ptr(w), _ptr(bias), _ptr(y),
+    _check(lib().wanvae_causal_conv3d(_ptr(x), _ptr(cache), _ptr(w.data), _ptr(bias), _ptr(y),
                                       C.byref(d), cin, cout, _dtype_code(x), _stream(stream)))
     return y
 
@@ -164,9 +202,9 @@ def causal_conv3d(x, w, bias=None, cache=None, out=None, stream=None):
 class ResBlock:
     """Device-resident parameters of one ResidualBlock.
 
-    ``from_host`` takes float32 numpy arrays with conv weights in the pages'
-    order [C_out, C_in, kD, kH, kW] and stores them channels-last
-    ([C_out, 3, 3, 3, C_in]) in the block's dtype, once, at setup.
+    ``w_a`` and ``w_b`` are PackedWeights.  ``from_host`` takes float32 numpy
+    arrays with conv weights in the pages' order [C_out, C_in, kD, kH, kW],
+    uploads them in the block's dtype and packs them on the GPU, once, at setup.
     """
 
     def __init__(self, in_dim, out_dim, dtype, gamma1, beta1, w_a, b_a, gamma2, beta2, w_b, b_b,
@@ -181,13 +219,17 @@ class ResBlock:
                       b_sc=(co,))
         for k, shp in shapes.items():
             _dev(self.tensors[k], k, torch.float32, shp)
-        _dev(w_a, "w_a", dtype, (co, 3, 3, 3, ci))
-        _dev(w_b, "w_b", dtype, (co, 3, 3, 3, co))
+        _packed(w_a, "w_a", dtype, ci, co)
+        _packed(w_b, "w_b", dtype, co, co)
         _dev(w_sc, "w_sc", dtype, (co, ci))
         self.c = ResblockParamsC(ci, co, BF16 if dtype == torch.bfloat16 else F32, self.eps,
-                                 *[None if self.tensors[k] is None else self.tensors[k].data_ptr()
+                                 *[None if self.tensors[k] is None else self._ptr_of(self.tensors[k])
                                    for k in ("gamma1", "beta1", "w_a", "b_a", "gamma2", "beta2",
                                              "w_b", "b_b", "w_sc", "b_sc")])
+
+    @staticmethod
+    def _ptr_of(t):
+        return t.data.data_ptr() if isinstance(t, PackedWeight) else t.data_ptr()
 
     @classmethod
     def from_host(cls, p: dict, dtype, device="cuda", eps: float = EPS):
@@ -197,16 +239,19 @@ class ResBlock:
         def f32(a):
             return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
 
-        def wt(a, conv3):
+        def wt(a):
             if a is None:
                 return None
-            a = np.ascontiguousarray(np.transpose(a, (0, 2, 3, 4, 1)) if conv3 else a, np.float32)
+            a = np.ascontiguousarray(a, np.float32)
             return torch.from_numpy(a).to(device=device, dtype=dtype).contiguous()
 
         ci, co = p["wa"].shape[1], p["wa"].shape[0]
-        return cls(ci, co, dtype, f32(p["gamma1"]), f32(p["beta1"]), wt(p["wa"], True), f32(p["ba"]),
-                   f32(p["gamma2"]), f32(p["beta2"]), wt(p["wb"], True), f32(p["bb"]),
-                   wt(p.get("ws"), False), f32(p.get("bs")), eps)
+        w_a = pack_conv3d_weights(wt(p["wa"]))
+        w_b = pack_conv3d_weights(wt(p["wb"]))
+        torch.cuda.synchronize()
+        return cls(ci, co, dtype, f32(p["gamma1"]), f32(p["beta1"]), w_a, f32(p["ba"]),
+                   f32(p["gamma2"]), f32(p["beta2"]), w_b, f32(p["bb"]),
+                   wt(p.get("ws")), f32(p.get("bs")), eps)
 
     def workspace_size(self, n, t, h, w) -> int:
         d = Dims(n, t, h, w)

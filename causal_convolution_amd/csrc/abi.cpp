@@ -277,6 +277,28 @@ int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const 
     return run_conv(c, dtype, static_cast<hipStream_t>(stream));
 }
 
+int wanvae_pack_conv3d_weights(const void *w, void *packed, int32_t cin, int32_t cout, int32_t dtype,
+                               void *stream) {
+    g_error.clear();
+    WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (dtype == WANVAE_BF16) {
+        WV_CHECK(cin >= 16 && cin <= 1024 && cin % 16 == 0 && cout >= 1 && cout <= 1024,
+                 WANVAE_ERR_SHAPE, "bf16 packing needs cin a multiple of 16 in [16, 1024] and cout in "
+                 "[1, 1024] (got %d, %d)", cin, cout);
+    } else {
+        WV_CHECK(cin >= 1 && cin <= 1024 && cout >= 1 && cout <= 1024, WANVAE_ERR_SHAPE,
+                 "fp32 packing needs cin, cout in [1, 1024] (got %d, %d)", cin, cout);
+    }
+    WV_CHECK(w && packed, WANVAE_ERR_NULL, "w and packed are required");
+    WV_CHECK(aligned16(w) && aligned16(packed), WANVAE_ERR_SHAPE, "pointers must be 16-byte aligned");
+    const size_t bytes = (size_t)27 * cin * cout * esize(dtype);
+    WV_CHECK(!overlaps(w, bytes, packed, bytes), WANVAE_ERR_ALIAS, "packed overlaps w");
+    const hipError_t e = wanvae::launch_pack_conv3d_weights(w, packed, cin, cout, dtype == WANVAE_BF16,
+                                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "weight packing launch failed: %s", hipGetErrorString(e));
+    return WANVAE_OK;
+}
+
 int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, const wanvae_dims *d,
                                    size_t *bytes) {
     g_error.clear();

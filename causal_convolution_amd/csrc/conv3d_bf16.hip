@@ -10,13 +10,16 @@
 //
 // GEMM view: M = output channels (MFMA A operand = weights), N = output
 // positions (MFMA B operand = input), K = 27 taps x C_in (+ C_res for the
-// fused 1x1x1 shortcut).  Both operands are K-contiguous in HBM (weights
-// [co][tap][ci], activations [pos][ci]), which is the per-lane operand layout
-// of the MFMA, so nothing is transposed.
+// fused 1x1x1 shortcut).  Both operands are K-contiguous in 16-channel units
+// (packed weights [kt][C_in/16][tap][co][16], activations [pos][ci]), which is
+// the per-lane operand layout of the MFMA, so nothing is transposed.  The
+// packed weight order makes a stage's weights for one tap one contiguous run
+// of C_out x 32 bytes: whole L2 lines, where [co][tap][ci] would cost one
+// 128-byte line request per 32 useful bytes.
 //
-// Workgroup tile: one frame t, HB = WM*FM output rows x 32 output columns x
-// NB = WN*FN*32 output channels; wave (wm, wn) owns FM rows x FN channel blocks
-// (FM*FN 32x32 fp32 accumulators).
+// Output tile: one frame t, HB = WM*FM output rows x 32 output columns x
+// NB = WN*FN*32 output channels; MFMA wave (wm, wn) owns FM rows x FN channel
+// blocks (FM*FN 32x32 fp32 accumulators).
 //
 // K loop in stages of (kt, 16 input channels):
 //   A tile (LDS): HB+2 input rows (the H halo) x 34 columns (the W halo) x 16
@@ -29,29 +32,35 @@
 // (3(FM+2) + 9 FN) / (9 FM FN) KB of LDS reads, against one fragment pair per
 // MFMA when every tap re-reads its operands.
 //
-// A workgroup has WM*WN MFMA waves and one load wave.  The load wave moves
-// every byte of the tile from L2 straight to LDS (buffer_load ... lds): each of
-// its instructions fills one 1 KB block of a stage buffer, lane l writing
-// bytes 16l..16l+15, so no VGPRs stage the data and no LDS-write instructions
-// run.  Issuing these loads stalls the issuing wave on the LDS-DMA queue; with
-// a wave of its own for them, the MFMA waves never wait on the memory pipe.
-// They are raw buffer loads over one frame slab: an input position outside
-// the image gets an out-of-range offset and the hardware writes zeros, so
-// padding costs no branch.  Because the tile already holds the H and W halo,
-// every per-lane load offset is fixed for the whole K loop; a stage only moves
-// the buffer base (frame and channel slice).  Stages rotate through a ring of
-// NBUF LDS buffers: stage s+NBUF-1 is requested while stage s computes; per
-// stage the load wave waits once (vmcnt) and all waves meet one barrier.
+// A workgroup has WM*WN MFMA waves and one load wave, and is persistent: one
+// per compute unit, looping over its share of the output tiles.  The load
+// wave moves every byte of every stage from L2 straight to LDS
+// (buffer_load ... lds): each instruction fills one 1 KB block of a stage
+// buffer, lane l writing bytes 16l..16l+15, so no VGPRs stage the data and no
+// LDS-write instructions run.  Issuing these loads stalls the issuing wave on
+// the LDS-DMA queue; with a wave of its own for them, the MFMA waves never
+// wait on the memory pipe.  They are raw buffer loads over one frame slab: an
+// input position outside the image gets an out-of-range offset and the
+// hardware writes zeros, so padding costs no branch.  Because the tile holds
+// the H and W halo, every per-lane load offset is fixed for a tile's K loop; a
+// stage only moves the buffer base (frame and channel slice).
+//
+// Stages rotate through a ring of NBUF LDS buffers, across tile boundaries (the
+// next tile's first stages load while the MFMA waves run the epilogue).  There
+// is no per-stage barrier: the load wave publishes in LDS how many stages have
+// landed, each MFMA wave publishes how many it has consumed, and a slot is
+// refilled once every MFMA wave has consumed the stage it held.  MFMA waves
+// thus drift apart by up to a few stages, which spreads their LDS read bursts
+// instead of lining them up behind a barrier.  Every wait on a flag is bounded.
 //
 // LDS layout: 32-byte units (16 bf16 channels of one position or one weight
-// row), the two 16-byte halves swapped when bit 3 of the unit index is set.
-// 16 lanes reading one half of 16 consecutive units then hit 16 distinct
-// 16-byte bank groups (gfx950 serves 16 lanes x 16 bytes per LDS cycle).  A
-// tile rows are padded to 40 units so a lane's swizzle bit for (row, kw) is a
-// compile-time function of the row parity.
+// row), A tile rows 34 units apart.  The two 16-byte halves of a unit are
+// swapped when bit 3 of its column (A) or unit index (B) is set: 16 lanes
+// reading one half of 16 consecutive units then hit 16 distinct 16-byte bank
+// groups (gfx950 serves 16 lanes x 16 bytes per LDS cycle).
 //
 // Causal pad: without a cache, the stages of a frame before 0 only add exact
-// zeros and are skipped (uniform per workgroup); with a cache they read it.
+// zeros and are skipped (uniform per tile); with a cache they read it.
 //
 // Epilogue: each lane owns one output position and 4 consecutive output
 // channels per accumulator quad; bias, then the identity residual or the
@@ -59,11 +68,12 @@
 // (8-byte stores).  The 1x1x1 shortcut GEMM runs as C_res/16 extra stages of
 // the same accumulators: A tile = x at the output positions, B tile = w_sc.
 //
-// Workgroup order: tiles are numbered output-channel-block slowest, then
-// batch, row block, column block, and frame fastest, and the dispatch index is
-// remapped so that each of the 8 XCDs walks a contiguous range of tiles: the
-// workgroups resident on one XCD then share one weight slice and the input
-// frames t-2..t of one spatial block through that XCD's L2.
+// Tile order: output-channel block slowest, then batch, row block, column
+// block, and frame fastest.  Each of the 8 XCDs (workgroup index mod 8) owns a
+// contiguous range of tiles, so the workgroups on one XCD share one weight
+// slice and the input frames t-2..t of one spatial block through its L2.
+#include <atomic>
+
 #include "bf16.h"
 #include "internal.h"
 
@@ -73,6 +83,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource word 3 for raw (unformatted, stride 0) buffers on gfx9-family
 // GPUs; loads past num_records return zero.
@@ -82,16 +93,25 @@ constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer: the load returns
 constexpr int kKC = 16;          // input channels per stage = one MFMA k-step
 constexpr int kUnit = 32;        // bytes per LDS unit (16 bf16)
 constexpr int kWB = 32;          // output columns per tile (one MFMA N block)
-constexpr int kAW = kWB + 2;     // A tile columns including the W halo
-constexpr int kAS = 40;          // A tile row stride in units (34 used)
+constexpr int kAS = kWB + 2;     // A tile columns including the W halo = row stride in units
 constexpr int kXCD = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kSyncBytes = 256;  // LDS for the stage flags
+// Bound on every flag wait: 2^15 polls ~64 cycles apart (about 2M cycles, far
+// beyond any real wait); past it the wave goes on, so a broken protocol can
+// only give wrong results, never a hung kernel.
+constexpr int kSpinCap = 1 << 15;
+
+// s_waitcnt immediate for "vmcnt <= n" (n <= 63), other counters left alone
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitVm0 = waitcnt_vm(0);
 
 enum Epilogue { EPI_BIAS = 0, EPI_IDENTITY = 1, EPI_SHORTCUT = 2 };
 
 struct Args {
     const uint16_t *x;      // conv input [n][t][h][w][cin]
     const uint16_t *cache;  // [n][2][h][w][cin] or null
-    const uint16_t *w;      // [cout][27][cin]
+    const uint16_t *w;      // packed: [3 kt][cin/16][9 taps][cout][16]
     const float *bias;      // [cout] or null
     const uint16_t *res;    // [n][t][h][w][cres] or null
     const uint16_t *wsc;    // [cout][cres] or null
@@ -100,6 +120,15 @@ struct Args {
     int64_t N, T, H, W;
     int cin, cout, cres;
     int tiles_w, tiles_h;
+    int64_t tiles;          // total tiles of the launch
+};
+
+// One output tile: batch item, frame, first row / column / output channel,
+// and its K stages (conv stages from temporal tap kt_begin, then shortcut).
+struct TileInfo {
+    int64_t nq, tq;
+    int h0, w0, n0;
+    int kt_begin, s_conv, s_total;
 };
 
 template <int WM, int WN, int FM, int FN>
@@ -113,33 +142,39 @@ struct Tile {
     static constexpr int B_BLOCKS = 9 * NB / 32;
     static constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;       // load instructions per stage
     static constexpr int STAGE_BYTES = BLOCKS * 1024;
-    static constexpr int NBUF = 3 * STAGE_BYTES <= 160 * 1024 ? 3 : 2;  // LDS ring depth
-    static_assert(NBUF * STAGE_BYTES <= 160 * 1024, "tile does not fit the 160 KB LDS");
-    static_assert(BLOCKS < 64, "vmcnt holds at most 63 outstanding loads");
+    static constexpr int kLds = 160 * 1024 - kSyncBytes;
+    static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
+    static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
+    static_assert(FM % 2 == 0, "the A fragment double buffer alternates on row parity");
+    static_assert(NWAVE + 1 <= kSyncBytes / 4, "one flag per wave");
+    static constexpr int kPerCU = (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes);
 };
 
-// byte offset of half `h` (0/1) of LDS unit `u`
-__device__ __host__ constexpr int lds_off(int u, int h) { return u * kUnit + ((h ^ ((u >> 3) & 1)) << 4); }
+// byte offset of half `h` (0/1) of A unit (row r, column c) and of B unit u
+__device__ __host__ constexpr int a_off(int r, int c, int h) {
+    return (r * kAS + c) * kUnit + ((h ^ ((c >> 3) & 1)) << 4);
+}
+__device__ __host__ constexpr int b_off(int u, int h) { return u * kUnit + ((h ^ ((u >> 3) & 1)) << 4); }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource (stride 0, num_records bytes) for a wave-uniform base.
+// Raw buffer resource (stride 0, num_records bytes) for a wave-uniform base
+// and size (made scalar explicitly: the resource must live in SGPRs).
 __device__ inline i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
     return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
-                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)), (int)bytes, kBufFlags};
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), kBufFlags};
 }
 
 // One wavefront-wide 16-byte-per-lane load from a buffer straight into LDS:
 // lane l's 16 bytes at byte offset voff land at LDS byte address
 // lds_addr + 16 * l (lds_addr wave-uniform).  Written as inline assembly so the
-// compiler does not wait for these loads before unrelated LDS reads; the
-// kernel orders them itself with explicit vmcnt waits and barriers.  M0 is set
-// inside the same statement, immediately before its only use.
+// compiler does not wait for these loads before unrelated LDS accesses; the
+// kernel orders them itself with explicit vmcnt waits.  M0 is set inside the
+// same statement, immediately before its only use.
 __device__ inline void lds_dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(voff), "s"(rsrc)
                  : "memory");
 }
 
@@ -147,70 +182,83 @@ __device__ inline uint32_t lds_address(const unsigned char *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
 }
 
+// compiler-only fence: no memory access moves across it
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
 template <int WM, int WN, int FM, int FN, int EPI>
 __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) {
     using TL = Tile<WM, WN, FM, FN>;
-    constexpr int NT = TL::kThreads;
     constexpr int HB = TL::HB;
     constexpr int NB = TL::NB;
+    constexpr int NBUF = TL::NBUF;
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[TL::NBUF * TL::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * TL::STAGE_BYTES];
+    // sync[0]: stages landed (load wave); sync[1 + w]: stages consumed by MFMA wave w
+    __shared__ int sync[kSyncBytes / 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // NWAVE = the load wave
-    const int wm = wave % WM;
-    const int wn = wave / WM;
-
-    // ---- XCD-aware tile index: XCD k runs a contiguous range of tiles
-    const int64_t nwg = gridDim.x;
-    const int64_t bid = blockIdx.x;
-    const int64_t q = nwg / kXCD, rmd = nwg % kXCD;
-    const int64_t xcd = bid % kXCD, loc = bid / kXCD;
-    int64_t tile = xcd < rmd ? xcd * (q + 1) + loc : rmd * (q + 1) + (xcd - rmd) * q + loc;
-
-    // frame fastest: consecutive tiles are the same spatial block in consecutive
-    // frames, so the input frames t-2..t of neighbouring workgroups overlap in L2
-    const int64_t tq = tile % a.T;
-    tile /= a.T;
-    const int wt = (int)(tile % a.tiles_w);
-    tile /= a.tiles_w;
-    const int ht = (int)(tile % a.tiles_h);
-    tile /= a.tiles_h;
-    const int64_t nq = tile % a.N;
-    const int ntile = (int)(tile / a.N);
-    const int h0 = ht * HB;
-    const int w0 = wt * kWB;
-    const int n0 = ntile * NB;
     const int H = (int)a.H, W = (int)a.W;
     const int64_t HW = (int64_t)H * W;
-
-    // ---- stage list: conv stages (kt from kt_begin, channel slice), then shortcut stages
     const int ck = a.cin / kKC;
-    const int kt_begin = (a.cache != nullptr || tq >= 2) ? 0 : (int)(2 - tq);
-    const int s_conv = (3 - kt_begin) * ck;
-    const int s_total = s_conv + (EPI == EPI_SHORTCUT ? a.cres / kKC : 0);
 
-    constexpr int NBUF = TL::NBUF;
+    if (tid <= TL::NWAVE) sync[tid] = 0;
+    __syncthreads();
+    // flag accesses: relaxed atomics on the LDS array itself, so they stay
+    // ds_read / ds_write (through a generic pointer they would become FLAT
+    // accesses, which the compiler must also wait for with vmcnt)
+    auto flag_read = [&](int i) { return __builtin_amdgcn_readfirstlane(__atomic_load_n(&sync[i], __ATOMIC_RELAXED)); };
+    auto flag_write = [&](int i, int v) { __atomic_store_n(&sync[i], v, __ATOMIC_RELAXED); };
+
+    // ---- this workgroup's tiles.  XCD x (= workgroup index mod 8) holds wg_x
+    // of the grid's workgroups and owns a contiguous tile range of matching
+    // share, [x_begin, x_begin + x_count); its workgroups take the tiles of
+    // that range round-robin.  (With at least as many tiles as workgroups,
+    // every workgroup gets one or more.)
+    const int64_t nwg = gridDim.x, bid = blockIdx.x;
+    const int64_t xcd = bid % kXCD, loc = bid / kXCD;
+    const int64_t wg_x = nwg / kXCD + (xcd < nwg % kXCD ? 1 : 0);
+    const int64_t wg_before = xcd * (nwg / kXCD) + (xcd < nwg % kXCD ? xcd : nwg % kXCD);
+    const int64_t x_begin = a.tiles * wg_before / nwg;
+    const int64_t x_count = a.tiles * (wg_before + wg_x) / nwg - x_begin;
+
+    auto decode = [&](int64_t tile) {
+        TileInfo ti;
+        ti.tq = tile % a.T;
+        tile /= a.T;
+        ti.w0 = (int)(tile % a.tiles_w) * kWB;
+        tile /= a.tiles_w;
+        ti.h0 = (int)(tile % a.tiles_h) * HB;
+        tile /= a.tiles_h;
+        ti.nq = tile % a.N;
+        ti.n0 = (int)(tile / a.N) * NB;
+        // without a cache the stages of frames before 0 only add zeros: skipped
+        const int kt_begin = (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
+        ti.kt_begin = kt_begin;
+        ti.s_conv = (3 - kt_begin) * ck;
+        ti.s_total = ti.s_conv + (EPI == EPI_SHORTCUT ? a.cres / kKC : 0);
+        return ti;
+    };
+
     const uint32_t smem_base = lds_address(smem);
 
     if (wave == TL::NWAVE) {
-        // ================= load wave: all global -> LDS traffic of the tile
-        // Block b of a stage: lane l writes half (l & 1) ^ swizzle(u) of unit
-        // u = 32 * b' + l / 2 (b' relative to the A or B region), so the lane
-        // fetches that half of that unit.  Offsets are fixed for the K loop; a
-        // stage only moves the buffer base (frame and channel slice).
+        // ================= load wave: all global -> LDS traffic of every tile.
+        // Block b of a stage: lane l writes physical half (l & 1) of unit
+        // 32 * b' + l / 2 (b' relative to the A or B region), so it fetches the
+        // logical half that the swizzle puts there.
         const uint32_t cs2 = (uint32_t)a.cin * 2;
-        const uint32_t wrow2 = (uint32_t)(27 * a.cin * 2), tap2 = (uint32_t)(a.cin * 2);
+        const uint32_t tap2 = (uint32_t)a.cout * kUnit;   // bytes per tap of a packed stage
         // byte offset of block b's piece for a conv stage (sc = false) or a
         // shortcut stage (sc = true: x at the output positions, w_sc as one tap)
-        auto block_off = [&](int b, bool sc) -> uint32_t {
+        auto block_off = [&](const TileInfo &ti, int b, bool sc) -> uint32_t {
             if (b < TL::A_BLOCKS) {
                 const int u = b * 32 + (lane >> 1);
-                const int hf = (lane & 1) ^ ((u >> 3) & 1);
                 const int r = u / kAS, c = u % kAS;
-                const int hh = h0 - 1 + r, ww = w0 - 1 + c;
-                const bool inside = r < TL::AR && c < kAW && hh >= 0 && hh < H && ww >= 0 && ww < W;
+                const int hf = (lane & 1) ^ ((c >> 3) & 1);
+                const int hh = ti.h0 - 1 + r, ww = ti.w0 - 1 + c;
+                const bool inside = r < TL::AR && hh >= 0 && hh < H && ww >= 0 && ww < W;
                 if (!sc) return inside ? (uint32_t)(hh * W + ww) * cs2 + hf * 16 : kOOB;
                 return inside && r >= 1 && r <= HB && c >= 1 && c <= kWB
                            ? (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + hf * 16
@@ -219,95 +267,130 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             const int u = (b - TL::A_BLOCKS) * 32 + (lane >> 1);
             const int hf = (lane & 1) ^ ((u >> 3) & 1);
             const int tap = u / NB, nl = u % NB;
-            if (!sc) return (uint32_t)(n0 + nl) * wrow2 + (uint32_t)tap * tap2 + hf * 16;
-            return tap == 0 ? (uint32_t)((n0 + nl) * a.cres * 2) + hf * 16 : kOOB;
+            if (!sc) return (uint32_t)tap * tap2 + (uint32_t)(ti.n0 + nl) * kUnit + hf * 16;
+            return tap == 0 ? (uint32_t)((ti.n0 + nl) * a.cres * 2) + hf * 16 : kOOB;
         };
-        uint32_t l_off[TL::BLOCKS];   // conv-stage offsets, kept for the whole K loop
-#pragma unroll
-        for (int b = 0; b < TL::BLOCKS; ++b) l_off[b] = block_off(b, false);
 
-        // request stage s into ring buffer s % NBUF (asynchronous; completion via vmcnt)
-        auto issue = [&](int s) {
-            i32x4 ar, br;
-            const bool sc = s >= s_conv;
+        // request cursor: stage si of local tile it (tile x_begin + it), ring slot
+        TileInfo ti{};
+        int64_t it = loc;
+        int si = 0, slot = 0;
+        uint32_t l_off[TL::BLOCKS];   // conv-stage offsets of the cursor's tile
+        auto start_tile = [&]() {
+            ti = decode(x_begin + it);
+#pragma unroll
+            for (int b = 0; b < TL::BLOCKS; ++b) l_off[b] = block_off(ti, b, false);
+        };
+        if (it < x_count) start_tile();
+
+        // request the cursor's stage into its ring slot (asynchronous; completion
+        // via vmcnt), then advance the cursor, into the next tile if need be
+        auto issue_next = [&]() __attribute__((always_inline)) {
+            const uint16_t *abase, *bbase;
+            uint32_t abytes, bbytes;
+            const bool sc = si >= ti.s_conv;
             if (!sc) {
-                const int kt = kt_begin + s / ck;
-                const int cc = s % ck;
-                const int64_t ts = tq + kt - 2;
-                const uint16_t *abase = (ts >= 0 ? a.x + ((nq * a.T + ts) * HW) * a.cin
-                                                 : a.cache + ((nq * 2 + (ts + 2)) * HW) * a.cin) +
-                                        cc * kKC;
-                ar = buffer_rsrc(abase, (uint32_t)(HW * a.cin * 2 - cc * kKC * 2));
-                const int wskip = (kt * 9) * a.cin + cc * kKC;   // elements before this slice
-                br = buffer_rsrc(a.w + wskip, (uint32_t)((int64_t)a.cout * 27 * a.cin * 2 - wskip * 2));
+                const int kt = ti.kt_begin + si / ck;
+                const int cc = si % ck;
+                const int64_t ts = ti.tq + kt - 2;
+                abase = (ts >= 0 ? a.x + ((ti.nq * a.T + ts) * HW) * a.cin
+                                 : a.cache + ((ti.nq * 2 + (ts + 2)) * HW) * a.cin) +
+                        cc * kKC;
+                abytes = (uint32_t)(HW * a.cin * 2 - cc * kKC * 2);
+                // elements of the packed weight before stage (kt, cc)
+                const int64_t wskip = (int64_t)(kt * ck + cc) * 9 * a.cout * kKC;
+                bbase = a.w + wskip;
+                bbytes = (uint32_t)(((int64_t)27 * a.cin * a.cout - wskip) * 2);
             } else {
-                const int cc = s - s_conv;
-                ar = buffer_rsrc(a.res + ((nq * a.T + tq) * HW) * a.cres + cc * kKC,
-                                 (uint32_t)(HW * a.cres * 2 - cc * kKC * 2));
-                br = buffer_rsrc(a.wsc + cc * kKC,
-                                 (uint32_t)((int64_t)a.cout * a.cres * 2 - cc * kKC * 2));
+                const int cc = si - ti.s_conv;
+                abase = a.res + ((ti.nq * a.T + ti.tq) * HW) * a.cres + cc * kKC;
+                abytes = (uint32_t)(HW * a.cres * 2 - cc * kKC * 2);
+                bbase = a.wsc + cc * kKC;
+                bbytes = (uint32_t)((int64_t)a.cout * a.cres * 2 - cc * kKC * 2);
             }
-            const uint32_t base = smem_base + (uint32_t)(s % NBUF) * TL::STAGE_BYTES;
+            // the cursor is uniform; buffer_rsrc makes that explicit to the compiler
+            const i32x4 ar = buffer_rsrc(abase, abytes);
+            const i32x4 br = buffer_rsrc(bbase, bbytes);
+            const uint32_t base = smem_base + (uint32_t)slot * TL::STAGE_BYTES;
 #pragma unroll
             for (int b = 0; b < TL::BLOCKS; ++b) {
                 uint32_t off = l_off[b];
                 if constexpr (EPI == EPI_SHORTCUT)
-                    if (sc) off = block_off(b, true);
+                    if (sc) off = block_off(ti, b, true);
                 lds_dma16(b < TL::A_BLOCKS ? ar : br, base + b * 1024, off);
+            }
+            slot = slot + 1 == NBUF ? 0 : slot + 1;
+            if (++si == ti.s_total) {
+                si = 0;
+                it += wg_x;
+                if (it < x_count) start_tile();
             }
         };
 
-        // s_waitcnt immediates for "vmcnt <= BLOCKS" (one stage may stay in
-        // flight) and "vmcnt = 0"; other counters left alone (gfx9 encoding:
-        // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-        constexpr int kWaitOne = (TL::BLOCKS & 15) | ((TL::BLOCKS >> 4) << 14) | (7 << 4) | (15 << 8);
-        constexpr int kWaitAll = (7 << 4) | (15 << 8);
-        for (int p = 0; p < NBUF - 1 && p < s_total; ++p) issue(p);
-        for (int s = 0; s < s_total; ++s) {
-            // stage s has landed in LDS once at most the next stage is outstanding
-            if (NBUF == 3 && s + 1 < s_total)
-                __builtin_amdgcn_s_waitcnt(kWaitOne);
-            else
-                __builtin_amdgcn_s_waitcnt(kWaitAll);
-            // A plain barrier, not __syncthreads(): its release fence would wait
-            // for every outstanding load, including the prefetched stage.
-            __builtin_amdgcn_s_barrier();
-            // the barrier also means every MFMA wave has finished stage s - 1, so
-            // its buffer ((s + NBUF - 1) % NBUF) can be refilled
-            if (s + NBUF - 1 < s_total) issue(s + NBUF - 1);
+        // the slowest MFMA wave's consumed-stage count
+        auto min_done = [&]() {
+            int m = flag_read(1);
+#pragma unroll
+            for (int w = 1; w < TL::NWAVE; ++w) {
+                const int d = flag_read(1 + w);
+                m = d < m ? d : m;
+            }
+            return m;
+        };
+
+        int issued = 0, landed = 0, done = 0;
+        for (;;) {
+            // request stages while a ring slot is free: the slot of stage
+            // `issued` last held stage issued - NBUF, which every MFMA wave
+            // must have consumed
+            while (it < x_count && issued < done + NBUF) {
+                issue_next();
+                ++issued;
+            }
+            if (landed < issued) {
+                // the oldest requested stage has landed once at most the loads
+                // requested after it are outstanding (vmcnt counts to 63 at most,
+                // and at most 63 loads are ever in flight)
+                switch (issued - landed - 1) {
+                    case 0: __builtin_amdgcn_s_waitcnt(kWaitVm0); break;
+                    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(TL::BLOCKS < 63 ? TL::BLOCKS : 63)); break;
+                    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * TL::BLOCKS < 63 ? 2 * TL::BLOCKS : 63)); break;
+                    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * TL::BLOCKS < 63 ? 3 * TL::BLOCKS : 63)); break;
+                }
+                compiler_fence();
+                ++landed;
+                if (lane == 0) flag_write(0, landed);
+                compiler_fence();
+                done = min_done();
+                continue;
+            }
+            if (it >= x_count) break;   // everything requested has landed and been published
+            // every slot holds a published, unconsumed stage: wait for the slowest wave
+            for (int spin = 0; spin < kSpinCap; ++spin) {
+                __builtin_amdgcn_s_sleep(1);
+                done = min_done();
+                if (issued < done + NBUF) break;
+            }
+            if (issued >= done + NBUF) done = issued - NBUF + 1;   // bound reached: go on
         }
         return;
     }
 
     // ================= MFMA waves
-    floatx16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
+    const int wm = wave % WM;
+    const int wn = wave / WM;
     const int l32 = lane & 31;
     const int g = lane >> 5;   // k-group: which 8-channel half of the 16-channel unit
     // B fragment (tap, fn): unit tap*NB + wn*FN*32 + fn*32 + l32; NB and 32 are
     // multiples of 16, so its swizzle bit is bit 3 of l32
-    const int b_rd0 = TL::A_BLOCKS * 1024 + lds_off(wn * FN * 32 + l32, g);
-    // A fragment (row wm*FM + qr, column l32 + kw): the swizzle bit is bit 3 of
-    // (row * 40 + l32 + kw) = parity(row) ^ bit 3 of (l32 + kw); a_rd[par] serves
-    // the rows qr with qr & 1 == par, whose parity is par ^ parity(wm * FM)
-    int a_rd[2][3];
+    const int b_rd0 = TL::A_BLOCKS * 1024 + b_off(wn * FN * 32 + l32, g);
+    // A fragment (row wm*FM + qr, column l32 + kw)
+    int a_rd[3];
 #pragma unroll
-    for (int kw = 0; kw < 3; ++kw)
-#pragma unroll
-        for (int par = 0; par < 2; ++par) {
-            const int u = l32 + kw;
-            const int row_par = par ^ ((wm * FM) & 1);
-            a_rd[par][kw] = (wm * FM) * kAS * kUnit + u * kUnit + ((g ^ ((u >> 3) & 1) ^ row_par) << 4);
-        }
+    for (int kw = 0; kw < 3; ++kw) a_rd[kw] = a_off(wm * FM, l32 + kw, g);
 
     auto ldA = [&](const unsigned char *buf, int qr, int kw) {
-        const int off = a_rd[qr & 1][kw] + qr * kAS * kUnit;
+        const int off = a_rd[kw] + qr * kAS * kUnit;
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
     };
     auto ldB = [&](const unsigned char *buf, int tap, int fn) {
@@ -315,6 +398,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
     };
 
+    floatx16 acc[FM][FN];
     constexpr int NROW = FM + 2;
     // One conv stage: 9 taps x FM rows x FN channel blocks of MFMAs.  LDS
     // reads complete in order, so they are issued in the order of first use:
@@ -372,57 +456,146 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         }
     };
 
-    // one barrier per stage, matching the load wave's: after it, stage s is in LDS
-    for (int s = 0; s < s_conv; ++s) {
-        __builtin_amdgcn_s_barrier();
-        compute_conv(smem + (s % NBUF) * TL::STAGE_BYTES);
-    }
-    if constexpr (EPI == EPI_SHORTCUT) {
-        for (int s = s_conv; s < s_total; ++s) {
-            __builtin_amdgcn_s_barrier();
-            compute_shortcut(smem + (s % NBUF) * TL::STAGE_BYTES);
+    int consumed = 0, seen = 0, slot = 0;
+    // wait until stage `consumed` has landed
+    auto wait_landed = [&]() {
+        for (int spin = 0; seen <= consumed && spin < kSpinCap; ++spin) {
+            seen = flag_read(0);
+            if (seen <= consumed) __builtin_amdgcn_s_sleep(1);
         }
-    }
+        compiler_fence();   // the stage's reads stay below the flag read
+    };
+    // stage consumed: its reads were issued (and, LDS being in order, execute)
+    // before this flag write
+    auto release = [&]() {
+        compiler_fence();
+        ++consumed;
+        if (lane == 0) flag_write(1 + wave, consumed);
+        slot = slot + 1 == NBUF ? 0 : slot + 1;
+    };
 
-    // ---- epilogue: lane owns position (row, w0 + l32) and channels 8j + 4g + [0,4)
+    for (int64_t i = loc; i < x_count; i += wg_x) {
+        const TileInfo ti = decode(x_begin + i);
+
+        // bias (+ shortcut bias) of this lane's output channels: requested now,
+        // first used in the epilogue, so the K loop hides the latency
+        float bsum[FN][4][4];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        const int hh = h0 + wm * FM + fm;
-        const int ww = w0 + l32;
-        if (hh >= H || ww >= W) continue;
-        const int64_t p = ((nq * a.T + tq) * H + hh) * (int64_t)W + ww;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
+        for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int co = n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * j + e];
-                if (a.bias) {
-                    const float4 bv = *reinterpret_cast<const float4 *>(a.bias + co);
-                    v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
-                }
-                if constexpr (EPI == EPI_IDENTITY) {
-                    const uint2 rv = *reinterpret_cast<const uint2 *>(a.res + p * a.cres + co);
-                    v[0] += bf16_bits_to_f32(rv.x & 0xffffu);
-                    v[1] += bf16_bits_to_f32(rv.x >> 16);
-                    v[2] += bf16_bits_to_f32(rv.y & 0xffffu);
-                    v[3] += bf16_bits_to_f32(rv.y >> 16);
-                }
+                const int co = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
+                float4 bv = a.bias ? *reinterpret_cast<const float4 *>(a.bias + co)
+                                   : float4{0.f, 0.f, 0.f, 0.f};
                 if constexpr (EPI == EPI_SHORTCUT) {
                     if (a.bsc) {
-                        const float4 bv = *reinterpret_cast<const float4 *>(a.bsc + co);
-                        v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
+                        const float4 sv = *reinterpret_cast<const float4 *>(a.bsc + co);
+                        bv.x += sv.x; bv.y += sv.y; bv.z += sv.z; bv.w += sv.w;
                     }
                 }
-                uint2 o;
-                o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                *reinterpret_cast<uint2 *>(a.y + p * a.cout + co) = o;
+                bsum[fn][j][0] = bv.x; bsum[fn][j][1] = bv.y;
+                bsum[fn][j][2] = bv.z; bsum[fn][j][3] = bv.w;
+            }
+
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+
+        for (int s = 0; s < ti.s_conv; ++s) {
+            wait_landed();
+            compute_conv(smem + slot * TL::STAGE_BYTES);
+            release();
+        }
+        if constexpr (EPI == EPI_SHORTCUT) {
+            for (int s = ti.s_conv; s < ti.s_total; ++s) {
+                wait_landed();
+                compute_shortcut(smem + slot * TL::STAGE_BYTES);
+                release();
+            }
+        }
+
+        // ---- epilogue: lane owns position (row, w0 + l32) and channels
+        // 8j + 4g + [0,4) of each channel block.  The load wave is meanwhile
+        // already filling the ring with the next tile's first stages.
+        const int ww = ti.w0 + l32;
+        const int64_t prow = (ti.nq * a.T + ti.tq) * H;
+        // identity residual: every load of the tile requested before any use
+        uint2 rv[EPI == EPI_IDENTITY ? FM : 1][FN][4];
+        if constexpr (EPI == EPI_IDENTITY) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int hh = ti.h0 + wm * FM + fm;
+                const bool ok = hh < H && ww < W;
+                const int64_t p = (prow + hh) * (int64_t)W + ww;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int co = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
+                        rv[fm][fn][j] = ok ? *reinterpret_cast<const uint2 *>(a.res + p * a.cres + co)
+                                           : uint2{0u, 0u};
+                    }
+            }
+        }
+        // One wait, outside every branch, for the residual and bias loads: left
+        // to itself the compiler waits again in each row's (conditional) block,
+        // where vmcnt also counts the stores of the rows before.  The fence
+        // keeps every load above the wait.
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int hh = ti.h0 + wm * FM + fm;
+            if (hh >= H || ww >= W) continue;
+            const int64_t p = (prow + hh) * (int64_t)W + ww;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int co = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * j + e] + bsum[fn][j][e];
+                    if constexpr (EPI == EPI_IDENTITY) {
+                        const uint2 r = rv[fm][fn][j];
+                        v[0] += bf16_bits_to_f32(r.x & 0xffffu);
+                        v[1] += bf16_bits_to_f32(r.x >> 16);
+                        v[2] += bf16_bits_to_f32(r.y & 0xffffu);
+                        v[3] += bf16_bits_to_f32(r.y >> 16);
+                    }
+                    uint2 o;
+                    o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                    o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                    *reinterpret_cast<uint2 *>(a.y + p * a.cout + co) = o;
+                }
             }
         }
     }
+}
+
+// Compute units of the current device (cached per device).
+hipError_t device_cu_count(int *out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) {
+            *out = v;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidDevice;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return hipSuccess;
 }
 
 template <int WM, int WN, int FM, int FN, int EPI>
@@ -446,10 +619,15 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.cres = c.cres;
     a.tiles_w = (int)((c.w_ + kWB - 1) / kWB);
     a.tiles_h = (int)((c.h + TL::HB - 1) / TL::HB);
-    const int64_t tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (c.cout / TL::NB);
-    if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    conv3d_bf16_kernel<WM, WN, FM, FN, EPI><<<dim3((unsigned)tiles), dim3(TL::kThreads), 0, s>>>(a);
+    a.tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (c.cout / TL::NB);
+    if (a.tiles <= 0) return hipSuccess;
+    // persistent grid: one workgroup per compute unit (the LDS ring takes most
+    // of a CU's 160 KB), each looping over its share of the tiles
+    int ncu = 0;
+    const hipError_t e = device_cu_count(&ncu);
+    if (e != hipSuccess) return e;
+    const int64_t grid = a.tiles < (int64_t)ncu * TL::kPerCU ? a.tiles : (int64_t)ncu * TL::kPerCU;
+    conv3d_bf16_kernel<WM, WN, FM, FN, EPI><<<dim3((unsigned)grid), dim3(TL::kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 

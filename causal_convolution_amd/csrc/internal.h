@@ -16,7 +16,7 @@ namespace wanvae {
 struct ConvLaunch {
     const void *x = nullptr;      // conv input [n][t][h][w][cin]
     const void *cache = nullptr;  // frames -2, -1: [n][2][h][w][cin], or null
-    const void *w = nullptr;      // [cout][3][3][3][cin]
+    const void *w = nullptr;      // packed by launch_pack_conv3d_weights
     const float *bias = nullptr;  // [cout] or null
     const void *res = nullptr;    // residual / shortcut input, or null
     const void *wsc = nullptr;    // [cout][cres] or null
@@ -37,6 +37,11 @@ hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, 
 // bf16 implicit-GEMM conv on MFMA: cin, cout (and cres) multiples of 32.
 bool conv3d_bf16_supported(int cin, int cout);
 hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
+
+// Packs PyTorch-layout conv weights [cout][cin][3][3][3] for the conv kernels
+// (bf16: [3][cin/16][3][3][cout][16], cin % 16 == 0; fp32: [cout][3][3][3][cin]).
+hipError_t launch_pack_conv3d_weights(const void *w, void *out, int cin, int cout, bool bf16,
+                                      hipStream_t s);
 
 // fp32 direct conv, any channel counts.
 hipError_t launch_conv3d_f32(const ConvLaunch &a, hipStream_t s);

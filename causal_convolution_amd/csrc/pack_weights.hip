@@ -1,0 +1,68 @@
+// Conv weight packing: from the PyTorch Conv3d layout [C_out][C_in][3][3][3]
+// (the weight of "Sharding of WAN 2.2 VAE", Available Sharding Dimensions)
+// into the layout each conv kernel streams.
+//
+//   fp32: [C_out][kt][kh][kw][C_in]        (the direct kernel walks C_in innermost)
+//   bf16: [kt][C_in/16][kh][kw][C_out][16]
+//
+// The bf16 layout follows the MFMA conv's K loop: one stage consumes temporal
+// tap kt and a 16-channel slice of C_in for all 9 (kh, kw) taps, so a stage's
+// weights for one tap are C_out x 32 bytes in one contiguous run (whole
+// 128-byte cache lines) instead of 32-byte pieces C_in * 54 bytes apart.
+// One thread per packed element; the gather is read once per call, at set-up.
+#include "internal.h"
+
+namespace wanvae {
+namespace {
+
+template <typename T>
+__global__ void pack_f32_kernel(const T *__restrict__ w, T *__restrict__ out, int cin, int cout,
+                                int64_t total) {
+    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        // o = ((co * 27) + tap) * cin + ci
+        const int ci = (int)(o % cin);
+        const int64_t r = o / cin;
+        const int tap = (int)(r % 27);
+        const int co = (int)(r / 27);
+        out[o] = w[((int64_t)co * cin + ci) * 27 + tap];
+    }
+}
+
+__global__ void pack_bf16_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ out, int cin,
+                                 int cout, int64_t total) {
+    const int slices = cin / 16;
+    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
+         o += (int64_t)gridDim.x * blockDim.x) {
+        // o = ((((kt * slices + cc) * 9 + khw) * cout + co) * 16 + c16
+        const int c16 = (int)(o % 16);
+        int64_t r = o / 16;
+        const int co = (int)(r % cout);
+        r /= cout;
+        const int khw = (int)(r % 9);
+        r /= 9;
+        const int cc = (int)(r % slices);
+        const int kt = (int)(r / slices);
+        const int ci = cc * 16 + c16;
+        out[o] = w[((int64_t)co * cin + ci) * 27 + kt * 9 + khw];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack_conv3d_weights(const void *w, void *out, int cin, int cout, bool bf16,
+                                      hipStream_t s) {
+    const int64_t total = (int64_t)27 * cin * cout;
+    if (total == 0) return hipSuccess;
+    const int64_t want = (total + 255) / 256;
+    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    if (bf16)
+        pack_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(w),
+                                              static_cast<uint16_t *>(out), cin, cout, total);
+    else
+        pack_f32_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(w),
+                                                    static_cast<float *>(out), cin, cout, total);
+    return hipGetLastError();
+}
+
+}  // namespace wanvae

@@ -14,10 +14,12 @@
  *  - Tensor pointers are DEVICE pointers to dense tensors.  Activations are
  *    channels-last [n][t][h][w][C] (C innermost), the NDHWC layout of
  *    "Closing the gap", gap #6; nothing is permuted inside the library.
- *  - 3x3x3 conv weights are [C_out][3][3][3][C_in] = [C_out][kt][kh][kw][C_in]:
- *    the pages' [C_out, C_in, kD, kH, kW] ("Sharding of WAN 2.2 VAE",
- *    Available Sharding Dimensions) with C_in moved innermost.  The 1x1x1
- *    shortcut weight is [C_out][C_in].
+ *  - 3x3x3 conv weights are passed PACKED: the buffer that
+ *    wanvae_pack_conv3d_weights fills from the pages' [C_out, C_in, kD, kH, kW]
+ *    weight ("Sharding of WAN 2.2 VAE", Available Sharding Dimensions; the
+ *    PyTorch Conv3d layout).  A packed weight holds the same 27*C_in*C_out
+ *    elements of the conv dtype, reordered for the kernel that streams it.
+ *    The 1x1x1 shortcut weight is plain [C_out][C_in].
  *  - dtype (wanvae_dtype) applies to activations and conv weights.  Norm
  *    scales/shifts and all biases are fp32 [C].  Arithmetic is fp32 (norm
  *    statistics, conv accumulation, bias and residual adds); bf16 outputs are
@@ -79,11 +81,11 @@ typedef struct {
     float eps;                /* clamp of the channel L2 norm (1e-12 in the decoder) */
     const float *gamma1;      /* [in_dim]  norm1 scale                                */
     const float *beta1;       /* [in_dim]  norm1 shift, or NULL for 0                 */
-    const void *w_a;          /* [out_dim][3][3][3][in_dim]  conv A weight            */
+    const void *w_a;          /* conv A weight (out_dim x in_dim), packed             */
     const float *b_a;         /* [out_dim] conv A bias, or NULL                        */
     const float *gamma2;      /* [out_dim] norm2 scale                                */
     const float *beta2;       /* [out_dim] norm2 shift, or NULL                        */
-    const void *w_b;          /* [out_dim][3][3][3][out_dim] conv B weight            */
+    const void *w_b;          /* conv B weight (out_dim x out_dim), packed            */
     const float *b_b;         /* [out_dim] conv B bias, or NULL                        */
     const void *w_sc;         /* [out_dim][in_dim] 1x1x1 shortcut weight, or NULL for
                                  the identity shortcut (requires in_dim == out_dim)   */
@@ -108,7 +110,7 @@ WANVAE_API int wanvae_rmsnorm_silu(const void *x, void *y, int64_t rows, int32_t
 
 /*
  * Causal 3x3x3 convolution, stride 1, with bias:
- *   y[n,t,h,w,co] = bias[co] + sum_{kt,kh,kw,ci} w[co,kt,kh,kw,ci] *
+ *   y[n,t,h,w,co] = bias[co] + sum_{kt,kh,kw,ci} w[co,ci,kt,kh,kw] *
  *                   Z[n, t+kt-2, h+kh-1, w+kw-1, ci]
  * ("Sharding of WAN 2.2 VAE", Available Sharding Dimensions, for the conv and
  * its weight; causal in time, zero pad of one pixel in H and W: "Closing the
@@ -118,11 +120,28 @@ WANVAE_API int wanvae_rmsnorm_silu(const void *x, void *y, int64_t rows, int32_t
  * VAE", Why depth sharding is not beneficial), else 0 (causal zero pad).
  *   x     : [d.n][d.t][d.h][d.w][cin] of dtype.
  *   cache : [d.n][2][d.h][d.w][cin] of dtype, or NULL.  Only read.
- *   w     : [cout][3][3][3][cin] of dtype.   bias: [cout] fp32 or NULL.
+ *   w     : packed weight (wanvae_pack_conv3d_weights, cin x cout, dtype).
+ *   bias  : [cout] fp32 or NULL.
  *   y     : [d.n][d.t][d.h][d.w][cout] of dtype; must not overlap x, cache, w.
  *   Channels: bf16 needs cin and cout multiples of 32 and <= 1024 (bf16 MFMA
  *   implicit GEMM); fp32 accepts 1..1024 (direct fp32 kernel).
  */
+/*
+ * Packs a 3x3x3 conv weight for wanvae_causal_conv3d and the ResidualBlock
+ * calls.  Input: w = [cout][cin][3][3][3] of dtype, the pages' weight layout
+ * [C_out, C_in, kD, kH, kW] ("Sharding of WAN 2.2 VAE", Available Sharding
+ * Dimensions).  Output: `packed`, 27*cin*cout elements of dtype, laid out as
+ *   fp32: [cout][kt][kh][kw][cin]
+ *   bf16: [kt][cin/16][kh][kw][cout][16]  (cin a multiple of 16)
+ * The bf16 order is the MFMA conv's K loop (temporal tap, 16-channel slice,
+ * then the 9 spatial taps), so each tap's slice for all output channels is
+ * one contiguous run.  Runs one GPU gather kernel on `stream`; meant for
+ * set-up, once per weight.  `packed` must not overlap `w`; both are owned by
+ * the caller.
+ */
+WANVAE_API int wanvae_pack_conv3d_weights(const void *w, void *packed, int32_t cin, int32_t cout,
+                                          int32_t dtype, void *stream);
+
 WANVAE_API int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const float *bias,
                          void *y, const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
                          void *stream);

@@ -79,6 +79,20 @@ def test_conv_validation():
                                   None) == wv.OK
 
 
+def test_pack_validation():
+    L = wv.lib()
+    p, q = C.c_void_p(1 << 24), C.c_void_p(1 << 30)
+    assert L.wanvae_pack_conv3d_weights(p, q, 64, 64, 7, None) == wv.ERR_DTYPE
+    assert L.wanvae_pack_conv3d_weights(p, q, 24, 64, wv.BF16, None) == wv.ERR_SHAPE   # cin % 16
+    assert L.wanvae_pack_conv3d_weights(p, q, 64, 0, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_pack_conv3d_weights(p, q, 2048, 64, wv.F32, None) == wv.ERR_SHAPE
+    assert L.wanvae_pack_conv3d_weights(None, q, 64, 64, wv.BF16, None) == wv.ERR_NULL
+    assert L.wanvae_pack_conv3d_weights(p, C.c_void_p((1 << 30) + 4), 64, 64, wv.BF16, None) == wv.ERR_SHAPE
+    # the packed buffer may not overlap the source
+    assert L.wanvae_pack_conv3d_weights(p, C.c_void_p((1 << 24) + 4096), 64, 64, wv.BF16, None) == wv.ERR_ALIAS
+    assert "overlap" in wv.last_error()
+
+
 def _params(cin=384, cout=192, dtype=wv.BF16, shortcut=True):
     a = 1 << 24
     vals = [a + i * (1 << 20) for i in range(10)]

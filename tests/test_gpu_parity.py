@@ -100,7 +100,7 @@ def test_causal_conv3d_bf16(torch, wv, shape, with_cache):
     b = rnd(rng, (Cout,), 0.1)
     cache = rnd(rng, (N, 2, H, W, Cin), 1.0, wl.BF16) if with_cache else None
     ref = oracle.causal_conv3d(x, w, b, cache)
-    y = wv.causal_conv3d(gu.to_dev(x, wl.BF16), gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.BF16),
+    y = wv.causal_conv3d(gu.to_dev(x, wl.BF16), wv.pack_conv3d_weights(gu.to_dev(w, wl.BF16)),
                          gu.to_dev(b, wl.F32),
                          None if cache is None else gu.to_dev(cache, wl.BF16))
     err = gu.rel_err(gu.to_host(y), ref)
@@ -118,7 +118,7 @@ def test_causal_conv3d_f32(torch, wv, shape, with_cache):
     b = rnd(rng, (Cout,), 0.1)
     cache = rnd(rng, (N, 2, H, W, Cin)) if with_cache else None
     ref = oracle.causal_conv3d(x, w, b, cache)
-    y = wv.causal_conv3d(gu.to_dev(x, wl.F32), gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.F32),
+    y = wv.causal_conv3d(gu.to_dev(x, wl.F32), wv.pack_conv3d_weights(gu.to_dev(w, wl.F32)),
                          gu.to_dev(b, wl.F32), None if cache is None else gu.to_dev(cache, wl.F32))
     err = gu.rel_err(gu.to_host(y), ref)
     gu.report(f"conv f32 {shape} cache={with_cache}", err, gu.TOL_F32)
@@ -129,10 +129,30 @@ def test_causal_conv3d_no_bias_and_empty(torch, wv):
     rng = np.random.default_rng(3)
     x = rnd(rng, (1, 2, 8, 32, 64), 1.0, wl.BF16)
     w = rnd(rng, (32, 64, 3, 3, 3), 0.05, wl.BF16)
-    y = wv.causal_conv3d(gu.to_dev(x, wl.BF16), gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.BF16))
+    pw = wv.pack_conv3d_weights(gu.to_dev(w, wl.BF16))
+    y = wv.causal_conv3d(gu.to_dev(x, wl.BF16), pw)
     assert gu.rel_err(gu.to_host(y), oracle.causal_conv3d(x, w)) <= gu.TOL_BF16
     e = torch.zeros((1, 0, 8, 32, 64), dtype=torch.bfloat16, device="cuda")
-    assert wv.causal_conv3d(e, gu.to_dev(np.transpose(w, (0, 2, 3, 4, 1)), wl.BF16)).shape == (1, 0, 8, 32, 32)
+    assert wv.causal_conv3d(e, pw).shape == (1, 0, 8, 32, 32)
+
+
+@pytest.mark.parametrize("cin,cout,dtype", [(16, 1, wl.BF16), (48, 96, wl.BF16), (384, 192, wl.BF16),
+                                            (3, 5, wl.F32), (64, 33, wl.F32)])
+def test_pack_conv3d_weights_layout(torch, wv, cin, cout, dtype):
+    """The packed order is the one the header documents, element for element
+    (a pure permutation: compared bit for bit)."""
+    rng = np.random.default_rng(cin * 1000 + cout)
+    w = rnd(rng, (cout, cin, 3, 3, 3), 1.0, dtype)
+    got = gu.to_host(wv.pack_conv3d_weights(gu.to_dev(w, dtype)).data)
+    taps = w.reshape(cout, cin, 27)
+    if dtype == wl.BF16:
+        # [kt][cin/16][kh*3+kw][cout][16]
+        want = taps.reshape(cout, cin // 16, 16, 3, 9).transpose(3, 1, 4, 0, 2).reshape(-1)
+    else:
+        # [cout][kt*9+kh*3+kw][cin]
+        want = taps.transpose(0, 2, 1).reshape(-1)
+    assert got.shape == want.shape
+    assert np.array_equal(got.astype(np.float32), want.astype(np.float32))
 
 
 # --------------------------------------------------------------------------- block, small
