@@ -73,6 +73,7 @@
 // contiguous range of tiles, so the workgroups on one XCD share one weight
 // slice and the input frames t-2..t of one spatial block through its L2.
 #include <atomic>
+#include <utility>
 
 #include "bf16.h"
 #include "internal.h"
@@ -84,6 +85,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Buffer resource word 3 for raw (unformatted, stride 0) buffers on gfx9-family
 // GPUs; loads past num_records return zero.
@@ -145,7 +147,6 @@ struct Tile {
     static constexpr int kLds = 160 * 1024 - kSyncBytes;
     static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
     static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
-    static_assert(FM % 2 == 0, "the A fragment double buffer alternates on row parity");
     static_assert(NWAVE + 1 <= kSyncBytes / 4, "one flag per wave");
     static constexpr int kPerCU = (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes);
 };
@@ -177,6 +178,19 @@ __device__ inline void lds_dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
                  : "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(voff), "s"(rsrc)
                  : "memory");
 }
+
+// The same resource as a typed value for the buffer load/store builtins.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)bytes), kBufFlags);
+}
+
+// rows of group gi when FM rows are taken EG at a time
+template <int FM, int EG>
+__device__ __host__ constexpr int group_rows(int gi) { return FM - gi * EG < EG ? FM - gi * EG : EG; }
 
 __device__ inline uint32_t lds_address(const unsigned char *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
@@ -520,58 +534,79 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // ---- epilogue: lane owns position (row, w0 + l32) and channels
         // 8j + 4g + [0,4) of each channel block.  The load wave is meanwhile
         // already filling the ring with the next tile's first stages.
-        const int ww = ti.w0 + l32;
-        const int64_t prow = (ti.nq * a.T + ti.tq) * H;
-        // identity residual: every load of the tile requested before any use
-        uint2 rv[EPI == EPI_IDENTITY ? FM : 1][FN][4];
-        if constexpr (EPI == EPI_IDENTITY) {
+        // Branch-free: residual loads and output stores are raw buffer
+        // accesses over this frame, and a position outside the image gets an
+        // out-of-range offset (its load returns zero, its store is dropped).
+        // The identity residual is fetched two rows at a time, one group ahead
+        // of the stores, with exact vmcnt waits.
+        const int64_t frame = ti.nq * a.T + ti.tq;
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y + frame * HW * a.cout, HW * a.cout * 2);
+        const int cbase = ti.n0 + wn * FN * 32 + 4 * g;   // this lane's first channel
+        auto pos_off = [&](int fm, int cstride) -> uint32_t {
+            const int hh = ti.h0 + wm * FM + fm, ww = ti.w0 + l32;
+            return hh < H && ww < W ? (uint32_t)((hh * W + ww) * cstride + cbase) * 2 : kOOB;
+        };
+        auto store_rows = [&](int f0, int nrows, const u32x2 (*res)[FN][4]) {
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int hh = ti.h0 + wm * FM + fm;
-                const bool ok = hh < H && ww < W;
-                const int64_t p = (prow + hh) * (int64_t)W + ww;
+            for (int e = 0; e < nrows; ++e) {
+                const uint32_t off = pos_off(f0 + e, a.cout);
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int co = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
-                        rv[fm][fn][j] = ok ? *reinterpret_cast<const uint2 *>(a.res + p * a.cres + co)
-                                           : uint2{0u, 0u};
+                        float v[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = acc[f0 + e][fn][4 * j + q] + bsum[fn][j][q];
+                        if (res != nullptr) {
+                            const u32x2 r = res[e][fn][j];
+                            v[0] += bf16_bits_to_f32(r.x & 0xffffu);
+                            v[1] += bf16_bits_to_f32(r.x >> 16);
+                            v[2] += bf16_bits_to_f32(r.y & 0xffffu);
+                            v[3] += bf16_bits_to_f32(r.y >> 16);
+                        }
+                        u32x2 o;
+                        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        __builtin_amdgcn_raw_buffer_store_b64(o, ry, off + fn * 64 + j * 16, 0, 0);
                     }
             }
-        }
-        // One wait, outside every branch, for the residual and bias loads: left
-        // to itself the compiler waits again in each row's (conditional) block,
-        // where vmcnt also counts the stores of the rows before.  The fence
-        // keeps every load above the wait.
-        compiler_fence();
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        };
+        if constexpr (EPI == EPI_IDENTITY) {
+            constexpr int EG = 2;                          // rows per residual group
+            constexpr int NG = (FM + EG - 1) / EG;
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.res + frame * HW * a.cres, HW * a.cres * 2);
+            u32x2 rv[2][EG][FN][4];
+            auto load_group = [&](int gi) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int hh = ti.h0 + wm * FM + fm;
-            if (hh >= H || ww >= W) continue;
-            const int64_t p = (prow + hh) * (int64_t)W + ww;
+                for (int e = 0; e < group_rows<FM, EG>(gi); ++e) {
+                    const uint32_t off = pos_off(gi * EG + e, a.cres);
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
+                    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int co = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * j + e] + bsum[fn][j][e];
-                    if constexpr (EPI == EPI_IDENTITY) {
-                        const uint2 r = rv[fm][fn][j];
-                        v[0] += bf16_bits_to_f32(r.x & 0xffffu);
-                        v[1] += bf16_bits_to_f32(r.x >> 16);
-                        v[2] += bf16_bits_to_f32(r.y & 0xffffu);
-                        v[3] += bf16_bits_to_f32(r.y >> 16);
-                    }
-                    uint2 o;
-                    o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                    o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                    *reinterpret_cast<uint2 *>(a.y + p * a.cout + co) = o;
+                        for (int j = 0; j < 4; ++j)
+                            rv[gi & 1][e][fn][j] = __builtin_amdgcn_raw_buffer_load_b64(rr, off + fn * 64 + j * 16, 0, 0);
                 }
-            }
+            };
+            load_group(0);
+            if (NG > 1) load_group(1);
+            // group GI has landed once at most the VMEM operations issued
+            // after its loads are outstanding: the stores of group GI - 1 and
+            // the loads of group GI + 1 (an immediate, hence the template)
+            auto step = [&]<int GI>() {
+                constexpr int kAfter = (GI >= 1 ? group_rows<FM, EG>(GI - 1) * FN * 4 : 0) +
+                                       (GI + 1 < NG ? group_rows<FM, EG>(GI + 1) * FN * 4 : 0);
+                static_assert(kAfter <= 63, "vmcnt counts to 63");
+                compiler_fence();
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAfter));
+                compiler_fence();
+                store_rows(GI * EG, group_rows<FM, EG>(GI), rv[GI & 1]);
+                if (GI + 2 < NG) load_group(GI + 2);
+            };
+            [&]<int... GI>(std::integer_sequence<int, GI...>) {
+                (step.template operator()<GI>(), ...);
+            }(std::make_integer_sequence<int, NG>{});
+        } else {
+            store_rows(0, FM, nullptr);
         }
     }
 }
@@ -645,19 +680,26 @@ bool conv3d_bf16_supported(int cin, int cout) {
            cout % 32 == 0;
 }
 
-// Tile choice per output-channel count (measured on the workload shapes):
-// 16 output rows x 32 columns per workgroup as a 2 x 2 grid of MFMA waves,
-// each wave 8 rows x 32 columns x 32 channels (128 accumulators), plus the
-// load wave; a 2 x 3 grid (96 channels) when C_out is a multiple of 96 but
-// not of 64; 16 rows x 32 channels from four 4-row waves otherwise.
+// Rows a tile height computes for an image height (the last tile is padded).
+int64_t rows_computed(int64_t h, int hb) { return (h + hb - 1) / hb * hb; }
+
+// Tile choice (measured on the workload shapes): a 2 x 2 grid of MFMA waves,
+// each 8 or 9 rows x 32 columns x 32 channels (128 or 144 accumulators), plus
+// the load wave; a 2 x 3 grid (96 channels) when C_out is a multiple of 96
+// but not of 64; 16 rows x 32 channels from four 4-row waves otherwise.  The
+// 18-row tile is taken unless it pads more rows than the 16-row one (every
+// decoder resolution, 90 x 160 up to 720 x 1280, is a multiple of 18 rows).
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
+    const bool tall = rows_computed(c.h, 18) <= rows_computed(c.h, 16);
     if (c.res != nullptr && c.wsc != nullptr) {
-        if (c.cout % 64 == 0) return launch_cfg<2, 2, 8, 1, EPI_SHORTCUT>(c, s);
-        if (c.cout % 96 == 0) return launch_cfg<2, 3, 8, 1, EPI_SHORTCUT>(c, s);
+        if (c.cout % 64 == 0)
+            return tall ? launch_cfg<2, 2, 9, 1, EPI_SHORTCUT>(c, s) : launch_cfg<2, 2, 8, 1, EPI_SHORTCUT>(c, s);
+        if (c.cout % 96 == 0)
+            return tall ? launch_cfg<2, 3, 9, 1, EPI_SHORTCUT>(c, s) : launch_cfg<2, 3, 8, 1, EPI_SHORTCUT>(c, s);
         return launch_cfg<4, 1, 4, 1, EPI_SHORTCUT>(c, s);
     }
-    if (c.cout % 64 == 0) return launch_plain<2, 2, 8, 1>(c, s);
-    if (c.cout % 96 == 0) return launch_plain<2, 3, 8, 1>(c, s);
+    if (c.cout % 64 == 0) return tall ? launch_plain<2, 2, 9, 1>(c, s) : launch_plain<2, 2, 8, 1>(c, s);
+    if (c.cout % 96 == 0) return tall ? launch_plain<2, 3, 9, 1>(c, s) : launch_plain<2, 3, 8, 1>(c, s);
     return launch_plain<4, 1, 4, 1>(c, s);
 }
 

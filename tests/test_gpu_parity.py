@@ -87,6 +87,10 @@ CONV_SHAPES = [
     (1, 1, 1, 1, 32, 64),        # one position, one frame
     (1, 4, 3, 35, 1024, 1024),   # widest channel count
     (1, 3, 6, 36, 160, 224),     # channel counts with odd multiples of 32
+    # image heights for which the 18-row tiles are chosen (exact and ragged)
+    (1, 3, 36, 40, 64, 128),     # 2 x 18 rows, 64-channel blocks
+    (2, 2, 35, 33, 96, 96),      # 35 rows: one 18-row tile padded by one row; Cout 96
+    (1, 4, 18, 64, 192, 192),    # one 18-row tile, 3 channel blocks
 ]
 
 
@@ -162,6 +166,9 @@ SMALL_BLOCKS = [
     wl.custom("id192_b2", wl.BF16, 2, 3, 9, 33, 192, 192),
     wl.custom("sc64_128", wl.BF16, 1, 5, 8, 64, 64, 128),
     wl.custom("f32_sc", wl.F32, 1, 3, 6, 10, 64, 32),
+    # 18-row tiles: identity and 1x1x1-shortcut epilogues, 64- and 96-channel tiles
+    wl.custom("id128_h36", wl.BF16, 1, 3, 36, 40, 128, 128),
+    wl.custom("sc192_96_h35", wl.BF16, 1, 3, 35, 40, 192, 96),
 ]
 
 
