@@ -98,6 +98,11 @@ constexpr int kWB = 32;          // output columns per tile (one MFMA N block)
 constexpr int kAS = kWB + 2;     // A tile columns including the W halo = row stride in units
 constexpr int kXCD = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int kSyncBytes = 256;  // LDS for the stage flags
+// Epilogue staging, per MFMA wave: one output row of 32 positions x 32
+// channels, positions 80 bytes apart (64 used; the pad spreads the 8-byte
+// writes of 16 lanes over distinct bank groups)
+constexpr int kEpiStride = 80;
+constexpr int kEpiBytes = 32 * kEpiStride;
 // Bound on every flag wait: 2^15 polls ~64 cycles apart (about 2M cycles, far
 // beyond any real wait); past it the wave goes on, so a broken protocol can
 // only give wrong results, never a hung kernel.
@@ -144,11 +149,11 @@ struct Tile {
     static constexpr int B_BLOCKS = 9 * NB / 32;
     static constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;       // load instructions per stage
     static constexpr int STAGE_BYTES = BLOCKS * 1024;
-    static constexpr int kLds = 160 * 1024 - kSyncBytes;
+    static constexpr int kLds = 160 * 1024 - kSyncBytes - NWAVE * kEpiBytes;
     static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
     static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
     static_assert(NWAVE + 1 <= kSyncBytes / 4, "one flag per wave");
-    static constexpr int kPerCU = (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes);
+    static constexpr int kPerCU = (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes + NWAVE * kEpiBytes);
 };
 
 // byte offset of half `h` (0/1) of A unit (row r, column c) and of B unit u
@@ -209,6 +214,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * TL::STAGE_BYTES];
     // sync[0]: stages landed (load wave); sync[1 + w]: stages consumed by MFMA wave w
     __shared__ int sync[kSyncBytes / 4];
+    __shared__ __attribute__((aligned(16))) unsigned char epi_stage[TL::NWAVE * kEpiBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -546,12 +552,18 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             const int hh = ti.h0 + wm * FM + fm, ww = ti.w0 + l32;
             return hh < H && ww < W ? (uint32_t)((hh * W + ww) * cstride + cbase) * 2 : kOOB;
         };
+        // A row of results goes out through this wave's LDS staging buffer:
+        // written as the MFMA layout holds it (lane = position, 4 channels per
+        // accumulator quad), read back as 16 bytes per lane with 4 lanes per
+        // position, and stored as 64 contiguous bytes per position, so a store
+        // touches 16 cache lines instead of 32 and there are half as many.
+        unsigned char *const epi = epi_stage + wave * kEpiBytes;
         auto store_rows = [&](int f0, int nrows, const u32x2 (*res)[FN][4]) {
 #pragma unroll
             for (int e = 0; e < nrows; ++e) {
-                const uint32_t off = pos_off(f0 + e, a.cout);
+                const int hh = ti.h0 + wm * FM + f0 + e;
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
+                for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         float v[4];
@@ -567,8 +579,20 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                         u32x2 o;
                         o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
                         o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                        __builtin_amdgcn_raw_buffer_store_b64(o, ry, off + fn * 64 + j * 16, 0, 0);
+                        *reinterpret_cast<u32x2 *>(epi + l32 * kEpiStride + j * 16 + g * 8) = o;
                     }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int p = (lane >> 2) + 16 * half, q = lane & 3;
+                        const u32x4 d = *reinterpret_cast<const u32x4 *>(epi + p * kEpiStride + q * 16);
+                        const int ww = ti.w0 + p;
+                        const uint32_t off =
+                            hh < H && ww < W
+                                ? (uint32_t)((hh * W + ww) * a.cout + ti.n0 + wn * FN * 32 + fn * 32) * 2 + q * 16
+                                : kOOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
+                    }
+                }
             }
         };
         if constexpr (EPI == EPI_IDENTITY) {
