@@ -7,202 +7,203 @@
 // decoder", section 4, with SiLU fused into the same pass as that section
 // describes for tt-metal's kernel.
 //
-// Mapping: a row of C channels is owned by a group of 16 consecutive lanes,
-// each holding E = C/16 contiguous channels, so one wavefront works on 4 rows
-// and every load instruction of the wavefront covers 4 x 2C contiguous bytes.
-// The sum of squares is reduced across the 16 lanes with xor shuffles (no LDS).
+// Mapping: 16 consecutive lanes own G consecutive rows, G the fewest rows
+// that span a whole number of 256-byte runs (G = 1 for 384 bf16 channels, 2
+// for 192, 4 for 96).  The G rows are cut into 16-byte pieces and piece p
+// belongs to lane p % 16, so every load or store instruction of a 16-lane
+// group covers one whole 256-byte run: each instruction uses its cache lines
+// entirely, which lets the accesses stream past the caches (nontemporal) at
+// close to the device's copy bandwidth.  Pieces never straddle rows (C is a
+// multiple of 8); a lane keeps one partial sum of squares per row of its
+// group, and each is reduced across the 16 lanes with xor shuffles (no LDS).
 // gamma * sqrt(C) and beta are held in registers for the whole grid-stride
-// loop; each lane keeps U rows in flight to cover HBM latency.  y may equal x
-// (in place): each element is read and then written by the same lane.  x is read once
-// and y written once: 2 * rows * C * sizeof(T) bytes of HBM traffic.
+// loop; U groups of rows are in flight per lane to cover HBM latency.  y may
+// equal x (in place): each element is read and then written by the same
+// lane.  x is read once and y written once: 2 * rows * C * sizeof(T) bytes of
+// HBM traffic.
 #include "bf16.h"
 #include "internal.h"
 
 namespace wanvae {
 namespace {
 
-constexpr int kLanesPerRow = 16;
+constexpr int kGroupLanes = 16;
 constexpr int kThreads = 256;
-constexpr int kRowsPerPass = kThreads / kLanesPerRow;  // 16 rows per block per pass
+constexpr int kGroups = kThreads / kGroupLanes;   // 16-lane groups per block
+constexpr int kGridCap = 16384;                   // blocks; the grid strides over the rows
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-
-// Load NDW dwords from a pointer aligned to VW dwords.
-template <int NDW, int VW>
-__device__ inline void load_dwords(const uint32_t *__restrict__ p, uint32_t (&d)[NDW]) {
-#pragma unroll
-    for (int i = 0; i < NDW; i += VW) {
-        if constexpr (VW == 4) {
-            uint4 q = *reinterpret_cast<const uint4 *>(p + i);
-            d[i] = q.x; d[i + 1] = q.y; d[i + 2] = q.z; d[i + 3] = q.w;
-        } else if constexpr (VW == 2) {
-            uint2 q = *reinterpret_cast<const uint2 *>(p + i);
-            d[i] = q.x; d[i + 1] = q.y;
-        } else {
-            d[i] = p[i];
-        }
-    }
-}
-
-template <int NDW, int VW>
-__device__ inline void store_dwords(uint32_t *__restrict__ p, const uint32_t (&d)[NDW]) {
-#pragma unroll
-    for (int i = 0; i < NDW; i += VW) {
-        if constexpr (VW == 4) {
-            *reinterpret_cast<uint4 *>(p + i) = make_uint4(d[i], d[i + 1], d[i + 2], d[i + 3]);
-        } else if constexpr (VW == 2) {
-            *reinterpret_cast<uint2 *>(p + i) = make_uint2(d[i], d[i + 1]);
-        } else {
-            p[i] = d[i];
-        }
-    }
-}
-
-constexpr int pow2_vec(int ndw) { return ndw % 4 == 0 ? 4 : (ndw % 2 == 0 ? 2 : 1); }
-
-// Per-element storage traits: E elements as NDW dwords.
-template <typename T, int E> struct Row;
-
-template <int E> struct Row<float, E> {
-    static constexpr int NDW = E;
-    static __device__ inline void unpack(const uint32_t (&d)[NDW], float (&v)[E]) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = __uint_as_float(d[e]);
-    }
-    static __device__ inline void pack(const float (&v)[E], uint32_t (&d)[NDW]) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) d[e] = __float_as_uint(v[e]);
-    }
-};
-
-template <int E> struct Row<uint16_t, E> {  // bf16 bits
-    static_assert(E % 2 == 0, "bf16 rows need an even count per lane");
-    static constexpr int NDW = E / 2;
-    static __device__ inline void unpack(const uint32_t (&d)[NDW], float (&v)[E]) {
-#pragma unroll
-        for (int i = 0; i < NDW; ++i) {
-            v[2 * i] = bf16_bits_to_f32(d[i] & 0xffffu);
-            v[2 * i + 1] = bf16_bits_to_f32(d[i] >> 16);
-        }
-    }
-    static __device__ inline void pack(const float (&v)[E], uint32_t (&d)[NDW]) {
-#pragma unroll
-        for (int i = 0; i < NDW; ++i)
-            d[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
-    }
-};
-
-// E consecutive fp32 values (16-byte aligned when E is a multiple of 4, 8-byte when even).
-template <int E>
-__device__ inline void load_params(const float *__restrict__ p, float (&v)[E]) {
-    constexpr int VW = E % 4 == 0 ? 4 : (E % 2 == 0 ? 2 : 1);
-    uint32_t d[E];
-    load_dwords<E, VW>(reinterpret_cast<const uint32_t *>(p), d);
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = __uint_as_float(d[e]);
-}
+constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 
 __device__ inline float silu(float u) {
     // u / (1 + exp(-u)); exp(-u) = inf for very negative u gives -0
     return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
 }
 
-template <typename T, int E, int U>
+// 16 bytes = EP elements of T as fp32 and back
+template <typename T> struct Piece;
+template <> struct Piece<float> {
+    static constexpr int EP = 4;
+    static __device__ inline void unpack(const u32x4 &d, float (&v)[4]) {
+        v[0] = __uint_as_float(d.x); v[1] = __uint_as_float(d.y);
+        v[2] = __uint_as_float(d.z); v[3] = __uint_as_float(d.w);
+    }
+    static __device__ inline u32x4 pack(const float (&v)[4]) {
+        return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                     __float_as_uint(v[3])};
+    }
+};
+template <> struct Piece<uint16_t> {  // bf16 bits
+    static constexpr int EP = 8;
+    static __device__ inline void unpack(const u32x4 &d, float (&v)[8]) {
+        const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = bf16_bits_to_f32(w[k] & 0xffffu);
+            v[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+        }
+    }
+    static __device__ inline u32x4 pack(const float (&v)[8]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+template <typename T, int C>
+struct Shape {
+    static constexpr int RB = C * (int)sizeof(T);          // row bytes
+    static constexpr int G = 256 / gcd(256, RB);           // rows per 16-lane group
+    static constexpr int NP = G * RB / 256;                // 16-byte pieces per lane
+    static constexpr int EP = Piece<T>::EP;                // elements per piece
+    // groups of rows in flight per lane: about 96 bytes of loads or more
+    static constexpr int U = NP * 16 >= 96 ? 1 : (96 + NP * 16 - 1) / (NP * 16) > 8 ? 8
+                                                    : (96 + NP * 16 - 1) / (NP * 16);
+    static constexpr int ROWS_PER_BLOCK = kGroups * G * U;  // per pass of the grid-stride loop
+};
+
+template <typename T, int C>
 __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
     const T *x, T *y, int64_t rows, const float *__restrict__ gamma,
     const float *__restrict__ beta, float eps, float sqrt_c) {
-    using R = Row<T, E>;
-    constexpr int NDW = R::NDW;
-    constexpr int VW = pow2_vec(NDW);
-    constexpr int C = E * kLanesPerRow;
-    constexpr int ROW_DW = C * (int)sizeof(T) / 4;
+    using S = Shape<T, C>;
+    using PC = Piece<T>;
+    constexpr int G = S::G, NP = S::NP, EP = S::EP, U = S::U;
 
-    const int lane = threadIdx.x % kLanesPerRow;
-    const int slot = threadIdx.x / kLanesPerRow;
+    const int lane = threadIdx.x % kGroupLanes;
+    const int grp = threadIdx.x / kGroupLanes;
 
-    // gamma * sqrt(C) and beta for this lane's E channels, loaded once
-    float g[E], b[E];
-    load_params<E>(gamma + lane * E, g);
+    // piece i of this lane: byte (i * 16 + lane) * 16 of its group's G rows,
+    // i.e. row prow[i] of the group, channels pch[i] .. pch[i] + EP - 1
+    int prow[NP], pch[NP];
 #pragma unroll
-    for (int e = 0; e < E; ++e) g[e] *= sqrt_c;
-    if (beta) {
-        load_params<E>(beta + lane * E, b);
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) b[e] = 0.0f;
+    for (int i = 0; i < NP; ++i) {
+        const int byte = (i * kGroupLanes + lane) * 16;
+        prow[i] = G == 1 ? 0 : byte / S::RB;
+        pch[i] = (byte % S::RB) / (int)sizeof(T);
     }
+    // gamma * sqrt(C) and beta of those channels, loaded once
+    float g[NP][EP], b[NP][EP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+#pragma unroll
+        for (int k = 0; k < EP; k += 4) {
+            const float4 gv = *reinterpret_cast<const float4 *>(gamma + pch[i] + k);
+            const float4 bv = beta ? *reinterpret_cast<const float4 *>(beta + pch[i] + k)
+                                   : float4{0.f, 0.f, 0.f, 0.f};
+            g[i][k] = gv.x * sqrt_c; g[i][k + 1] = gv.y * sqrt_c;
+            g[i][k + 2] = gv.z * sqrt_c; g[i][k + 3] = gv.w * sqrt_c;
+            b[i][k] = bv.x; b[i][k + 1] = bv.y; b[i][k + 2] = bv.z; b[i][k + 3] = bv.w;
+        }
 
-    const uint32_t *xs = reinterpret_cast<const uint32_t *>(x);
-    uint32_t *ys = reinterpret_cast<uint32_t *>(y);
-    const int64_t step = (int64_t)gridDim.x * kRowsPerPass * U;
+    const unsigned char *xb = reinterpret_cast<const unsigned char *>(x);
+    unsigned char *yb = reinterpret_cast<unsigned char *>(y);
+    const int64_t step = (int64_t)gridDim.x * S::ROWS_PER_BLOCK;
 
-    for (int64_t r0 = (int64_t)blockIdx.x * kRowsPerPass * U; r0 < rows; r0 += step) {
-        uint32_t d[U][NDW];
+    for (int64_t r0 = (int64_t)blockIdx.x * S::ROWS_PER_BLOCK; r0 < rows; r0 += step) {
+        u32x4 d[U][NP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t r = r0 + u * kRowsPerPass + slot;
-            if (r < rows) {
-                load_dwords<NDW, VW>(xs + r * ROW_DW + lane * NDW, d[u]);
-            } else {
+            const int64_t g0 = r0 + (int64_t)(u * kGroups + grp) * G;   // the group's first row
 #pragma unroll
-                for (int i = 0; i < NDW; ++i) d[u][i] = 0u;
+            for (int i = 0; i < NP; ++i) {
+                if (g0 + prow[i] < rows)
+                    d[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                        xb + g0 * S::RB + (i * kGroupLanes + lane) * 16));
+                else
+                    d[u][i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t r = r0 + u * kRowsPerPass + slot;
-            float v[E];
-            R::unpack(d[u], v);
-            float ss = 0.0f;
+            const int64_t g0 = r0 + (int64_t)(u * kGroups + grp) * G;
+            float v[NP][EP];
+            float ss[G];
 #pragma unroll
-            for (int e = 0; e < E; ++e) ss = fmaf(v[e], v[e], ss);
-            // all 64 lanes take part: the xor masks stay inside each 16-lane group
-            ss += __shfl_xor(ss, 1);
-            ss += __shfl_xor(ss, 2);
-            ss += __shfl_xor(ss, 4);
-            ss += __shfl_xor(ss, 8);
-            const float inv = 1.0f / fmaxf(sqrtf(ss), eps);
+            for (int q = 0; q < G; ++q) ss[q] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[e] = silu(fmaf(v[e] * inv, g[e], b[e]));
-            uint32_t o[NDW];
-            R::pack(v, o);
-            if (r < rows) store_dwords<NDW, VW>(ys + r * ROW_DW + lane * NDW, o);
+            for (int i = 0; i < NP; ++i) {
+                PC::unpack(d[u][i], v[i]);
+                float s = 0.0f;
+#pragma unroll
+                for (int k = 0; k < EP; ++k) s = fmaf(v[i][k], v[i][k], s);
+#pragma unroll
+                for (int q = 0; q < G; ++q) ss[q] += prow[i] == q ? s : 0.0f;
+            }
+            float inv[G];
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                // all 64 lanes take part: the xor masks stay inside each 16-lane group
+                float t = ss[q];
+                t += __shfl_xor(t, 1);
+                t += __shfl_xor(t, 2);
+                t += __shfl_xor(t, 4);
+                t += __shfl_xor(t, 8);
+                inv[q] = 1.0f / fmaxf(sqrtf(t), eps);
+            }
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                float ip = inv[0];
+#pragma unroll
+                for (int q = 1; q < G; ++q) ip = prow[i] == q ? inv[q] : ip;
+#pragma unroll
+                for (int k = 0; k < EP; ++k) v[i][k] = silu(fmaf(v[i][k] * ip, g[i][k], b[i][k]));
+                if (g0 + prow[i] < rows)
+                    __builtin_nontemporal_store(PC::pack(v[i]), reinterpret_cast<u32x4 *>(
+                        yb + g0 * S::RB + (i * kGroupLanes + lane) * 16));
+            }
         }
     }
 }
 
-template <typename T, int E>
-hipError_t launch_e(const void *x, void *y, int64_t rows, int C, const float *gamma,
-                    const float *beta, float eps, hipStream_t s) {
-    // rows in flight per lane: at least ~96 bytes of loads outstanding per lane
-    constexpr int ROW_BYTES = E * (int)sizeof(T);
-    constexpr int U = ROW_BYTES >= 96 ? 1 : (96 + ROW_BYTES - 1) / ROW_BYTES > 8 ? 8
-                                                 : (96 + ROW_BYTES - 1) / ROW_BYTES;
-    const int64_t per_block = (int64_t)kRowsPerPass * U;
-    int64_t blocks = (rows + per_block - 1) / per_block;
-    // a resident grid (8 blocks of 256 threads per CU on 256 CUs) that strides over the rows
-    if (blocks > 2048) blocks = 2048;
+template <typename T, int C>
+hipError_t launch_c(const void *x, void *y, int64_t rows, const float *gamma, const float *beta,
+                    float eps, hipStream_t s) {
+    using S = Shape<T, C>;
+    int64_t blocks = (rows + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
+    if (blocks > kGridCap) blocks = kGridCap;
     if (blocks < 1) blocks = 1;
-    rmsnorm_silu_kernel<T, E, U><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-        static_cast<const T *>(x), static_cast<T *>(y), rows, gamma, beta, eps,
-        sqrtf((float)C));
+    rmsnorm_silu_kernel<T, C><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+        static_cast<const T *>(x), static_cast<T *>(y), rows, gamma, beta, eps, sqrtf((float)C));
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch(const void *x, void *y, int64_t rows, int C, const float *gamma,
                     const float *beta, float eps, hipStream_t s) {
-    switch (C / kLanesPerRow) {
-#define WANVAE_NORM_CASE(E) \
-    case E: return launch_e<T, E>(x, y, rows, C, gamma, beta, eps, s);
-        WANVAE_NORM_CASE(2) WANVAE_NORM_CASE(4) WANVAE_NORM_CASE(6) WANVAE_NORM_CASE(8)
-        WANVAE_NORM_CASE(10) WANVAE_NORM_CASE(12) WANVAE_NORM_CASE(14) WANVAE_NORM_CASE(16)
-        WANVAE_NORM_CASE(18) WANVAE_NORM_CASE(20) WANVAE_NORM_CASE(22) WANVAE_NORM_CASE(24)
-        WANVAE_NORM_CASE(26) WANVAE_NORM_CASE(28) WANVAE_NORM_CASE(30) WANVAE_NORM_CASE(32)
-        WANVAE_NORM_CASE(34) WANVAE_NORM_CASE(36) WANVAE_NORM_CASE(38) WANVAE_NORM_CASE(40)
-        WANVAE_NORM_CASE(42) WANVAE_NORM_CASE(44) WANVAE_NORM_CASE(46) WANVAE_NORM_CASE(48)
-        WANVAE_NORM_CASE(50) WANVAE_NORM_CASE(52) WANVAE_NORM_CASE(54) WANVAE_NORM_CASE(56)
-        WANVAE_NORM_CASE(58) WANVAE_NORM_CASE(60) WANVAE_NORM_CASE(62) WANVAE_NORM_CASE(64)
+    switch (C) {
+#define WANVAE_NORM_CASE(K) \
+    case 32 * K: return launch_c<T, 32 * K>(x, y, rows, gamma, beta, eps, s);
+        WANVAE_NORM_CASE(1) WANVAE_NORM_CASE(2) WANVAE_NORM_CASE(3) WANVAE_NORM_CASE(4)
+        WANVAE_NORM_CASE(5) WANVAE_NORM_CASE(6) WANVAE_NORM_CASE(7) WANVAE_NORM_CASE(8)
+        WANVAE_NORM_CASE(9) WANVAE_NORM_CASE(10) WANVAE_NORM_CASE(11) WANVAE_NORM_CASE(12)
+        WANVAE_NORM_CASE(13) WANVAE_NORM_CASE(14) WANVAE_NORM_CASE(15) WANVAE_NORM_CASE(16)
+        WANVAE_NORM_CASE(17) WANVAE_NORM_CASE(18) WANVAE_NORM_CASE(19) WANVAE_NORM_CASE(20)
+        WANVAE_NORM_CASE(21) WANVAE_NORM_CASE(22) WANVAE_NORM_CASE(23) WANVAE_NORM_CASE(24)
+        WANVAE_NORM_CASE(25) WANVAE_NORM_CASE(26) WANVAE_NORM_CASE(27) WANVAE_NORM_CASE(28)
+        WANVAE_NORM_CASE(29) WANVAE_NORM_CASE(30) WANVAE_NORM_CASE(31) WANVAE_NORM_CASE(32)
 #undef WANVAE_NORM_CASE
         default: return hipErrorInvalidValue;
     }
