@@ -65,8 +65,10 @@
 // Epilogue: each lane owns one output position and 4 consecutive output
 // channels per accumulator quad; bias, then the identity residual or the
 // shortcut bias, are added in fp32 and the result is rounded once to bf16
-// (8-byte stores).  The 1x1x1 shortcut GEMM runs as C_res/16 extra stages of
-// the same accumulators: A tile = x at the output positions, B tile = w_sc.
+// (8-byte stores).  The 1x1x1 shortcut GEMM runs as extra stages of the same
+// accumulators, each holding two 16-channel slices (one when two do not fit a
+// stage buffer) of x at the output positions and of w_sc, one 1 KB block per
+// row of positions: every load of such a stage is useful data.
 //
 // Tile order: output-channel block slowest, then batch, row block, column
 // block, and frame fastest.  Each of the 8 XCDs (workgroup index mod 8) owns a
@@ -154,6 +156,12 @@ struct Tile {
     static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
     static_assert(NWAVE + 1 <= kSyncBytes / 4, "one flag per wave");
     static constexpr int kPerCU = (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes + NWAVE * kEpiBytes);
+    // shortcut stages: SCS 16-channel slices, each HB rows of x at the output
+    // positions (one 1 KB block per row) followed by NB units of w_sc
+    static constexpr int SC_UNITS = HB * kWB + NB;                // units per slice
+    static constexpr int SCS = 2 * SC_UNITS / 32 <= BLOCKS ? 2 : 1;
+    static constexpr int SC_BLOCKS = SCS * SC_UNITS / 32;         // useful loads per stage
+    static_assert(SC_BLOCKS <= BLOCKS, "a shortcut slice fits a stage buffer");
 };
 
 // byte offset of half `h` (0/1) of A unit (row r, column c) and of B unit u
@@ -257,7 +265,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         const int kt_begin = (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
         ti.kt_begin = kt_begin;
         ti.s_conv = (3 - kt_begin) * ck;
-        ti.s_total = ti.s_conv + (EPI == EPI_SHORTCUT ? a.cres / kKC : 0);
+        ti.s_total = ti.s_conv + (EPI == EPI_SHORTCUT ? a.cres / (kKC * TL::SCS) : 0);
         return ti;
     };
 
@@ -272,23 +280,42 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         const uint32_t tap2 = (uint32_t)a.cout * kUnit;   // bytes per tap of a packed stage
         // byte offset of block b's piece for a conv stage (sc = false) or a
         // shortcut stage (sc = true: x at the output positions, w_sc as one tap)
-        auto block_off = [&](const TileInfo &ti, int b, bool sc) -> uint32_t {
+        auto block_off = [&](const TileInfo &ti, int b) -> uint32_t {
             if (b < TL::A_BLOCKS) {
                 const int u = b * 32 + (lane >> 1);
                 const int r = u / kAS, c = u % kAS;
                 const int hf = (lane & 1) ^ ((c >> 3) & 1);
                 const int hh = ti.h0 - 1 + r, ww = ti.w0 - 1 + c;
                 const bool inside = r < TL::AR && hh >= 0 && hh < H && ww >= 0 && ww < W;
-                if (!sc) return inside ? (uint32_t)(hh * W + ww) * cs2 + hf * 16 : kOOB;
-                return inside && r >= 1 && r <= HB && c >= 1 && c <= kWB
-                           ? (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + hf * 16
-                           : kOOB;
+                return inside ? (uint32_t)(hh * W + ww) * cs2 + hf * 16 : kOOB;
             }
             const int u = (b - TL::A_BLOCKS) * 32 + (lane >> 1);
             const int hf = (lane & 1) ^ ((u >> 3) & 1);
             const int tap = u / NB, nl = u % NB;
-            if (!sc) return (uint32_t)tap * tap2 + (uint32_t)(ti.n0 + nl) * kUnit + hf * 16;
-            return tap == 0 ? (uint32_t)((ti.n0 + nl) * a.cres * 2) + hf * 16 : kOOB;
+            return (uint32_t)tap * tap2 + (uint32_t)(ti.n0 + nl) * kUnit + hf * 16;
+        };
+        // shortcut stage: block b is row b of slice j's x (at the output
+        // positions) or a piece of slice j's w_sc; j selects the 16 channels
+        // 32 bytes further on.  Blocks past the useful ones load zeros into
+        // the unused tail of the buffer, so every stage issues BLOCKS loads
+        // (the vmcnt accounting counts whole stages).  Returns the offset and
+        // whether it is relative to the w_sc resource.
+        auto sc_block_off = [&](const TileInfo &ti, int b, bool &from_w) -> uint32_t {
+            constexpr int SB = TL::SC_UNITS / 32;   // blocks per slice
+            from_w = false;
+            if (b >= TL::SC_BLOCKS) return kOOB;
+            const int j = b / SB, bb = b % SB;
+            const int c = lane >> 1;
+            if (bb < HB) {
+                const int hf = (lane & 1) ^ ((c >> 3) & 1);
+                const int hh = ti.h0 + bb, ww = ti.w0 + c;
+                return hh < H && ww < W ? (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + j * kUnit + hf * 16
+                                        : kOOB;
+            }
+            from_w = true;
+            const int nl = (bb - HB) * 32 + c;
+            const int hf = (lane & 1) ^ ((nl >> 3) & 1);
+            return (uint32_t)((ti.n0 + nl) * a.cres * 2) + j * kUnit + hf * 16;
         };
 
         // request cursor: stage si of local tile it (tile x_begin + it), ring slot
@@ -299,7 +326,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         auto start_tile = [&]() {
             ti = decode(x_begin + it);
 #pragma unroll
-            for (int b = 0; b < TL::BLOCKS; ++b) l_off[b] = block_off(ti, b, false);
+            for (int b = 0; b < TL::BLOCKS; ++b) l_off[b] = block_off(ti, b);
         };
         if (it < x_count) start_tile();
 
@@ -322,7 +349,8 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                 bbase = a.w + wskip;
                 bbytes = (uint32_t)(((int64_t)27 * a.cin * a.cout - wskip) * 2);
             } else {
-                const int cc = si - ti.s_conv;
+                // first 16-channel slice of this shortcut stage
+                const int cc = (si - ti.s_conv) * TL::SCS;
                 abase = a.res + ((ti.nq * a.T + ti.tq) * HW) * a.cres + cc * kKC;
                 abytes = (uint32_t)(HW * a.cres * 2 - cc * kKC * 2);
                 bbase = a.wsc + cc * kKC;
@@ -335,9 +363,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 #pragma unroll
             for (int b = 0; b < TL::BLOCKS; ++b) {
                 uint32_t off = l_off[b];
+                bool from_b = b >= TL::A_BLOCKS;
                 if constexpr (EPI == EPI_SHORTCUT)
-                    if (sc) off = block_off(ti, b, true);
-                lds_dma16(b < TL::A_BLOCKS ? ar : br, base + b * 1024, off);
+                    if (sc) off = sc_block_off(ti, b, from_b);
+                lds_dma16(from_b ? br : ar, base + b * 1024, off);
             }
             slot = slot + 1 == NBUF ? 0 : slot + 1;
             if (++si == ti.s_total) {
@@ -462,17 +491,25 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         }
     };
 
-    // One shortcut stage: the centre position of each output row, w_sc as the only tap.
+    // One shortcut stage: SCS slices of 16 channels, each x at this wave's
+    // output rows times that slice of w_sc.
+    auto ldU = [&](const unsigned char *buf, int u) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + b_off(u, g)));
+    };
     auto compute_shortcut = [&](const unsigned char *buf) {
-        bf16x8 fw[FN];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) fw[fn] = ldB(buf, 0, fn);
+        for (int j = 0; j < TL::SCS; ++j) {
+            const int u0 = j * TL::SC_UNITS;
+            bf16x8 fw[FN];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const bf16x8 fx = ldA(buf, fm + 1, 1);
+            for (int fn = 0; fn < FN; ++fn) fw[fn] = ldU(buf, u0 + HB * kWB + wn * FN * 32 + fn * 32 + l32);
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fn], fx, acc[fm][fn], 0, 0, 0);
+            for (int fm = 0; fm < FM; ++fm) {
+                const bf16x8 fx = ldU(buf, u0 + (wm * FM + fm) * kWB + l32);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fn], fx, acc[fm][fn], 0, 0, 0);
+            }
         }
     };
 
