@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -27,21 +28,44 @@ COMMON = ["-O3", "-std=c++20", "-fPIC", "-fvisibility=hidden", f"-I{INCLUDE}", f
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def check_resources(src: str, remarks: str) -> None:
+    """Fails the build if a kernel of `src` spills registers or uses scratch
+    memory: every kernel here is meant to keep its working set in registers
+    and LDS, and scratch traffic in an MFMA loop costs an order of magnitude."""
+    bad, name = [], "?"
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
+        if m and int(m.group(2)) > 0 and not (m.group(1) == "SGPRs Spill" and int(m.group(2)) <= 32):
+            bad.append(f"{name}: {m.group(1)} = {m.group(2)}")
+    if bad:
+        raise RuntimeError(f"{src}: kernels spill or use scratch:\n" + "\n".join(bad))
+
+
 def _compile(src: str, verbose: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(OBJDIR, src + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE + ["-c", path, "-o", obj]
+    cmd = [HIPCC] + COMMON + DEVICE + [RESOURCE_REMARKS, "-c", path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON + ["-x", "hip"] + DEVICE + ["-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "kernel-resource-usage")
+    out = r.stdout + r.stderr
+    msgs = "\n".join(l for l in out.splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{msgs}")
     if msgs.strip() and verbose:
         print(msgs)
+    if src.endswith(".hip"):
+        check_resources(src, out)
     return obj
 
 

@@ -151,11 +151,17 @@ struct Tile {
     static constexpr int B_BLOCKS = 9 * NB / 32;
     static constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;       // load instructions per stage
     static constexpr int STAGE_BYTES = BLOCKS * 1024;
-    static constexpr int kLds = 160 * 1024 - kSyncBytes - NWAVE * kEpiBytes;
+    // FN > 1: each wave owns several channel blocks and walks the taps kh by kh
+    // (9 FN weight fragments in registers would not fit beside the
+    // accumulators), and the bias sits in LDS instead of registers
+    static constexpr bool KH_OUTER = FN > 1;
+    static constexpr int kBiasBytes = KH_OUTER ? 4 * 1024 : 0;   // [cout] fp32, cout <= 1024
+    static constexpr int kLds = 160 * 1024 - kSyncBytes - NWAVE * kEpiBytes - kBiasBytes;
     static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
     static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
     static_assert(NWAVE + 1 <= kSyncBytes / 4, "one flag per wave");
-    static constexpr int kPerCU = (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes + NWAVE * kEpiBytes);
+    static constexpr int kPerCU =
+        (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes + NWAVE * kEpiBytes + kBiasBytes);
     // shortcut stages: SCS 16-channel slices, each HB rows of x at the output
     // positions (one 1 KB block per row) followed by NB units of w_sc
     static constexpr int SC_UNITS = HB * kWB + NB;                // units per slice
@@ -223,6 +229,8 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // sync[0]: stages landed (load wave); sync[1 + w]: stages consumed by MFMA wave w
     __shared__ int sync[kSyncBytes / 4];
     __shared__ __attribute__((aligned(16))) unsigned char epi_stage[TL::NWAVE * kEpiBytes];
+    // bias (+ shortcut bias) of every output channel, for the KH_OUTER tiles
+    __shared__ __attribute__((aligned(16))) float bias_lds[TL::kBiasBytes / 4 > 0 ? TL::kBiasBytes / 4 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -232,6 +240,14 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int ck = a.cin / kKC;
 
     if (tid <= TL::NWAVE) sync[tid] = 0;
+    if constexpr (TL::KH_OUTER) {
+        for (int c = tid; c < a.cout; c += TL::kThreads) {
+            float b = a.bias ? a.bias[c] : 0.0f;
+            if constexpr (EPI == EPI_SHORTCUT)
+                if (a.bsc) b += a.bsc[c];
+            bias_lds[c] = b;
+        }
+    }
     __syncthreads();
     // flag accesses: relaxed atomics on the LDS array itself, so they stay
     // ds_read / ds_write (through a generic pointer they would become FLAT
@@ -251,7 +267,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int64_t x_begin = a.tiles * wg_before / nwg;
     const int64_t x_count = a.tiles * (wg_before + wg_x) / nwg - x_begin;
 
-    auto decode = [&](int64_t tile) {
+    auto decode = [&](int64_t tile) __attribute__((always_inline)) {
         TileInfo ti;
         ti.tq = tile % a.T;
         tile /= a.T;
@@ -280,7 +296,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         const uint32_t tap2 = (uint32_t)a.cout * kUnit;   // bytes per tap of a packed stage
         // byte offset of block b's piece for a conv stage (sc = false) or a
         // shortcut stage (sc = true: x at the output positions, w_sc as one tap)
-        auto block_off = [&](const TileInfo &ti, int b) -> uint32_t {
+        auto block_off = [&](const TileInfo &ti, int b) __attribute__((always_inline)) -> uint32_t {
             if (b < TL::A_BLOCKS) {
                 const int u = b * 32 + (lane >> 1);
                 const int r = u / kAS, c = u % kAS;
@@ -300,7 +316,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // the unused tail of the buffer, so every stage issues BLOCKS loads
         // (the vmcnt accounting counts whole stages).  Returns the offset and
         // whether it is relative to the w_sc resource.
-        auto sc_block_off = [&](const TileInfo &ti, int b, bool &from_w) -> uint32_t {
+        auto sc_block_off = [&](const TileInfo &ti, int b, bool &from_w) __attribute__((always_inline)) -> uint32_t {
             constexpr int SB = TL::SC_UNITS / 32;   // blocks per slice
             from_w = false;
             if (b >= TL::SC_BLOCKS) return kOOB;
@@ -323,7 +339,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         int64_t it = loc;
         int si = 0, slot = 0;
         uint32_t l_off[TL::BLOCKS];   // conv-stage offsets of the cursor's tile
-        auto start_tile = [&]() {
+        auto start_tile = [&]() __attribute__((always_inline)) {
             ti = decode(x_begin + it);
 #pragma unroll
             for (int b = 0; b < TL::BLOCKS; ++b) l_off[b] = block_off(ti, b);
@@ -377,7 +393,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         };
 
         // the slowest MFMA wave's consumed-stage count
-        auto min_done = [&]() {
+        auto min_done = [&]() __attribute__((always_inline)) {
             int m = flag_read(1);
 #pragma unroll
             for (int w = 1; w < TL::NWAVE; ++w) {
@@ -438,11 +454,11 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 #pragma unroll
     for (int kw = 0; kw < 3; ++kw) a_rd[kw] = a_off(wm * FM, l32 + kw, g);
 
-    auto ldA = [&](const unsigned char *buf, int qr, int kw) {
+    auto ldA = [&](const unsigned char *buf, int qr, int kw) __attribute__((always_inline)) {
         const int off = a_rd[kw] + qr * kAS * kUnit;
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
     };
-    auto ldB = [&](const unsigned char *buf, int tap, int fn) {
+    auto ldB = [&](const unsigned char *buf, int tap, int fn) __attribute__((always_inline)) {
         const int off = b_rd0 + (tap * NB + fn * 32) * kUnit;
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
     };
@@ -453,7 +469,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // reads complete in order, so they are issued in the order of first use:
     // input row 0 and the kh = 0 weights, then the kh = 1 weights and row 1
     // (used from row group 1 on), then the kh = 2 weights (row group 2).
-    auto compute_conv = [&](const unsigned char *buf) {
+    auto compute_conv = [&](const unsigned char *buf) __attribute__((always_inline)) {
         bf16x8 fw[9][FN];
         bf16x8 fx[2][3];
 #pragma unroll
@@ -491,12 +507,53 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         }
     };
 
+    // The same stage for KH_OUTER tiles: for each kh, the 3 kw x FN weight
+    // fragments of that kernel row, then each output row fm with input row
+    // fm + kh.  The next input row is read while the current one computes,
+    // and the weights of kh + 1 replace those of kh, kw by kw, during the last
+    // row of kh.
+    auto compute_conv_kh = [&](const unsigned char *buf) __attribute__((always_inline)) {
+        bf16x8 fw[3][FN];
+        bf16x8 fx[2][3];
+#pragma unroll
+        for (int kw = 0; kw < 3; ++kw) fx[0][kw] = ldA(buf, 0, kw);
+#pragma unroll
+        for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) fw[kw][fn] = ldB(buf, kw, fn);
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int cur = (kh * FM + fm) & 1;
+                const bool last_row = fm + 1 == FM;
+                if (!(kh == 2 && last_row)) {
+                    const int nr = last_row ? kh + 1 : fm + 1 + kh;   // next iteration's input row
+#pragma unroll
+                    for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(buf, nr, kw);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kw = 0; kw < 3; ++kw) {
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kw][fn], fx[cur][kw],
+                                                                              acc[fm][fn], 0, 0, 0);
+                    if (last_row && kh < 2) {
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn) fw[kw][fn] = ldB(buf, (kh + 1) * 3 + kw, fn);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    };
+
     // One shortcut stage: SCS slices of 16 channels, each x at this wave's
     // output rows times that slice of w_sc.
-    auto ldU = [&](const unsigned char *buf, int u) {
+    auto ldU = [&](const unsigned char *buf, int u) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + b_off(u, g)));
     };
-    auto compute_shortcut = [&](const unsigned char *buf) {
+    auto compute_shortcut = [&](const unsigned char *buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < TL::SCS; ++j) {
             const int u0 = j * TL::SC_UNITS;
@@ -515,7 +572,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
     int consumed = 0, seen = 0, slot = 0;
     // wait until stage `consumed` has landed
-    auto wait_landed = [&]() {
+    auto wait_landed = [&]() __attribute__((always_inline)) {
         for (int spin = 0; seen <= consumed && spin < kSpinCap; ++spin) {
             seen = flag_read(0);
             if (seen <= consumed) __builtin_amdgcn_s_sleep(1);
@@ -524,7 +581,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     };
     // stage consumed: its reads were issued (and, LDS being in order, execute)
     // before this flag write
-    auto release = [&]() {
+    auto release = [&]() __attribute__((always_inline)) {
         compiler_fence();
         ++consumed;
         if (lane == 0) flag_write(1 + wave, consumed);
@@ -536,9 +593,9 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
         // bias (+ shortcut bias) of this lane's output channels: requested now,
         // first used in the epilogue, so the K loop hides the latency
-        float bsum[FN][4][4];
+        float bsum[TL::KH_OUTER ? 1 : FN][4][4];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+        for (int fn = 0; fn < (TL::KH_OUTER ? 0 : FN); ++fn)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int co = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
@@ -563,7 +620,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
         for (int s = 0; s < ti.s_conv; ++s) {
             wait_landed();
-            compute_conv(smem + slot * TL::STAGE_BYTES);
+            if constexpr (TL::KH_OUTER)
+                compute_conv_kh(smem + slot * TL::STAGE_BYTES);
+            else
+                compute_conv(smem + slot * TL::STAGE_BYTES);
             release();
         }
         if constexpr (EPI == EPI_SHORTCUT) {
@@ -585,7 +645,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         const int64_t frame = ti.nq * a.T + ti.tq;
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y + frame * HW * a.cout, HW * a.cout * 2);
         const int cbase = ti.n0 + wn * FN * 32 + 4 * g;   // this lane's first channel
-        auto pos_off = [&](int fm, int cstride) -> uint32_t {
+        auto pos_off = [&](int fm, int cstride) __attribute__((always_inline)) -> uint32_t {
             const int hh = ti.h0 + wm * FM + fm, ww = ti.w0 + l32;
             return hh < H && ww < W ? (uint32_t)((hh * W + ww) * cstride + cbase) * 2 : kOOB;
         };
@@ -595,7 +655,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // position, and stored as 64 contiguous bytes per position, so a store
         // touches 16 cache lines instead of 32 and there are half as many.
         unsigned char *const epi = epi_stage + wave * kEpiBytes;
-        auto store_rows = [&](int f0, int nrows, const u32x2 (*res)[FN][4]) {
+        auto store_rows = [&](int f0, int nrows, const u32x2 (*res)[FN][4]) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < nrows; ++e) {
                 const int hh = ti.h0 + wm * FM + f0 + e;
@@ -605,7 +665,15 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     for (int j = 0; j < 4; ++j) {
                         float v[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) v[q] = acc[f0 + e][fn][4 * j + q] + bsum[fn][j][q];
+                        for (int q = 0; q < 4; ++q) v[q] = acc[f0 + e][fn][4 * j + q];
+                        if constexpr (TL::KH_OUTER) {
+                            const float4 bv = *reinterpret_cast<const float4 *>(
+                                bias_lds + ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g);
+                            v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) v[q] += bsum[fn][j][q];
+                        }
                         if (res != nullptr) {
                             const u32x2 r = res[e][fn][j];
                             v[0] += bf16_bits_to_f32(r.x & 0xffffu);
@@ -637,7 +705,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             constexpr int NG = (FM + EG - 1) / EG;
             const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.res + frame * HW * a.cres, HW * a.cres * 2);
             u32x2 rv[2][EG][FN][4];
-            auto load_group = [&](int gi) {
+            auto load_group = [&](int gi) __attribute__((always_inline)) {
 #pragma unroll
                 for (int e = 0; e < group_rows<FM, EG>(gi); ++e) {
                     const uint32_t off = pos_off(gi * EG + e, a.cres);
@@ -653,7 +721,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             // group GI has landed once at most the VMEM operations issued
             // after its loads are outstanding: the stores of group GI - 1 and
             // the loads of group GI + 1 (an immediate, hence the template)
-            auto step = [&]<int GI>() {
+            auto step = [&]<int GI>() __attribute__((always_inline)) {
                 constexpr int kAfter = (GI >= 1 ? group_rows<FM, EG>(GI - 1) * FN * 4 : 0) +
                                        (GI + 1 < NG ? group_rows<FM, EG>(GI + 1) * FN * 4 : 0);
                 static_assert(kAfter <= 63, "vmcnt counts to 63");
@@ -744,23 +812,25 @@ bool conv3d_bf16_supported(int cin, int cout) {
 // Rows a tile height computes for an image height (the last tile is padded).
 int64_t rows_computed(int64_t h, int hb) { return (h + hb - 1) / hb * hb; }
 
-// Tile choice (measured on the workload shapes): a 2 x 2 grid of MFMA waves,
-// each 8 or 9 rows x 32 columns x 32 channels (128 or 144 accumulators), plus
-// the load wave; a 2 x 3 grid (96 channels) when C_out is a multiple of 96
-// but not of 64; 16 rows x 32 channels from four 4-row waves otherwise.  The
-// 18-row tile is taken unless it pads more rows than the 16-row one (every
-// decoder resolution, 90 x 160 up to 720 x 1280, is a multiple of 18 rows).
+// Tile choice (measured on the workload shapes):
+//  - C_out a multiple of 64: a 2 x 2 grid of MFMA waves, each 8 or 9 rows x 32
+//    columns x 32 channels (128 or 144 accumulators), plus the load wave.  The
+//    18-row tile is taken unless it pads more rows than the 16-row one (every
+//    decoder resolution, 90 x 160 up to 720 x 1280, is a multiple of 18 rows).
+//  - other multiples of 96: four MFMA waves of 3 rows x 96 channels (one wave
+//    per SIMD; a 2 x 3 grid of 32-channel waves puts two waves on two of the
+//    four SIMDs and one on the others, and measured 7% slower).
+//  - other multiples of 32: four waves of 4 rows x 32 channels.
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
     const bool tall = rows_computed(c.h, 18) <= rows_computed(c.h, 16);
     if (c.res != nullptr && c.wsc != nullptr) {
         if (c.cout % 64 == 0)
             return tall ? launch_cfg<2, 2, 9, 1, EPI_SHORTCUT>(c, s) : launch_cfg<2, 2, 8, 1, EPI_SHORTCUT>(c, s);
-        if (c.cout % 96 == 0)
-            return tall ? launch_cfg<2, 3, 9, 1, EPI_SHORTCUT>(c, s) : launch_cfg<2, 3, 8, 1, EPI_SHORTCUT>(c, s);
+        if (c.cout % 96 == 0) return launch_cfg<4, 1, 3, 3, EPI_SHORTCUT>(c, s);
         return launch_cfg<4, 1, 4, 1, EPI_SHORTCUT>(c, s);
     }
     if (c.cout % 64 == 0) return tall ? launch_plain<2, 2, 9, 1>(c, s) : launch_plain<2, 2, 8, 1>(c, s);
-    if (c.cout % 96 == 0) return tall ? launch_plain<2, 3, 9, 1>(c, s) : launch_plain<2, 3, 8, 1>(c, s);
+    if (c.cout % 96 == 0) return launch_plain<4, 1, 3, 3>(c, s);
     return launch_plain<4, 1, 4, 1>(c, s);
 }
 

@@ -31,6 +31,7 @@ constexpr int kGroupLanes = 16;
 constexpr int kThreads = 256;
 constexpr int kGroups = kThreads / kGroupLanes;   // 16-lane groups per block
 constexpr int kGridCap = 16384;                   // blocks; the grid strides over the rows
+constexpr int kNoRow = 1 << 20;                   // row index of a ragged group's empty pieces
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -75,13 +76,22 @@ template <> struct Piece<uint16_t> {  // bf16 bits
 template <typename T, int C>
 struct Shape {
     static constexpr int RB = C * (int)sizeof(T);          // row bytes
-    static constexpr int G = 256 / gcd(256, RB);           // rows per 16-lane group
-    static constexpr int NP = G * RB / 256;                // 16-byte pieces per lane
+    static constexpr int G0 = 256 / gcd(256, RB);          // fewest rows spanning whole runs
+    // Channel counts whose G0 rows would give a lane more than 16 pieces
+    // (odd multiples of 32 above 512) take one row per group instead, its last
+    // 256-byte run only partly used ("ragged": some lanes own one piece less).
+    static constexpr bool RAGGED = G0 * RB / 256 > 16;
+    static constexpr int G = RAGGED ? 1 : G0;              // rows per 16-lane group
+    static constexpr int NP = RAGGED ? (RB + 255) / 256 : G * RB / 256;   // 16-byte pieces per lane
     static constexpr int EP = Piece<T>::EP;                // elements per piece
     // groups of rows in flight per lane: about 96 bytes of loads or more
     static constexpr int U = NP * 16 >= 96 ? 1 : (96 + NP * 16 - 1) / (NP * 16) > 8 ? 8
                                                     : (96 + NP * 16 - 1) / (NP * 16);
     static constexpr int ROWS_PER_BLOCK = kGroups * G * U;  // per pass of the grid-stride loop
+    // gamma, beta and the unpacked values of a lane's pieces stay in registers
+    // when there are few; otherwise (channel counts with many pieces per lane)
+    // gamma and beta are re-read from the cache and the pieces unpacked twice
+    static constexpr bool IN_REGS = NP * EP <= 48;
 };
 
 template <typename T, int C>
@@ -103,11 +113,14 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
         const int byte = (i * kGroupLanes + lane) * 16;
         prow[i] = G == 1 ? 0 : byte / S::RB;
         pch[i] = (byte % S::RB) / (int)sizeof(T);
+        // a ragged group's pieces past the row: no data, channel 0's gamma
+        if (S::RAGGED && byte >= S::RB) prow[i] = kNoRow, pch[i] = 0;
     }
     // gamma * sqrt(C) and beta of those channels, loaded once
-    float g[NP][EP], b[NP][EP];
+    constexpr int NR = S::IN_REGS ? NP : 1;
+    float g[NR][EP], b[NR][EP];
 #pragma unroll
-    for (int i = 0; i < NP; ++i)
+    for (int i = 0; i < (S::IN_REGS ? NP : 0); ++i)
 #pragma unroll
         for (int k = 0; k < EP; k += 4) {
             const float4 gv = *reinterpret_cast<const float4 *>(gamma + pch[i] + k);
@@ -129,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
             const int64_t g0 = r0 + (int64_t)(u * kGroups + grp) * G;   // the group's first row
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                if (g0 + prow[i] < rows)
+                if ((!S::RAGGED || prow[i] != kNoRow) && g0 + prow[i] < rows)
                     d[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
                         xb + g0 * S::RB + (i * kGroupLanes + lane) * 16));
                 else
@@ -139,16 +152,17 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t g0 = r0 + (int64_t)(u * kGroups + grp) * G;
-            float v[NP][EP];
+            float v[NR][EP];
             float ss[G];
 #pragma unroll
             for (int q = 0; q < G; ++q) ss[q] = 0.0f;
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                PC::unpack(d[u][i], v[i]);
+                float (&vi)[EP] = v[S::IN_REGS ? i : 0];
+                PC::unpack(d[u][i], vi);
                 float s = 0.0f;
 #pragma unroll
-                for (int k = 0; k < EP; ++k) s = fmaf(v[i][k], v[i][k], s);
+                for (int k = 0; k < EP; ++k) s = fmaf(vi[k], vi[k], s);
 #pragma unroll
                 for (int q = 0; q < G; ++q) ss[q] += prow[i] == q ? s : 0.0f;
             }
@@ -168,10 +182,25 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
                 float ip = inv[0];
 #pragma unroll
                 for (int q = 1; q < G; ++q) ip = prow[i] == q ? inv[q] : ip;
+                float (&vi)[EP] = v[S::IN_REGS ? i : 0];
+                if constexpr (S::IN_REGS) {
 #pragma unroll
-                for (int k = 0; k < EP; ++k) v[i][k] = silu(fmaf(v[i][k] * ip, g[i][k], b[i][k]));
-                if (g0 + prow[i] < rows)
-                    __builtin_nontemporal_store(PC::pack(v[i]), reinterpret_cast<u32x4 *>(
+                    for (int k = 0; k < EP; ++k) vi[k] = silu(fmaf(vi[k] * ip, g[i][k], b[i][k]));
+                } else {
+                    PC::unpack(d[u][i], vi);
+#pragma unroll
+                    for (int k = 0; k < EP; k += 4) {
+                        const float4 gv = *reinterpret_cast<const float4 *>(gamma + pch[i] + k);
+                        const float4 bv = beta ? *reinterpret_cast<const float4 *>(beta + pch[i] + k)
+                                               : float4{0.f, 0.f, 0.f, 0.f};
+                        vi[k] = silu(fmaf(vi[k] * ip, gv.x * sqrt_c, bv.x));
+                        vi[k + 1] = silu(fmaf(vi[k + 1] * ip, gv.y * sqrt_c, bv.y));
+                        vi[k + 2] = silu(fmaf(vi[k + 2] * ip, gv.z * sqrt_c, bv.z));
+                        vi[k + 3] = silu(fmaf(vi[k + 3] * ip, gv.w * sqrt_c, bv.w));
+                    }
+                }
+                if ((!S::RAGGED || prow[i] != kNoRow) && g0 + prow[i] < rows)
+                    __builtin_nontemporal_store(PC::pack(vi), reinterpret_cast<u32x4 *>(
                         yb + g0 * S::RB + (i * kGroupLanes + lane) * 16));
             }
         }

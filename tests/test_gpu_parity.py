@@ -45,7 +45,9 @@ def tol(dt):
 
 # --------------------------------------------------------------------------- norm
 @pytest.mark.parametrize("dt", [wl.F32, wl.BF16])
-@pytest.mark.parametrize("C", [32, 64, 96, 192, 384, 1024])
+# 544 and 992: one row per 16-lane group with a partly used last run (odd
+# multiples of 32 above 512); 1024: the widest row
+@pytest.mark.parametrize("C", [32, 64, 96, 192, 384, 544, 992, 1024])
 @pytest.mark.parametrize("rows", [1, 17, 70001])
 def test_rmsnorm_silu(torch, wv, dt, C, rows):
     rng = np.random.default_rng(C * 1000 + rows)
@@ -91,6 +93,9 @@ CONV_SHAPES = [
     (1, 3, 36, 40, 64, 128),     # 2 x 18 rows, 64-channel blocks
     (2, 2, 35, 33, 96, 96),      # 35 rows: one 18-row tile padded by one row; Cout 96
     (1, 4, 18, 64, 192, 192),    # one 18-row tile, 3 channel blocks
+    # C_out a multiple of 96 but not 64: 12-row tiles of 96 channels
+    (1, 2, 13, 40, 96, 288),     # 3 channel blocks, ragged H (13 = 12 + 1) and W
+    (1, 3, 24, 32, 32, 96),      # exact tiles, smallest input slice count
 ]
 
 
@@ -169,6 +174,7 @@ SMALL_BLOCKS = [
     # 18-row tiles: identity and 1x1x1-shortcut epilogues, 64- and 96-channel tiles
     wl.custom("id128_h36", wl.BF16, 1, 3, 36, 40, 128, 128),
     wl.custom("sc192_96_h35", wl.BF16, 1, 3, 35, 40, 192, 96),
+    wl.custom("sc96_288", wl.BF16, 1, 3, 13, 36, 96, 288),   # 96-channel tiles, 3 blocks, shortcut
 ]
 
 
