@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--cpu-frames", type=int, default=4,
                     help="frames of the clip the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, copy a MIB-MiB buffer 3 times (a plain copy "
+                         "kernel of known size, to scale HBM byte counters by)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -161,6 +164,15 @@ def main():
                  "avg_launch_ms": norm_avg_ms, "launches": n_norm},
         "cpu_baseline": None,
     }
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 copies of {nbytes} bytes", file=sys.stderr, flush=True)
+        del src, dst
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline on {args.cpu_frames} frame(s) ...", file=sys.stderr,
               flush=True)

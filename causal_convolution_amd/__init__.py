@@ -278,7 +278,9 @@ class ResBlock:
         return y
 
     def new_caches(self, n, h, w, device="cuda"):
-        """Zero caches for a fresh stream: ([n,2,h,w,in_dim], [n,2,h,w,out_dim])."""
+        """Zero caches for a fresh stream, n*2*h*w*in_dim and n*2*h*w*out_dim
+        elements shaped [n,2,h,w,C].  Their contents are the library's own
+        conv-input frames (16-channel slices for bf16), opaque to callers."""
         torch = _torch()
         return (torch.zeros((n, 2, h, w, self.in_dim), dtype=self.dtype, device=device),
                 torch.zeros((n, 2, h, w, self.out_dim), dtype=self.dtype, device=device))

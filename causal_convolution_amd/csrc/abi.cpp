@@ -128,6 +128,17 @@ int run_norm(const void *x, void *y, int64_t rows, int C, const float *g, const 
     });
 }
 
+// Norm into the conv input layout: 16-channel slices per frame for bf16 (the
+// MFMA conv reads whole cache lines of them), channels-last for fp32.
+int run_norm_conv_input(const void *x, void *y, int64_t rows, int C, int64_t hw, const float *g,
+                        const float *b, float eps, int32_t dt, hipStream_t s) {
+    if (dt != WANVAE_BF16) return run_norm(x, y, rows, C, g, b, eps, dt, s);
+    if (rows == 0) return WANVAE_OK;
+    return timed_launch(WANVAE_KERNEL_NORM, s, "rmsnorm_silu", [&] {
+        return wanvae::launch_rmsnorm_silu_bf16_sliced(x, y, rows, C, hw, g, b, eps, s);
+    });
+}
+
 int run_conv(const wanvae::ConvLaunch &c, int32_t dt, hipStream_t s) {
     if (c.n * c.t * c.h * c.w_ == 0) return WANVAE_OK;
     if (dt == WANVAE_BF16)
@@ -182,9 +193,13 @@ int check_params(const wanvae_resblock_params *p) {
     return WANVAE_OK;
 }
 
+// Workspace: [conv input region | conv A output a].  The conv input region
+// holds n1 (the conv A input), then n2 (the conv B input) once conv A has
+// consumed n1: P * max(in_dim, out_dim) elements.  bf16 writes n1 and n2 in
+// the sliced conv input layout; fp32 normalises a in place into n2.
 struct Plan {
     int64_t P = 0;
-    size_t x_bytes = 0, y_bytes = 0, n1_off = 0, n1_bytes = 0, a_off = 0, a_bytes = 0, total = 0;
+    size_t x_bytes = 0, y_bytes = 0, n_off = 0, n_bytes = 0, a_off = 0, a_bytes = 0, total = 0;
 };
 
 int plan_block(const wanvae_resblock_params *p, const wanvae_dims *d, Plan *pl) {
@@ -195,9 +210,9 @@ int plan_block(const wanvae_resblock_params *p, const wanvae_dims *d, Plan *pl) 
     const size_t es = esize(p->dtype);
     pl->x_bytes = (size_t)pl->P * p->in_dim * es;
     pl->y_bytes = (size_t)pl->P * p->out_dim * es;
-    pl->n1_off = 0;
-    pl->n1_bytes = pl->x_bytes;
-    pl->a_off = round_up(pl->n1_bytes);
+    pl->n_off = 0;
+    pl->n_bytes = pl->x_bytes > pl->y_bytes ? pl->x_bytes : pl->y_bytes;
+    pl->a_off = round_up(pl->n_bytes);
     pl->a_bytes = pl->y_bytes;
     pl->total = pl->a_off + round_up(pl->a_bytes);
     return WANVAE_OK;
@@ -318,12 +333,17 @@ int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void
     if (int r = check_block_buffers(p, pl, x, y, workspace, ws_bytes)) return r;
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
-    void *n1 = ws + pl.n1_off;
+    void *n1 = ws + pl.n_off;
     void *a = ws + pl.a_off;
+    const bool sliced = p->dtype == WANVAE_BF16;
+    void *n2 = sliced ? n1 : a;
+    const int64_t hw = d->h * d->w;
 
-    if (int r = run_norm(x, n1, pl.P, p->in_dim, p->gamma1, p->beta1, p->eps, p->dtype, s)) return r;
+    if (int r = run_norm_conv_input(x, n1, pl.P, p->in_dim, hw, p->gamma1, p->beta1, p->eps, p->dtype, s))
+        return r;
     wanvae::ConvLaunch ca;
     ca.x = n1;
+    ca.x_sliced = sliced;
     ca.w = p->w_a;
     ca.bias = p->b_a;
     ca.y = a;
@@ -334,9 +354,10 @@ int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void
     ca.cin = p->in_dim;
     ca.cout = p->out_dim;
     if (int r = run_conv(ca, p->dtype, s)) return r;
-    if (int r = run_norm(a, a, pl.P, p->out_dim, p->gamma2, p->beta2, p->eps, p->dtype, s)) return r;
+    if (int r = run_norm_conv_input(a, n2, pl.P, p->out_dim, hw, p->gamma2, p->beta2, p->eps, p->dtype, s))
+        return r;
     wanvae::ConvLaunch cb = ca;
-    cb.x = a;
+    cb.x = n2;
     cb.w = p->w_b;
     cb.bias = p->b_b;
     cb.res = x;
@@ -373,13 +394,18 @@ int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_c
              WANVAE_ERR_ALIAS, "caches overlap each other, x, y or the workspace");
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
-    void *n1 = ws + pl.n1_off;
+    void *n1 = ws + pl.n_off;
     void *a = ws + pl.a_off;
+    const bool sliced = p->dtype == WANVAE_BF16;
+    void *n2 = sliced ? n1 : a;
+    const int64_t hw = d->h * d->w;
 
-    if (int r = run_norm(x_chunk, n1, pl.P, p->in_dim, p->gamma1, p->beta1, p->eps, p->dtype, s))
+    if (int r = run_norm_conv_input(x_chunk, n1, pl.P, p->in_dim, hw, p->gamma1, p->beta1, p->eps,
+                                    p->dtype, s))
         return r;
     wanvae::ConvLaunch ca;
     ca.x = n1;
+    ca.x_sliced = sliced;
     ca.cache = cache_a;
     ca.w = p->w_a;
     ca.bias = p->b_a;
@@ -395,9 +421,12 @@ int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_c
             return wanvae::launch_roll_cache(cache_a, n1, d->n, d->t, (int64_t)slab_a, s);
         }))
         return r;
-    if (int r = run_norm(a, a, pl.P, p->out_dim, p->gamma2, p->beta2, p->eps, p->dtype, s)) return r;
+    // n2 may take n1's place: the roll above has been enqueued before it
+    if (int r = run_norm_conv_input(a, n2, pl.P, p->out_dim, hw, p->gamma2, p->beta2, p->eps,
+                                    p->dtype, s))
+        return r;
     wanvae::ConvLaunch cb = ca;
-    cb.x = a;
+    cb.x = n2;
     cb.cache = cache_b;
     cb.w = p->w_b;
     cb.bias = p->b_b;
@@ -409,7 +438,7 @@ int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_c
     cb.cin = p->out_dim;
     if (int r = run_conv(cb, p->dtype, s)) return r;
     return timed_launch(WANVAE_KERNEL_ROLL, s, "roll_cache", [&] {
-        return wanvae::launch_roll_cache(cache_b, a, d->n, d->t, (int64_t)slab_b, s);
+        return wanvae::launch_roll_cache(cache_b, n2, d->n, d->t, (int64_t)slab_b, s);
     });
 }
 

@@ -17,6 +17,13 @@
 // of C_out x 32 bytes: whole L2 lines, where [co][tap][ci] would cost one
 // 128-byte line request per 32 useful bytes.
 //
+// Input layout: each frame of x (and of the cache) is either channels-last,
+// [h][w][cin], or cut into 16-channel slices, [cin/16][h][w][16] (the layout
+// the ResidualBlock's norm writes for its convs).  A stage's input is then one
+// slice of one frame either way; in the sliced layout its positions are
+// contiguous 32-byte units, so the loads move whole cache lines (a
+// channels-last stage reads 32 bytes of every position's line).
+//
 // Output tile: one frame t, HB = WM*FM output rows x 32 output columns x
 // NB = WN*FN*32 output channels; MFMA wave (wm, wn) owns FM rows x FN channel
 // blocks (FM*FN 32x32 fp32 accumulators).
@@ -130,6 +137,7 @@ struct Args {
     int cin, cout, cres;
     int tiles_w, tiles_h;
     int64_t tiles;          // total tiles of the launch
+    int x_sliced;           // x and cache frames are [cin/16][h][w][16], not [h][w][cin]
 };
 
 // One output tile: batch item, frame, first row / column / output channel,
@@ -292,7 +300,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // Block b of a stage: lane l writes physical half (l & 1) of unit
         // 32 * b' + l / 2 (b' relative to the A or B region), so it fetches the
         // logical half that the swizzle puts there.
-        const uint32_t cs2 = (uint32_t)a.cin * 2;
+        // bytes between neighbouring positions of a frame slab, and elements
+        // between its 16-channel slices
+        const uint32_t cs2 = a.x_sliced ? (uint32_t)kUnit : (uint32_t)a.cin * 2;
+        const int64_t slice_elems = a.x_sliced ? HW * kKC : kKC;
         const uint32_t tap2 = (uint32_t)a.cout * kUnit;   // bytes per tap of a packed stage
         // byte offset of block b's piece for a conv stage (sc = false) or a
         // shortcut stage (sc = true: x at the output positions, w_sc as one tap)
@@ -353,13 +364,26 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             uint32_t abytes, bbytes;
             const bool sc = si >= ti.s_conv;
             if (!sc) {
-                const int kt = ti.kt_begin + si / ck;
-                const int cc = si % ck;
+                int kt, cc;
+                if (a.x_sliced) {
+                    // 16-channel slice outer, temporal tap inner: the tiles of
+                    // frames t, t+1, t+2, which run side by side on one XCD,
+                    // then read each slice of a frame within a few stages of
+                    // each other, while it is still in the L2
+                    const int nkt = 3 - ti.kt_begin;
+                    cc = si / nkt;
+                    kt = ti.kt_begin + (si - cc * nkt);
+                } else {
+                    // channels-last input: the slices of one frame share cache
+                    // lines, so they are read back to back
+                    kt = ti.kt_begin + si / ck;
+                    cc = si % ck;
+                }
                 const int64_t ts = ti.tq + kt - 2;
                 abase = (ts >= 0 ? a.x + ((ti.nq * a.T + ts) * HW) * a.cin
                                  : a.cache + ((ti.nq * 2 + (ts + 2)) * HW) * a.cin) +
-                        cc * kKC;
-                abytes = (uint32_t)(HW * a.cin * 2 - cc * kKC * 2);
+                        cc * slice_elems;
+                abytes = (uint32_t)(HW * a.cin * 2 - cc * slice_elems * 2);
                 // elements of the packed weight before stage (kt, cc)
                 const int64_t wskip = (int64_t)(kt * ck + cc) * 9 * a.cout * kKC;
                 bbase = a.w + wskip;
@@ -781,6 +805,7 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.cin = c.cin;
     a.cout = c.cout;
     a.cres = c.cres;
+    a.x_sliced = c.x_sliced ? 1 : 0;
     a.tiles_w = (int)((c.w_ + kWB - 1) / kWB);
     a.tiles_h = (int)((c.h + TL::HB - 1) / TL::HB);
     a.tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (c.cout / TL::NB);

@@ -24,6 +24,9 @@ struct ConvLaunch {
     void *y = nullptr;            // [n][t][h][w][cout]
     int64_t n = 0, t = 0, h = 0, w_ = 0;
     int cin = 0, cout = 0, cres = 0;
+    // bf16 only: x and cache frames are [cin/16][h][w][16] (16-channel
+    // slices) instead of [h][w][cin]; res and y stay channels-last
+    bool x_sliced = false;
 };
 
 // Fused RMS_norm + SiLU over rows of C channels (C % 32 == 0, 32..1024).
@@ -31,6 +34,12 @@ bool rmsnorm_silu_supported(int C);
 hipError_t launch_rmsnorm_silu_bf16(const void *x, void *y, int64_t rows, int C,
                                     const float *gamma, const float *beta, float eps,
                                     hipStream_t s);
+// The same over rows that are the positions of frames of hw positions each,
+// writing y in the 16-channel-slice layout the bf16 conv reads:
+// y[f][c / 16][q][c % 16] for row f * hw + q.  bf16 only; y must not overlap x.
+hipError_t launch_rmsnorm_silu_bf16_sliced(const void *x, void *y, int64_t rows, int C, int64_t hw,
+                                           const float *gamma, const float *beta, float eps,
+                                           hipStream_t s);
 hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, const float *gamma,
                                    const float *beta, float eps, hipStream_t s);
 

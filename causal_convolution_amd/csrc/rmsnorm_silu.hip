@@ -21,6 +21,14 @@
 // equal x (in place): each element is read and then written by the same
 // lane.  x is read once and y written once: 2 * rows * C * sizeof(T) bytes of
 // HBM traffic.
+//
+// A second form writes y in the layout the bf16 conv reads: rows are the
+// positions of frames of hw positions, and each frame is stored as 16-channel
+// slices, [C/16][hw][16].  A block then normalises its R = 16 G U rows of a
+// pass, loaded as above, into LDS in slice order and stores each slice of the
+// tile as one contiguous run of R * 32 bytes (1 KB for C = 384, 2 KB for 192,
+// 4 KB for 96): whole cache lines and long DRAM bursts, where storing the
+// pieces straight from their lanes would leave lines half written.
 #include "bf16.h"
 #include "internal.h"
 
@@ -94,10 +102,12 @@ struct Shape {
     static constexpr bool IN_REGS = NP * EP <= 48;
 };
 
-template <typename T, int C>
+// SLICED: y is written in the conv input layout, frame f = row / hw cut into
+// 16-channel slices, y[f][c / 16][row % hw][c % 16] (inv_hw = 1 / hw).
+template <typename T, int C, bool SLICED>
 __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
     const T *x, T *y, int64_t rows, const float *__restrict__ gamma,
-    const float *__restrict__ beta, float eps, float sqrt_c) {
+    const float *__restrict__ beta, float eps, float sqrt_c, int64_t hw, double inv_hw) {
     using S = Shape<T, C>;
     using PC = Piece<T>;
     constexpr int G = S::G, NP = S::NP, EP = S::EP, U = S::U;
@@ -133,13 +143,21 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
 
     const unsigned char *xb = reinterpret_cast<const unsigned char *>(x);
     unsigned char *yb = reinterpret_cast<unsigned char *>(y);
+
+    // SLICED: the block's R rows of a pass are normalised into LDS in slice
+    // order, [C/16][R][16] with a 16-byte pad per slice against bank
+    // conflicts, and stored from there as R * 32 contiguous bytes per slice.
+    constexpr int R = S::ROWS_PER_BLOCK;
+    constexpr int SLICE_STRIDE = R * 32 + 16;
+    __shared__ __attribute__((aligned(16))) unsigned char tile_lds[SLICED ? (C / 16) * SLICE_STRIDE : 16];
+    auto group_row0 = [&](int64_t r0, int u) -> int64_t { return r0 + (int64_t)(u * kGroups + grp) * G; };
     const int64_t step = (int64_t)gridDim.x * S::ROWS_PER_BLOCK;
 
-    for (int64_t r0 = (int64_t)blockIdx.x * S::ROWS_PER_BLOCK; r0 < rows; r0 += step) {
-        u32x4 d[U][NP];
+    // this lane's pieces of the pass starting at row r0
+    auto load_pass = [&](int64_t r0, u32x4 (&d)[U][NP]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g0 = r0 + (int64_t)(u * kGroups + grp) * G;   // the group's first row
+            const int64_t g0 = group_row0(r0, u);   // the group's first row
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
                 if ((!S::RAGGED || prow[i] != kNoRow) && g0 + prow[i] < rows)
@@ -149,9 +167,26 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
                     d[u][i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
+    };
+    // SLICED passes end in a block barrier and an LDS round trip, so the next
+    // pass's loads are issued before this pass is processed
+    u32x4 d_next[SLICED ? U : 1][NP];
+    if constexpr (SLICED) load_pass((int64_t)blockIdx.x * S::ROWS_PER_BLOCK, d_next);
+
+    for (int64_t r0 = (int64_t)blockIdx.x * S::ROWS_PER_BLOCK; r0 < rows; r0 += step) {
+        u32x4 d[U][NP];
+        if constexpr (SLICED) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < NP; ++i) d[u][i] = d_next[u][i];
+            if (r0 + step < rows) load_pass(r0 + step, d_next);
+        } else {
+            load_pass(r0, d);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g0 = r0 + (int64_t)(u * kGroups + grp) * G;
+            const int64_t g0 = group_row0(r0, u);
             float v[NR][EP];
             float ss[G];
 #pragma unroll
@@ -199,32 +234,65 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
                         vi[k + 3] = silu(fmaf(vi[k + 3] * ip, gv.w * sqrt_c, bv.w));
                     }
                 }
-                if ((!S::RAGGED || prow[i] != kNoRow) && g0 + prow[i] < rows)
+                if constexpr (SLICED) {
+                    if (!S::RAGGED || prow[i] != kNoRow) {
+                        const int rt = (u * kGroups + grp) * G + prow[i];   // row within the block tile
+                        *reinterpret_cast<u32x4 *>(tile_lds + (pch[i] / 16) * SLICE_STRIDE + rt * 32 +
+                                                   (pch[i] % 16) * (int)sizeof(T)) = PC::pack(vi);
+                    }
+                } else if ((!S::RAGGED || prow[i] != kNoRow) && g0 + prow[i] < rows) {
                     __builtin_nontemporal_store(PC::pack(vi), reinterpret_cast<u32x4 *>(
                         yb + g0 * S::RB + (i * kGroupLanes + lane) * 16));
+                }
             }
+        }
+        if constexpr (SLICED) {
+            __syncthreads();   // the whole tile is in LDS
+            constexpr int TOTAL = R * S::RB;   // bytes of the block tile
+            const int64_t t0 = r0;
+            // frame and position of the tile's first row: a double-precision
+            // quotient, exact after one correction step
+            int64_t f0 = (int64_t)((double)t0 * inv_hw);
+            int64_t q0 = t0 - f0 * hw;
+            if (q0 < 0) --f0, q0 += hw;
+            else if (q0 >= hw) ++f0, q0 -= hw;
+#pragma unroll
+            for (int j = 0; j < (TOTAL + kThreads * 16 - 1) / (kThreads * 16); ++j) {
+                const int o = (j * kThreads + (int)threadIdx.x) * 16;   // byte of the tile in [C/16][R][32] order
+                const int k = o / (R * 32), rem = o % (R * 32);
+                const int rt = rem / 32;
+                if (o < TOTAL && t0 + rt < rows) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(tile_lds + k * SLICE_STRIDE + rem);
+                    int64_t f = f0, q = q0 + rt;
+                    while (q >= hw) q -= hw, ++f;   // at most R / hw + 1 steps
+                    const int64_t off = ((f * C + k * 16) * hw + q * 16) * (int64_t)sizeof(T) + rem % 32;
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(yb + off));
+                }
+            }
+            __syncthreads();   // read back before the next pass overwrites the tile
         }
     }
 }
 
-template <typename T, int C>
+template <typename T, int C, bool SLICED>
 hipError_t launch_c(const void *x, void *y, int64_t rows, const float *gamma, const float *beta,
-                    float eps, hipStream_t s) {
+                    float eps, int64_t hw, hipStream_t s) {
     using S = Shape<T, C>;
     int64_t blocks = (rows + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
     if (blocks > kGridCap) blocks = kGridCap;
     if (blocks < 1) blocks = 1;
-    rmsnorm_silu_kernel<T, C><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-        static_cast<const T *>(x), static_cast<T *>(y), rows, gamma, beta, eps, sqrtf((float)C));
+    rmsnorm_silu_kernel<T, C, SLICED><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+        static_cast<const T *>(x), static_cast<T *>(y), rows, gamma, beta, eps, sqrtf((float)C), hw,
+        1.0 / (double)hw);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool SLICED>
 hipError_t dispatch(const void *x, void *y, int64_t rows, int C, const float *gamma,
-                    const float *beta, float eps, hipStream_t s) {
+                    const float *beta, float eps, int64_t hw, hipStream_t s) {
     switch (C) {
 #define WANVAE_NORM_CASE(K) \
-    case 32 * K: return launch_c<T, 32 * K>(x, y, rows, gamma, beta, eps, s);
+    case 32 * K: return launch_c<T, 32 * K, SLICED>(x, y, rows, gamma, beta, eps, hw, s);
         WANVAE_NORM_CASE(1) WANVAE_NORM_CASE(2) WANVAE_NORM_CASE(3) WANVAE_NORM_CASE(4)
         WANVAE_NORM_CASE(5) WANVAE_NORM_CASE(6) WANVAE_NORM_CASE(7) WANVAE_NORM_CASE(8)
         WANVAE_NORM_CASE(9) WANVAE_NORM_CASE(10) WANVAE_NORM_CASE(11) WANVAE_NORM_CASE(12)
@@ -245,12 +313,19 @@ bool rmsnorm_silu_supported(int C) { return C >= 32 && C <= 1024 && C % 32 == 0;
 hipError_t launch_rmsnorm_silu_bf16(const void *x, void *y, int64_t rows, int C,
                                     const float *gamma, const float *beta, float eps,
                                     hipStream_t s) {
-    return dispatch<uint16_t>(x, y, rows, C, gamma, beta, eps, s);
+    return dispatch<uint16_t, false>(x, y, rows, C, gamma, beta, eps, 1, s);
+}
+
+hipError_t launch_rmsnorm_silu_bf16_sliced(const void *x, void *y, int64_t rows, int C, int64_t hw,
+                                           const float *gamma, const float *beta, float eps,
+                                           hipStream_t s) {
+    if (hw <= 0) return hipErrorInvalidValue;
+    return dispatch<uint16_t, true>(x, y, rows, C, gamma, beta, eps, hw, s);
 }
 
 hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, const float *gamma,
                                    const float *beta, float eps, hipStream_t s) {
-    return dispatch<float>(x, y, rows, C, gamma, beta, eps, s);
+    return dispatch<float, false>(x, y, rows, C, gamma, beta, eps, 1, s);
 }
 
 }  // namespace wanvae

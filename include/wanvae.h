@@ -148,10 +148,15 @@ WANVAE_API int wanvae_causal_conv3d(const void *x, const void *cache, const void
 
 /*
  * Workspace bytes that wanvae_resblock_forward / wanvae_resblock_stream_step
- * need for extent *d (for the stream step, d->t is the chunk length):
- * the conv A input (n1, [P][in_dim]) and the conv A output, normalised in
- * place into the conv B input ([P][out_dim]), P = n*t*h*w, each 256-byte
- * aligned.  Validates p and d as the forward call does.
+ * need for extent *d (for the stream step, d->t is the chunk length), with
+ * P = n*t*h*w, two 256-byte aligned regions:
+ *   - the conv inputs, P * max(in_dim, out_dim) elements: n1 (conv A's input),
+ *     then n2 (conv B's input) once conv A has read n1;
+ *   - conv A's output a, P * out_dim elements.
+ * For bf16 the norms write n1 and n2 in the MFMA conv's input layout (each
+ * frame cut into 16-channel slices, [C/16][h][w][16]); for fp32 n1 is
+ * channels-last and n2 is a normalised in place.  Validates p and d as the
+ * forward call does.
  */
 WANVAE_API int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, const wanvae_dims *d,
                                    size_t *bytes);
@@ -179,13 +184,16 @@ WANVAE_API int wanvae_resblock_forward(const wanvae_resblock_params *p, const vo
  * ("Sharding of WAN 2.2 VAE", Why depth sharding is not beneficial: one frame
  * at a time with a cache of the last frames of every CausalConv3d's input;
  * "Closing the gap", section 1: the per-frame decode loop carrying feat_cache).
- *   cache_a : [d.n][2][d.h][d.w][in_dim]  conv A input frames -2, -1 (in/out)
- *   cache_b : [d.n][2][d.h][d.w][out_dim] conv B input frames -2, -1 (in/out)
+ *   cache_a : d.n*2*d.h*d.w*in_dim elements: conv A input frames -2, -1 (in/out)
+ *   cache_b : d.n*2*d.h*d.w*out_dim elements: conv B input frames -2, -1 (in/out)
  * Each conv reads its cache as the two frames before the chunk; afterwards
  * the cache holds the last two frames of [cache, this chunk's conv input].
- * A fresh stream starts from zero-filled caches (zero is the causal pad), so
- * running a clip chunk by chunk gives the full-T result.  Caches must not
- * overlap each other, x, y or the workspace.
+ * The frames are stored as the library stores conv inputs: [n][2][h][w][C]
+ * for fp32, [n][2][C/16][h][w][16] (16-channel slices) for bf16; callers
+ * treat the caches as opaque state.  A fresh stream starts from zero-filled
+ * caches (zero is the causal pad in either layout), so running a clip chunk
+ * by chunk gives the full-T result.  Caches must not overlap each other, x,
+ * y or the workspace.
  */
 WANVAE_API int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_chunk,
                                 void *y_chunk, const wanvae_dims *d, void *cache_a, void *cache_b,

@@ -112,6 +112,10 @@ def test_workspace_size():
     P = 41 * 180 * 320
     assert b.value >= P * (384 + 192) * 2 and b.value < P * (384 + 192) * 2 + 1024
     assert b.value % 256 == 0
+    # the conv input region holds n1 and later n2: max(in_dim, out_dim) per position
+    pw = _params(cin=96, cout=192)
+    assert L.wanvae_resblock_workspace_size(C.byref(pw), C.byref(d), C.byref(b)) == wv.OK
+    assert b.value >= P * (192 + 192) * 2 and b.value < P * (192 + 192) * 2 + 1024
     # identity shortcut with in != out is rejected
     p2 = _params(shortcut=False)
     assert L.wanvae_resblock_workspace_size(C.byref(p2), C.byref(d), C.byref(b)) == wv.ERR_SHAPE

@@ -175,6 +175,8 @@ SMALL_BLOCKS = [
     wl.custom("id128_h36", wl.BF16, 1, 3, 36, 40, 128, 128),
     wl.custom("sc192_96_h35", wl.BF16, 1, 3, 35, 40, 192, 96),
     wl.custom("sc96_288", wl.BF16, 1, 3, 13, 36, 96, 288),   # 96-channel tiles, 3 blocks, shortcut
+    # a wide odd channel count (norm rows cut raggedly) with norm tiles crossing frames
+    wl.custom("sc544_32", wl.BF16, 1, 3, 5, 37, 544, 32),
 ]
 
 
