@@ -74,13 +74,18 @@
 // shortcut bias, are added in fp32 and the result is rounded once to bf16
 // (8-byte stores).  The 1x1x1 shortcut GEMM runs as extra stages of the same
 // accumulators, each holding two 16-channel slices (one when two do not fit a
-// stage buffer) of x at the output positions and of w_sc, one 1 KB block per
-// row of positions: every load of such a stage is useful data.
+// stage buffer) of x at the output positions and of w_sc: every load of such
+// a stage is useful data, and x (channels-last) comes in 64-byte pieces per
+// position, which the LDS-DMA moves at twice the rate of 32-byte ones.
 //
-// Tile order: output-channel block slowest, then batch, row block, column
-// block, and frame fastest.  Each of the 8 XCDs (workgroup index mod 8) owns a
-// contiguous range of tiles, so the workgroups on one XCD share one weight
-// slice and the input frames t-2..t of one spatial block through its L2.
+// Tile order: batch slowest, then row block, column block, frame, and
+// output-channel block fastest.  Each of the 8 XCDs (workgroup index mod 8)
+// owns a contiguous range of tiles, so the workgroups on one XCD work on
+// neighbouring frames of one spatial block, all channel blocks of each side
+// by side: every input frame (and the residual / shortcut input) of the block
+// comes from HBM once and is then shared through the XCD's L2 by the tiles of
+// frames t .. t+2 and of every channel block, and the weights (at most 2 MB
+// for 384 -> 384 channels in bf16... 5.3 MB for 1024) stay in L2 as well.
 #include <atomic>
 #include <utility>
 
@@ -161,20 +166,23 @@ struct Tile {
     static constexpr int STAGE_BYTES = BLOCKS * 1024;
     // FN > 1: each wave owns several channel blocks and walks the taps kh by kh
     // (9 FN weight fragments in registers would not fit beside the
-    // accumulators), and the bias sits in LDS instead of registers
+    // accumulators).  The bias of every tile sits in LDS, not in registers.
     static constexpr bool KH_OUTER = FN > 1;
-    static constexpr int kBiasBytes = KH_OUTER ? 4 * 1024 : 0;   // [cout] fp32, cout <= 1024
+    static constexpr int kBiasBytes = 4 * 1024;   // bias in LDS: [cout] fp32, cout <= 1024
     static constexpr int kLds = 160 * 1024 - kSyncBytes - NWAVE * kEpiBytes - kBiasBytes;
     static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
     static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
     static_assert(NWAVE + 1 <= kSyncBytes / 4, "one flag per wave");
     static constexpr int kPerCU =
         (160 * 1024) / (NBUF * STAGE_BYTES + kSyncBytes + NWAVE * kEpiBytes + kBiasBytes);
-    // shortcut stages: SCS 16-channel slices, each HB rows of x at the output
-    // positions (one 1 KB block per row) followed by NB units of w_sc
+    // shortcut stages: SCS 16-channel slices of x at the output positions
+    // and of w_sc.  SCS = 2 (when it fits): x as 64-byte pieces (32 channels)
+    // per position, two 1 KB blocks per row, then the two slices' w_sc units.
+    // SCS = 1: one slice, one 1 KB block per row of x, then its w_sc units.
     static constexpr int SC_UNITS = HB * kWB + NB;                // units per slice
     static constexpr int SCS = 2 * SC_UNITS / 32 <= BLOCKS ? 2 : 1;
     static constexpr int SC_BLOCKS = SCS * SC_UNITS / 32;         // useful loads per stage
+    static constexpr int SC_W_UNIT0 = SCS * HB * kWB;             // first w_sc unit
     static_assert(SC_BLOCKS <= BLOCKS, "a shortcut slice fits a stage buffer");
 };
 
@@ -237,8 +245,8 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // sync[0]: stages landed (load wave); sync[1 + w]: stages consumed by MFMA wave w
     __shared__ int sync[kSyncBytes / 4];
     __shared__ __attribute__((aligned(16))) unsigned char epi_stage[TL::NWAVE * kEpiBytes];
-    // bias (+ shortcut bias) of every output channel, for the KH_OUTER tiles
-    __shared__ __attribute__((aligned(16))) float bias_lds[TL::kBiasBytes / 4 > 0 ? TL::kBiasBytes / 4 : 1];
+    // bias (+ shortcut bias) of every output channel
+    __shared__ __attribute__((aligned(16))) float bias_lds[TL::kBiasBytes / 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -248,13 +256,11 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int ck = a.cin / kKC;
 
     if (tid <= TL::NWAVE) sync[tid] = 0;
-    if constexpr (TL::KH_OUTER) {
-        for (int c = tid; c < a.cout; c += TL::kThreads) {
-            float b = a.bias ? a.bias[c] : 0.0f;
-            if constexpr (EPI == EPI_SHORTCUT)
-                if (a.bsc) b += a.bsc[c];
-            bias_lds[c] = b;
-        }
+    for (int c = tid; c < a.cout; c += TL::kThreads) {
+        float b = a.bias ? a.bias[c] : 0.0f;
+        if constexpr (EPI == EPI_SHORTCUT)
+            if (a.bsc) b += a.bsc[c];
+        bias_lds[c] = b;
     }
     __syncthreads();
     // flag accesses: relaxed atomics on the LDS array itself, so they stay
@@ -275,16 +281,18 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int64_t x_begin = a.tiles * wg_before / nwg;
     const int64_t x_count = a.tiles * (wg_before + wg_x) / nwg - x_begin;
 
+    const int ncb = a.cout / NB;   // output-channel blocks
     auto decode = [&](int64_t tile) __attribute__((always_inline)) {
         TileInfo ti;
+        ti.n0 = (int)(tile % ncb) * NB;
+        tile /= ncb;
         ti.tq = tile % a.T;
         tile /= a.T;
         ti.w0 = (int)(tile % a.tiles_w) * kWB;
         tile /= a.tiles_w;
         ti.h0 = (int)(tile % a.tiles_h) * HB;
         tile /= a.tiles_h;
-        ti.nq = tile % a.N;
-        ti.n0 = (int)(tile / a.N) * NB;
+        ti.nq = tile;
         // without a cache the stages of frames before 0 only add zeros: skipped
         const int kt_begin = (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
         ti.kt_begin = kt_begin;
@@ -321,26 +329,37 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             const int tap = u / NB, nl = u % NB;
             return (uint32_t)tap * tap2 + (uint32_t)(ti.n0 + nl) * kUnit + hf * 16;
         };
-        // shortcut stage: block b is row b of slice j's x (at the output
-        // positions) or a piece of slice j's w_sc; j selects the 16 channels
-        // 32 bytes further on.  Blocks past the useful ones load zeros into
-        // the unused tail of the buffer, so every stage issues BLOCKS loads
-        // (the vmcnt accounting counts whole stages).  Returns the offset and
-        // whether it is relative to the w_sc resource.
-        auto sc_block_off = [&](const TileInfo &ti, int b, bool &from_w) __attribute__((always_inline)) -> uint32_t {
-            constexpr int SB = TL::SC_UNITS / 32;   // blocks per slice
+        // shortcut stage, SCS = 2: block b < 2 HB holds row b / 2, positions
+        // 16 (b % 2) .. +15 of x, 64 bytes (the stage's 32 channels) each:
+        // lane l fetches position l / 4, 16-byte quarter q = (l % 4) ^ ((pos
+        // >> 2) & 3), so each position's four quarters stay in four
+        // consecutive lanes (one 64-byte piece per lane quad) and a fragment
+        // read (one quarter of 16 positions) hits 16 distinct bank groups.
+        // SCS = 1: block b < HB is row b of x, 32 bytes per position.  Then
+        // the w_sc units of the SCS slices.  Blocks past the useful ones load
+        // zeros into the unused tail of the buffer, so every stage issues
+        // BLOCKS loads (the vmcnt accounting counts whole stages).  Returns
+        // the offset and whether it is relative to the w_sc resource.
+        auto sc_block_off = [&](const TileInfo &ti, int b, bool &from_w) -> uint32_t {
             from_w = false;
             if (b >= TL::SC_BLOCKS) return kOOB;
-            const int j = b / SB, bb = b % SB;
-            const int c = lane >> 1;
-            if (bb < HB) {
-                const int hf = (lane & 1) ^ ((c >> 3) & 1);
-                const int hh = ti.h0 + bb, ww = ti.w0 + c;
-                return hh < H && ww < W ? (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + j * kUnit + hf * 16
-                                        : kOOB;
+            if (b < TL::SCS * HB) {
+                int r, c, q;
+                if constexpr (TL::SCS == 2) {
+                    r = b / 2;
+                    c = (b % 2) * 16 + (lane >> 2);
+                    q = (lane & 3) ^ ((c >> 2) & 3);
+                } else {
+                    r = b;
+                    c = lane >> 1;
+                    q = (lane & 1) ^ ((c >> 3) & 1);
+                }
+                const int hh = ti.h0 + r, ww = ti.w0 + c;
+                return hh < H && ww < W ? (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + q * 16 : kOOB;
             }
             from_w = true;
-            const int nl = (bb - HB) * 32 + c;
+            const int u = (b - TL::SCS * HB) * 32 + (lane >> 1);   // w_sc unit: slice j, channel nl
+            const int j = u / NB, nl = u % NB;
             const int hf = (lane & 1) ^ ((nl >> 3) & 1);
             return (uint32_t)((ti.n0 + nl) * a.cres * 2) + j * kUnit + hf * 16;
         };
@@ -362,8 +381,9 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         auto issue_next = [&]() __attribute__((always_inline)) {
             const uint16_t *abase, *bbase;
             uint32_t abytes, bbytes;
-            const bool sc = si >= ti.s_conv;
+            const bool sc = si >= ti.s_conv;   // conv stages first, then the shortcut stages
             if (!sc) {
+                const int cs = si;   // conv stage index
                 int kt, cc;
                 if (a.x_sliced) {
                     // 16-channel slice outer, temporal tap inner: the tiles of
@@ -371,13 +391,13 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     // then read each slice of a frame within a few stages of
                     // each other, while it is still in the L2
                     const int nkt = 3 - ti.kt_begin;
-                    cc = si / nkt;
-                    kt = ti.kt_begin + (si - cc * nkt);
+                    cc = cs / nkt;
+                    kt = ti.kt_begin + (cs - cc * nkt);
                 } else {
                     // channels-last input: the slices of one frame share cache
                     // lines, so they are read back to back
-                    kt = ti.kt_begin + si / ck;
-                    cc = si % ck;
+                    kt = ti.kt_begin + cs / ck;
+                    cc = cs % ck;
                 }
                 const int64_t ts = ti.tq + kt - 2;
                 abase = (ts >= 0 ? a.x + ((ti.nq * a.T + ts) * HW) * a.cin
@@ -577,16 +597,26 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     auto ldU = [&](const unsigned char *buf, int u) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + b_off(u, g)));
     };
+    // x fragment of slice j at tile row `row`: position l32, quarter 2j + g
+    auto ldX = [&](const unsigned char *buf, int row, int j) __attribute__((always_inline)) {
+        if constexpr (TL::SCS == 2) {
+            const int q = (2 * j + g) ^ ((l32 >> 2) & 3);
+            const int off = ((row * 2 + (l32 >> 4)) * 64 + (l32 & 15) * 4 + q) * 16;
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(buf + off));
+        } else {
+            return ldU(buf, row * kWB + l32);
+        }
+    };
     auto compute_shortcut = [&](const unsigned char *buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < TL::SCS; ++j) {
-            const int u0 = j * TL::SC_UNITS;
             bf16x8 fw[FN];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) fw[fn] = ldU(buf, u0 + HB * kWB + wn * FN * 32 + fn * 32 + l32);
+            for (int fn = 0; fn < FN; ++fn)
+                fw[fn] = ldU(buf, TL::SC_W_UNIT0 + j * NB + wn * FN * 32 + fn * 32 + l32);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                const bf16x8 fx = ldU(buf, u0 + (wm * FM + fm) * kWB + l32);
+                const bf16x8 fx = ldX(buf, wm * FM + fm, j);
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fn], fx, acc[fm][fn], 0, 0, 0);
@@ -614,26 +644,6 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
     for (int64_t i = loc; i < x_count; i += wg_x) {
         const TileInfo ti = decode(x_begin + i);
-
-        // bias (+ shortcut bias) of this lane's output channels: requested now,
-        // first used in the epilogue, so the K loop hides the latency
-        float bsum[TL::KH_OUTER ? 1 : FN][4][4];
-#pragma unroll
-        for (int fn = 0; fn < (TL::KH_OUTER ? 0 : FN); ++fn)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int co = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
-                float4 bv = a.bias ? *reinterpret_cast<const float4 *>(a.bias + co)
-                                   : float4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (EPI == EPI_SHORTCUT) {
-                    if (a.bsc) {
-                        const float4 sv = *reinterpret_cast<const float4 *>(a.bsc + co);
-                        bv.x += sv.x; bv.y += sv.y; bv.z += sv.z; bv.w += sv.w;
-                    }
-                }
-                bsum[fn][j][0] = bv.x; bsum[fn][j][1] = bv.y;
-                bsum[fn][j][2] = bv.z; bsum[fn][j][3] = bv.w;
-            }
 
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
@@ -690,13 +700,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                         float v[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) v[q] = acc[f0 + e][fn][4 * j + q];
-                        if constexpr (TL::KH_OUTER) {
+                        {
                             const float4 bv = *reinterpret_cast<const float4 *>(
                                 bias_lds + ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g);
                             v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) v[q] += bsum[fn][j][q];
                         }
                         if (res != nullptr) {
                             const u32x2 r = res[e][fn][j];
