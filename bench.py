@@ -16,6 +16,10 @@ The run prints one JSON line:
   MFMA peak;
 * norm: the fused RMS_norm + SiLU kernel's achieved GB/s (2 * P * C * 2 bytes
   per launch) against the 8 TB/s HBM peak;
+* traffic (in roofline and norm): HBM bytes per launch measured by rocprofv3
+  FETCH_SIZE / WRITE_SIZE passes (scaled by what they read for a plain copy of
+  known size), from profiles/traffic.json; null once the kernel sources
+  differ from the ones it was measured on;
 * cpu_baseline: the CPU oracle timed on this host on a bounded sample (the
   whole block over the clip's first frame(s); causal, so those frames are
   exactly the clip's first output frames), scaled to frames per second.
@@ -50,6 +54,37 @@ def conv_flops(w):
 def norm_bytes(w, esize):
     P = w.positions
     return 2.0 * P * w.cin * esize, 2.0 * P * w.cout * esize
+
+
+# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, kept in
+# profiles/traffic.json with the sha256 of the kernel sources it was measured
+# on: reported only while those sources are unchanged (else null).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["causal_convolution_amd/csrc/conv3d_bf16.hip",
+                  "causal_convolution_amd/csrc/rmsnorm_silu.hip",
+                  "causal_convolution_amd/csrc/abi.cpp"]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` ("conv" or "norm") at `workload`, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    e = t.get("workloads", {}).get(workload, {}).get(kernel)
+    return None if e is None else e["read_bytes"] + e["write_bytes"]
 
 
 def cpu_baseline(w, p, x_dev, frames):
@@ -155,12 +190,13 @@ def main():
                                f"x [{w.n},{w.t},{w.h},{w.w},{w.cin}] {w.dtype}, full-T",
                    "frames": w.t, "positions": w.positions, "parallelism": "1 GPU"},
         "roofline": {"bound": "mfma", "achieved": conv_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": conv_tflops / peak, "traffic": None,
+                     "frac": conv_tflops / peak, "traffic": measured_traffic(args.workload, "conv"),
                      "kernel": "conv3d_bf16_kernel (conv A and conv B launches)",
                      "flop_per_launch": conv_flop_per_launch, "avg_launch_ms": conv_avg_ms,
                      "launches": n_conv},
         "norm": {"bound": "hbm", "achieved": norm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": norm_gbs / PEAK_HBM_GBS, "bytes_per_launch": (nb1 + nb2) / 2.0,
+                 "traffic": measured_traffic(args.workload, "norm"),
                  "avg_launch_ms": norm_avg_ms, "launches": n_norm},
         "cpu_baseline": None,
     }
