@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--cpu-frames", type=int, default=4,
                     help="frames of the clip the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
+                    help="time the streaming mode instead: a step runs the clip through "
+                         "wanvae_resblock_stream_step in chunks of N frames (caches zeroed first)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-MiB buffer 3 times (a plain copy "
                          "kernel of known size, to scale HBM byte counters by)")
@@ -140,8 +143,24 @@ def main():
     stream = torch.cuda.current_stream()
     print(f"[bench] {w.desc}; steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
 
+    if args.stream_chunk > 0:
+        # streaming mode: chunks of N frames through the feat_cache entry point
+        assert w.n == 1, "the frame-chunk views below are contiguous for batch 1"
+        N = args.stream_chunk
+        ca, cb = blk.new_caches(w.n, w.h, w.w)
+        ws = blk.workspace(w.n, min(N, w.t), w.h, w.w)
+
+        def step():
+            ca.zero_()
+            cb.zero_()
+            for t0 in range(0, w.t, N):
+                blk.stream_step(x[:, t0:t0 + N], ca, cb, out=y[:, t0:t0 + N], workspace=ws)
+    else:
+        def step():
+            blk.forward(x, out=y, workspace=ws)
+
     for _ in range(args.warmup):
-        blk.forward(x, out=y, workspace=ws)
+        step()
     torch.cuda.synchronize()
 
     wv.timing_reset()
@@ -151,7 +170,7 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        blk.forward(x, out=y, workspace=ws)
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
     wv.timing_enable(False)
@@ -164,12 +183,15 @@ def main():
 
     fa, fb = conv_flops(w)
     conv_avg_ms = conv_ms / n_conv
-    conv_flop_per_launch = (fa + fb) / 2.0
+    # algorithmic work of the timed steps spread over their launches (one conv A
+    # and one conv B per step full-T; one of each per chunk when streaming)
+    conv_flop_per_launch = (fa + fb) * args.steps / n_conv
     conv_tflops = conv_flop_per_launch / (conv_avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == wl.BF16 else PEAK_F32_TFLOPS
     nb1, nb2 = norm_bytes(w, esize)
     norm_avg_ms = norm_ms / n_norm
-    norm_gbs = (nb1 + nb2) / 2.0 / (norm_avg_ms * 1e-3) / 1e9
+    norm_bytes_per_launch = (nb1 + nb2) * args.steps / n_norm
+    norm_gbs = norm_bytes_per_launch / (norm_avg_ms * 1e-3) / 1e9
 
     ms_per_step = total_ms / args.steps
     out = {
@@ -187,16 +209,19 @@ def main():
         "data": "synthetic (seeded N(0,1) input, random-init weights)",
         "config": {"workload": f"ResidualBlock {w.cin}->{w.cout} "
                                f"{'identity' if w.cin == w.cout else '1x1x1'} shortcut, "
-                               f"x [{w.n},{w.t},{w.h},{w.w},{w.cin}] {w.dtype}, full-T",
+                               f"x [{w.n},{w.t},{w.h},{w.w},{w.cin}] {w.dtype}, "
+                               + (f"streamed in chunks of {args.stream_chunk} frames with the feat_cache"
+                                  if args.stream_chunk > 0 else "full-T"),
                    "frames": w.t, "positions": w.positions, "parallelism": "1 GPU"},
         "roofline": {"bound": "mfma", "achieved": conv_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": conv_tflops / peak, "traffic": measured_traffic(args.workload, "conv"),
+                     "frac": conv_tflops / peak,
+                     "traffic": None if args.stream_chunk else measured_traffic(args.workload, "conv"),
                      "kernel": "conv3d_bf16_kernel (conv A and conv B launches)",
                      "flop_per_launch": conv_flop_per_launch, "avg_launch_ms": conv_avg_ms,
                      "launches": n_conv},
         "norm": {"bound": "hbm", "achieved": norm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                 "frac": norm_gbs / PEAK_HBM_GBS, "bytes_per_launch": (nb1 + nb2) / 2.0,
-                 "traffic": measured_traffic(args.workload, "norm"),
+                 "frac": norm_gbs / PEAK_HBM_GBS, "bytes_per_launch": norm_bytes_per_launch,
+                 "traffic": None if args.stream_chunk else measured_traffic(args.workload, "norm"),
                  "avg_launch_ms": norm_avg_ms, "launches": n_norm},
         "cpu_baseline": None,
     }
