@@ -103,6 +103,78 @@ def cpu_baseline(w, p, x_dev, frames):
                       f"[{w.n},{w.t},{w.h},{w.w},{w.cin}] -> {w.cout}: {dt:.1f} s"}
 
 
+def head_tail(torch, wv, steps, warmup):
+    """The decoder's head and tail around its ResidualBlocks, at the Wan 2.2
+    720p decoder shapes: conv_in on the 16-channel latent [1,21,90,160,16] to
+    384 channels, post_quant_conv (1x1x1, 16 -> 16) on the latent, and
+    norm_out (RMS_norm + SiLU, 96 channels) + conv_out (96 -> 3) on the
+    output-resolution activation [1,81,720,1280,96].  Seeded synthetic bf16
+    values.  Per op: average launch time over `steps` launches, algorithmic
+    FLOPs and HBM bytes (read inputs once, write outputs once), and the
+    fraction of the bound that limits it (the larger of FLOPs / 2.5 PFLOP/s
+    and bytes / 8 TB/s)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+
+    def randn(*shape, scale=1.0):
+        return (torch.randn(shape, device="cuda", generator=g) * scale).to(torch.bfloat16)
+
+    z = randn(1, 21, 90, 160, 16)
+    act = randn(1, 81, 720, 1280, 96)
+    w_in = wv.pack_conv3d_weights(randn(384, 16, 3, 3, 3, scale=(1 / 432) ** 0.5))
+    w_out = wv.pack_conv3d_weights(randn(3, 96, 3, 3, 3, scale=(1 / 2592) ** 0.5))
+    w_pq = randn(16, 16, scale=0.25)
+    b384 = torch.randn(384, device="cuda", generator=g) * 0.1
+    b3 = torch.randn(3, device="cuda", generator=g) * 0.1
+    b16 = torch.randn(16, device="cuda", generator=g) * 0.1
+    gam = torch.rand(96, device="cuda", generator=g) + 0.5
+    bet = torch.randn(96, device="cuda", generator=g) * 0.3
+    y_in = torch.empty((1, 21, 90, 160, 384), dtype=torch.bfloat16, device="cuda")
+    y_pq = torch.empty_like(z)
+    n_out = torch.empty_like(act)
+    y_out = torch.empty((1, 81, 720, 1280, 3), dtype=torch.bfloat16, device="cuda")
+    P_lat, P_out = 21 * 90 * 160, 81 * 720 * 1280
+    ops = [
+        ("conv_in 16->384, causal 3x3x3, [1,21,90,160,16]", wv.KERNEL_CONV_BF16,
+         lambda: wv.causal_conv3d(z, w_in, b384, out=y_in),
+         2.0 * P_lat * 384 * 27 * 16, 2.0 * P_lat * (16 + 384)),
+        ("post_quant_conv 16->16, 1x1x1, [1,21,90,160,16]", wv.KERNEL_POINTWISE,
+         lambda: wv.pointwise_conv(z, w_pq, b16, out=y_pq),
+         2.0 * P_lat * 16 * 16, 2.0 * P_lat * (16 + 16)),
+        ("norm_out RMS_norm+SiLU, C=96, [1,81,720,1280,96]", wv.KERNEL_NORM,
+         lambda: wv.rmsnorm_silu(act, gam, bet, out=n_out),
+         0.0, 2.0 * P_out * 96 * 2),
+        ("conv_out 96->3, causal 3x3x3, [1,81,720,1280,96]", wv.KERNEL_CONV_BF16,
+         lambda: wv.causal_conv3d(n_out, w_out, b3, out=y_out),
+         2.0 * P_out * 3 * 27 * 96, 2.0 * P_out * (96 + 3)),
+    ]
+    res = []
+    for name, kind, fn, flop, nbytes in ops:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        wv.timing_reset()
+        wv.timing_enable(True)
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        wv.timing_enable(False)
+        n, ms = wv.timing_read(kind)
+        wv.timing_reset()
+        avg = ms / n
+        t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        res.append({"op": name, "avg_launch_ms": avg, "flop": flop, "bytes": nbytes,
+                    "tflops": flop / (avg * 1e-3) / 1e12, "gbs": nbytes / (avg * 1e-3) / 1e9,
+                    "bound": bound, "frac": max(t_mfma, t_hbm) / avg})
+        print(f"[bench] {name}: {avg:.3f} ms, {res[-1]['frac']:.1%} of its {bound} bound",
+              file=sys.stderr, flush=True)
+    return {"metric": "decoder head/tail ops, average launch time (1 GPU)", "unit": "ms",
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic (seeded)",
+            "steps": steps, "warmup": warmup, "ops": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +187,10 @@ def main():
     ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
                     help="time the streaming mode instead: a step runs the clip through "
                          "wanvae_resblock_stream_step in chunks of N frames (caches zeroed first)")
+    ap.add_argument("--head-tail", action="store_true",
+                    help="time the decoder's head and tail ops instead (conv_in 16->384, "
+                         "post_quant_conv 16->16, norm_out + conv_out 96->3) at the "
+                         "decoder's shapes, one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-MiB buffer 3 times (a plain copy "
                          "kernel of known size, to scale HBM byte counters by)")
@@ -130,6 +206,10 @@ def main():
 
     import causal_convolution_amd as wv
     from causal_convolution_amd import workloads as wl
+
+    if args.head_tail:
+        print(json.dumps(head_tail(torch, wv, args.steps, args.warmup)), flush=True)
+        return
 
     w = wl.WORKLOADS[args.workload]
     dt = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libwanvae.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(7)
 F32, BF16 = 0, 1
-KERNEL_NORM, KERNEL_CONV_BF16, KERNEL_CONV_F32, KERNEL_ROLL = range(4)
+KERNEL_NORM, KERNEL_CONV_BF16, KERNEL_CONV_F32, KERNEL_ROLL, KERNEL_POINTWISE = range(5)
 EPS = 1e-12
 
 
@@ -60,6 +60,10 @@ EXPORTS = {
     "wanvae_resblock_stream_step": (C.c_int, [C.POINTER(ResblockParamsC), C.c_void_p, C.c_void_p,
                                               C.POINTER(Dims), C.c_void_p, C.c_void_p,
                                               C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wanvae_packed_conv3d_weight_elems": (C.c_int, [C.c_int32, C.c_int32, C.c_int32,
+                                                    C.POINTER(C.c_int64)]),
+    "wanvae_pointwise_conv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+                                        C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
     "wanvae_last_error": (C.c_char_p, []),
     "wanvae_timing_enable": (C.c_int, [C.c_int]),
     "wanvae_timing_reset": (C.c_int, []),
@@ -148,7 +152,8 @@ def rmsnorm_silu(x, gamma, beta=None, eps: float = EPS, out=None, stream=None):
 
 class PackedWeight:
     """A 3x3x3 conv weight packed by ``wanvae_pack_conv3d_weights``: ``data`` is
-    a flat device tensor of 27 * cin * cout elements."""
+    a flat device tensor of ``packed_conv3d_weight_elems(cin, cout, dtype)``
+    elements (27 * cin * cout, with cout rounded up to 32 for bf16)."""
 
     def __init__(self, data, cin: int, cout: int):
         self.data, self.cin, self.cout = data, int(cin), int(cout)
@@ -166,10 +171,18 @@ def pack_conv3d_weights(w, stream=None) -> PackedWeight:
         raise ValueError(f"w must be [C_out, C_in, 3, 3, 3], got {tuple(w.shape)}")
     _dev(w, "w")
     cout, cin = int(w.shape[0]), int(w.shape[1])
-    out = torch.empty(w.numel(), dtype=w.dtype, device=w.device)
+    out = torch.empty(packed_conv3d_weight_elems(cin, cout, _dtype_code(w)), dtype=w.dtype,
+                      device=w.device)
     _check(lib().wanvae_pack_conv3d_weights(_ptr(w), _ptr(out), cin, cout, _dtype_code(w),
                                             _stream(stream)))
     return PackedWeight(out, cin, cout)
+
+
+def packed_conv3d_weight_elems(cin: int, cout: int, dtype_code: int) -> int:
+    """Elements of a packed conv weight (``wanvae_packed_conv3d_weight_elems``)."""
+    n = C.c_int64(0)
+    _check(lib().wanvae_packed_conv3d_weight_elems(int(cin), int(cout), int(dtype_code), C.byref(n)))
+    return n.value
 
 
 def _packed(w, name, dtype, cin, cout):
@@ -177,7 +190,25 @@ def _packed(w, name, dtype, cin, cout):
         raise TypeError(f"{name} must be a PackedWeight (see pack_conv3d_weights)")
     if (w.cin, w.cout) != (cin, cout):
         raise ValueError(f"{name} is {w.cin}->{w.cout}, expected {cin}->{cout}")
-    _dev(w.data, name, dtype, (27 * cin * cout,))
+    _dev(w.data, name, dtype, (packed_conv3d_weight_elems(cin, cout, _dtype_code(w.data)),))
+
+
+def pointwise_conv(x, w, bias=None, out=None, stream=None):
+    """Pointwise (1x1x1) conv (``wanvae_pointwise_conv``): x [..., Cin]
+    channels-last, w [Cout, Cin] of x's dtype, bias [Cout] fp32 or None ->
+    [..., Cout]."""
+    torch = _torch()
+    cin = int(x.shape[-1])
+    cout = int(w.shape[0])
+    _dev(x, "x")
+    _dev(w, "w", x.dtype, (cout, cin))
+    _dev(bias, "bias", torch.float32, (cout,))
+    y = torch.empty(tuple(x.shape[:-1]) + (cout,), dtype=x.dtype, device=x.device) if out is None else out
+    _dev(y, "out", x.dtype, tuple(x.shape[:-1]) + (cout,))
+    rows = x.numel() // cin if cin else 0
+    _check(lib().wanvae_pointwise_conv(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), rows, cin, cout,
+                                       _dtype_code(x), _stream(stream)))
+    return y
 
 
 def causal_conv3d(x, w, bias=None, cache=None, out=None, stream=None):

@@ -161,8 +161,8 @@ int check_conv_slab(const wanvae_dims *d, int32_t c, int32_t dt) {
 int check_conv_channels(int32_t cin, int32_t cout, int32_t dt) {
     if (dt == WANVAE_BF16) {
         WV_CHECK(wanvae::conv3d_bf16_supported(cin, cout), WANVAE_ERR_SHAPE,
-                 "bf16 conv needs cin, cout multiples of 32 in [32, 1024] (got %d, %d)", cin,
-                 cout);
+                 "bf16 conv needs cin a multiple of 16 in [16, 1024] and cout in [1, 1024] "
+                 "(got %d, %d)", cin, cout);
     } else {
         WV_CHECK(cin >= 1 && cin <= 1024 && cout >= 1 && cout <= 1024, WANVAE_ERR_SHAPE,
                  "fp32 conv needs cin, cout in [1, 1024] (got %d, %d)", cin, cout);
@@ -274,7 +274,7 @@ int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const 
     const size_t es = esize(dtype);
     const size_t xb = (size_t)P * cin * es, yb = (size_t)P * cout * es;
     const size_t cb = (size_t)d->n * 2 * d->h * d->w * cin * es;
-    const size_t wb = (size_t)cout * 27 * cin * es;
+    const size_t wb = (size_t)wanvae::packed_conv3d_weight_elems(cin, cout, dtype == WANVAE_BF16) * es;
     WV_CHECK(!overlaps(y, yb, x, xb) && !overlaps(y, yb, cache, cb) && !overlaps(y, yb, w, wb),
              WANVAE_ERR_ALIAS, "y overlaps x, cache or w");
     wanvae::ConvLaunch c;
@@ -307,11 +307,47 @@ int wanvae_pack_conv3d_weights(const void *w, void *packed, int32_t cin, int32_t
     WV_CHECK(w && packed, WANVAE_ERR_NULL, "w and packed are required");
     WV_CHECK(aligned16(w) && aligned16(packed), WANVAE_ERR_SHAPE, "pointers must be 16-byte aligned");
     const size_t bytes = (size_t)27 * cin * cout * esize(dtype);
-    WV_CHECK(!overlaps(w, bytes, packed, bytes), WANVAE_ERR_ALIAS, "packed overlaps w");
+    const size_t pbytes =
+        (size_t)wanvae::packed_conv3d_weight_elems(cin, cout, dtype == WANVAE_BF16) * esize(dtype);
+    WV_CHECK(!overlaps(w, bytes, packed, pbytes), WANVAE_ERR_ALIAS, "packed overlaps w");
     const hipError_t e = wanvae::launch_pack_conv3d_weights(w, packed, cin, cout, dtype == WANVAE_BF16,
                                                             static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "weight packing launch failed: %s", hipGetErrorString(e));
     return WANVAE_OK;
+}
+
+int wanvae_packed_conv3d_weight_elems(int32_t cin, int32_t cout, int32_t dtype, int64_t *elems) {
+    g_error.clear();
+    WV_CHECK(elems != nullptr, WANVAE_ERR_NULL, "elems is NULL");
+    WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
+    WV_CHECK(cin >= 1 && cin <= 1024 && cout >= 1 && cout <= 1024 &&
+                 (dtype != WANVAE_BF16 || cin % 16 == 0),
+             WANVAE_ERR_SHAPE, "unsupported channel counts %d -> %d", cin, cout);
+    *elems = wanvae::packed_conv3d_weight_elems(cin, cout, dtype == WANVAE_BF16);
+    return WANVAE_OK;
+}
+
+int wanvae_pointwise_conv(const void *x, const void *w, const float *bias, void *y, int64_t rows,
+                          int32_t cin, int32_t cout, int32_t dtype, void *stream) {
+    g_error.clear();
+    WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
+    WV_CHECK(cin >= 1 && cin <= 64 && cout >= 1 && cout <= 64, WANVAE_ERR_SHAPE,
+             "pointwise conv needs cin, cout in [1, 64] (got %d, %d)", cin, cout);
+    WV_CHECK(rows >= 0 && rows <= (INT64_MAX >> 12), WANVAE_ERR_SHAPE, "bad row count %lld",
+             (long long)rows);
+    if (rows == 0) return WANVAE_OK;
+    WV_CHECK(x && w && y, WANVAE_ERR_NULL, "x, w and y are required");
+    WV_CHECK(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(bias), WANVAE_ERR_SHAPE,
+             "pointers must be 16-byte aligned");
+    const size_t es = esize(dtype);
+    const size_t xb = (size_t)rows * cin * es, yb = (size_t)rows * cout * es;
+    WV_CHECK(!overlaps(y, yb, x, xb) && !overlaps(y, yb, w, (size_t)cout * cin * es) &&
+                 !overlaps(y, yb, bias, (size_t)cout * 4),
+             WANVAE_ERR_ALIAS, "y overlaps x, w or bias");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return timed_launch(WANVAE_KERNEL_POINTWISE, s, "pointwise_conv", [&] {
+        return wanvae::launch_pointwise_conv(x, w, bias, y, rows, cin, cout, dtype == WANVAE_BF16, s);
+    });
 }
 
 int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, const wanvae_dims *d,

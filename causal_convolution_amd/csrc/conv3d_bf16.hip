@@ -140,6 +140,7 @@ struct Args {
     uint16_t *y;            // [n][t][h][w][cout]
     int64_t N, T, H, W;
     int cin, cout, cres;
+    int cout_p;             // cout rounded up to 32: the packed weight's channel count
     int tiles_w, tiles_h;
     int64_t tiles;          // total tiles of the launch
     int x_sliced;           // x and cache frames are [cin/16][h][w][16], not [h][w][cin]
@@ -256,10 +257,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int ck = a.cin / kKC;
 
     if (tid <= TL::NWAVE) sync[tid] = 0;
-    for (int c = tid; c < a.cout; c += TL::kThreads) {
-        float b = a.bias ? a.bias[c] : 0.0f;
+    for (int c = tid; c < a.cout_p; c += TL::kThreads) {
+        float b = a.bias && c < a.cout ? a.bias[c] : 0.0f;
         if constexpr (EPI == EPI_SHORTCUT)
-            if (a.bsc) b += a.bsc[c];
+            if (a.bsc && c < a.cout) b += a.bsc[c];
         bias_lds[c] = b;
     }
     __syncthreads();
@@ -281,7 +282,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int64_t x_begin = a.tiles * wg_before / nwg;
     const int64_t x_count = a.tiles * (wg_before + wg_x) / nwg - x_begin;
 
-    const int ncb = a.cout / NB;   // output-channel blocks
+    const int ncb = a.cout_p / NB;   // output-channel blocks (the last may be partly padding)
     auto decode = [&](int64_t tile) __attribute__((always_inline)) {
         TileInfo ti;
         ti.n0 = (int)(tile % ncb) * NB;
@@ -312,7 +313,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // between its 16-channel slices
         const uint32_t cs2 = a.x_sliced ? (uint32_t)kUnit : (uint32_t)a.cin * 2;
         const int64_t slice_elems = a.x_sliced ? HW * kKC : kKC;
-        const uint32_t tap2 = (uint32_t)a.cout * kUnit;   // bytes per tap of a packed stage
+        const uint32_t tap2 = (uint32_t)a.cout_p * kUnit;   // bytes per tap of a packed stage
         // byte offset of block b's piece for a conv stage (sc = false) or a
         // shortcut stage (sc = true: x at the output positions, w_sc as one tap)
         auto block_off = [&](const TileInfo &ti, int b) __attribute__((always_inline)) -> uint32_t {
@@ -405,9 +406,9 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                         cc * slice_elems;
                 abytes = (uint32_t)(HW * a.cin * 2 - cc * slice_elems * 2);
                 // elements of the packed weight before stage (kt, cc)
-                const int64_t wskip = (int64_t)(kt * ck + cc) * 9 * a.cout * kKC;
+                const int64_t wskip = (int64_t)(kt * ck + cc) * 9 * a.cout_p * kKC;
                 bbase = a.w + wskip;
-                bbytes = (uint32_t)(((int64_t)27 * a.cin * a.cout - wskip) * 2);
+                bbytes = (uint32_t)(((int64_t)27 * a.cin * a.cout_p - wskip) * 2);
             } else {
                 // first 16-channel slice of this shortcut stage
                 const int cc = (si - ti.s_conv) * TL::SCS;
@@ -689,6 +690,13 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // position, and stored as 64 contiguous bytes per position, so a store
         // touches 16 cache lines instead of 32 and there are half as many.
         unsigned char *const epi = epi_stage + wave * kEpiBytes;
+        // A tile whose channel block runs past C_out (C_out not a multiple of
+        // 32), or whose rows are not 16-byte aligned (C_out % 8 != 0), stores
+        // each valid output channel by itself instead.  Only the 32-channel
+        // tile with a bias epilogue meets such C_out (the others need
+        // multiples of 64 or 96, the residual epilogues multiples of 32).
+        constexpr bool CAN_NARROW = EPI == EPI_BIAS && NB == 32;
+        const bool narrow = CAN_NARROW && ((a.cout & 7) != 0 || ti.n0 + NB > a.cout);
         auto store_rows = [&](int f0, int nrows, const u32x2 (*res)[FN][4]) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < nrows; ++e) {
@@ -712,11 +720,23 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                             v[2] += bf16_bits_to_f32(r.y & 0xffffu);
                             v[3] += bf16_bits_to_f32(r.y >> 16);
                         }
+                        if (narrow) {
+                            const int ww = ti.w0 + l32;
+                            const int c0 = ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (hh < H && ww < W && c0 + q < a.cout)
+                                    __builtin_amdgcn_raw_buffer_store_b16(
+                                        (unsigned short)f32_to_bf16_bits(v[q]), ry,
+                                        (uint32_t)((hh * W + ww) * a.cout + c0 + q) * 2, 0, 0);
+                            continue;
+                        }
                         u32x2 o;
                         o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
                         o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
                         *reinterpret_cast<u32x2 *>(epi + l32 * kEpiStride + j * 16 + g * 8) = o;
                     }
+                    if (narrow) continue;
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const int p = (lane >> 2) + 16 * half, q = lane & 3;
@@ -811,11 +831,12 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.W = c.w_;
     a.cin = c.cin;
     a.cout = c.cout;
+    a.cout_p = (c.cout + 31) / 32 * 32;
     a.cres = c.cres;
     a.x_sliced = c.x_sliced ? 1 : 0;
     a.tiles_w = (int)((c.w_ + kWB - 1) / kWB);
     a.tiles_h = (int)((c.h + TL::HB - 1) / TL::HB);
-    a.tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (c.cout / TL::NB);
+    a.tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (a.cout_p / TL::NB);
     if (a.tiles <= 0) return hipSuccess;
     // persistent grid: one workgroup per compute unit (the LDS ring takes most
     // of a CU's 160 KB), each looping over its share of the tiles
@@ -837,8 +858,7 @@ hipError_t launch_plain(const ConvLaunch &c, hipStream_t s) {
 }  // namespace
 
 bool conv3d_bf16_supported(int cin, int cout) {
-    return cin >= 32 && cin <= 1024 && cin % 32 == 0 && cout >= 32 && cout <= 1024 &&
-           cout % 32 == 0;
+    return cin >= 16 && cin <= 1024 && cin % 16 == 0 && cout >= 1 && cout <= 1024;
 }
 
 // Rows a tile height computes for an image height (the last tile is padded).
@@ -852,7 +872,8 @@ int64_t rows_computed(int64_t h, int hb) { return (h + hb - 1) / hb * hb; }
 //  - other multiples of 96: four MFMA waves of 3 rows x 96 channels (one wave
 //    per SIMD; a 2 x 3 grid of 32-channel waves puts two waves on two of the
 //    four SIMDs and one on the others, and measured 7% slower).
-//  - other multiples of 32: four waves of 4 rows x 32 channels.
+//  - any other C_out: four waves of 4 rows x 32 channels, the last channel
+//    block padded with zero weights (the decoder's 3-channel conv_out).
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
     const bool tall = rows_computed(c.h, 18) <= rows_computed(c.h, 16);
     if (c.res != nullptr && c.wsc != nullptr) {

@@ -43,14 +43,23 @@ hipError_t launch_rmsnorm_silu_bf16_sliced(const void *x, void *y, int64_t rows,
 hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, const float *gamma,
                                    const float *beta, float eps, hipStream_t s);
 
-// bf16 implicit-GEMM conv on MFMA: cin, cout (and cres) multiples of 32.
+// bf16 implicit-GEMM conv on MFMA: cin a multiple of 16, any cout (padded to a
+// multiple of 32 in the packed weight); cres (the block's shortcut input) a
+// multiple of 32.
 bool conv3d_bf16_supported(int cin, int cout);
 hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
 
 // Packs PyTorch-layout conv weights [cout][cin][3][3][3] for the conv kernels
-// (bf16: [3][cin/16][3][3][cout][16], cin % 16 == 0; fp32: [cout][3][3][3][cin]).
+// (bf16: [3][cin/16][3][3][cout_p][16], cin % 16 == 0, cout_p = cout rounded
+// up to 32 with zero weights in the padding; fp32: [cout][3][3][3][cin]).
+int64_t packed_conv3d_weight_elems(int cin, int cout, bool bf16);
 hipError_t launch_pack_conv3d_weights(const void *w, void *out, int cin, int cout, bool bf16,
                                       hipStream_t s);
+
+// 1x1x1 conv over rows of channels: y[r][co] = bias[co] + sum_ci w[co][ci] * x[r][ci],
+// x, w, y of one dtype, fp32 accumulation; cin, cout in [1, 64]; y must not overlap x.
+hipError_t launch_pointwise_conv(const void *x, const void *w, const float *bias, void *y,
+                                 int64_t rows, int cin, int cout, bool bf16, hipStream_t s);
 
 // fp32 direct conv, any channel counts.
 hipError_t launch_conv3d_f32(const ConvLaunch &a, hipStream_t s);

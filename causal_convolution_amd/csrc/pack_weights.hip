@@ -3,7 +3,8 @@
 // into the layout each conv kernel streams.
 //
 //   fp32: [C_out][kt][kh][kw][C_in]        (the direct kernel walks C_in innermost)
-//   bf16: [kt][C_in/16][kh][kw][C_out][16]
+//   bf16: [kt][C_in/16][kh][kw][C_out_p][16], C_out_p = C_out rounded up to 32
+//         (the MFMA tile's channel block), zero weights in the padding
 //
 // The bf16 layout follows the MFMA conv's K loop: one stage consumes temporal
 // tap kt and a 16-channel slice of C_in for all 9 (kh, kw) taps, so a stage's
@@ -30,35 +31,41 @@ __global__ void pack_f32_kernel(const T *__restrict__ w, T *__restrict__ out, in
 }
 
 __global__ void pack_bf16_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ out, int cin,
-                                 int cout, int64_t total) {
+                                 int cout, int cout_p, int64_t total) {
     const int slices = cin / 16;
     for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
          o += (int64_t)gridDim.x * blockDim.x) {
-        // o = ((((kt * slices + cc) * 9 + khw) * cout + co) * 16 + c16
+        // o = ((((kt * slices + cc) * 9 + khw) * cout_p + co) * 16 + c16
         const int c16 = (int)(o % 16);
         int64_t r = o / 16;
-        const int co = (int)(r % cout);
-        r /= cout;
+        const int co = (int)(r % cout_p);
+        r /= cout_p;
         const int khw = (int)(r % 9);
         r /= 9;
         const int cc = (int)(r % slices);
         const int kt = (int)(r / slices);
         const int ci = cc * 16 + c16;
-        out[o] = w[((int64_t)co * cin + ci) * 27 + kt * 9 + khw];
+        // output channels past cout are padding: zero weights
+        out[o] = co < cout ? w[((int64_t)co * cin + ci) * 27 + kt * 9 + khw] : (uint16_t)0;
     }
 }
 
 }  // namespace
 
+int64_t packed_conv3d_weight_elems(int cin, int cout, bool bf16) {
+    return (int64_t)27 * cin * (bf16 ? (cout + 31) / 32 * 32 : cout);
+}
+
 hipError_t launch_pack_conv3d_weights(const void *w, void *out, int cin, int cout, bool bf16,
                                       hipStream_t s) {
-    const int64_t total = (int64_t)27 * cin * cout;
+    const int64_t total = packed_conv3d_weight_elems(cin, cout, bf16);
     if (total == 0) return hipSuccess;
     const int64_t want = (total + 255) / 256;
     const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
     if (bf16)
         pack_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(w),
-                                              static_cast<uint16_t *>(out), cin, cout, total);
+                                              static_cast<uint16_t *>(out), cin, cout,
+                                              (cout + 31) / 32 * 32, total);
     else
         pack_f32_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(w),
                                                     static_cast<float *>(out), cin, cout, total);

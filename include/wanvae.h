@@ -123,24 +123,50 @@ WANVAE_API int wanvae_rmsnorm_silu(const void *x, void *y, int64_t rows, int32_t
  *   w     : packed weight (wanvae_pack_conv3d_weights, cin x cout, dtype).
  *   bias  : [cout] fp32 or NULL.
  *   y     : [d.n][d.t][d.h][d.w][cout] of dtype; must not overlap x, cache, w.
- *   Channels: bf16 needs cin and cout multiples of 32 and <= 1024 (bf16 MFMA
- *   implicit GEMM); fp32 accepts 1..1024 (direct fp32 kernel).
+ *   Channels: bf16 (MFMA implicit GEMM) needs cin a multiple of 16 in
+ *   [16, 1024] and cout in [1, 1024] (the decoder's conv_in, 16 latent
+ *   channels in, and conv_out, 3 channels out, included); fp32 (direct
+ *   kernel) accepts 1..1024 for both.
  */
 /*
  * Packs a 3x3x3 conv weight for wanvae_causal_conv3d and the ResidualBlock
  * calls.  Input: w = [cout][cin][3][3][3] of dtype, the pages' weight layout
  * [C_out, C_in, kD, kH, kW] ("Sharding of WAN 2.2 VAE", Available Sharding
- * Dimensions).  Output: `packed`, 27*cin*cout elements of dtype, laid out as
- *   fp32: [cout][kt][kh][kw][cin]
- *   bf16: [kt][cin/16][kh][kw][cout][16]  (cin a multiple of 16)
- * The bf16 order is the MFMA conv's K loop (temporal tap, 16-channel slice,
- * then the 9 spatial taps), so each tap's slice for all output channels is
- * one contiguous run.  Runs one GPU gather kernel on `stream`; meant for
- * set-up, once per weight.  `packed` must not overlap `w`; both are owned by
- * the caller.
+ * Dimensions).  Output: `packed`, wanvae_packed_conv3d_weight_elems elements
+ * of dtype, laid out as
+ *   fp32: [cout][kt][kh][kw][cin]                    (27*cin*cout elements)
+ *   bf16: [kt][cin/16][kh][kw][cout_p][16]           (27*cin*cout_p elements)
+ * with cout_p = cout rounded up to a multiple of 32 (the MFMA tile's channel
+ * block) and zero weights for the padding channels; cin a multiple of 16 for
+ * bf16.  The bf16 order is the MFMA conv's K loop (temporal tap, 16-channel
+ * slice, then the 9 spatial taps), so each tap's slice for all output
+ * channels is one contiguous run.  Runs one GPU gather kernel on `stream`;
+ * meant for set-up, once per weight.  `packed` must not overlap `w`; both are
+ * owned by the caller.
  */
 WANVAE_API int wanvae_pack_conv3d_weights(const void *w, void *packed, int32_t cin, int32_t cout,
                                           int32_t dtype, void *stream);
+
+/* Elements of a packed conv weight (cin -> cout, dtype): the buffer size
+ * wanvae_pack_conv3d_weights fills.  Host only; writes *elems. */
+WANVAE_API int wanvae_packed_conv3d_weight_elems(int32_t cin, int32_t cout, int32_t dtype,
+                                                 int64_t *elems);
+
+/*
+ * Pointwise (1x1x1) conv over `rows` positions:
+ *   y[r][co] = bias[co] + sum_ci w[co][ci] * x[r][ci]
+ * The decoder's post_quant_conv, a CausalConv3d of kernel size 1 over the
+ * latent channels ("Sharding of WAN 2.2 VAE", the decoder module tree); with
+ * kernel size 1 there is no causal pad and no cache.  fp32 accumulation over
+ * ascending ci, bias added last, one rounding for bf16 outputs.
+ *   x : [rows][cin] of dtype (channels-last positions);  y : [rows][cout] of
+ *       dtype, must not overlap x, w or bias.
+ *   w : [cout][cin] of dtype;  bias : [cout] fp32 or NULL.
+ *   cin, cout in [1, 64] (small-channel kernel: one thread per output value).
+ */
+WANVAE_API int wanvae_pointwise_conv(const void *x, const void *w, const float *bias, void *y,
+                                     int64_t rows, int32_t cin, int32_t cout, int32_t dtype,
+                                     void *stream);
 
 WANVAE_API int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const float *bias,
                          void *y, const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
@@ -209,11 +235,12 @@ WANVAE_API const char *wanvae_last_error(void);
  * stream.  wanvae_timing_read waits for the recorded events and returns, for
  * one kernel kind, the number of launches and their summed duration in ms.
  * Kinds: 0 = fused RMS_norm+SiLU, 1 = bf16 MFMA conv, 2 = fp32 conv,
- * 3 = cache roll.  wanvae_timing_reset forgets all records.  Timing state is
- * process-wide; enable it only while one thread drives the library.
+ * 3 = cache roll, 4 = pointwise conv.  wanvae_timing_reset forgets all
+ * records.  Timing state is process-wide; enable it only while one thread
+ * drives the library.
  */
 enum { WANVAE_KERNEL_NORM = 0, WANVAE_KERNEL_CONV_BF16 = 1, WANVAE_KERNEL_CONV_F32 = 2,
-       WANVAE_KERNEL_ROLL = 3, WANVAE_KERNEL_KINDS = 4 };
+       WANVAE_KERNEL_ROLL = 3, WANVAE_KERNEL_POINTWISE = 4, WANVAE_KERNEL_KINDS = 5 };
 WANVAE_API int wanvae_timing_enable(int on);
 WANVAE_API int wanvae_timing_reset(void);
 WANVAE_API int wanvae_timing_read(int32_t kind, int64_t *launches, double *total_ms);

@@ -187,6 +187,24 @@ def shortcut(blk: Block, x):
     return y
 
 
+def pointwise_conv(x, w, bias=None):
+    """1x1x1 conv over channels-last positions: x [..., Cin], w [Cout, Cin]
+    -> [..., Cout], y = bias + sum_ci w[co, ci] x[..., ci] (fp64 sum, one
+    rounding).  The decoder's post_quant_conv is a CausalConv3d of kernel 1
+    ("Sharding of WAN 2.2 VAE", decoder module tree); kernel 1 has no causal
+    pad.  Same routine as the block's 1x1x1 shortcut."""
+    x = _f32(x)
+    w = _f32(w)
+    cout, cin = w.shape
+    assert x.shape[-1] == cin
+    bias = None if bias is None else _f32(bias)
+    rows = x.reshape(1, 1, 1, -1, cin)
+    y = np.empty(rows.shape[:-1] + (cout,), np.float32)
+    cb = _Block(cin, cout, 0.0, None, None, None, None, None, None, None, None, _ptr(w), _ptr(bias))
+    lib().oracle_shortcut(C.byref(cb), _ptr(np.ascontiguousarray(rows)), _ptr(y), 1, 1, 1, rows.shape[3])
+    return y.reshape(x.shape[:-1] + (cout,))
+
+
 def resblock_full(blk: Block, x):
     x = _f32(x)
     N, T, H, W, Cin = x.shape

@@ -63,7 +63,10 @@ def test_conv_validation():
     L = wv.lib()
     p = C.c_void_p(1 << 24)
     d = _dims()
-    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(d), 48, 64, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(d), 24, 64, wv.BF16, None) == wv.ERR_SHAPE
+    assert "multiple of 16" in wv.last_error()
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(d), 64, 0, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(d), 64, 1025, wv.BF16, None) == wv.ERR_SHAPE
     assert L.wanvae_causal_conv3d(p, None, p, None, p, C.byref(d), 64, 2048, wv.F32, None) == wv.ERR_SHAPE
     assert L.wanvae_causal_conv3d(p, None, p, None, p, None, 64, 64, wv.BF16, None) == wv.ERR_NULL
     assert L.wanvae_causal_conv3d(None, None, p, None, p, C.byref(d), 64, 64, wv.BF16, None) == wv.ERR_NULL
@@ -77,6 +80,37 @@ def test_conv_validation():
     empty = _dims(1, 0, 3, 4)
     assert L.wanvae_causal_conv3d(None, None, None, None, None, C.byref(empty), 64, 64, wv.BF16,
                                   None) == wv.OK
+
+
+def test_packed_weight_elems():
+    L = wv.lib()
+    n = C.c_int64(0)
+    assert L.wanvae_packed_conv3d_weight_elems(96, 3, wv.BF16, C.byref(n)) == wv.OK
+    assert n.value == 27 * 96 * 32                 # bf16: C_out padded to the 32-channel block
+    assert L.wanvae_packed_conv3d_weight_elems(16, 384, wv.BF16, C.byref(n)) == wv.OK
+    assert n.value == 27 * 16 * 384
+    assert L.wanvae_packed_conv3d_weight_elems(3, 5, wv.F32, C.byref(n)) == wv.OK
+    assert n.value == 27 * 3 * 5                   # fp32: no padding
+    assert L.wanvae_packed_conv3d_weight_elems(24, 3, wv.BF16, C.byref(n)) == wv.ERR_SHAPE
+    assert L.wanvae_packed_conv3d_weight_elems(16, 0, wv.BF16, C.byref(n)) == wv.ERR_SHAPE
+    assert L.wanvae_packed_conv3d_weight_elems(16, 3, 5, C.byref(n)) == wv.ERR_DTYPE
+    assert L.wanvae_packed_conv3d_weight_elems(16, 3, wv.BF16, None) == wv.ERR_NULL
+
+
+def test_pointwise_validation():
+    L = wv.lib()
+    p, q = C.c_void_p(1 << 24), C.c_void_p(1 << 30)
+    assert L.wanvae_pointwise_conv(p, p, None, q, 10, 65, 16, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_pointwise_conv(p, p, None, q, 10, 16, 0, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_pointwise_conv(p, p, None, q, -1, 16, 16, wv.BF16, None) == wv.ERR_SHAPE
+    assert L.wanvae_pointwise_conv(p, p, None, q, 10, 16, 16, 3, None) == wv.ERR_DTYPE
+    assert L.wanvae_pointwise_conv(None, p, None, q, 10, 16, 16, wv.BF16, None) == wv.ERR_NULL
+    assert L.wanvae_pointwise_conv(p, p, None, C.c_void_p((1 << 30) + 2), 10, 16, 16, wv.BF16,
+                                   None) == wv.ERR_SHAPE
+    # y may not overlap x
+    assert L.wanvae_pointwise_conv(p, q, None, C.c_void_p((1 << 24) + 16), 10, 16, 16, wv.BF16,
+                                   None) == wv.ERR_ALIAS
+    assert L.wanvae_pointwise_conv(None, None, None, None, 0, 16, 16, wv.BF16, None) == wv.OK
 
 
 def test_pack_validation():

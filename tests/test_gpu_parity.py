@@ -96,6 +96,12 @@ CONV_SHAPES = [
     # C_out a multiple of 96 but not 64: 12-row tiles of 96 channels
     (1, 2, 13, 40, 96, 288),     # 3 channel blocks, ragged H (13 = 12 + 1) and W
     (1, 3, 24, 32, 32, 96),      # exact tiles, smallest input slice count
+    # the decoder's head and tail: 16 latent channels in (conv_in), 3 out (conv_out)
+    (1, 3, 10, 40, 16, 384),     # one 16-channel stage per temporal tap
+    (1, 3, 12, 40, 96, 3),       # C_out padded to one 32-channel block, 2-byte stores
+    (2, 2, 9, 33, 16, 3),        # both at once, batch 2
+    (1, 2, 5, 35, 32, 40),       # a partial second channel block (40 = 32 + 8)
+    (1, 2, 6, 33, 48, 100),      # C_out % 8 != 0 (rows not 16-byte aligned)
 ]
 
 
@@ -145,7 +151,8 @@ def test_causal_conv3d_no_bias_and_empty(torch, wv):
     assert wv.causal_conv3d(e, pw).shape == (1, 0, 8, 32, 32)
 
 
-@pytest.mark.parametrize("cin,cout,dtype", [(16, 1, wl.BF16), (48, 96, wl.BF16), (384, 192, wl.BF16),
+@pytest.mark.parametrize("cin,cout,dtype", [(16, 1, wl.BF16), (16, 3, wl.BF16), (48, 96, wl.BF16),
+                                            (96, 40, wl.BF16), (384, 192, wl.BF16),
                                             (3, 5, wl.F32), (64, 33, wl.F32)])
 def test_pack_conv3d_weights_layout(torch, wv, cin, cout, dtype):
     """The packed order is the one the header documents, element for element
@@ -155,13 +162,34 @@ def test_pack_conv3d_weights_layout(torch, wv, cin, cout, dtype):
     got = gu.to_host(wv.pack_conv3d_weights(gu.to_dev(w, dtype)).data)
     taps = w.reshape(cout, cin, 27)
     if dtype == wl.BF16:
-        # [kt][cin/16][kh*3+kw][cout][16]
-        want = taps.reshape(cout, cin // 16, 16, 3, 9).transpose(3, 1, 4, 0, 2).reshape(-1)
+        # [kt][cin/16][kh*3+kw][cout_p][16], cout_p = cout rounded up to 32, zero padding
+        cout_p = (cout + 31) // 32 * 32
+        taps = np.concatenate([taps, np.zeros((cout_p - cout, cin, 27), taps.dtype)])
+        want = taps.reshape(cout_p, cin // 16, 16, 3, 9).transpose(3, 1, 4, 0, 2).reshape(-1)
     else:
         # [cout][kt*9+kh*3+kw][cin]
         want = taps.transpose(0, 2, 1).reshape(-1)
     assert got.shape == want.shape
     assert np.array_equal(got.astype(np.float32), want.astype(np.float32))
+
+
+# --------------------------------------------------------------------------- pointwise
+@pytest.mark.parametrize("dt", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("cin,cout", [(16, 16), (16, 3), (64, 48), (1, 1)])
+@pytest.mark.parametrize("rows", [1, 1000, 70001])
+def test_pointwise_conv(torch, wv, dt, cin, cout, rows):
+    """1x1x1 conv (the decoder's post_quant_conv, 16 -> 16) against the oracle."""
+    rng = np.random.default_rng(cin * 7 + cout * 3 + rows)
+    x = rnd(rng, (rows, cin), 1.0, dt)
+    w = rnd(rng, (cout, cin), 1 / math.sqrt(cin), dt)
+    b = rnd(rng, (cout,), 0.1)
+    ref = oracle.pointwise_conv(x, w, b)
+    y = wv.pointwise_conv(gu.to_dev(x, dt), gu.to_dev(w, dt), gu.to_dev(b, wl.F32))
+    err = gu.rel_err(gu.to_host(y), ref)
+    gu.report(f"pointwise {dt} {cin}->{cout} rows={rows}", err, tol(dt))
+    assert err <= tol(dt)
+    y0 = wv.pointwise_conv(gu.to_dev(x, dt), gu.to_dev(w, dt), None)
+    assert gu.rel_err(gu.to_host(y0), oracle.pointwise_conv(x, w, None)) <= tol(dt)
 
 
 # --------------------------------------------------------------------------- block, small

@@ -263,6 +263,21 @@ def test_conv_cache_is_prepended_frames(orc):
 
 
 # --------------------------------------------------------------------------- shortcut
+def test_pointwise_conv_is_a_channel_matmul(orc):
+    """post_quant_conv (1x1x1): against an fp64 matmul, with and without bias,
+    for a batch of positions of any leading shape."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((2, 3, 4, 16)).astype(np.float32)
+    w = rng.standard_normal((5, 16)).astype(np.float32)
+    b = rng.standard_normal(5).astype(np.float32)
+    want = np.einsum("...i,oi->...o", x.astype(np.float64), w.astype(np.float64)) + b
+    got = orc.pointwise_conv(x, w, b)
+    assert got.shape == (2, 3, 4, 5)
+    assert np.array_equal(got, want.astype(np.float32))
+    want0 = np.einsum("...i,oi->...o", x.astype(np.float64), w.astype(np.float64))
+    assert np.array_equal(orc.pointwise_conv(x, w, None), want0.astype(np.float32))
+
+
 def test_shortcut_identity_and_matmul(orc):
     p = block_params(6, 6)
     x = rnd(1, 2, 3, 4, 6)
