@@ -81,6 +81,10 @@ def lib():
         L.oracle_resblock_stream.argtypes = [C.POINTER(_Block), _f32p, _f32p,
                                              _i64, _i64, _i64, _i64, _i64]
         L.oracle_resblock_window.argtypes = [C.POINTER(_Block), _f32p] + [_i64] * 16 + [_f32p]
+        L.oracle_attention_frame.argtypes = [_f32p, _i64, C.c_int, _f32p, _f32p, C.c_double,
+                                             _f32p, _f32p, _f32p, _f32p, C.POINTER(C.c_int64),
+                                             _i64, _f32p]
+        L.oracle_attention_frame.restype = None
         for f in ("oracle_norm_silu", "oracle_rms_norm", "oracle_causal_conv3d", "oracle_shortcut",
                   "oracle_resblock_full", "oracle_resblock_stream_step",
                   "oracle_resblock_stream", "oracle_resblock_window"):
@@ -203,6 +207,43 @@ def pointwise_conv(x, w, bias=None):
     cb = _Block(cin, cout, 0.0, None, None, None, None, None, None, None, None, _ptr(w), _ptr(bias))
     lib().oracle_shortcut(C.byref(cb), _ptr(np.ascontiguousarray(rows)), _ptr(y), 1, 1, 1, rows.shape[3])
     return y.reshape(x.shape[:-1] + (cout,))
+
+
+def attention_block(x, gamma, beta, wqkv, bqkv, wo, bo, eps: float = EPS, frame=None,
+                    queries=None):
+    """Decoder mid-block attention (readings in oracle.c, oracle_attention_frame).
+
+    x [N,T,H,W,C]; wqkv [3C,C], bqkv [3C] (q, k, v rows in that order); wo [C,C],
+    bo [C].  Returns y [N,T,H,W,C] for every frame, or, with frame=(n, t) and
+    queries (flat h*W+w indices of that frame), y at those positions [nq, C]."""
+    x = _f32(x)
+    N, T, H, W, C_ = x.shape
+    HW = H * W
+    g, wqkv, wo = _f32(gamma), _f32(wqkv), _f32(wo)
+    b = None if beta is None else _f32(beta)
+    bq = None if bqkv is None else _f32(bqkv)
+    bo_ = None if bo is None else _f32(bo)
+    assert wqkv.shape == (3 * C_, C_) and wo.shape == (C_, C_)
+
+    def run(frame_x, qidx):
+        fx = np.ascontiguousarray(frame_x.reshape(HW, C_))
+        nq = HW if qidx is None else len(qidx)
+        y = np.empty((nq, C_), np.float32)
+        qi = None if qidx is None else np.ascontiguousarray(qidx, dtype=np.int64)
+        lib().oracle_attention_frame(
+            _ptr(fx), HW, C_, _ptr(g), _ptr(b), float(eps), _ptr(wqkv), _ptr(bq), _ptr(wo),
+            _ptr(bo_), None if qi is None else qi.ctypes.data_as(C.POINTER(C.c_int64)), nq,
+            _ptr(y))
+        return y
+
+    if frame is not None:
+        n, t = frame
+        return run(x[n, t], queries)
+    out = np.empty_like(x)
+    for n in range(N):
+        for t in range(T):
+            out[n, t] = run(x[n, t], None).reshape(H, W, C_)
+    return out
 
 
 def resblock_full(blk: Block, x):

@@ -410,3 +410,102 @@ void oracle_resblock_window(const oracle_block *p, const float *x_region, int64_
 
     free(n1); free(a); free(n2);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decoder mid-block attention over one frame.                               */
+/* "Closing the gap: Wan 2.2 14B VAE decoder", section 5: the decoder's one  */
+/* attention block is a spatial self-attention in which, within a frame,     */
+/* every position attends to every other; the sequence is the H*W grid and  */
+/* each (batch, frame) is an independent problem.  "Sharding of WAN 2.2     */
+/* VAE", decoder module tree: WanAttentionBlock(384) between the mid-block's */
+/* two ResidualBlocks.  The pages give nothing more; the readings used:      */
+/*   u = RMS_norm(x; gamma, beta)          (the decoder's norm, no SiLU)     */
+/*   [q | k | v] = wqkv u + bqkv           (one 1x1x1 projection, [3C][C];   */
+/*                                           rows 0..C-1 q, C..2C-1 k, then v)*/
+/*   p_ij = softmax_j(q_i . k_j / sqrt(C)) (one head of width C, over all    */
+/*                                           H*W positions j of the frame)   */
+/*   o_i = sum_j p_ij v_j                                                    */
+/*   y_i = x_i + wo o_i + bo               (1x1x1 output projection, [C][C], */
+/*                                           and the residual)              */
+/* u, q, k, v and o are stored as fp32; every sum runs in fp64 in ascending  */
+/* index order; the softmax subtracts the row maximum before exp (exact in   */
+/* real arithmetic).                                                         */
+/* x: one frame [HW][C]; y: [nq][C] for the query positions qidx[0..nq-1]    */
+/* (qidx NULL: all HW positions in order, nq = HW).                          */
+/* ------------------------------------------------------------------------ */
+void oracle_attention_frame(const float *x, int64_t HW, int C, const float *gamma,
+                            const float *beta, double eps, const float *wqkv, const float *bqkv,
+                            const float *wo, const float *bo, const int64_t *qidx, int64_t nq,
+                            float *y)
+{
+    float *u = (float *)malloc(sizeof(float) * (size_t)(HW * C));
+    float *k = (float *)malloc(sizeof(float) * (size_t)(HW * C));
+    float *v = (float *)malloc(sizeof(float) * (size_t)(HW * C));
+    if (!u || !k || !v) { fprintf(stderr, "oracle: out of memory\n"); abort(); }
+    oracle_rms_norm(x, u, HW, C, gamma, beta, eps);
+
+    /* k and v of every position of the frame */
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < HW; ++j) {
+        const float *uj = u + j * (int64_t)C;
+        for (int c = 0; c < C; ++c) {
+            double sk = 0.0, sv = 0.0;
+            const float *wk = wqkv + ((int64_t)C + c) * C;
+            const float *wv = wqkv + ((int64_t)2 * C + c) * C;
+            for (int i = 0; i < C; ++i) {
+                sk += (double)wk[i] * (double)uj[i];
+                sv += (double)wv[i] * (double)uj[i];
+            }
+            k[j * (int64_t)C + c] = (float)(sk + (bqkv ? (double)bqkv[C + c] : 0.0));
+            v[j * (int64_t)C + c] = (float)(sv + (bqkv ? (double)bqkv[2 * C + c] : 0.0));
+        }
+    }
+
+    const double scale = 1.0 / sqrt((double)C);
+    #pragma omp parallel
+    {
+        float *q = (float *)malloc(sizeof(float) * (size_t)C);
+        float *o = (float *)malloc(sizeof(float) * (size_t)C);
+        double *s = (double *)malloc(sizeof(double) * (size_t)HW);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)C);
+        if (!q || !o || !s || !acc) { fprintf(stderr, "oracle: out of memory\n"); abort(); }
+        #pragma omp for schedule(static)
+        for (int64_t r = 0; r < nq; ++r) {
+            const int64_t i = qidx ? qidx[r] : r;
+            const float *ui = u + i * (int64_t)C;
+            for (int c = 0; c < C; ++c) {
+                double sq = 0.0;
+                const float *wq = wqkv + (int64_t)c * C;
+                for (int t = 0; t < C; ++t) sq += (double)wq[t] * (double)ui[t];
+                q[c] = (float)(sq + (bqkv ? (double)bqkv[c] : 0.0));
+            }
+            double m = -INFINITY;
+            for (int64_t j = 0; j < HW; ++j) {
+                double d = 0.0;
+                const float *kj = k + j * (int64_t)C;
+                for (int c = 0; c < C; ++c) d += (double)q[c] * (double)kj[c];
+                s[j] = d * scale;
+                if (s[j] > m) m = s[j];
+            }
+            double z = 0.0;
+            for (int c = 0; c < C; ++c) acc[c] = 0.0;
+            for (int64_t j = 0; j < HW; ++j) {
+                const double e = exp(s[j] - m);
+                z += e;
+                const float *vj = v + j * (int64_t)C;
+                for (int c = 0; c < C; ++c) acc[c] += e * (double)vj[c];
+            }
+            for (int c = 0; c < C; ++c) o[c] = (float)(acc[c] / z);
+            const float *xi = x + i * (int64_t)C;
+            for (int co = 0; co < C; ++co) {
+                double t = 0.0;
+                const float *w = wo + (int64_t)co * C;
+                for (int c = 0; c < C; ++c) t += (double)w[c] * (double)o[c];
+                y[r * (int64_t)C + co] =
+                    (float)((double)xi[co] + t + (bo ? (double)bo[co] : 0.0));
+            }
+        }
+        free(q); free(o); free(s); free(acc);
+    }
+    free(u); free(k); free(v);
+}

@@ -36,6 +36,13 @@ MUTANTS = {
                               "roll_cache(cache_a, x, N, Tc, H, W, p->cin);"),
     "window_halo_too_small": ("int64_t ah0 = max64(bh0 - 1, 0), ah1 = min64(bh1 + 1, H);",
                               "int64_t ah0 = bh0, ah1 = bh1;"),
+    "attention_missing_scale": ("s[j] = d * scale;", "s[j] = d;"),
+    "attention_not_normalised": ("o[c] = (float)(acc[c] / z);", "o[c] = (float)acc[c];"),
+    "attention_dropped_residual": ("(float)((double)xi[co] + t +", "(float)(t +"),
+    "attention_k_v_swapped": ("const float *wk = wqkv + ((int64_t)C + c) * C;",
+                              "const float *wk = wqkv + ((int64_t)2 * C + c) * C;"),
+    "attention_query_from_raw_input": ("sq += (double)wq[t] * (double)ui[t];",
+                                       "sq += (double)wq[t] * (double)x[i * (int64_t)C + t];"),
 }
 
 

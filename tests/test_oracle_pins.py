@@ -380,3 +380,127 @@ def test_window_equals_full_bitwise(orc, box):
     got = orc.resblock_window(blk, xr, reg, (T, H, W), box)
     t0, t1, h0, h1, w0, w1 = box
     assert np.array_equal(got, full[:, t0:t1, h0:h1, w0:w1])
+
+
+# --------------------------------------------------------------------------- attention
+def _attn_params(rng, C, scale=1.0):
+    g = rng.uniform(0.5, 1.5, C).astype(np.float32)
+    b = (rng.standard_normal(C) * 0.3).astype(np.float32)
+    wqkv = (rng.standard_normal((3 * C, C)) * scale / np.sqrt(C)).astype(np.float32)
+    bqkv = (rng.standard_normal(3 * C) * 0.1).astype(np.float32)
+    wo = (rng.standard_normal((C, C)) / np.sqrt(C)).astype(np.float32)
+    bo = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    return g, b, wqkv, bqkv, wo, bo
+
+
+def _attn_torch(x, g, b, wqkv, bqkv, wo, bo):
+    """The same block from library routines in fp64: F.normalize for the norm,
+    scaled_dot_product_attention (one head, default 1/sqrt(C) scale), matmul."""
+    import torch
+    N, T, H, W, C = x.shape
+    X = torch.from_numpy(x).double()
+    t = lambda a: torch.from_numpy(a).double()
+    u = torch.nn.functional.normalize(X, dim=-1, eps=1e-12) * C ** 0.5 * t(g) + t(b)
+    q, k, v = (u @ t(wqkv).T + t(bqkv)).split(C, -1)
+    shp = (N * T, 1, H * W, C)
+    o = torch.nn.functional.scaled_dot_product_attention(q.reshape(shp), k.reshape(shp), v.reshape(shp))
+    return (X + (o.reshape(N, T, H, W, C) @ t(wo).T + t(bo))).numpy()
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 3, 5, 8), (2, 1, 4, 4, 16), (1, 3, 1, 7, 4)])
+def test_attention_matches_library_routines(orc, shape):
+    rng = np.random.default_rng(sum(shape))
+    x = rng.standard_normal(shape).astype(np.float32)
+    p = _attn_params(rng, shape[-1], scale=2.0)
+    y = orc.attention_block(x, *p)
+    ref = _attn_torch(x, *p)
+    assert np.abs(y - ref).max() <= 2e-6 * np.abs(ref).max()
+
+
+def test_attention_zero_output_projection_is_identity(orc):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((1, 2, 3, 4, 8)).astype(np.float32)
+    g, b, wqkv, bqkv, wo, bo = _attn_params(rng, 8)
+    y = orc.attention_block(x, g, b, wqkv, bqkv, np.zeros_like(wo), np.zeros_like(bo))
+    assert np.array_equal(y, x)
+
+
+def test_attention_constant_values(orc):
+    """v = c at every position (value weights 0, value bias c): any softmax
+    weights average to c, so y = x + wo c + bo whatever q and k are."""
+    rng = np.random.default_rng(2)
+    C = 8
+    x = rng.standard_normal((1, 2, 3, 4, C)).astype(np.float32)
+    g, b, wqkv, bqkv, wo, bo = _attn_params(rng, C)
+    wqkv[2 * C:] = 0.0
+    c = rng.standard_normal(C).astype(np.float32)
+    bqkv[2 * C:] = c
+    y = orc.attention_block(x, g, b, wqkv, bqkv, wo, bo)
+    want = x.astype(np.float64) + (wo.astype(np.float64) @ c.astype(np.float64) + bo)
+    assert np.abs(y - want).max() <= 1e-6 * np.abs(want).max()
+
+
+def test_attention_uniform_scores_average_values(orc):
+    """k = 0 (key weights and bias 0): every score is 0, the softmax is uniform
+    and o is the mean of v over the frame's positions."""
+    rng = np.random.default_rng(3)
+    C, H, W = 8, 3, 5
+    x = rng.standard_normal((1, 2, H, W, C)).astype(np.float32)
+    g, b, wqkv, bqkv, wo, bo = _attn_params(rng, C)
+    wqkv[C:2 * C] = 0.0
+    bqkv[C:2 * C] = 0.0
+    y = orc.attention_block(x, g, b, wqkv, bqkv, wo, bo)
+    u = orc.rms_norm(x, g, b).astype(np.float64)
+    v = u @ wqkv[2 * C:].astype(np.float64).T + bqkv[2 * C:]
+    mean_v = v.mean(axis=(2, 3), keepdims=True)
+    want = x + mean_v @ wo.astype(np.float64).T + bo
+    assert np.abs(y - want).max() <= 1e-5 * np.abs(want).max()
+
+
+def test_attention_single_position_returns_its_value(orc):
+    """One position per frame: the softmax has one term, o = v."""
+    rng = np.random.default_rng(4)
+    C = 16
+    x = rng.standard_normal((1, 3, 1, 1, C)).astype(np.float32)
+    g, b, wqkv, bqkv, wo, bo = _attn_params(rng, C)
+    y = orc.attention_block(x, g, b, wqkv, bqkv, wo, bo)
+    u = orc.rms_norm(x, g, b).astype(np.float64)
+    v = u @ wqkv[2 * C:].astype(np.float64).T + bqkv[2 * C:]
+    want = x + v @ wo.astype(np.float64).T + bo
+    assert np.abs(y - want).max() <= 1e-5 * np.abs(want).max()
+
+
+def test_attention_frames_are_independent(orc):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 3, 3, 4, 8)).astype(np.float32)
+    p = _attn_params(rng, 8)
+    y = orc.attention_block(x, *p)
+    x2 = x.copy()
+    x2[1, 2] += 1.0
+    x2[0, 0] *= 3.0
+    y2 = orc.attention_block(x2, *p)
+    assert np.array_equal(y2[0, 1:], y[0, 1:]) and np.array_equal(y2[1, :2], y[1, :2])
+    assert not np.array_equal(y2[1, 2], y[1, 2])
+
+
+def test_attention_permutation_equivariant(orc):
+    """Permuting the positions of a frame permutes its output."""
+    rng = np.random.default_rng(6)
+    H, W, C = 3, 5, 8
+    x = rng.standard_normal((1, 1, H, W, C)).astype(np.float32)
+    p = _attn_params(rng, C)
+    y = orc.attention_block(x, *p).reshape(H * W, C)
+    perm = rng.permutation(H * W)
+    xp = x.reshape(H * W, C)[perm].reshape(1, 1, H, W, C)
+    yp = orc.attention_block(xp, *p).reshape(H * W, C)
+    assert np.abs(yp - y[perm]).max() <= 1e-6 * np.abs(y).max()
+
+
+def test_attention_sampled_queries_equal_full(orc):
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 2, 4, 6, 8)).astype(np.float32)
+    p = _attn_params(rng, 8)
+    y = orc.attention_block(x, *p)
+    q = [23, 0, 7, 7, 11]
+    ys = orc.attention_block(x, *p, frame=(0, 1), queries=q)
+    assert np.array_equal(ys, y[0, 1].reshape(-1, 8)[q])
