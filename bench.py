@@ -175,6 +175,59 @@ def head_tail(torch, wv, steps, warmup):
             "steps": steps, "warmup": warmup, "ops": res}
 
 
+def attention(torch, wv, wl, steps, warmup):
+    """The decoder mid-block attention block (wanvae_attention_block) over the
+    latent clip [1,21,90,160,384] bf16: frames/s of the whole block, and per
+    kernel kind the average launch time and its roofline fraction.  The flash
+    kernel's work is 4 * F * HW^2 * C FLOP (scores and the value product); the
+    projections' 2 * P * C * 4C; norm and transpose are counted in bytes."""
+    w = wl.custom("attention", wl.BF16, 1, 21, 90, 160, 384, 384)
+    p = wl.make_attention_params(384, seed=0)
+    blk = wv.AttentionBlock.from_host(p)
+    x = wl.make_x_device(w, seed=0)
+    y = torch.empty_like(x)
+    ws = blk.workspace(w.n, w.t, w.h, w.w)
+    for _ in range(warmup):
+        blk.forward(x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    wv.timing_reset()
+    wv.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(steps):
+        blk.forward(x, out=y, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wv.timing_enable(False)
+    total_ms = e0.elapsed_time(e1)
+    P, F, HW, C = w.positions, w.n * w.t, w.h * w.w, 384
+    kinds = {"flash attention": (wv.KERNEL_ATTENTION, 4.0 * F * HW * HW * C, None),
+             "q/k/v + output projections (MFMA GEMM)": (wv.KERNEL_GEMM, 2.0 * P * C * 4 * C / 2, None),
+             "RMS_norm": (wv.KERNEL_NORM, None, 2.0 * P * C * 2),
+             "v transpose": (wv.KERNEL_TRANSPOSE, None, 2.0 * P * C * 2)}
+    ops = []
+    for name, (kind, flop, nbytes) in kinds.items():
+        n, ms = wv.timing_read(kind)
+        avg = ms / n
+        e = {"op": name, "launches": n, "avg_launch_ms": avg}
+        if flop is not None:
+            e.update(bound="mfma", achieved=flop / (avg * 1e-3) / 1e12, unit="TFLOP/s",
+                     peak=PEAK_BF16_TFLOPS, frac=flop / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
+        else:
+            e.update(bound="hbm", achieved=nbytes / (avg * 1e-3) / 1e9, unit="GB/s", peak=PEAK_HBM_GBS,
+                     frac=nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS)
+        ops.append(e)
+        print(f"[bench] {name}: {avg:.3f} ms per launch, {e['frac']:.1%} of the {e['bound']} peak",
+              file=sys.stderr, flush=True)
+    wv.timing_reset()
+    return {"metric": "decoder mid-block attention block frames/sec, 1 GPU", "value": w.t * steps / (total_ms * 1e-3),
+            "unit": "frames/s", "higher_is_better": True, "ms_per_step": total_ms / steps, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) input, random-init weights)",
+            "config": {"workload": "attention block, one head of width 384, x [1,21,90,160,384] bf16, all frames"},
+            "steps": steps, "warmup": warmup, "kernels": ops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +244,9 @@ def main():
                     help="time the decoder's head and tail ops instead (conv_in 16->384, "
                          "post_quant_conv 16->16, norm_out + conv_out 96->3) at the "
                          "decoder's shapes, one JSON line")
+    ap.add_argument("--attention", action="store_true",
+                    help="time the decoder mid-block attention block instead, at the latent "
+                         "shape [1,21,90,160,384] (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-MiB buffer 3 times (a plain copy "
                          "kernel of known size, to scale HBM byte counters by)")
@@ -209,6 +265,9 @@ def main():
 
     if args.head_tail:
         print(json.dumps(head_tail(torch, wv, args.steps, args.warmup)), flush=True)
+        return
+    if args.attention:
+        print(json.dumps(attention(torch, wv, wl, args.steps, args.warmup)), flush=True)
         return
 
     w = wl.WORKLOADS[args.workload]

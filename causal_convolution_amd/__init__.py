@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "libwanvae.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(7)
 F32, BF16 = 0, 1
-KERNEL_NORM, KERNEL_CONV_BF16, KERNEL_CONV_F32, KERNEL_ROLL, KERNEL_POINTWISE = range(5)
+(KERNEL_NORM, KERNEL_CONV_BF16, KERNEL_CONV_F32, KERNEL_ROLL, KERNEL_POINTWISE, KERNEL_GEMM,
+ KERNEL_TRANSPOSE, KERNEL_ATTENTION) = range(8)
 EPS = 1e-12
 
 
@@ -64,6 +65,9 @@ EXPORTS = {
                                                     C.POINTER(C.c_int64)]),
     "wanvae_pointwise_conv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
                                         C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
+    "wanvae_attention_workspace_size": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_size_t)]),
+    "wanvae_attention_block": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_size_t, C.c_void_p]),
     "wanvae_last_error": (C.c_char_p, []),
     "wanvae_timing_enable": (C.c_int, [C.c_int]),
     "wanvae_timing_reset": (C.c_int, []),
@@ -336,6 +340,57 @@ class ResBlock:
 
 
 # --------------------------------------------------------------------------- timing
+class AttentionParamsC(C.Structure):
+    _fields_ = [("dim", C.c_int32), ("eps", C.c_float), ("gamma", C.c_void_p), ("beta", C.c_void_p),
+                ("w_qkv", C.c_void_p), ("b_qkv", C.c_void_p), ("w_o", C.c_void_p),
+                ("b_o", C.c_void_p)]
+
+
+class AttentionBlock:
+    """Device-resident parameters of the decoder mid-block attention block
+    (``wanvae_attention_block``): bf16 projection weights, fp32 norm and biases."""
+
+    def __init__(self, dim, gamma, beta, w_qkv, b_qkv, w_o, b_o, eps: float = EPS):
+        self.dim, self.eps = int(dim), float(eps)
+        self.tensors = dict(gamma=gamma, beta=beta, w_qkv=w_qkv, b_qkv=b_qkv, w_o=w_o, b_o=b_o)
+        t = self.tensors
+        self.c = AttentionParamsC(self.dim, self.eps, _ptr(t["gamma"]), _ptr(t["beta"]),
+                                  _ptr(t["w_qkv"]), _ptr(t["b_qkv"]), _ptr(t["w_o"]), _ptr(t["b_o"]))
+
+    @classmethod
+    def from_host(cls, p: dict, device="cuda", eps: float = EPS):
+        """From float32 numpy arrays gamma, beta, wqkv [3C, C], bqkv, wo [C, C], bo."""
+        torch = _torch()
+        f32 = lambda a: None if a is None else torch.from_numpy(a).to(device)
+        bf = lambda a: torch.from_numpy(a).to(device).to(torch.bfloat16).contiguous()
+        C_ = int(p["gamma"].shape[0])
+        return cls(C_, f32(p["gamma"]), f32(p.get("beta")), bf(p["wqkv"]), f32(p.get("bqkv")),
+                   bf(p["wo"]), f32(p.get("bo")), eps)
+
+    def workspace_size(self, n, t, h, w) -> int:
+        d = Dims(n, t, h, w)
+        b = C.c_size_t(0)
+        _check(lib().wanvae_attention_workspace_size(C.byref(self.c), C.byref(d), C.byref(b)))
+        return b.value
+
+    def workspace(self, n, t, h, w, device="cuda"):
+        torch = _torch()
+        return torch.empty(max(self.workspace_size(n, t, h, w), 1), dtype=torch.uint8, device=device)
+
+    def forward(self, x, out=None, workspace=None, stream=None):
+        """x [n,t,h,w,dim] bf16 -> y, the block's output."""
+        torch = _torch()
+        n, t, h, w, c = x.shape
+        _dev(x, "x", torch.bfloat16, (n, t, h, w, self.dim))
+        y = torch.empty_like(x) if out is None else out
+        _dev(y, "out", torch.bfloat16, (n, t, h, w, self.dim))
+        ws = self.workspace(n, t, h, w, x.device) if workspace is None else workspace
+        d = Dims(n, t, h, w)
+        _check(lib().wanvae_attention_block(C.byref(self.c), _ptr(x), _ptr(y), C.byref(d), _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(stream)))
+        return y
+
+
 def timing_enable(on: bool = True):
     _check(lib().wanvae_timing_enable(1 if on else 0))
 

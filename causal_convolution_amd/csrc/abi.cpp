@@ -478,6 +478,106 @@ int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_c
     });
 }
 
+namespace {
+struct AttnPlan {
+    int64_t P = 0, F = 0, HW = 0, HWp = 0;
+    size_t x_bytes = 0, u_off = 0, qkv_off = 0, vt_off = 0, o_off = 0, total = 0;
+};
+
+int plan_attention(const wanvae_attention_params *p, const wanvae_dims *d, AttnPlan *pl) {
+    WV_CHECK(p != nullptr, WANVAE_ERR_NULL, "params is NULL");
+    WV_CHECK(wanvae::attention_supported(p->dim), WANVAE_ERR_SHAPE,
+             "attention dim must be 64, 128 or 384 (got %d)", p->dim);
+    WV_CHECK(std::isfinite(p->eps) && p->eps >= 0.0f, WANVAE_ERR_SHAPE, "eps must be finite and >= 0");
+    WV_CHECK(p->gamma && p->w_qkv && p->w_o, WANVAE_ERR_NULL, "gamma, w_qkv and w_o are required");
+    const void *ptrs[] = {p->gamma, p->beta, p->w_qkv, p->b_qkv, p->w_o, p->b_o};
+    for (const void *q : ptrs)
+        WV_CHECK(aligned16(q), WANVAE_ERR_SHAPE, "parameter pointers must be 16-byte aligned");
+    if (int r = positions(d, &pl->P)) return r;
+    WV_CHECK(d->h * d->w <= (1 << 30), WANVAE_ERR_SHAPE, "h*w too large");
+    if (int r = check_conv_slab(d, 3 * p->dim, WANVAE_BF16)) return r;
+    const int64_t C = p->dim;
+    pl->F = d->n * d->t;
+    pl->HW = d->h * d->w;
+    pl->HWp = wanvae::attention_keys_padded(pl->HW);
+    pl->x_bytes = (size_t)pl->P * C * 2;
+    pl->u_off = 0;
+    pl->qkv_off = round_up(pl->x_bytes);
+    pl->vt_off = pl->qkv_off + round_up((size_t)pl->P * 3 * C * 2);
+    pl->o_off = pl->vt_off + round_up((size_t)pl->F * C * pl->HWp * 2);
+    pl->total = pl->o_off + round_up(pl->x_bytes);
+    return WANVAE_OK;
+}
+}  // namespace
+
+int wanvae_attention_workspace_size(const wanvae_attention_params *p, const wanvae_dims *d, size_t *bytes) {
+    g_error.clear();
+    WV_CHECK(bytes != nullptr, WANVAE_ERR_NULL, "bytes is NULL");
+    AttnPlan pl;
+    if (int r = plan_attention(p, d, &pl)) return r;
+    *bytes = pl.total;
+    return WANVAE_OK;
+}
+
+int wanvae_attention_block(const wanvae_attention_params *p, const void *x, void *y, const wanvae_dims *d,
+                           void *workspace, size_t ws_bytes, void *stream) {
+    g_error.clear();
+    AttnPlan pl;
+    if (int r = plan_attention(p, d, &pl)) return r;
+    if (pl.P == 0) return WANVAE_OK;
+    WV_CHECK(x && y, WANVAE_ERR_NULL, "x and y are required");
+    WV_CHECK(aligned16(x) && aligned16(y), WANVAE_ERR_SHAPE, "x and y must be 16-byte aligned");
+    WV_CHECK(!overlaps(x, pl.x_bytes, y, pl.x_bytes), WANVAE_ERR_ALIAS, "y overlaps x");
+    WV_CHECK(workspace != nullptr, WANVAE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", pl.total);
+    WV_CHECK(ws_bytes >= pl.total, WANVAE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes,
+             pl.total);
+    WV_CHECK(aligned16(workspace), WANVAE_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    WV_CHECK(!overlaps(workspace, pl.total, x, pl.x_bytes) && !overlaps(workspace, pl.total, y, pl.x_bytes),
+             WANVAE_ERR_ALIAS, "workspace overlaps x or y");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *u = ws + pl.u_off, *qkv = ws + pl.qkv_off, *vt = ws + pl.vt_off, *o = ws + pl.o_off;
+    const int C = p->dim;
+
+    if (int r = timed_launch(WANVAE_KERNEL_NORM, s, "rms_norm", [&] {
+            return wanvae::launch_rms_norm_bf16(x, u, pl.P, C, p->gamma, p->beta, p->eps, s);
+        }))
+        return r;
+    wanvae::ConvLaunch g;
+    g.gemm = true;
+    g.x = u;
+    g.w = p->w_qkv;
+    g.bias = p->b_qkv;
+    g.y = qkv;
+    g.n = d->n;
+    g.t = d->t;
+    g.h = d->h;
+    g.w_ = d->w;
+    g.cin = C;
+    g.cout = 3 * C;
+    if (int r = timed_launch(WANVAE_KERNEL_GEMM, s, "qkv projection",
+                             [&] { return wanvae::launch_gemm_bf16(g, s); }))
+        return r;
+    if (int r = timed_launch(WANVAE_KERNEL_TRANSPOSE, s, "v transpose", [&] {
+            return wanvae::launch_transpose_v(qkv, vt, pl.F, (int)pl.HW, C, s);
+        }))
+        return r;
+    if (int r = timed_launch(WANVAE_KERNEL_ATTENTION, s, "flash attention", [&] {
+            return wanvae::launch_flash_attention(qkv, vt, o, pl.F, (int)pl.HW, C, s);
+        }))
+        return r;
+    wanvae::ConvLaunch go = g;
+    go.x = o;
+    go.w = p->w_o;
+    go.bias = p->b_o;
+    go.res = x;
+    go.cres = C;
+    go.y = y;
+    go.cout = C;
+    return timed_launch(WANVAE_KERNEL_GEMM, s, "output projection",
+                        [&] { return wanvae::launch_gemm_bf16(go, s); });
+}
+
 int wanvae_timing_enable(int on) {
     std::lock_guard<std::mutex> lk(g_tm_mu);
     g_timing = on != 0;

@@ -1,0 +1,369 @@
+// Decoder mid-block attention core: per frame, o = softmax(q k^T / sqrt(D)) v
+// over the frame's H*W positions ("Closing the gap: Wan 2.2 14B VAE decoder",
+// section 5: a spatial self-attention in which, within a frame, every position
+// attends to every other; each (batch, frame) is an independent problem).
+// One head of width D = C.
+//
+// Inputs: qkv [F][HW][3D] bf16 (q, k, v of each position side by side, the
+// output of the block's 1x1x1 projection) and vt [F][D][HWp] bf16, v
+// transposed per frame (transpose_v_kernel, keys padded with zeros to HWp, a
+// multiple of 32).  Output o [F][HW][D] bf16.
+//
+// Flash-attention form, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and
+// accumulation, the scores never leave the chip.  A workgroup owns 128 queries
+// of one frame and walks the frame's keys in blocks of 32; its 8 waves are 4
+// query groups of 32 x 2 halves of the head width:
+//  - wave (qg, hf) keeps q of its 32 queries, dims [hf D/2, (hf+1) D/2), in
+//    registers (D/32 fragments) and the matching half of O^T;
+//  - per key block it computes the partial scores S^T = K q^T over its half
+//    (keys as the MFMA M rows, queries as N columns), the two halves add
+//    their partials through LDS (half 0 + half 1, in that order, in both
+//    waves, so both hold identical scores), and both run the same online
+//    softmax: row maximum, exp2, running sum, rescale of O;
+//  - then O^T += V^T P^T over its half: P is used straight from the score
+//    registers as the MFMA B operand.  A lane holds the scores of one query
+//    for keys 8j + 4g + i (j, i < 4; g = lane / 32); taking j = 2ks, 2ks + 1
+//    as MFMA k-step ks, the 8 k values of lane group g are keys 16ks + 4g +
+//    {0..3, 8..11}, and the V^T operand is read in that same key order (two
+//    8-byte pieces per fragment), so no transpose of P is needed;
+//  - the K and V^T blocks (2 x 24 KB at D = 384) are staged by LDS-DMA
+//    (buffer_load ... lds, 6 instructions per wave and block) into a 2-slot
+//    ring, the next block loading while the current one computes; two
+//    barriers per block: one for the score exchange, one for the ring.
+// LDS: K rows are swizzled in 16-byte chunks (chunk ^ (key & 15)) and V^T rows
+// (64 bytes) by (d >> 2) & 3, so fragment reads spread over the banks.
+// Scores of keys past HW are -inf; queries past HW compute on zero q and are
+// not stored.
+#include "bf16.h"
+#include "internal.h"
+
+namespace wanvae {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBufFlags = 0x00020000;   // raw buffer, loads past num_records return zeros
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kBQ = 128;                // queries per workgroup
+constexpr int kBK = 32;                 // keys per block
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }   // lgkmcnt(0), others untouched
+
+__device__ inline i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), kBufFlags};
+}
+
+// one wavefront-wide 16-byte-per-lane load into LDS at lds_addr + 16 * lane
+__device__ inline void lds_dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane((int)lds_addr)), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+__device__ inline uint32_t lds_address(const unsigned char *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
+
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
+template <int D>
+struct AttnShape {
+    static constexpr int DH = D / 2;                    // head dims per wave
+    static constexpr int KS = DH / 16;                  // MFMA k-steps of the score product
+    static constexpr int DT = DH / 32;                  // O^T tiles per wave
+    static constexpr int CPR = D / 8;                   // 16-byte chunks per K row
+    static constexpr int KSWZ = CPR < 16 ? CPR - 1 : 15;   // chunk swizzle mask of K rows
+    static constexpr int K_BYTES = kBK * D * 2;         // one K block
+    static constexpr int V_BYTES = D * kBK * 2;         // one V^T block
+    static constexpr int SLOT = K_BYTES + V_BYTES;
+    static constexpr int DMA_PER_BLOCK = SLOT / 1024;   // 1 KB per instruction
+    static constexpr int DMA_PER_WAVE = DMA_PER_BLOCK / kWaves;
+    static constexpr int SX_BYTES = 4 * 2 * 64 * 16 * 4;   // partial scores: [qg][hf][lane][16] fp32
+    static_assert(D % 64 == 0 && D <= 512, "head width a multiple of 64");
+    static_assert(DMA_PER_BLOCK % kWaves == 0, "every wave issues the same number of loads");
+    static_assert(2 * SLOT + SX_BYTES <= 160 * 1024, "LDS");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_t *__restrict__ qkv,
+                                                                   const uint16_t *__restrict__ vt,
+                                                                   uint16_t *__restrict__ o, int64_t frames,
+                                                                   int HW, int HWp, float scale_log2) {
+    using S = AttnShape<D>;
+    constexpr int DH = S::DH, KS = S::KS, DT = S::DT;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * S::SLOT];
+    __shared__ __attribute__((aligned(16))) float sx[S::SX_BYTES / 4];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qg = wave >> 1, hf = wave & 1;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int qblocks = (HW + kBQ - 1) / kBQ;
+    const int64_t f = blockIdx.x / qblocks;
+    const int q0 = (int)(blockIdx.x % qblocks) * kBQ + qg * 32;   // this wave's first query
+    const int row3 = 3 * D;                                        // qkv row stride (elements)
+    const uint16_t *qkv_f = qkv + f * (int64_t)HW * row3;
+    const uint16_t *vt_f = vt + f * (int64_t)D * HWp;
+    const int nblk = (HW + kBK - 1) / kBK;
+
+    // ---- q fragments of this wave's queries and head half, in registers
+    bf16x8 qf[KS];
+    {
+        const int q = q0 + l32;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 d = u32x4{0u, 0u, 0u, 0u};
+            if (q < HW)
+                d = *reinterpret_cast<const u32x4 *>(qkv_f + (int64_t)q * row3 + hf * DH + 16 * s + 8 * g);
+            qf[s] = __builtin_bit_cast(bf16x8, d);
+        }
+    }
+
+    // ---- LDS-DMA of key block j into ring slot sl: this wave's pieces.
+    // Piece P (16 bytes) of a slot: P < K_BYTES / 16 is K row P / CPR, stored
+    // chunk P % CPR = global chunk ^ (row & KSWZ); the rest is V^T row d (64
+    // bytes = 4 chunks), stored chunk = global chunk ^ ((d >> 2) & 3).
+    const uint32_t ring_base = lds_address(ring);
+    const i32x4 rk = buffer_rsrc(qkv_f + D, (uint32_t)((int64_t)HW * row3 * 2 - D * 2));
+    const i32x4 rv = buffer_rsrc(vt_f, (uint32_t)((int64_t)D * HWp * 2));
+    auto issue_block = [&](int j, int sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < S::DMA_PER_WAVE; ++i) {
+            const int b = wave * S::DMA_PER_WAVE + i;   // 1 KB block of the slot
+            const int P = b * 64 + lane;
+            const uint32_t lds = ring_base + (uint32_t)(sl * S::SLOT + b * 1024);
+            if (P < S::K_BYTES / 16) {
+                const int row = P / S::CPR, cs = P % S::CPR;
+                const int c = cs ^ (row & S::KSWZ);
+                const int key = j * kBK + row;
+                const uint32_t off = key < HW ? (uint32_t)key * (uint32_t)(row3 * 2) + (uint32_t)c * 16 : kOOB;
+                lds_dma16(rk, lds, off);
+            } else {
+                const int Pv = P - S::K_BYTES / 16;
+                const int d = Pv >> 2, cs = Pv & 3;
+                const int c = cs ^ ((d >> 2) & 3);
+                const uint32_t off = (uint32_t)d * (uint32_t)(HWp * 2) + (uint32_t)(j * kBK * 2) + (uint32_t)c * 16;
+                lds_dma16(rv, lds, off);
+            }
+        }
+    };
+    // Note: a wave's pieces are either all K or all V^T when DMA_PER_WAVE * 64
+    // pieces divide the K part; the branch above is per lane and stays valid
+    // either way (both paths issue exactly one load).
+
+    // fragment reads
+    auto ldK = [&](const unsigned char *slot, int s) __attribute__((always_inline)) {
+        const int row = l32;                              // key of this lane
+        const int c = (hf * DH / 8 + 2 * s + g) ^ (row & S::KSWZ);
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + (row * S::CPR + c) * 16));
+    };
+    // V^T fragment of tile t, k-step ks: d = hf DH + 32 t + l32, keys
+    // 16 ks + 4 g + {0..3} and 16 ks + 8 + 4 g + {0..3}
+    auto ldV = [&](const unsigned char *slot, int t, int ks) __attribute__((always_inline)) {
+        const int d = hf * DH + 32 * t + l32;
+        const unsigned char *row = slot + S::K_BYTES + d * (kBK * 2);
+        const int sw = (d >> 2) & 3;
+        const int b0 = (16 * ks + 4 * g) * 2, b1 = b0 + 16;   // byte offsets within the 64-byte row
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + (((b0 >> 4) ^ sw) << 4) + (b0 & 15));
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + (((b1 >> 4) ^ sw) << 4) + (b1 & 15));
+        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    };
+
+    floatx16 acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    float *const sx_mine = sx + ((qg * 2 + hf) * 64 + lane) * 16;
+    const float *const sx_0 = sx + ((qg * 2 + 0) * 64 + lane) * 16;
+    const float *const sx_1 = sx + ((qg * 2 + 1) * 64 + lane) * 16;
+
+    issue_block(0, 0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+
+    for (int j = 0; j < nblk; ++j) {
+        const int sl = j & 1;
+        const unsigned char *slot = ring + sl * S::SLOT;
+        if (j + 1 < nblk) issue_block(j + 1, sl ^ 1);
+
+        // partial scores over this wave's head half
+        floatx16 sp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sp[r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ldK(slot, s), qf[s], sp, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; r += 4)
+            *reinterpret_cast<float4 *>(sx_mine + r) = float4{sp[r], sp[r + 1], sp[r + 2], sp[r + 3]};
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        float sc[16];
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+            const float4 a = *reinterpret_cast<const float4 *>(sx_0 + r);
+            const float4 b = *reinterpret_cast<const float4 *>(sx_1 + r);
+            sc[r] = a.x + b.x; sc[r + 1] = a.y + b.y; sc[r + 2] = a.z + b.z; sc[r + 3] = a.w + b.w;
+        }
+
+        // online softmax for this lane's query (column l32), keys 8jj + 4g + i
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = j * kBK + 8 * (r >> 2) + 4 * g + (r & 3);
+            sc[r] = key < HW ? sc[r] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sc[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float ls = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sc[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
+            ls += sc[r];
+        }
+        ls += __shfl_xor(ls, 32);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+
+        // O^T += V^T P^T over this wave's head half
+        bf16x8 pf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = f32_to_bf16_bits(sc[8 * ks + 2 * e]) | (f32_to_bf16_bits(sc[8 * ks + 2 * e + 1]) << 16);
+            pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ldV(slot, t, ks), pf[ks], acc[t], 0, 0, 0);
+
+        // the next block has landed (own loads), and every wave is done with
+        // this slot and with the score exchange
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & waitcnt_lgkm0());
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+    }
+
+    // ---- o = O / l for this lane's query: d = hf DH + 32 t + 8 jj + 4 g + i
+    const int q = q0 + l32;
+    if (q < HW) {
+        const float inv = 1.0f / l_run;
+        uint16_t *orow = o + (f * (int64_t)HW + q) * D + hf * DH;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float v0 = acc[t][4 * jj], v1 = acc[t][4 * jj + 1];
+                const float v2 = acc[t][4 * jj + 2], v3 = acc[t][4 * jj + 3];
+                u32x2 w;
+                w.x = f32_to_bf16_bits(v0 * inv) | (f32_to_bf16_bits(v1 * inv) << 16);
+                w.y = f32_to_bf16_bits(v2 * inv) | (f32_to_bf16_bits(v3 * inv) << 16);
+                *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * jj + 4 * g) = w;
+            }
+    }
+}
+
+// vt[f][d][k] = v of key k (qkv[f][k][2D + d]) for k < HW, 0 for HW <= k < HWp.
+// 64 keys x 64 dims per block through LDS: 16-byte reads along d, 16-byte
+// writes along k.
+constexpr int kTT = 64;
+__global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *__restrict__ qkv, uint16_t *__restrict__ vt,
+                                                          int64_t frames, int HW, int HWp, int D) {
+    __shared__ uint16_t tile[kTT][kTT + 2];
+    const int kb = (HWp + kTT - 1) / kTT, db = D / kTT;
+    int64_t bid = blockIdx.x;
+    const int dbi = (int)(bid % db);
+    bid /= db;
+    const int kbi = (int)(bid % kb);
+    const int64_t f = bid / kb;
+    const int k0 = kbi * kTT, d0 = dbi * kTT;
+    const int tid = threadIdx.x;
+    // read: 64 keys x 8 pieces of 8 dims
+    for (int p = tid; p < kTT * 8; p += 256) {
+        const int kr = p >> 3, dc = (p & 7) * 8;
+        const int key = k0 + kr;
+        u32x4 d = u32x4{0u, 0u, 0u, 0u};
+        if (key < HW) d = *reinterpret_cast<const u32x4 *>(qkv + (f * HW + key) * (int64_t)(3 * D) + 2 * D + d0 + dc);
+        const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[kr][dc + e] = (uint16_t)(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xffffu);
+    }
+    __syncthreads();
+    // write: 64 dims x 8 pieces of 8 keys
+    for (int p = tid; p < kTT * 8; p += 256) {
+        const int dr = p >> 3, kc = (p & 7) * 8;
+        if (k0 + kc >= HWp) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[kc + 2 * e][dr] | ((uint32_t)tile[kc + 2 * e + 1][dr] << 16);
+        *reinterpret_cast<u32x4 *>(vt + (f * D + d0 + dr) * (int64_t)HWp + k0 + kc) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+template <int D>
+hipError_t launch_flash(const void *qkv, const void *vt, void *o, int64_t frames, int HW, int HWp, hipStream_t s) {
+    const int64_t qblocks = (HW + kBQ - 1) / kBQ;
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+    flash_attention_kernel<D><<<dim3((unsigned)(frames * qblocks)), dim3(kThreads), 0, s>>>(
+        static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(vt), static_cast<uint16_t *>(o), frames,
+        HW, HWp, scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool attention_supported(int D) { return D == 64 || D == 128 || D == 384; }
+
+int64_t attention_keys_padded(int64_t hw) { return (hw + kBK - 1) / kBK * kBK; }
+
+hipError_t launch_transpose_v(const void *qkv, void *vt, int64_t frames, int HW, int D, hipStream_t s) {
+    const int HWp = (int)attention_keys_padded(HW);
+    const int64_t blocks = frames * ((HWp + kTT - 1) / kTT) * (D / kTT);
+    if (blocks == 0) return hipSuccess;
+    transpose_v_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(static_cast<const uint16_t *>(qkv),
+                                                                    static_cast<uint16_t *>(vt), frames, HW, HWp, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_flash_attention(const void *qkv, const void *vt, void *o, int64_t frames, int HW, int D,
+                                  hipStream_t s) {
+    if (frames == 0 || HW == 0) return hipSuccess;
+    const int HWp = (int)attention_keys_padded(HW);
+    switch (D) {
+        case 64: return launch_flash<64>(qkv, vt, o, frames, HW, HWp, s);
+        case 128: return launch_flash<128>(qkv, vt, o, frames, HW, HWp, s);
+        case 384: return launch_flash<384>(qkv, vt, o, frames, HW, HWp, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace wanvae

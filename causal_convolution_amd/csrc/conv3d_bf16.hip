@@ -144,6 +144,13 @@ struct Args {
     int tiles_w, tiles_h;
     int64_t tiles;          // total tiles of the launch
     int x_sliced;           // x and cache frames are [cin/16][h][w][16], not [h][w][cin]
+    // 1x1x1 stages (SC kernels): input [n][t][h][w][sc_c] at the output
+    // positions and weight wsc [cout][sc_c]: the block's shortcut (sc_in =
+    // res), or the whole product of a GEMM launch (gemm = 1: no 3x3x3 stages,
+    // sc_in = x)
+    const uint16_t *sc_in;
+    int sc_c;
+    int gemm;
 };
 
 // One output tile: batch item, frame, first row / column / output channel,
@@ -169,7 +176,7 @@ struct Tile {
     // (9 FN weight fragments in registers would not fit beside the
     // accumulators).  The bias of every tile sits in LDS, not in registers.
     static constexpr bool KH_OUTER = FN > 1;
-    static constexpr int kBiasBytes = 4 * 1024;   // bias in LDS: [cout] fp32, cout <= 1024
+    static constexpr int kBiasBytes = 8 * 1024;   // bias in LDS: [cout_p] fp32, cout <= 2048
     static constexpr int kLds = 160 * 1024 - kSyncBytes - NWAVE * kEpiBytes - kBiasBytes;
     static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
     static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
@@ -235,7 +242,7 @@ __device__ inline uint32_t lds_address(const unsigned char *p) {
 // compiler-only fence: no memory access moves across it
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
-template <int WM, int WN, int FM, int FN, int EPI>
+template <int WM, int WN, int FM, int FN, int EPI, bool SC>
 __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) {
     using TL = Tile<WM, WN, FM, FN>;
     constexpr int HB = TL::HB;
@@ -259,7 +266,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     if (tid <= TL::NWAVE) sync[tid] = 0;
     for (int c = tid; c < a.cout_p; c += TL::kThreads) {
         float b = a.bias && c < a.cout ? a.bias[c] : 0.0f;
-        if constexpr (EPI == EPI_SHORTCUT)
+        if constexpr (SC)
             if (a.bsc && c < a.cout) b += a.bsc[c];
         bias_lds[c] = b;
     }
@@ -297,8 +304,8 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // without a cache the stages of frames before 0 only add zeros: skipped
         const int kt_begin = (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
         ti.kt_begin = kt_begin;
-        ti.s_conv = (3 - kt_begin) * ck;
-        ti.s_total = ti.s_conv + (EPI == EPI_SHORTCUT ? a.cres / (kKC * TL::SCS) : 0);
+        ti.s_conv = a.gemm ? 0 : (3 - kt_begin) * ck;
+        ti.s_total = ti.s_conv + (SC ? a.sc_c / (kKC * TL::SCS) : 0);
         return ti;
     };
 
@@ -356,13 +363,13 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     q = (lane & 1) ^ ((c >> 3) & 1);
                 }
                 const int hh = ti.h0 + r, ww = ti.w0 + c;
-                return hh < H && ww < W ? (uint32_t)(hh * W + ww) * (uint32_t)(a.cres * 2) + q * 16 : kOOB;
+                return hh < H && ww < W ? (uint32_t)(hh * W + ww) * (uint32_t)(a.sc_c * 2) + q * 16 : kOOB;
             }
             from_w = true;
             const int u = (b - TL::SCS * HB) * 32 + (lane >> 1);   // w_sc unit: slice j, channel nl
             const int j = u / NB, nl = u % NB;
             const int hf = (lane & 1) ^ ((nl >> 3) & 1);
-            return (uint32_t)((ti.n0 + nl) * a.cres * 2) + j * kUnit + hf * 16;
+            return (uint32_t)((ti.n0 + nl) * a.sc_c * 2) + j * kUnit + hf * 16;
         };
 
         // request cursor: stage si of local tile it (tile x_begin + it), ring slot
@@ -412,10 +419,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             } else {
                 // first 16-channel slice of this shortcut stage
                 const int cc = (si - ti.s_conv) * TL::SCS;
-                abase = a.res + ((ti.nq * a.T + ti.tq) * HW) * a.cres + cc * kKC;
-                abytes = (uint32_t)(HW * a.cres * 2 - cc * kKC * 2);
+                abase = a.sc_in + ((ti.nq * a.T + ti.tq) * HW) * a.sc_c + cc * kKC;
+                abytes = (uint32_t)(HW * a.sc_c * 2 - cc * kKC * 2);
                 bbase = a.wsc + cc * kKC;
-                bbytes = (uint32_t)((int64_t)a.cout * a.cres * 2 - cc * kKC * 2);
+                bbytes = (uint32_t)((int64_t)a.cout * a.sc_c * 2 - cc * kKC * 2);
             }
             // the cursor is uniform; buffer_rsrc makes that explicit to the compiler
             const i32x4 ar = buffer_rsrc(abase, abytes);
@@ -425,7 +432,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             for (int b = 0; b < TL::BLOCKS; ++b) {
                 uint32_t off = l_off[b];
                 bool from_b = b >= TL::A_BLOCKS;
-                if constexpr (EPI == EPI_SHORTCUT)
+                if constexpr (SC)
                     if (sc) off = sc_block_off(ti, b, from_b);
                 lds_dma16(from_b ? br : ar, base + b * 1024, off);
             }
@@ -661,7 +668,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                 compute_conv(smem + slot * TL::STAGE_BYTES);
             release();
         }
-        if constexpr (EPI == EPI_SHORTCUT) {
+        if constexpr (SC) {
             for (int s = ti.s_conv; s < ti.s_total; ++s) {
                 wait_landed();
                 compute_shortcut(smem + slot * TL::STAGE_BYTES);
@@ -752,7 +759,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             }
         };
         if constexpr (EPI == EPI_IDENTITY) {
-            constexpr int EG = 2;                          // rows per residual group
+            constexpr int EG = FN > 1 ? 1 : 2;             // rows per residual group (registers)
             constexpr int NG = (FM + EG - 1) / EG;
             const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.res + frame * HW * a.cres, HW * a.cres * 2);
             u32x2 rv[2][EG][FN][4];
@@ -813,7 +820,7 @@ hipError_t device_cu_count(int *out) {
     return hipSuccess;
 }
 
-template <int WM, int WN, int FM, int FN, int EPI>
+template <int WM, int WN, int FM, int FN, int EPI, bool SC = EPI == EPI_SHORTCUT>
 hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     using TL = Tile<WM, WN, FM, FN>;
     Args a;
@@ -834,6 +841,10 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.cout_p = (c.cout + 31) / 32 * 32;
     a.cres = c.cres;
     a.x_sliced = c.x_sliced ? 1 : 0;
+    a.gemm = c.gemm ? 1 : 0;
+    a.sc_in = static_cast<const uint16_t *>(c.gemm ? c.x : c.res);
+    a.sc_c = c.gemm ? c.cin : c.cres;
+    if (c.gemm) a.wsc = static_cast<const uint16_t *>(c.w);
     a.tiles_w = (int)((c.w_ + kWB - 1) / kWB);
     a.tiles_h = (int)((c.h + TL::HB - 1) / TL::HB);
     a.tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (a.cout_p / TL::NB);
@@ -844,7 +855,7 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
     const int64_t grid = a.tiles < (int64_t)ncu * TL::kPerCU ? a.tiles : (int64_t)ncu * TL::kPerCU;
-    conv3d_bf16_kernel<WM, WN, FM, FN, EPI><<<dim3((unsigned)grid), dim3(TL::kThreads), 0, s>>>(a);
+    conv3d_bf16_kernel<WM, WN, FM, FN, EPI, SC><<<dim3((unsigned)grid), dim3(TL::kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -875,6 +886,7 @@ int64_t rows_computed(int64_t h, int hb) { return (h + hb - 1) / hb * hb; }
 //  - any other C_out: four waves of 4 rows x 32 channels, the last channel
 //    block padded with zero weights (the decoder's 3-channel conv_out).
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
+    if (c.cout < 1 || c.cout > 1024) return hipErrorInvalidValue;
     const bool tall = rows_computed(c.h, 18) <= rows_computed(c.h, 16);
     if (c.res != nullptr && c.wsc != nullptr) {
         if (c.cout % 64 == 0)
@@ -885,6 +897,24 @@ hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
     if (c.cout % 64 == 0) return tall ? launch_plain<2, 2, 9, 1>(c, s) : launch_plain<2, 2, 8, 1>(c, s);
     if (c.cout % 96 == 0) return launch_plain<4, 1, 3, 3>(c, s);
     return launch_plain<4, 1, 4, 1>(c, s);
+}
+
+// The same kernels with only 1x1x1 stages: y = w x + bias (+ res), the plain
+// channel GEMM of a pointwise projection, tiled like the conv.
+template <int WM, int WN, int FM, int FN>
+hipError_t launch_gemm_cfg(const ConvLaunch &c, hipStream_t s) {
+    return c.res ? launch_cfg<WM, WN, FM, FN, EPI_IDENTITY, true>(c, s)
+                 : launch_cfg<WM, WN, FM, FN, EPI_BIAS, true>(c, s);
+}
+
+hipError_t launch_gemm_bf16(const ConvLaunch &c, hipStream_t s) {
+    // the bias of every output channel must fit the kernel's LDS copy; the 1x1x1
+    // stages take 32 input channels at a time
+    if (!c.gemm || c.cout < 1 || c.cout > 2048 || c.cin < 32 || c.cin % 32 != 0) return hipErrorInvalidValue;
+    const bool tall = rows_computed(c.h, 18) <= rows_computed(c.h, 16);
+    if (c.cout % 64 == 0) return tall ? launch_gemm_cfg<2, 2, 9, 1>(c, s) : launch_gemm_cfg<2, 2, 8, 1>(c, s);
+    if (c.cout % 96 == 0) return launch_gemm_cfg<4, 1, 3, 3>(c, s);
+    return launch_gemm_cfg<4, 1, 4, 1>(c, s);
 }
 
 }  // namespace wanvae

@@ -27,6 +27,9 @@ struct ConvLaunch {
     // bf16 only: x and cache frames are [cin/16][h][w][16] (16-channel
     // slices) instead of [h][w][cin]; res and y stay channels-last
     bool x_sliced = false;
+    // GEMM launch (launch_gemm_bf16): y = w x + bias (+ res), w plain
+    // [cout][cin], x channels-last; cin a multiple of 32, cout of 32
+    bool gemm = false;
 };
 
 // Fused RMS_norm + SiLU over rows of C channels (C % 32 == 0, 32..1024).
@@ -40,6 +43,9 @@ hipError_t launch_rmsnorm_silu_bf16(const void *x, void *y, int64_t rows, int C,
 hipError_t launch_rmsnorm_silu_bf16_sliced(const void *x, void *y, int64_t rows, int C, int64_t hw,
                                            const float *gamma, const float *beta, float eps,
                                            hipStream_t s);
+// The norm alone (no SiLU), channels-last bf16 in and out; y == x allowed.
+hipError_t launch_rms_norm_bf16(const void *x, void *y, int64_t rows, int C, const float *gamma,
+                                const float *beta, float eps, hipStream_t s);
 hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, const float *gamma,
                                    const float *beta, float eps, hipStream_t s);
 
@@ -48,6 +54,20 @@ hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, 
 // multiple of 32.
 bool conv3d_bf16_supported(int cin, int cout);
 hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
+
+// Channel GEMM over positions (a pointwise projection) on the conv kernel's
+// 1x1x1 stages: ConvLaunch with gemm = true.
+hipError_t launch_gemm_bf16(const ConvLaunch &a, hipStream_t s);
+
+// Attention core of the decoder mid-block (attention.hip): head width D in
+// {64, 128, 384}; keys padded to a multiple of 32 in the transposed v.
+bool attention_supported(int D);
+int64_t attention_keys_padded(int64_t hw);
+// vt[f][d][k] = qkv[f][k][2D + d] (zero for HW <= k < HWp)
+hipError_t launch_transpose_v(const void *qkv, void *vt, int64_t frames, int HW, int D, hipStream_t s);
+// o[f][q] = softmax_k(q . k / sqrt(D)) v over the frame's HW positions
+hipError_t launch_flash_attention(const void *qkv, const void *vt, void *o, int64_t frames, int HW, int D,
+                                  hipStream_t s);
 
 // Packs PyTorch-layout conv weights [cout][cin][3][3][3] for the conv kernels
 // (bf16: [3][cin/16][3][3][cout_p][16], cin % 16 == 0, cout_p = cout rounded

@@ -50,6 +50,12 @@ __device__ inline float silu(float u) {
     return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
 }
 
+template <bool ACT>
+__device__ inline float act(float u) {
+    if constexpr (ACT) return silu(u);
+    return u;
+}
+
 // 16 bytes = EP elements of T as fp32 and back
 template <typename T> struct Piece;
 template <> struct Piece<float> {
@@ -104,7 +110,9 @@ struct Shape {
 
 // SLICED: y is written in the conv input layout, frame f = row / hw cut into
 // 16-channel slices, y[f][c / 16][row % hw][c % 16] (inv_hw = 1 / hw).
-template <typename T, int C, bool SLICED>
+// ACT: SiLU after the norm (the ResidualBlock); without it, the plain
+// RMS_norm (the attention block's input norm).
+template <typename T, int C, bool SLICED, bool ACT>
 __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
     const T *x, T *y, int64_t rows, const float *__restrict__ gamma,
     const float *__restrict__ beta, float eps, float sqrt_c, int64_t hw, double inv_hw) {
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
                 float (&vi)[EP] = v[S::IN_REGS ? i : 0];
                 if constexpr (S::IN_REGS) {
 #pragma unroll
-                    for (int k = 0; k < EP; ++k) vi[k] = silu(fmaf(vi[k] * ip, g[i][k], b[i][k]));
+                    for (int k = 0; k < EP; ++k) vi[k] = act<ACT>(fmaf(vi[k] * ip, g[i][k], b[i][k]));
                 } else {
                     PC::unpack(d[u][i], vi);
 #pragma unroll
@@ -228,10 +236,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
                         const float4 gv = *reinterpret_cast<const float4 *>(gamma + pch[i] + k);
                         const float4 bv = beta ? *reinterpret_cast<const float4 *>(beta + pch[i] + k)
                                                : float4{0.f, 0.f, 0.f, 0.f};
-                        vi[k] = silu(fmaf(vi[k] * ip, gv.x * sqrt_c, bv.x));
-                        vi[k + 1] = silu(fmaf(vi[k + 1] * ip, gv.y * sqrt_c, bv.y));
-                        vi[k + 2] = silu(fmaf(vi[k + 2] * ip, gv.z * sqrt_c, bv.z));
-                        vi[k + 3] = silu(fmaf(vi[k + 3] * ip, gv.w * sqrt_c, bv.w));
+                        vi[k] = act<ACT>(fmaf(vi[k] * ip, gv.x * sqrt_c, bv.x));
+                        vi[k + 1] = act<ACT>(fmaf(vi[k + 1] * ip, gv.y * sqrt_c, bv.y));
+                        vi[k + 2] = act<ACT>(fmaf(vi[k + 2] * ip, gv.z * sqrt_c, bv.z));
+                        vi[k + 3] = act<ACT>(fmaf(vi[k + 3] * ip, gv.w * sqrt_c, bv.w));
                     }
                 }
                 if constexpr (SLICED) {
@@ -274,25 +282,25 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
     }
 }
 
-template <typename T, int C, bool SLICED>
+template <typename T, int C, bool SLICED, bool ACT>
 hipError_t launch_c(const void *x, void *y, int64_t rows, const float *gamma, const float *beta,
                     float eps, int64_t hw, hipStream_t s) {
     using S = Shape<T, C>;
     int64_t blocks = (rows + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
     if (blocks > kGridCap) blocks = kGridCap;
     if (blocks < 1) blocks = 1;
-    rmsnorm_silu_kernel<T, C, SLICED><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+    rmsnorm_silu_kernel<T, C, SLICED, ACT><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
         static_cast<const T *>(x), static_cast<T *>(y), rows, gamma, beta, eps, sqrtf((float)C), hw,
         1.0 / (double)hw);
     return hipGetLastError();
 }
 
-template <typename T, bool SLICED>
+template <typename T, bool SLICED, bool ACT = true>
 hipError_t dispatch(const void *x, void *y, int64_t rows, int C, const float *gamma,
                     const float *beta, float eps, int64_t hw, hipStream_t s) {
     switch (C) {
 #define WANVAE_NORM_CASE(K) \
-    case 32 * K: return launch_c<T, 32 * K, SLICED>(x, y, rows, gamma, beta, eps, hw, s);
+    case 32 * K: return launch_c<T, 32 * K, SLICED, ACT>(x, y, rows, gamma, beta, eps, hw, s);
         WANVAE_NORM_CASE(1) WANVAE_NORM_CASE(2) WANVAE_NORM_CASE(3) WANVAE_NORM_CASE(4)
         WANVAE_NORM_CASE(5) WANVAE_NORM_CASE(6) WANVAE_NORM_CASE(7) WANVAE_NORM_CASE(8)
         WANVAE_NORM_CASE(9) WANVAE_NORM_CASE(10) WANVAE_NORM_CASE(11) WANVAE_NORM_CASE(12)
@@ -321,6 +329,11 @@ hipError_t launch_rmsnorm_silu_bf16_sliced(const void *x, void *y, int64_t rows,
                                            hipStream_t s) {
     if (hw <= 0) return hipErrorInvalidValue;
     return dispatch<uint16_t, true>(x, y, rows, C, gamma, beta, eps, hw, s);
+}
+
+hipError_t launch_rms_norm_bf16(const void *x, void *y, int64_t rows, int C, const float *gamma,
+                                const float *beta, float eps, hipStream_t s) {
+    return dispatch<uint16_t, false, false>(x, y, rows, C, gamma, beta, eps, 1, s);
 }
 
 hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, const float *gamma,

@@ -118,6 +118,23 @@ def make_params(wl: Workload, seed: int = 0):
     return p
 
 
+def make_attention_params(C: int, seed: int = 0):
+    """Attention-block parameters as float32 numpy arrays, drawn like the
+    ResidualBlock's: gamma ~ U(0.5, 1.5), beta ~ N(0, 0.1), projection weights
+    ~ N(0, 1/C) (variance 1 / fan_in), biases ~ N(0, 0.01); the weights rounded
+    to bf16 values.  Keys gamma, beta, wqkv [3C, C] (q, k, v rows), bqkv [3C],
+    wo [C, C], bo [C]."""
+    rng = np.random.default_rng(seed + 77)
+    f32 = np.float32
+
+    def normal(var, shape):
+        return rng.normal(0.0, np.sqrt(var), size=shape).astype(f32)
+
+    return {"gamma": rng.uniform(0.5, 1.5, size=C).astype(f32), "beta": normal(0.1, C),
+            "wqkv": round_bf16(normal(1.0 / C, (3 * C, C))), "bqkv": normal(0.01, 3 * C),
+            "wo": round_bf16(normal(1.0 / C, (C, C))), "bo": normal(0.01, C)}
+
+
 def make_x_host(wl: Workload, seed: int = 0) -> np.ndarray:
     """x ~ N(0, 1) as float32 [N,T,H,W,Cin] on the host (small workloads);
     rounded to bf16 values for bf16 workloads."""

@@ -225,6 +225,49 @@ WANVAE_API int wanvae_resblock_stream_step(const wanvae_resblock_params *p, cons
                                 void *y_chunk, const wanvae_dims *d, void *cache_a, void *cache_b,
                                 void *workspace, size_t ws_bytes, void *stream);
 
+/* Parameters of the decoder mid-block attention block (bf16).  All pointers
+ * are device pointers. */
+typedef struct {
+    int32_t dim;              /* C: channels = head width (64, 128 or 384)        */
+    float eps;                /* clamp of the channel L2 norm                       */
+    const float *gamma;       /* [dim] norm scale                                   */
+    const float *beta;        /* [dim] norm shift, or NULL                          */
+    const void *w_qkv;        /* [3*dim][dim] bf16: rows of q, then k, then v       */
+    const float *b_qkv;       /* [3*dim] or NULL                                     */
+    const void *w_o;          /* [dim][dim] bf16 output projection                  */
+    const float *b_o;         /* [dim] or NULL                                       */
+} wanvae_attention_params;
+
+/*
+ * Workspace bytes of wanvae_attention_block for extent *d (P = n*t*h*w
+ * positions, F = n*t frames, HWp = h*w rounded up to 32): u [P][C], qkv
+ * [P][3C], v transposed per frame [F][C][HWp] and o [P][C], bf16, each region
+ * 256-byte aligned.
+ */
+WANVAE_API int wanvae_attention_workspace_size(const wanvae_attention_params *p, const wanvae_dims *d,
+                                               size_t *bytes);
+
+/*
+ * The decoder mid-block's attention block over every frame ("Closing the gap:
+ * Wan 2.2 14B VAE decoder", section 5: a spatial self-attention in which,
+ * within a frame, every position attends to every other, the sequence being
+ * the H*W grid and each (batch, frame) an independent problem; "Sharding of
+ * WAN 2.2 VAE", decoder module tree: WanAttentionBlock(384)).  The pages give
+ * no more; this computes, per frame and position i:
+ *   u = RMS_norm(x; gamma, beta)               (the decoder's norm, no SiLU)
+ *   [q | k | v] = w_qkv u + b_qkv              (1x1x1 projection)
+ *   o_i = sum_j softmax_j(q_i . k_j / sqrt(C)) v_j   (one head, all H*W j)
+ *   y_i = x_i + w_o o_i + b_o
+ * bf16 activations and weights, fp32 norm statistics, accumulation and
+ * softmax; u, q, k, v, o and y rounded to bf16.
+ *   x, y: [d.n][d.t][d.h][d.w][dim] bf16, channels-last; y must not overlap x.
+ * Five launches on `stream`: norm, q/k/v projection (MFMA GEMM), v transpose,
+ * flash attention (MFMA, scores kept on chip), output projection with the
+ * residual add (MFMA GEMM).
+ */
+WANVAE_API int wanvae_attention_block(const wanvae_attention_params *p, const void *x, void *y,
+                                      const wanvae_dims *d, void *workspace, size_t ws_bytes, void *stream);
+
 /* Text of this thread's most recent error (library-owned, valid until the
  * thread's next call into the library).  "" when there was none. */
 WANVAE_API const char *wanvae_last_error(void);
@@ -235,12 +278,14 @@ WANVAE_API const char *wanvae_last_error(void);
  * stream.  wanvae_timing_read waits for the recorded events and returns, for
  * one kernel kind, the number of launches and their summed duration in ms.
  * Kinds: 0 = fused RMS_norm+SiLU, 1 = bf16 MFMA conv, 2 = fp32 conv,
- * 3 = cache roll, 4 = pointwise conv.  wanvae_timing_reset forgets all
+ * 3 = cache roll, 4 = pointwise conv, 5 = attention projection GEMM,
+ * 6 = v transpose, 7 = flash attention.  wanvae_timing_reset forgets all
  * records.  Timing state is process-wide; enable it only while one thread
  * drives the library.
  */
 enum { WANVAE_KERNEL_NORM = 0, WANVAE_KERNEL_CONV_BF16 = 1, WANVAE_KERNEL_CONV_F32 = 2,
-       WANVAE_KERNEL_ROLL = 3, WANVAE_KERNEL_POINTWISE = 4, WANVAE_KERNEL_KINDS = 5 };
+       WANVAE_KERNEL_ROLL = 3, WANVAE_KERNEL_POINTWISE = 4, WANVAE_KERNEL_GEMM = 5,
+       WANVAE_KERNEL_TRANSPOSE = 6, WANVAE_KERNEL_ATTENTION = 7, WANVAE_KERNEL_KINDS = 8 };
 WANVAE_API int wanvae_timing_enable(int on);
 WANVAE_API int wanvae_timing_reset(void);
 WANVAE_API int wanvae_timing_read(int32_t kind, int64_t *launches, double *total_ms);

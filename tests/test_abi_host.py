@@ -195,3 +195,26 @@ def test_timing_kind_validation():
     n, ms = C.c_int64(0), C.c_double(0)
     assert L.wanvae_timing_read(99, C.byref(n), C.byref(ms)) == wv.ERR_SHAPE
     assert L.wanvae_timing_read(0, None, C.byref(ms)) == wv.ERR_NULL
+
+
+def test_attention_validation():
+    L = wv.lib()
+    ptr = 1 << 24
+    d = wv.Dims(1, 2, 8, 32)
+    b = C.c_size_t(0)
+    p = wv.AttentionParamsC(384, 1e-12, ptr, None, ptr + (1 << 20), None, ptr + (2 << 20), None)
+    assert L.wanvae_attention_workspace_size(C.byref(p), C.byref(d), C.byref(b)) == wv.OK
+    P, HWp = 2 * 8 * 32, 256
+    assert b.value >= P * 384 * 2 * 5 + 2 * 384 * HWp * 2 - P * 384 * 2   # u, qkv, v^T, o
+    bad = wv.AttentionParamsC(96, 1e-12, ptr, None, ptr, None, ptr, None)
+    assert L.wanvae_attention_workspace_size(C.byref(bad), C.byref(d), C.byref(b)) == wv.ERR_SHAPE
+    nul = wv.AttentionParamsC(384, 1e-12, None, None, ptr, None, ptr, None)
+    assert L.wanvae_attention_workspace_size(C.byref(nul), C.byref(d), C.byref(b)) == wv.ERR_NULL
+    x, y, ws = C.c_void_p(1 << 34), C.c_void_p(1 << 35), C.c_void_p(1 << 36)
+    need = C.c_size_t(0)
+    assert L.wanvae_attention_workspace_size(C.byref(p), C.byref(d), C.byref(need)) == wv.OK
+    assert L.wanvae_attention_block(C.byref(p), x, y, C.byref(d), ws, need.value - 1, None) == wv.ERR_WORKSPACE
+    assert L.wanvae_attention_block(C.byref(p), x, x, C.byref(d), ws, need.value, None) == wv.ERR_ALIAS
+    assert L.wanvae_attention_block(C.byref(p), None, y, C.byref(d), ws, need.value, None) == wv.ERR_NULL
+    empty = wv.Dims(1, 0, 8, 32)
+    assert L.wanvae_attention_block(C.byref(p), None, None, C.byref(empty), None, 0, None) == wv.OK

@@ -331,3 +331,62 @@ def test_timing_counts_launches(torch, wv):
     wv.timing_reset()
     assert n_norm == 4 and n_conv == 4
     assert ms_norm > 0 and ms_conv > 0
+
+
+# --------------------------------------------------------------------------- attention
+def _attn_check(torch, wv, x_host, p, label, frames=None, nq=None, seed=0):
+    """Run the attention block on x and compare with the oracle: the whole
+    output and, separately, the attention branch y - x (which the residual
+    would otherwise dwarf); on full-size inputs only sampled queries of some
+    frames."""
+    blk = wv.AttentionBlock.from_host(p)
+    xd = gu.to_dev(x_host, wl.BF16)
+    y = gu.to_host(blk.forward(xd))
+    args = (p["gamma"], p["beta"], p["wqkv"], p["bqkv"], p["wo"], p["bo"])
+    N, T, H, W, C_ = x_host.shape
+    if frames is None:
+        ref = oracle.attention_block(x_host, *args)
+        got, xs = y, x_host
+    else:
+        rng = np.random.default_rng(seed)
+        refs, gots, xss = [], [], []
+        for (n, t) in frames:
+            q = np.unique(np.concatenate([[0, W - 1, (H - 1) * W, H * W - 1],
+                                          rng.integers(0, H * W, size=nq)]))
+            refs.append(oracle.attention_block(x_host, *args, frame=(n, t), queries=q))
+            gots.append(y[n, t].reshape(-1, C_)[q])
+            xss.append(x_host[n, t].reshape(-1, C_)[q])
+        ref, got, xs = np.concatenate(refs), np.concatenate(gots), np.concatenate(xss)
+    err = gu.rel_err(got, ref)
+    err_branch = gu.rel_err(got - xs, ref - xs)
+    gu.report(f"attention {label}", err, gu.TOL_BF16, f"branch y-x: {err_branch:.3e} pcc={gu.pcc(got - xs, ref - xs):.6f}")
+    assert err <= gu.TOL_BF16
+    assert err_branch <= gu.TOL_BF16
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 2, 5, 7, 64),      # 35 positions: one query block, a ragged second key block
+    (1, 1, 12, 13, 128),   # 156 positions: 2 query blocks, 5 key blocks
+    (2, 2, 9, 16, 384),    # the decoder's width, batch 2
+    (1, 1, 17, 31, 384),   # 527 positions: ragged query and key blocks
+    (1, 2, 1, 1, 64),      # one position per frame: o = v
+])
+def test_attention_block_small(torch, wv, shape):
+    rng = np.random.default_rng(sum(shape))
+    x = wl.round_bf16(rng.standard_normal(shape).astype(np.float32))
+    p = wl.make_attention_params(shape[-1], seed=sum(shape))
+    _attn_check(torch, wv, x, p, f"{shape}")
+
+
+def test_attention_block_latent_sampled(torch, wv):
+    """The latent-resolution mid-block, [1, 21, 90, 160, 384], on sampled
+    queries (corners and random positions) of the first, a middle and the
+    last frame; the oracle computes k and v of each sampled frame in full."""
+    w = wl.custom("attn", wl.BF16, 1, 21, 90, 160, 384, 384)
+    xd = wl.make_x_device(w, seed=3)
+    x = xd.float().cpu().numpy()
+    del xd
+    p = wl.make_attention_params(384, seed=3)
+    _attn_check(torch, wv, x, p, "latent [1,21,90,160,384] sampled", frames=[(0, 0), (0, 10), (0, 20)],
+                nq=24, seed=3)
+    torch.cuda.empty_cache()
