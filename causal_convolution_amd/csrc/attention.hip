@@ -28,8 +28,9 @@
 //    8-byte pieces per fragment), so no transpose of P is needed;
 //  - the K and V^T blocks (2 x 24 KB at D = 384) are staged by LDS-DMA
 //    (buffer_load ... lds, 6 instructions per wave and block) into a 2-slot
-//    ring, the next block loading while the current one computes; two
-//    barriers per block: one for the score exchange, one for the ring.
+//    ring, and the partial scores into a double buffer, which lets one barrier
+//    per key block serve both: K of block j + 2 and V^T of block j + 1 are
+//    requested right after block j's barrier, a full block ahead of use.
 // LDS: K rows are swizzled in 16-byte chunks (chunk ^ (key & 15)) and V^T rows
 // (64 bytes) by (d >> 2) & 3, so fragment reads spread over the banks.
 // Scores of keys past HW are -inf; queries past HW compute on zero q and are
@@ -88,11 +89,11 @@ struct AttnShape {
     static constexpr int K_BYTES = kBK * D * 2;         // one K block
     static constexpr int V_BYTES = D * kBK * 2;         // one V^T block
     static constexpr int SLOT = K_BYTES + V_BYTES;
-    static constexpr int DMA_PER_BLOCK = SLOT / 1024;   // 1 KB per instruction
-    static constexpr int DMA_PER_WAVE = DMA_PER_BLOCK / kWaves;
-    static constexpr int SX_BYTES = 4 * 2 * 64 * 16 * 4;   // partial scores: [qg][hf][lane][16] fp32
-    static_assert(D % 64 == 0 && D <= 512, "head width a multiple of 64");
-    static_assert(DMA_PER_BLOCK % kWaves == 0, "every wave issues the same number of loads");
+    static constexpr int KB = K_BYTES / 1024;           // 1 KB LDS-DMA blocks of K
+    static constexpr int VB = V_BYTES / 1024;           // and of V^T
+    // partial scores, double-buffered: [2][qg][hf][lane][16] fp32
+    static constexpr int SX_BYTES = 2 * 4 * 2 * 64 * 16 * 4;
+    static_assert(D % 64 == 0 && D <= 384, "head width a multiple of 64, at most 384");
     static_assert(2 * SLOT + SX_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -131,37 +132,33 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         }
     }
 
-    // ---- LDS-DMA of key block j into ring slot sl: this wave's pieces.
-    // Piece P (16 bytes) of a slot: P < K_BYTES / 16 is K row P / CPR, stored
-    // chunk P % CPR = global chunk ^ (row & KSWZ); the rest is V^T row d (64
-    // bytes = 4 chunks), stored chunk = global chunk ^ ((d >> 2) & 3).
+    // ---- LDS-DMA of key block j into ring slot sl, K and V^T parts apart;
+    // wave w takes the 1 KB blocks w, w + 8, ...  Piece P (16 bytes) of the K
+    // part is K row P / CPR, stored chunk P % CPR = global chunk ^ (row &
+    // KSWZ); piece P of the V^T part is V^T row d = P / 4 (64 bytes, 4
+    // chunks), stored chunk = global chunk ^ ((d >> 2) & 3).
     const uint32_t ring_base = lds_address(ring);
     const i32x4 rk = buffer_rsrc(qkv_f + D, (uint32_t)((int64_t)HW * row3 * 2 - D * 2));
     const i32x4 rv = buffer_rsrc(vt_f, (uint32_t)((int64_t)D * HWp * 2));
-    auto issue_block = [&](int j, int sl) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < S::DMA_PER_WAVE; ++i) {
-            const int b = wave * S::DMA_PER_WAVE + i;   // 1 KB block of the slot
+    auto issue_k = [&](int j, int sl) __attribute__((always_inline)) {
+        for (int b = wave; b < S::KB; b += kWaves) {
             const int P = b * 64 + lane;
-            const uint32_t lds = ring_base + (uint32_t)(sl * S::SLOT + b * 1024);
-            if (P < S::K_BYTES / 16) {
-                const int row = P / S::CPR, cs = P % S::CPR;
-                const int c = cs ^ (row & S::KSWZ);
-                const int key = j * kBK + row;
-                const uint32_t off = key < HW ? (uint32_t)key * (uint32_t)(row3 * 2) + (uint32_t)c * 16 : kOOB;
-                lds_dma16(rk, lds, off);
-            } else {
-                const int Pv = P - S::K_BYTES / 16;
-                const int d = Pv >> 2, cs = Pv & 3;
-                const int c = cs ^ ((d >> 2) & 3);
-                const uint32_t off = (uint32_t)d * (uint32_t)(HWp * 2) + (uint32_t)(j * kBK * 2) + (uint32_t)c * 16;
-                lds_dma16(rv, lds, off);
-            }
+            const int row = P / S::CPR, cs = P % S::CPR;
+            const int c = cs ^ (row & S::KSWZ);
+            const int key = j * kBK + row;
+            const uint32_t off = key < HW ? (uint32_t)key * (uint32_t)(row3 * 2) + (uint32_t)c * 16 : kOOB;
+            lds_dma16(rk, ring_base + (uint32_t)(sl * S::SLOT + b * 1024), off);
         }
     };
-    // Note: a wave's pieces are either all K or all V^T when DMA_PER_WAVE * 64
-    // pieces divide the K part; the branch above is per lane and stays valid
-    // either way (both paths issue exactly one load).
+    auto issue_v = [&](int j, int sl) __attribute__((always_inline)) {
+        for (int b = wave; b < S::VB; b += kWaves) {
+            const int P = b * 64 + lane;
+            const int d = P >> 2, cs = P & 3;
+            const int c = cs ^ ((d >> 2) & 3);
+            const uint32_t off = (uint32_t)d * (uint32_t)(HWp * 2) + (uint32_t)(j * kBK * 2) + (uint32_t)c * 16;
+            lds_dma16(rv, ring_base + (uint32_t)(sl * S::SLOT + S::K_BYTES + b * 1024), off);
+        }
+    };
 
     // fragment reads
     auto ldK = [&](const unsigned char *slot, int s) __attribute__((always_inline)) {
@@ -188,11 +185,19 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    float *const sx_mine = sx + ((qg * 2 + hf) * 64 + lane) * 16;
-    const float *const sx_0 = sx + ((qg * 2 + 0) * 64 + lane) * 16;
-    const float *const sx_1 = sx + ((qg * 2 + 1) * 64 + lane) * 16;
+    // this lane's partial scores of buffer sb, and the two halves of its pair
+    auto sx_at = [&](int sb, int half) __attribute__((always_inline)) {
+        return sx + (((sb * 4 + qg) * 2 + half) * 64 + lane) * 16;
+    };
 
-    issue_block(0, 0);
+    // One barrier per key block.  Block j: scores from K_j, partials
+    // published, own loads of K_{j+1} and V_j waited for, barrier; then K_{j+2}
+    // goes into K_j's place and V_{j+1} into V_{j-1}'s (both free: every wave
+    // has passed the barrier after its last read of them), and the softmax and
+    // the value product of block j run on data every wave saw land.
+    issue_k(0, 0);
+    issue_v(0, 0);
+    if (nblk > 1) issue_k(1, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     compiler_fence();
     __builtin_amdgcn_s_barrier();
@@ -201,7 +206,6 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
     for (int j = 0; j < nblk; ++j) {
         const int sl = j & 1;
         const unsigned char *slot = ring + sl * S::SLOT;
-        if (j + 1 < nblk) issue_block(j + 1, sl ^ 1);
 
         // partial scores over this wave's head half
         floatx16 sp;
@@ -209,18 +213,23 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         for (int r = 0; r < 16; ++r) sp[r] = 0.0f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ldK(slot, s), qf[s], sp, 0, 0, 0);
+        float *const mine = sx_at(sl, hf);
 #pragma unroll
         for (int r = 0; r < 16; r += 4)
-            *reinterpret_cast<float4 *>(sx_mine + r) = float4{sp[r], sp[r + 1], sp[r + 2], sp[r + 3]};
+            *reinterpret_cast<float4 *>(mine + r) = float4{sp[r], sp[r + 1], sp[r + 2], sp[r + 3]};
         compiler_fence();
-        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & waitcnt_lgkm0());
         __builtin_amdgcn_s_barrier();
         compiler_fence();
+        if (j + 2 < nblk) issue_k(j + 2, sl);
+        if (j + 1 < nblk) issue_v(j + 1, sl ^ 1);
         float sc[16];
+        const float *const h0 = sx_at(sl, 0);
+        const float *const h1 = sx_at(sl, 1);
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
-            const float4 a = *reinterpret_cast<const float4 *>(sx_0 + r);
-            const float4 b = *reinterpret_cast<const float4 *>(sx_1 + r);
+            const float4 a = *reinterpret_cast<const float4 *>(h0 + r);
+            const float4 b = *reinterpret_cast<const float4 *>(h1 + r);
             sc[r] = a.x + b.x; sc[r + 1] = a.y + b.y; sc[r + 2] = a.z + b.z; sc[r + 3] = a.w + b.w;
         }
 
@@ -264,13 +273,6 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ldV(slot, t, ks), pf[ks], acc[t], 0, 0, 0);
-
-        // the next block has landed (own loads), and every wave is done with
-        // this slot and with the score exchange
-        compiler_fence();
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & waitcnt_lgkm0());
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
     }
 
     // ---- o = O / l for this lane's query: d = hf DH + 32 t + 8 jj + 4 g + i
