@@ -97,6 +97,18 @@ struct AttnShape {
     static_assert(2 * SLOT + SX_BYTES <= 160 * 1024, "LDS");
 };
 
+// max and sum of v over lanes l and l ^ 32.  v_permlane32_swap on two copies
+// of v leaves each lane holding its own value and its partner's, one in each
+// result, so the combination needs no knowledge of which is which.
+__device__ __forceinline__ float halves_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_t *__restrict__ qkv,
                                                                    const uint16_t *__restrict__ vt,
@@ -233,30 +245,37 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
             sc[r] = a.x + b.x; sc[r + 1] = a.y + b.y; sc[r + 2] = a.z + b.z; sc[r + 3] = a.w + b.w;
         }
 
-        // online softmax for this lane's query (column l32), keys 8jj + 4g + i
-        float mx = -INFINITY;
+        // online softmax for this lane's query (column l32), keys 8jj + 4g + i.
+        // The maximum is taken over the raw scores (the scale is positive),
+        // and only the last block can hold keys past HW.
+        if (j * kBK + kBK > HW) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (j * kBK + 8 * (r >> 2) + 4 * g + (r & 3) >= HW) sc[r] = -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        mx = halves_max(mx) * scale_log2;
+        // Rescale only when some query's maximum grew: otherwise the factor
+        // is exp2(0) = 1 for every lane, and skipping it changes no bit.
+        if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+            m_run = m_new;
+        }
+        // l_run: this lane's share (its 16 keys of every block); the two
+        // halves of the wave are added at the end
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int key = j * kBK + 8 * (r >> 2) + 4 * g + (r & 3);
-            sc[r] = key < HW ? sc[r] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sc[r]);
+            sc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], scale_log2, -m_run));
+            l_run += sc[r];
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float ls = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            sc[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
-            ls += sc[r];
-        }
-        ls += __shfl_xor(ls, 32);
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
 
         // O^T += V^T P^T over this wave's head half
         bf16x8 pf[2];
@@ -277,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
 
     // ---- o = O / l for this lane's query: d = hf DH + 32 t + 8 jj + 4 g + i
     const int q = q0 + l32;
+    l_run = halves_sum(l_run);
     if (q < HW) {
         const float inv = 1.0f / l_run;
         uint16_t *orow = o + (f * (int64_t)HW + q) * D + hf * DH;
