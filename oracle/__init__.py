@@ -85,6 +85,9 @@ def lib():
                                              _f32p, _f32p, _f32p, _f32p, C.POINTER(C.c_int64),
                                              _i64, _f32p]
         L.oracle_attention_frame.restype = None
+        L.oracle_upsample2d_conv.argtypes = [_f32p, _i64, _i64, _i64, C.c_int, C.c_int, _f32p, _f32p,
+                                             _i64, _i64, _f32p]
+        L.oracle_upsample2d_conv.restype = None
         for f in ("oracle_norm_silu", "oracle_rms_norm", "oracle_causal_conv3d", "oracle_shortcut",
                   "oracle_resblock_full", "oracle_resblock_stream_step",
                   "oracle_resblock_stream", "oracle_resblock_window"):
@@ -304,3 +307,29 @@ def resblock_window(blk: Block, x_region, region, dims, box):
                                  rt1 - rt0, rh1 - rh0, rw1 - rw0, t0, t1, h0, h1, w0, w1,
                                  _ptr(y))
     return y
+
+
+def upsample2d_conv(x, w, bias=None, frames=None, rows=None):
+    """The decoder's spatial upsampler (readings in oracle.c,
+    oracle_upsample2d_conv): nearest-neighbour x2 in H and W, then a 3x3 conv
+    with zero padding 1, frame by frame.
+
+    x [N,T,H,W,Cin]; w [Cout,Cin,3,3]; bias [Cout] or None.  Returns y
+    [N,T,2H,2W,Cout], or with frames (a list of (n, t)) and rows (r0, r1) only
+    those output rows of those frames, [len(frames), r1 - r0, 2W, Cout]."""
+    x = _f32(x)
+    w = _f32(w)
+    N, T, H, W, cin = x.shape
+    cout = w.shape[0]
+    assert w.shape == (cout, cin, 3, 3)
+    bias = None if bias is None else _f32(bias)
+    r0, r1 = (0, 2 * H) if rows is None else rows
+    assert 0 <= r0 <= r1 <= 2 * H
+    if frames is None:
+        xs = x.reshape(N * T, H, W, cin)
+    else:
+        xs = np.ascontiguousarray(np.stack([x[n, t] for (n, t) in frames]))
+    nf = xs.shape[0]
+    y = np.empty((nf, r1 - r0, 2 * W, cout), np.float32)
+    lib().oracle_upsample2d_conv(_ptr(xs), nf, H, W, cin, cout, _ptr(w), _ptr(bias), r0, r1, _ptr(y))
+    return y.reshape(N, T, r1 - r0, 2 * W, cout) if frames is None else y

@@ -509,3 +509,50 @@ void oracle_attention_frame(const float *x, int64_t HW, int C, const float *gamm
     }
     free(u); free(k); free(v);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Spatial upsampler of the decoder (upsample2d): every frame doubled in H   */
+/* and W by nearest neighbour, then one 3x3 conv over the frame.             */
+/* "Sharding of WAN 2.2 VAE", decoder module tree: the up blocks end in an    */
+/* upsample2d or upsample3d; "Further sharding consideration: WanResample"   */
+/* names the upsampler's conv, resample[1], and its C_out.  The tree's       */
+/* channel counts (an up block that ends at 384 channels feeds one that      */
+/* starts at 192) make that conv halve the channels, and the decoder goes    */
+/* from the 90 x 160 latent to 720 x 1280 through three upsamplers, x2 each. */
+/* The pages say no more; the readings used:                                 */
+/*   up[h][w][ci] = x[h / 2][w / 2][ci]       (nearest, integer division)    */
+/*   y[h][w][co]  = sum_{kh, kw, ci} w[co][ci][kh][kw] up[h+kh-1][w+kw-1][ci] */
+/*                  + b[co]                    (zero outside the 2H x 2W image)*/
+/* frame by frame, with no temporal taps (the temporal half of upsample3d is */
+/* not described on the pages and is not modelled here).  The sum runs in    */
+/* fp64 in ascending (kh, kw, ci) order, the bias last, one rounding.        */
+/* x: nf frames [nf][H][W][cin]; w: [cout][cin][3][3]; b: [cout] or NULL;     */
+/* y: rows [r0, r1) of each upsampled frame, [nf][r1 - r0][2W][cout].        */
+/* ------------------------------------------------------------------------ */
+void oracle_upsample2d_conv(const float *x, int64_t nf, int64_t H, int64_t W, int cin, int cout,
+                            const float *w, const float *b, int64_t r0, int64_t r1, float *y)
+{
+    const int64_t Ho = 2 * H, Wo = 2 * W, nr = r1 - r0;
+    #pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < nf * nr * Wo; ++o) {
+        const int64_t f = o / (nr * Wo), h = r0 + (o / Wo) % nr, wc = o % Wo;
+        const float *xf = x + f * H * W * (int64_t)cin;
+        float *yo = y + o * (int64_t)cout;
+        for (int co = 0; co < cout; ++co) {
+            double acc = 0.0;
+            for (int kh = 0; kh < 3; ++kh) {
+                const int64_t uh = h + kh - 1;
+                if (uh < 0 || uh >= Ho) continue;
+                for (int kw = 0; kw < 3; ++kw) {
+                    const int64_t uw = wc + kw - 1;
+                    if (uw < 0 || uw >= Wo) continue;
+                    const float *xs = xf + ((uh / 2) * W + uw / 2) * (int64_t)cin;
+                    for (int ci = 0; ci < cin; ++ci)
+                        acc += (double)w[(((int64_t)co * cin + ci) * 3 + kh) * 3 + kw] * (double)xs[ci];
+                }
+            }
+            if (b) acc += (double)b[co];
+            yo[co] = (float)acc;
+        }
+    }
+}

@@ -43,6 +43,12 @@ MUTANTS = {
                               "const float *wk = wqkv + ((int64_t)2 * C + c) * C;"),
     "attention_query_from_raw_input": ("sq += (double)wq[t] * (double)ui[t];",
                                        "sq += (double)wq[t] * (double)x[i * (int64_t)C + t];"),
+    "upsample_rounds_up": ("xf + ((uh / 2) * W + uw / 2) * (int64_t)cin;",
+                           "xf + ((uh / 2) * W + (uw + 1) / 2 % W) * (int64_t)cin;"),
+    "upsample_pad_shift": ("const int64_t uh = h + kh - 1;", "const int64_t uh = h + kh;"),
+    "upsample_kh_kw_transposed": ("* cin + ci) * 3 + kh) * 3 + kw]", "* cin + ci) * 3 + kw) * 3 + kh]"),
+    "upsample_dropped_bias": ("if (b) acc += (double)b[co];", "if (b) acc += 0.0;"),
+    "upsample_row_stride": ("xf + ((uh / 2) * W + uw / 2)", "xf + ((uh / 2) * 2 * W / 2 + uw / 2 + uh % 2)"),
 }
 
 

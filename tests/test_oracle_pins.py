@@ -504,3 +504,102 @@ def test_attention_sampled_queries_equal_full(orc):
     q = [23, 0, 7, 7, 11]
     ys = orc.attention_block(x, *p, frame=(0, 1), queries=q)
     assert np.array_equal(ys, y[0, 1].reshape(-1, 8)[q])
+
+
+# --------------------------------------------------------------------------- upsample2d
+def _up_params(rng, cin, cout):
+    w = (rng.standard_normal((cout, cin, 3, 3)) / np.sqrt(9 * cin)).astype(np.float32)
+    b = (rng.standard_normal(cout) * 0.1).astype(np.float32)
+    return w, b
+
+
+@pytest.mark.parametrize("shape,cout", [((1, 2, 3, 5, 8), 4), ((2, 1, 4, 4, 16), 8), ((1, 1, 1, 1, 3), 5)])
+def test_upsample2d_matches_library_routines(orc, shape, cout):
+    """torch fp64: F.interpolate(scale_factor=2, mode='nearest') then
+    F.conv2d(padding=1), frame by frame."""
+    import torch
+    rng = np.random.default_rng(sum(shape) + cout)
+    x = rng.standard_normal(shape).astype(np.float32)
+    w, b = _up_params(rng, shape[-1], cout)
+    y = orc.upsample2d_conv(x, w, b)
+    N, T, H, W, C = shape
+    X = torch.from_numpy(x).double().reshape(N * T, H, W, C).permute(0, 3, 1, 2)
+    U = torch.nn.functional.interpolate(X, scale_factor=2, mode="nearest")
+    R = torch.nn.functional.conv2d(U, torch.from_numpy(w).double(), torch.from_numpy(b).double(), padding=1)
+    ref = R.permute(0, 2, 3, 1).reshape(N, T, 2 * H, 2 * W, cout).numpy()
+    assert y.shape == ref.shape
+    assert np.abs(y - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_upsample2d_brute_force(orc):
+    """Pure-Python loops over the definition, with explicit bounds checks."""
+    rng = np.random.default_rng(5)
+    H, W, cin, cout = 2, 3, 2, 3
+    x = rng.standard_normal((1, 1, H, W, cin)).astype(np.float32)
+    w, b = _up_params(rng, cin, cout)
+    y = orc.upsample2d_conv(x, w, b)
+    for h in range(2 * H):
+        for c in range(2 * W):
+            for co in range(cout):
+                acc = float(b[co])
+                for kh in range(3):
+                    for kw in range(3):
+                        uh, uw = h + kh - 1, c + kw - 1
+                        if 0 <= uh < 2 * H and 0 <= uw < 2 * W:
+                            for ci in range(cin):
+                                acc += float(w[co, ci, kh, kw]) * float(x[0, 0, uh // 2, uw // 2, ci])
+                assert abs(y[0, 0, h, c, co] - acc) <= 1e-6 * (1 + abs(acc))
+
+
+def test_upsample2d_equals_conv3d_current_tap_on_repeated_input(orc):
+    """Against the pinned causal conv: the frames repeated 2x2 (np.repeat)
+    through a 3x3x3 conv whose only nonzero temporal tap is the current
+    frame's give the same sums in the same order: bitwise equal."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((1, 3, 4, 5, 16)).astype(np.float32)
+    w, b = _up_params(rng, 16, 8)
+    up = np.repeat(np.repeat(x, 2, axis=2), 2, axis=3)
+    w3 = np.zeros((8, 16, 3, 3, 3), np.float32)
+    w3[:, :, 2] = w
+    ref = orc.causal_conv3d(up, w3, b)
+    y = orc.upsample2d_conv(x, w, b)
+    assert np.array_equal(y, ref)
+
+
+def test_upsample2d_centre_tap_gives_2x2_blocks(orc):
+    """Only the centre tap: each input position becomes a 2x2 block of one
+    value, the pointwise conv of that position."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 2, 3, 4, 16)).astype(np.float32)
+    w, b = _up_params(rng, 16, 8)
+    wc = np.zeros_like(w)
+    wc[:, :, 1, 1] = w[:, :, 1, 1]
+    y = orc.upsample2d_conv(x, wc, b)
+    pw = orc.pointwise_conv(x, np.ascontiguousarray(w[:, :, 1, 1]), b)
+    for a in range(2):
+        for c in range(2):
+            assert np.array_equal(y[:, :, a::2, c::2], pw)
+
+
+def test_upsample2d_constant_input(orc):
+    """x = c everywhere: the interior sees all 9 taps, the top-left corner the
+    four taps kh, kw in {1, 2}, the right edge the six taps kw in {0, 1}."""
+    rng = np.random.default_rng(8)
+    cin, cout, c = 8, 4, 0.75
+    x = np.full((1, 1, 3, 3, cin), c, np.float32)
+    w, b = _up_params(rng, cin, cout)
+    y = orc.upsample2d_conv(x, w, b).astype(np.float64)
+    s = w.astype(np.float64).sum(axis=1)                       # [cout, 3, 3]
+    np.testing.assert_allclose(y[0, 0, 2, 2], b + c * s.sum(axis=(1, 2)), rtol=1e-6)
+    np.testing.assert_allclose(y[0, 0, 0, 0], b + c * s[:, 1:, 1:].sum(axis=(1, 2)), rtol=1e-6)
+    np.testing.assert_allclose(y[0, 0, 3, 5], b + c * s[:, :, :2].sum(axis=(1, 2)), rtol=1e-6)
+
+
+def test_upsample2d_rows_and_frames_equal_full(orc):
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((2, 3, 5, 4, 16)).astype(np.float32)
+    w, b = _up_params(rng, 16, 8)
+    full = orc.upsample2d_conv(x, w, b)
+    part = orc.upsample2d_conv(x, w, b, frames=[(1, 2), (0, 0)], rows=(3, 8))
+    assert np.array_equal(part[0], full[1, 2, 3:8])
+    assert np.array_equal(part[1], full[0, 0, 3:8])
