@@ -148,6 +148,15 @@ def head_tail(torch, wv, steps, warmup):
          lambda: wv.causal_conv3d(n_out, w_out, b3, out=y_out),
          2.0 * P_out * 3 * 27 * 96, 2.0 * P_out * (96 + 3)),
     ]
+    return {"metric": "decoder head/tail ops, average launch time (1 GPU)", "unit": "ms",
+            "higher_is_better": False, "dtype": "bf16", "data": "synthetic (seeded)",
+            "steps": steps, "warmup": warmup, "ops": time_ops(torch, wv, ops, steps, warmup)}
+
+
+def time_ops(torch, wv, ops, steps, warmup):
+    """Per op (name, kernel kind, launch, FLOPs, bytes): `warmup` untimed
+    launches, then the library's hipEvent timing over `steps` launches; the
+    bound is the larger of FLOPs / 2.5 PFLOP/s and bytes / 8 TB/s."""
     res = []
     for name, kind, fn, flop, nbytes in ops:
         for _ in range(warmup):
@@ -170,7 +179,34 @@ def head_tail(torch, wv, steps, warmup):
                     "bound": bound, "frac": max(t_mfma, t_hbm) / avg})
         print(f"[bench] {name}: {avg:.3f} ms, {res[-1]['frac']:.1%} of its {bound} bound",
               file=sys.stderr, flush=True)
-    return {"metric": "decoder head/tail ops, average launch time (1 GPU)", "unit": "ms",
+    return res
+
+
+def upsample(torch, wv, steps, warmup):
+    """The decoder's spatial upsamplers (wanvae_upsample2d_conv: nearest x2,
+    then the 3x3 conv halving the channels) at the Wan 2.2 720p decoder
+    shapes, with the frame counts of the blocks around them: 384 -> 192 from
+    90 x 160 (21 frames) and from 180 x 320 (41 frames), 192 -> 96 from
+    360 x 640 (81 frames).  Seeded synthetic bf16 values."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    res = []
+    for (t, h, w, cin, cout) in [(21, 90, 160, 384, 192), (41, 180, 320, 384, 192), (81, 360, 640, 192, 96)]:
+        x = torch.empty((1, t, h, w, cin), dtype=torch.bfloat16, device="cuda")
+        for i in range(t):
+            x[0, i].copy_(torch.randn((h, w, cin), device="cuda", generator=g))
+        wp = wv.pack_conv2d_weights((torch.randn((cout, cin, 3, 3), device="cuda", generator=g)
+                                     * (1.0 / (9 * cin)) ** 0.5).to(torch.bfloat16))
+        b = torch.randn(cout, device="cuda", generator=g) * 0.1
+        y = torch.empty((1, t, 2 * h, 2 * w, cout), dtype=torch.bfloat16, device="cuda")
+        P_in, P_out = t * h * w, t * 4 * h * w
+        ops = [(f"upsample2d {cin}->{cout}, [1,{t},{h},{w},{cin}] -> [1,{t},{2 * h},{2 * w},{cout}]",
+                wv.KERNEL_UPSAMPLE, lambda: wv.upsample2d_conv(x, wp, b, out=y),
+                2.0 * P_out * cout * 9 * cin, 2.0 * (P_in * cin + P_out * cout))]
+        res += time_ops(torch, wv, ops, steps, warmup)
+        del x, y
+        torch.cuda.empty_cache()
+    return {"metric": "decoder spatial upsampler conv, average launch time (1 GPU)", "unit": "ms",
             "higher_is_better": False, "dtype": "bf16", "data": "synthetic (seeded)",
             "steps": steps, "warmup": warmup, "ops": res}
 
@@ -247,6 +283,9 @@ def main():
     ap.add_argument("--attention", action="store_true",
                     help="time the decoder mid-block attention block instead, at the latent "
                          "shape [1,21,90,160,384] (one JSON line)")
+    ap.add_argument("--upsample", action="store_true",
+                    help="time the decoder's spatial upsampler conv instead (nearest x2 + 3x3 "
+                         "conv) at the three decoder upsampler shapes (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-MiB buffer 3 times (a plain copy "
                          "kernel of known size, to scale HBM byte counters by)")
@@ -268,6 +307,9 @@ def main():
         return
     if args.attention:
         print(json.dumps(attention(torch, wv, wl, args.steps, args.warmup)), flush=True)
+        return
+    if args.upsample:
+        print(json.dumps(upsample(torch, wv, args.steps, args.warmup)), flush=True)
         return
 
     w = wl.WORKLOADS[args.workload]

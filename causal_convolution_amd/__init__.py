@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libwanvae.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(7)
 F32, BF16 = 0, 1
 (KERNEL_NORM, KERNEL_CONV_BF16, KERNEL_CONV_F32, KERNEL_ROLL, KERNEL_POINTWISE, KERNEL_GEMM,
- KERNEL_TRANSPOSE, KERNEL_ATTENTION) = range(8)
+ KERNEL_TRANSPOSE, KERNEL_ATTENTION, KERNEL_UPSAMPLE) = range(9)
 EPS = 1e-12
 
 
@@ -68,6 +68,12 @@ EXPORTS = {
     "wanvae_attention_workspace_size": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_size_t)]),
     "wanvae_attention_block": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                          C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wanvae_upsample2d_conv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(Dims),
+                                         C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
+    "wanvae_pack_conv2d_weights": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                             C.c_void_p]),
+    "wanvae_packed_conv2d_weight_elems": (C.c_int, [C.c_int32, C.c_int32, C.c_int32,
+                                                    C.POINTER(C.c_int64)]),
     "wanvae_last_error": (C.c_char_p, []),
     "wanvae_timing_enable": (C.c_int, [C.c_int]),
     "wanvae_timing_reset": (C.c_int, []),
@@ -230,6 +236,58 @@ def causal_conv3d(x, w, bias=None, cache=None, out=None, stream=None):
     d = Dims(n, t, h, wd)
     _check(lib().wanvae_causal_conv3d(_ptr(x), _ptr(cache), _ptr(w.data), _ptr(bias), _ptr(y),
                                       C.byref(d), cin, cout, _dtype_code(x), _stream(stream)))
+    return y
+
+
+# --------------------------------------------------------------------------- upsampler
+class PackedWeight2d:
+    """A 3x3 conv weight packed by ``wanvae_pack_conv2d_weights`` (bf16):
+    ``data`` holds ``packed_conv2d_weight_elems(cin, cout)`` elements."""
+
+    def __init__(self, data, cin: int, cout: int):
+        self.data, self.cin, self.cout = data, int(cin), int(cout)
+
+
+def packed_conv2d_weight_elems(cin: int, cout: int) -> int:
+    """Elements of a packed 2D conv weight (``wanvae_packed_conv2d_weight_elems``)."""
+    n = C.c_int64(0)
+    _check(lib().wanvae_packed_conv2d_weight_elems(int(cin), int(cout), BF16, C.byref(n)))
+    return n.value
+
+
+def pack_conv2d_weights(w, stream=None) -> PackedWeight2d:
+    """Pack a 3x3 conv weight [C_out, C_in, 3, 3] (bf16, on the GPU) for
+    ``upsample2d_conv``."""
+    torch = _torch()
+    if w.dim() != 4 or tuple(w.shape[2:]) != (3, 3):
+        raise ValueError(f"w must be [C_out, C_in, 3, 3], got {tuple(w.shape)}")
+    _dev(w, "w", torch.bfloat16)
+    cout, cin = int(w.shape[0]), int(w.shape[1])
+    out = torch.empty(packed_conv2d_weight_elems(cin, cout), dtype=w.dtype, device=w.device)
+    _check(lib().wanvae_pack_conv2d_weights(_ptr(w), _ptr(out), cin, cout, BF16, _stream(stream)))
+    return PackedWeight2d(out, cin, cout)
+
+
+def upsample2d_conv(x, w, bias=None, out=None, stream=None):
+    """The decoder's spatial upsampler (``wanvae_upsample2d_conv``): x
+    [n,t,h,w,Cin] bf16, w a PackedWeight2d (Cin -> Cout), bias [Cout] fp32 or
+    None -> [n,t,2h,2w,Cout]: nearest-neighbour x2, then the 3x3 conv."""
+    torch = _torch()
+    n, t, h, wd, cin = x.shape
+    if not isinstance(w, PackedWeight2d):
+        raise TypeError("w must be a PackedWeight2d (see pack_conv2d_weights)")
+    if w.cin != cin:
+        raise ValueError(f"w is {w.cin}->{w.cout}, x has {cin} channels")
+    cout = w.cout
+    _dev(x, "x", torch.bfloat16)
+    _dev(w.data, "w", torch.bfloat16, (packed_conv2d_weight_elems(cin, cout),))
+    _dev(bias, "bias", torch.float32, (cout,))
+    shape = (n, t, 2 * h, 2 * wd, cout)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    _dev(y, "out", x.dtype, shape)
+    d = Dims(n, t, h, wd)
+    _check(lib().wanvae_upsample2d_conv(_ptr(x), _ptr(w.data), _ptr(bias), _ptr(y), C.byref(d), cin, cout,
+                                        BF16, _stream(stream)))
     return y
 
 

@@ -327,6 +327,70 @@ int wanvae_packed_conv3d_weight_elems(int32_t cin, int32_t cout, int32_t dtype, 
     return WANVAE_OK;
 }
 
+int wanvae_packed_conv2d_weight_elems(int32_t cin, int32_t cout, int32_t dtype, int64_t *elems) {
+    g_error.clear();
+    WV_CHECK(elems != nullptr, WANVAE_ERR_NULL, "elems is NULL");
+    WV_CHECK(dtype == WANVAE_BF16, WANVAE_ERR_DTYPE, "2D conv weights are bf16 only (got dtype %d)", dtype);
+    WV_CHECK(wanvae::conv3d_bf16_supported(cin, cout), WANVAE_ERR_SHAPE,
+             "bf16 conv needs cin a multiple of 16 in [16, 1024] and cout in [1, 1024] (got %d, %d)", cin, cout);
+    *elems = wanvae::packed_conv2d_weight_elems(cin, cout);
+    return WANVAE_OK;
+}
+
+int wanvae_pack_conv2d_weights(const void *w, void *packed, int32_t cin, int32_t cout, int32_t dtype,
+                               void *stream) {
+    int64_t elems = 0;
+    if (int r = wanvae_packed_conv2d_weight_elems(cin, cout, dtype, &elems)) return r;
+    WV_CHECK(w && packed, WANVAE_ERR_NULL, "w and packed are required");
+    WV_CHECK(aligned16(w) && aligned16(packed), WANVAE_ERR_SHAPE, "pointers must be 16-byte aligned");
+    WV_CHECK(!overlaps(w, (size_t)9 * cin * cout * 2, packed, (size_t)elems * 2), WANVAE_ERR_ALIAS,
+             "packed overlaps w");
+    const hipError_t e = wanvae::launch_pack_conv2d_weights(w, packed, cin, cout, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "weight packing launch failed: %s", hipGetErrorString(e));
+    return WANVAE_OK;
+}
+
+int wanvae_upsample2d_conv(const void *x, const void *w, const float *bias, void *y, const wanvae_dims *d,
+                           int32_t cin, int32_t cout, int32_t dtype, void *stream) {
+    g_error.clear();
+    WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
+    WV_CHECK(dtype == WANVAE_BF16, WANVAE_ERR_DTYPE, "the upsampler conv is bf16 only");
+    int64_t P = 0;
+    if (int r = positions(d, &P)) return r;
+    if (int r = check_conv_channels(cin, cout, dtype)) return r;
+    // the output frame is 2h x 2w
+    wanvae_dims od = *d;
+    od.h = 2 * d->h;
+    od.w = 2 * d->w;
+    int64_t Po = 0;
+    if (int r = positions(&od, &Po)) return r;
+    if (int r = check_conv_slab(d, cin, dtype)) return r;
+    if (int r = check_conv_slab(&od, cout, dtype)) return r;
+    if (P == 0) return WANVAE_OK;
+    WV_CHECK(x && w && y, WANVAE_ERR_NULL, "x, w and y are required");
+    WV_CHECK(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(bias), WANVAE_ERR_SHAPE,
+             "pointers must be 16-byte aligned");
+    const size_t xb = (size_t)P * cin * 2, yb = (size_t)Po * cout * 2;
+    const size_t wb = (size_t)wanvae::packed_conv2d_weight_elems(cin, cout) * 2;
+    WV_CHECK(!overlaps(y, yb, x, xb) && !overlaps(y, yb, w, wb) && !overlaps(y, yb, bias, (size_t)cout * 4),
+             WANVAE_ERR_ALIAS, "y overlaps x, w or bias");
+    wanvae::ConvLaunch c;
+    c.x = x;
+    c.w = w;
+    c.bias = bias;
+    c.y = y;
+    c.n = od.n;
+    c.t = od.t;
+    c.h = od.h;
+    c.w_ = od.w;
+    c.cin = cin;
+    c.cout = cout;
+    c.up2 = true;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return timed_launch(WANVAE_KERNEL_UPSAMPLE, s, "upsample2d conv",
+                        [&] { return wanvae::launch_conv3d_bf16(c, s); });
+}
+
 int wanvae_pointwise_conv(const void *x, const void *w, const float *bias, void *y, int64_t rows,
                           int32_t cin, int32_t cout, int32_t dtype, void *stream) {
     g_error.clear();

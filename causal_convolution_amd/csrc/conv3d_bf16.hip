@@ -151,6 +151,11 @@ struct Args {
     const uint16_t *sc_in;
     int sc_c;
     int gemm;
+    // upsampler conv (up2 = 1): x holds frames of (H/2) x (W/2) positions,
+    // read as their nearest-neighbour doubling (position (h, w) of the H x W
+    // image is x[h/2][w/2]); only the current frame's taps, packed weight
+    // [cin/16][9 taps][cout][16]; no cache
+    int up2;
 };
 
 // One output tile: batch item, frame, first row / column / output channel,
@@ -302,7 +307,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         tile /= a.tiles_h;
         ti.nq = tile;
         // without a cache the stages of frames before 0 only add zeros: skipped
-        const int kt_begin = (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
+        const int kt_begin = a.up2 ? 2 : (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
         ti.kt_begin = kt_begin;
         ti.s_conv = a.gemm ? 0 : (3 - kt_begin) * ck;
         ti.s_total = ti.s_conv + (SC ? a.sc_c / (kKC * TL::SCS) : 0);
@@ -318,8 +323,12 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // logical half that the swizzle puts there.
         // bytes between neighbouring positions of a frame slab, and elements
         // between its 16-channel slices
+        // the input frame: H x W, or (H/2) x (W/2) read doubled (up2)
+        const int up = a.up2;
+        const int Wi = W >> up;
+        const int64_t HWi = HW >> (2 * up);
         const uint32_t cs2 = a.x_sliced ? (uint32_t)kUnit : (uint32_t)a.cin * 2;
-        const int64_t slice_elems = a.x_sliced ? HW * kKC : kKC;
+        const int64_t slice_elems = a.x_sliced ? HWi * kKC : kKC;
         const uint32_t tap2 = (uint32_t)a.cout_p * kUnit;   // bytes per tap of a packed stage
         // byte offset of block b's piece for a conv stage (sc = false) or a
         // shortcut stage (sc = true: x at the output positions, w_sc as one tap)
@@ -330,7 +339,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                 const int hf = (lane & 1) ^ ((c >> 3) & 1);
                 const int hh = ti.h0 - 1 + r, ww = ti.w0 - 1 + c;
                 const bool inside = r < TL::AR && hh >= 0 && hh < H && ww >= 0 && ww < W;
-                return inside ? (uint32_t)(hh * W + ww) * cs2 + hf * 16 : kOOB;
+                return inside ? (uint32_t)((hh >> up) * Wi + (ww >> up)) * cs2 + hf * 16 : kOOB;
             }
             const int u = (b - TL::A_BLOCKS) * 32 + (lane >> 1);
             const int hf = (lane & 1) ^ ((u >> 3) & 1);
@@ -408,14 +417,16 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     cc = cs % ck;
                 }
                 const int64_t ts = ti.tq + kt - 2;
-                abase = (ts >= 0 ? a.x + ((ti.nq * a.T + ts) * HW) * a.cin
-                                 : a.cache + ((ti.nq * 2 + (ts + 2)) * HW) * a.cin) +
+                abase = (ts >= 0 ? a.x + ((ti.nq * a.T + ts) * HWi) * a.cin
+                                 : a.cache + ((ti.nq * 2 + (ts + 2)) * HWi) * a.cin) +
                         cc * slice_elems;
-                abytes = (uint32_t)(HW * a.cin * 2 - cc * slice_elems * 2);
-                // elements of the packed weight before stage (kt, cc)
-                const int64_t wskip = (int64_t)(kt * ck + cc) * 9 * a.cout_p * kKC;
+                abytes = (uint32_t)(HWi * a.cin * 2 - cc * slice_elems * 2);
+                // elements of the packed weight before stage (kt, cc); an
+                // upsampler's weight holds the current frame's taps only
+                const int wkt = up ? kt - 2 : kt;
+                const int64_t wskip = (int64_t)(wkt * ck + cc) * 9 * a.cout_p * kKC;
                 bbase = a.w + wskip;
-                bbytes = (uint32_t)(((int64_t)27 * a.cin * a.cout_p - wskip) * 2);
+                bbytes = (uint32_t)(((int64_t)(up ? 9 : 27) * a.cin * a.cout_p - wskip) * 2);
             } else {
                 // first 16-channel slice of this shortcut stage
                 const int cc = (si - ti.s_conv) * TL::SCS;
@@ -842,6 +853,7 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.cres = c.cres;
     a.x_sliced = c.x_sliced ? 1 : 0;
     a.gemm = c.gemm ? 1 : 0;
+    a.up2 = c.up2 ? 1 : 0;
     a.sc_in = static_cast<const uint16_t *>(c.gemm ? c.x : c.res);
     a.sc_c = c.gemm ? c.cin : c.cres;
     if (c.gemm) a.wsc = static_cast<const uint16_t *>(c.w);

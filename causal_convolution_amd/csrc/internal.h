@@ -30,6 +30,10 @@ struct ConvLaunch {
     // GEMM launch (launch_gemm_bf16): y = w x + bias (+ res), w plain
     // [cout][cin], x channels-last; cin a multiple of 32, cout of 32
     bool gemm = false;
+    // upsampler conv (bf16): h, w_ are the output's (even) sizes, x frames are
+    // (h/2) x (w/2) read by nearest neighbour, w packed by
+    // launch_pack_conv2d_weights; no cache, no residual
+    bool up2 = false;
 };
 
 // Fused RMS_norm + SiLU over rows of C channels (C % 32 == 0, 32..1024).
@@ -73,6 +77,9 @@ hipError_t launch_flash_attention(const void *qkv, const void *vt, void *o, int6
 // (bf16: [3][cin/16][3][3][cout_p][16], cin % 16 == 0, cout_p = cout rounded
 // up to 32 with zero weights in the padding; fp32: [cout][3][3][3][cin]).
 int64_t packed_conv3d_weight_elems(int cin, int cout, bool bf16);
+// 2D 3x3 weights [cout][cin][3][3] (bf16) -> [cin/16][9][cout_p][16]
+int64_t packed_conv2d_weight_elems(int cin, int cout);
+hipError_t launch_pack_conv2d_weights(const void *w, void *out, int cin, int cout, hipStream_t s);
 hipError_t launch_pack_conv3d_weights(const void *w, void *out, int cin, int cout, bool bf16,
                                       hipStream_t s);
 

@@ -6,6 +6,9 @@
 //   bf16: [kt][C_in/16][kh][kw][C_out_p][16], C_out_p = C_out rounded up to 32
 //         (the MFMA tile's channel block), zero weights in the padding
 //
+// A 2D 3x3 weight [C_out][C_in][3][3] (the decoder upsampler's conv) packs
+// the same way with one temporal tap: [C_in/16][kh][kw][C_out_p][16].
+//
 // The bf16 layout follows the MFMA conv's K loop: one stage consumes temporal
 // tap kt and a 16-channel slice of C_in for all 9 (kh, kw) taps, so a stage's
 // weights for one tap are C_out x 32 bytes in one contiguous run (whole
@@ -30,8 +33,9 @@ __global__ void pack_f32_kernel(const T *__restrict__ w, T *__restrict__ out, in
     }
 }
 
+// kd: temporal taps of the source weight (3, or 1 for a 2D weight)
 __global__ void pack_bf16_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ out, int cin,
-                                 int cout, int cout_p, int64_t total) {
+                                 int cout, int cout_p, int kd, int64_t total) {
     const int slices = cin / 16;
     for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total;
          o += (int64_t)gridDim.x * blockDim.x) {
@@ -46,7 +50,7 @@ __global__ void pack_bf16_kernel(const uint16_t *__restrict__ w, uint16_t *__res
         const int kt = (int)(r / slices);
         const int ci = cc * 16 + c16;
         // output channels past cout are padding: zero weights
-        out[o] = co < cout ? w[((int64_t)co * cin + ci) * 27 + kt * 9 + khw] : (uint16_t)0;
+        out[o] = co < cout ? w[(((int64_t)co * cin + ci) * kd + kt) * 9 + khw] : (uint16_t)0;
     }
 }
 
@@ -65,10 +69,22 @@ hipError_t launch_pack_conv3d_weights(const void *w, void *out, int cin, int cou
     if (bf16)
         pack_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(w),
                                               static_cast<uint16_t *>(out), cin, cout,
-                                              (cout + 31) / 32 * 32, total);
+                                              (cout + 31) / 32 * 32, 3, total);
     else
         pack_f32_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(w),
                                                     static_cast<float *>(out), cin, cout, total);
+    return hipGetLastError();
+}
+
+int64_t packed_conv2d_weight_elems(int cin, int cout) { return (int64_t)9 * cin * ((cout + 31) / 32 * 32); }
+
+hipError_t launch_pack_conv2d_weights(const void *w, void *out, int cin, int cout, hipStream_t s) {
+    const int64_t total = packed_conv2d_weight_elems(cin, cout);
+    if (total == 0) return hipSuccess;
+    const int64_t want = (total + 255) / 256;
+    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    pack_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(w), static_cast<uint16_t *>(out), cin,
+                                          cout, (cout + 31) / 32 * 32, 1, total);
     return hipGetLastError();
 }
 

@@ -135,6 +135,16 @@ def make_attention_params(C: int, seed: int = 0):
             "wo": round_bf16(normal(1.0 / C, (C, C))), "bo": normal(0.01, C)}
 
 
+def make_upsample_params(cin: int, cout: int, seed: int = 0):
+    """Upsampler conv parameters as float32 numpy arrays: w [cout, cin, 3, 3]
+    ~ N(0, 1/(9 cin)) (variance 1 / fan_in) rounded to bf16 values, b ~ N(0,
+    0.01)."""
+    rng = np.random.default_rng(seed + 91)
+    w = rng.normal(0.0, np.sqrt(1.0 / (9 * cin)), size=(cout, cin, 3, 3)).astype(np.float32)
+    b = rng.normal(0.0, 0.1, size=cout).astype(np.float32)
+    return round_bf16(w), b
+
+
 def make_x_host(wl: Workload, seed: int = 0) -> np.ndarray:
     """x ~ N(0, 1) as float32 [N,T,H,W,Cin] on the host (small workloads);
     rounded to bf16 values for bf16 workloads."""

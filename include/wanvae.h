@@ -153,6 +153,42 @@ WANVAE_API int wanvae_packed_conv3d_weight_elems(int32_t cin, int32_t cout, int3
                                                  int64_t *elems);
 
 /*
+ * Decoder upsampler, spatial part (upsample2d): each frame doubled in H and W
+ * by nearest neighbour, then a 3x3 conv with zero padding 1 over the frame
+ * ("Sharding of WAN 2.2 VAE": the decoder module tree ends three up blocks
+ * with an upsampler, and "Further sharding consideration: WanResample" names
+ * its conv, resample[1], with a C_out to split; the tree's channel counts make
+ * that conv halve the channels):
+ *   y[n][t][h][w][co] = bias[co] + sum_{kh,kw,ci} w[co][ci][kh][kw] *
+ *                       x[n][t][(h+kh-1)/2][(w+kw-1)/2][ci]
+ * with the terms outside the 2h x 2w image left out.  The doubled image is
+ * never stored: the conv reads each input position for the output positions
+ * it covers.  bf16 only (other dtypes: WANVAE_ERR_DTYPE); fp32 accumulation,
+ * bias added in fp32, one RNE rounding.  The temporal half of upsample3d is
+ * not described on the pages and is not provided.
+ *   x     : [n][t][h][w][cin] bf16, channels-last (d gives this extent).
+ *   w     : packed by wanvae_pack_conv2d_weights (cin x cout).
+ *   bias  : [cout] fp32 or NULL.
+ *   y     : [n][t][2h][2w][cout] bf16, channels-last; must not overlap x or w.
+ *   cin a multiple of 16 in [16, 1024]; cout in [1, 1024]; a frame of x and of
+ *   y below 2 GiB.  Asynchronous on `stream`; allocates nothing.
+ */
+WANVAE_API int wanvae_upsample2d_conv(const void *x, const void *w, const float *bias, void *y,
+                                      const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
+                                      void *stream);
+
+/* Packs a 2D 3x3 conv weight [cout][cin][3][3] (bf16) for
+ * wanvae_upsample2d_conv into [cin/16][kh][kw][cout_p][16] (cout_p = cout
+ * rounded up to 32, zero padding): the bf16 conv layout with one temporal
+ * tap.  Same rules as wanvae_pack_conv3d_weights; bf16 only. */
+WANVAE_API int wanvae_pack_conv2d_weights(const void *w, void *packed, int32_t cin, int32_t cout,
+                                          int32_t dtype, void *stream);
+
+/* Elements of a packed 2D conv weight (9*cin*cout_p).  Host only. */
+WANVAE_API int wanvae_packed_conv2d_weight_elems(int32_t cin, int32_t cout, int32_t dtype,
+                                                 int64_t *elems);
+
+/*
  * Pointwise (1x1x1) conv over `rows` positions:
  *   y[r][co] = bias[co] + sum_ci w[co][ci] * x[r][ci]
  * The decoder's post_quant_conv, a CausalConv3d of kernel size 1 over the
@@ -285,7 +321,8 @@ WANVAE_API const char *wanvae_last_error(void);
  */
 enum { WANVAE_KERNEL_NORM = 0, WANVAE_KERNEL_CONV_BF16 = 1, WANVAE_KERNEL_CONV_F32 = 2,
        WANVAE_KERNEL_ROLL = 3, WANVAE_KERNEL_POINTWISE = 4, WANVAE_KERNEL_GEMM = 5,
-       WANVAE_KERNEL_TRANSPOSE = 6, WANVAE_KERNEL_ATTENTION = 7, WANVAE_KERNEL_KINDS = 8 };
+       WANVAE_KERNEL_TRANSPOSE = 6, WANVAE_KERNEL_ATTENTION = 7, WANVAE_KERNEL_UPSAMPLE = 8,
+       WANVAE_KERNEL_KINDS = 9 };
 WANVAE_API int wanvae_timing_enable(int on);
 WANVAE_API int wanvae_timing_reset(void);
 WANVAE_API int wanvae_timing_read(int32_t kind, int64_t *launches, double *total_ms);

@@ -218,3 +218,33 @@ def test_attention_validation():
     assert L.wanvae_attention_block(C.byref(p), None, y, C.byref(d), ws, need.value, None) == wv.ERR_NULL
     empty = wv.Dims(1, 0, 8, 32)
     assert L.wanvae_attention_block(C.byref(p), None, None, C.byref(empty), None, 0, None) == wv.OK
+
+
+def test_upsample2d_validation():
+    L = wv.lib()
+    p, q = C.c_void_p(1 << 24), C.c_void_p(1 << 34)
+    d = _dims()
+    up = L.wanvae_upsample2d_conv
+    assert up(p, p, None, q, C.byref(d), 64, 32, wv.F32, None) == wv.ERR_DTYPE     # bf16 only
+    assert up(p, p, None, q, C.byref(d), 64, 32, 5, None) == wv.ERR_DTYPE
+    assert up(p, p, None, q, C.byref(d), 24, 32, wv.BF16, None) == wv.ERR_SHAPE    # cin % 16
+    assert up(p, p, None, q, C.byref(d), 64, 0, wv.BF16, None) == wv.ERR_SHAPE
+    assert up(p, p, None, q, C.byref(d), 64, 1025, wv.BF16, None) == wv.ERR_SHAPE
+    assert up(p, p, None, q, None, 64, 32, wv.BF16, None) == wv.ERR_NULL
+    assert up(None, p, None, q, C.byref(d), 64, 32, wv.BF16, None) == wv.ERR_NULL
+    assert up(p, p, None, C.c_void_p((1 << 34) + 8), C.byref(d), 64, 32, wv.BF16, None) == wv.ERR_SHAPE
+    # the output frame (2h x 2w x cout) must stay below 2 GiB
+    big = _dims(1, 1, 4096, 4096)
+    assert up(p, p, None, q, C.byref(big), 64, 32, wv.BF16, None) == wv.ERR_SHAPE
+    # y may not overlap x (x: 1*2*3*4*64*2 = 3 KB from 1 << 24)
+    assert up(p, q, None, C.c_void_p((1 << 24) + 1024), C.byref(d), 64, 32, wv.BF16, None) == wv.ERR_ALIAS
+    empty = _dims(0, 2, 3, 4)
+    assert up(None, None, None, None, C.byref(empty), 64, 32, wv.BF16, None) == wv.OK
+    n = C.c_int64(0)
+    assert L.wanvae_packed_conv2d_weight_elems(384, 192, wv.BF16, C.byref(n)) == wv.OK
+    assert n.value == 9 * 384 * 192
+    assert L.wanvae_packed_conv2d_weight_elems(192, 3, wv.BF16, C.byref(n)) == wv.OK
+    assert n.value == 9 * 192 * 32
+    assert L.wanvae_packed_conv2d_weight_elems(192, 96, wv.F32, C.byref(n)) == wv.ERR_DTYPE
+    assert L.wanvae_pack_conv2d_weights(p, C.c_void_p((1 << 24) + 4096), 64, 64, wv.BF16, None) == wv.ERR_ALIAS
+    assert L.wanvae_pack_conv2d_weights(None, q, 64, 64, wv.BF16, None) == wv.ERR_NULL

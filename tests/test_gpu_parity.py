@@ -390,3 +390,61 @@ def test_attention_block_latent_sampled(torch, wv):
     _attn_check(torch, wv, x, p, "latent [1,21,90,160,384] sampled", frames=[(0, 0), (0, 10), (0, 20)],
                 nq=24, seed=3)
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- upsampler
+def _upsample_check(torch, wv, xd, x_host, w, b, label, frames=None, rows=None):
+    """upsample2d_conv on the device input xd against the oracle on x_host
+    (the same values): the whole output, or the given output rows of the
+    given frames (x_host then holds just those frames, in that order)."""
+    wp = wv.pack_conv2d_weights(torch.from_numpy(w).to("cuda").to(torch.bfloat16))
+    y = wv.upsample2d_conv(xd, wp, torch.from_numpy(b).to("cuda"))
+    torch.cuda.synchronize()
+    if frames is None:
+        got = gu.to_host(y)
+        ref = oracle.upsample2d_conv(x_host, w, b)
+    else:
+        got, ref = [], []
+        for (r0, r1) in rows:
+            ref.append(oracle.upsample2d_conv(x_host, w, b, frames=[(0, i) for i in range(len(frames))],
+                                              rows=(r0, r1)))
+            got.append(np.stack([gu.to_host(y[n, t, r0:r1]) for (n, t) in frames]))
+        got, ref = np.concatenate(got, axis=1), np.concatenate(ref, axis=1)
+    del y
+    err = gu.rel_err(got, ref)
+    gu.report(f"upsample2d {label}", err, gu.TOL_BF16, f"pcc={gu.pcc(got, ref):.6f}")
+    assert err <= gu.TOL_BF16
+
+
+@pytest.mark.parametrize("shape,cout", [
+    ((1, 2, 5, 17, 16), 32),     # 10 x 34 out: ragged row and column tiles, one 32-channel block
+    ((1, 3, 9, 16, 64), 64),     # 18-row tiles
+    ((2, 1, 7, 20, 384), 192),   # the decoder's 384 -> 192, batch 2
+    ((1, 2, 6, 12, 192), 96),    # 96-channel (kh-outer) tiles
+    ((1, 2, 4, 9, 96), 40),      # a padded channel block
+    ((1, 1, 1, 1, 32), 3),       # one input position, 3 output channels (2-byte stores)
+])
+def test_upsample2d_small(torch, wv, shape, cout):
+    rng = np.random.default_rng(sum(shape) + cout)
+    x = wl.round_bf16(rng.standard_normal(shape).astype(np.float32))
+    w, b = wl.make_upsample_params(shape[-1], cout, seed=sum(shape))
+    _upsample_check(torch, wv, gu.to_dev(x, wl.BF16), x, w, b, f"{shape} -> {cout}")
+
+
+@pytest.mark.parametrize("shape,cout", [
+    ((1, 21, 90, 160, 384), 192),    # after the latent-resolution up block
+    ((1, 81, 360, 640, 192), 96),    # the last upsampler, to 720 x 1280 (output 14 GB)
+])
+def test_upsample2d_decoder_sampled(torch, wv, shape, cout):
+    """Decoder-size upsamplers: the first, a middle and the last frame, the
+    output rows at the top and bottom edges and in the middle."""
+    n, t, h, w_, cin = shape
+    xd = wl.make_x_device(wl.custom("up", wl.BF16, n, t, h, w_, cin, cout), seed=5)
+    frames = [(0, 0), (0, t // 2), (0, t - 1)]
+    x_host = np.stack([xd[0, tt].float().cpu().numpy() for (_, tt) in frames])[None]
+    w, b = wl.make_upsample_params(cin, cout, seed=5)
+    H2 = 2 * h
+    rows = [(0, 3), (H2 // 2 - 1, H2 // 2 + 2), (H2 - 3, H2)]
+    _upsample_check(torch, wv, xd, x_host, w, b, f"{shape} -> {cout} sampled", frames=frames, rows=rows)
+    del xd
+    torch.cuda.empty_cache()
