@@ -7,7 +7,8 @@
 // Inputs: qkv [F][HW][3D] bf16 (q, k, v of each position side by side, the
 // output of the block's 1x1x1 projection) and vt [F][D][HWp] bf16, v
 // transposed per frame (transpose_v_kernel, keys padded with zeros to HWp, a
-// multiple of 32).  Output o [F][HW][D] bf16.
+// multiple of 32; within every 16 keys the groups of 4 are stored in the
+// order 0, 2, 1, 3, see below).  Output o [F][HW][D] bf16.
 //
 // Flash-attention form, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and
 // accumulation, the scores never leave the chip.  A workgroup owns 128 queries
@@ -24,8 +25,9 @@
 //    registers as the MFMA B operand.  A lane holds the scores of one query
 //    for keys 8j + 4g + i (j, i < 4; g = lane / 32); taking j = 2ks, 2ks + 1
 //    as MFMA k-step ks, the 8 k values of lane group g are keys 16ks + 4g +
-//    {0..3, 8..11}, and the V^T operand is read in that same key order (two
-//    8-byte pieces per fragment), so no transpose of P is needed;
+//    {0..3, 8..11}, and the V^T operand is read in that same key order: vt
+//    stores the 4-key groups of every 16 keys as 0, 2, 1, 3, so that order is
+//    16 contiguous bytes (one read per fragment) and P needs no transpose;
 //  - the K and V^T blocks (2 x 24 KB at D = 384) are staged by LDS-DMA
 //    (buffer_load ... lds, 6 instructions per wave and block) into a 2-slot
 //    ring, and the partial scores into a double buffer, which lets one barrier
@@ -178,16 +180,14 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         const int c = (hf * DH / 8 + 2 * s + g) ^ (row & S::KSWZ);
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + (row * S::CPR + c) * 16));
     };
-    // V^T fragment of tile t, k-step ks: d = hf DH + 32 t + l32, keys
-    // 16 ks + 4 g + {0..3} and 16 ks + 8 + 4 g + {0..3}
+    // V^T fragment of tile t, k-step ks: d = hf DH + 32 t + l32, keys 16 ks +
+    // 4 g + {0..3} and 16 ks + 8 + 4 g + {0..3}, stored as 16 contiguous bytes
+    // (logical chunk 2 ks + g of the 64-byte row, swizzled by (d >> 2) & 3)
     auto ldV = [&](const unsigned char *slot, int t, int ks) __attribute__((always_inline)) {
         const int d = hf * DH + 32 * t + l32;
         const unsigned char *row = slot + S::K_BYTES + d * (kBK * 2);
-        const int sw = (d >> 2) & 3;
-        const int b0 = (16 * ks + 4 * g) * 2, b1 = b0 + 16;   // byte offsets within the 64-byte row
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + (((b0 >> 4) ^ sw) << 4) + (b0 & 15));
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + (((b1 >> 4) ^ sw) << 4) + (b1 & 15));
-        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        const int c = (2 * ks + g) ^ ((d >> 2) & 3);
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + c * 16));
     };
 
     floatx16 acc[DT];
@@ -235,14 +235,14 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         compiler_fence();
         if (j + 2 < nblk) issue_k(j + 2, sl);
         if (j + 1 < nblk) issue_v(j + 1, sl ^ 1);
+        // own partial + the partner's: the same sum in both waves (addition
+        // commutes), so both run the softmax on identical scores
         float sc[16];
-        const float *const h0 = sx_at(sl, 0);
-        const float *const h1 = sx_at(sl, 1);
+        const float *const other = sx_at(sl, hf ^ 1);
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
-            const float4 a = *reinterpret_cast<const float4 *>(h0 + r);
-            const float4 b = *reinterpret_cast<const float4 *>(h1 + r);
-            sc[r] = a.x + b.x; sc[r + 1] = a.y + b.y; sc[r + 2] = a.z + b.z; sc[r + 3] = a.w + b.w;
+            const float4 b = *reinterpret_cast<const float4 *>(other + r);
+            sc[r] = sp[r] + b.x; sc[r + 1] = sp[r + 1] + b.y; sc[r + 2] = sp[r + 2] + b.z; sc[r + 3] = sp[r + 3] + b.w;
         }
 
         // online softmax for this lane's query (column l32), keys 8jj + 4g + i.
@@ -283,8 +283,7 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         for (int ks = 0; ks < 2; ++ks) {
             uint32_t w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[e] = f32_to_bf16_bits(sc[8 * ks + 2 * e]) | (f32_to_bf16_bits(sc[8 * ks + 2 * e + 1]) << 16);
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(sc[8 * ks + 2 * e], sc[8 * ks + 2 * e + 1]);
             pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
         }
 #pragma unroll
@@ -307,16 +306,18 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
                 const float v0 = acc[t][4 * jj], v1 = acc[t][4 * jj + 1];
                 const float v2 = acc[t][4 * jj + 2], v3 = acc[t][4 * jj + 3];
                 u32x2 w;
-                w.x = f32_to_bf16_bits(v0 * inv) | (f32_to_bf16_bits(v1 * inv) << 16);
-                w.y = f32_to_bf16_bits(v2 * inv) | (f32_to_bf16_bits(v3 * inv) << 16);
+                w.x = pack_bf16x2(v0 * inv, v1 * inv);
+                w.y = pack_bf16x2(v2 * inv, v3 * inv);
                 *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * jj + 4 * g) = w;
             }
     }
 }
 
-// vt[f][d][k] = v of key k (qkv[f][k][2D + d]) for k < HW, 0 for HW <= k < HWp.
-// 64 keys x 64 dims per block through LDS: 16-byte reads along d, 16-byte
-// writes along k.
+// vt[f][d][s] = v of key key(s) (qkv[f][key][2D + d]) for key < HW, 0 for HW
+// <= key < HWp, where stored position s = 16 m + 4 a + b holds key 16 m +
+// 4 sigma(a) + b, sigma = (0, 2, 1, 3): the 4-key groups of every 16 keys in
+// the order the attention kernel's value product reads them.  64 keys x 64
+// dims per block through LDS: 16-byte reads along d, 16-byte writes along s.
 constexpr int kTT = 64;
 __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *__restrict__ qkv, uint16_t *__restrict__ vt,
                                                           int64_t frames, int HW, int HWp, int D) {
@@ -346,7 +347,12 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *__rest
         if (k0 + kc >= HWp) continue;
         uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[kc + 2 * e][dr] | ((uint32_t)tile[kc + 2 * e + 1][dr] << 16);
+        for (int e = 0; e < 4; ++e) {
+            // stored positions kc + 2e, kc + 2e + 1 (same 4-key group)
+            const int s = (kc & 15) + 2 * e, a = s >> 2;
+            const int key = (kc & ~15) + 4 * (((a & 1) << 1) | (a >> 1)) + (s & 3);
+            w[e] = (uint32_t)tile[key][dr] | ((uint32_t)tile[key + 1][dr] << 16);
+        }
         *reinterpret_cast<u32x4 *>(vt + (f * D + d0 + dr) * (int64_t)HWp + k0 + kc) = u32x4{w[0], w[1], w[2], w[3]};
     }
 }

@@ -15,4 +15,12 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
 }
 
+// two values rounded to nearest even and packed, lo in bits 0..15 (one
+// v_cvt_pk_bf16_f32)
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+
 }  // namespace wanvae
