@@ -619,8 +619,14 @@ int wanvae_attention_block(const wanvae_attention_params *p, const void *x, void
     g.w_ = d->w;
     g.cin = C;
     g.cout = 3 * C;
-    if (int r = timed_launch(WANVAE_KERNEL_GEMM, s, "qkv projection",
-                             [&] { return wanvae::launch_gemm_bf16(g, s); }))
+    // the projections: the dedicated GEMM kernel where its tiles fit the
+    // channel counts, else the conv kernel's GEMM mode
+    auto project = [&](const wanvae::ConvLaunch &c) {
+        if (wanvae::gemm_bf16_tiled_supported(c.cin, c.cout))
+            return wanvae::launch_gemm_bf16_tiled(c.x, c.w, c.bias, c.res, c.y, pl.P, c.cin, c.cout, s);
+        return wanvae::launch_gemm_bf16(c, s);
+    };
+    if (int r = timed_launch(WANVAE_KERNEL_GEMM, s, "qkv projection", [&] { return project(g); }))
         return r;
     if (int r = timed_launch(WANVAE_KERNEL_TRANSPOSE, s, "v transpose", [&] {
             return wanvae::launch_transpose_v(qkv, vt, pl.F, (int)pl.HW, C, s);
@@ -638,8 +644,7 @@ int wanvae_attention_block(const wanvae_attention_params *p, const void *x, void
     go.cres = C;
     go.y = y;
     go.cout = C;
-    return timed_launch(WANVAE_KERNEL_GEMM, s, "output projection",
-                        [&] { return wanvae::launch_gemm_bf16(go, s); });
+    return timed_launch(WANVAE_KERNEL_GEMM, s, "output projection", [&] { return project(go); });
 }
 
 int wanvae_timing_enable(int on) {

@@ -809,7 +809,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     }
 }
 
-// Compute units of the current device (cached per device).
+}  // namespace
+
+// Compute units of the current device (cached per device; also used by the
+// other persistent kernels).
 hipError_t device_cu_count(int *out) {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -830,6 +833,8 @@ hipError_t device_cu_count(int *out) {
     *out = n;
     return hipSuccess;
 }
+
+namespace {
 
 template <int WM, int WN, int FM, int FN, int EPI, bool SC = EPI == EPI_SHORTCUT>
 hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
