@@ -142,8 +142,10 @@ int run_norm_conv_input(const void *x, void *y, int64_t rows, int C, int64_t hw,
 int run_conv(const wanvae::ConvLaunch &c, int32_t dt, hipStream_t s) {
     if (c.n * c.t * c.h * c.w_ == 0) return WANVAE_OK;
     if (dt == WANVAE_BF16)
-        return timed_launch(WANVAE_KERNEL_CONV_BF16, s, "conv3d_bf16",
-                            [&] { return wanvae::launch_conv3d_bf16(c, s); });
+        return timed_launch(WANVAE_KERNEL_CONV_BF16, s, "conv3d_bf16", [&] {
+            return wanvae::conv3d_narrow_supported(c) ? wanvae::launch_conv3d_narrow(c, s)
+                                                      : wanvae::launch_conv3d_bf16(c, s);
+        });
     return timed_launch(WANVAE_KERNEL_CONV_F32, s, "conv3d_f32",
                         [&] { return wanvae::launch_conv3d_f32(c, s); });
 }

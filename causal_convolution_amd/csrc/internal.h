@@ -57,6 +57,11 @@ hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, 
 // multiple of 32 in the packed weight); cres (the block's shortcut input) a
 // multiple of 32.
 bool conv3d_bf16_supported(int cin, int cout);
+// The bf16 causal conv for C_out <= 3 (the taps on the MFMA M dimension, then
+// a tap sum per output): channels-last x and cache, 16 <= C_in <= 96, C_in a
+// multiple of 16; no residual or shortcut.
+bool conv3d_narrow_supported(const ConvLaunch &c);
+hipError_t launch_conv3d_narrow(const ConvLaunch &c, hipStream_t s);
 hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
 
 // Channel GEMM over positions (a pointwise projection) on the conv kernel's

@@ -102,6 +102,10 @@ CONV_SHAPES = [
     (2, 2, 9, 33, 16, 3),        # both at once, batch 2
     (1, 2, 5, 35, 32, 40),       # a partial second channel block (40 = 32 + 8)
     (1, 2, 6, 33, 48, 100),      # C_out % 8 != 0 (rows not 16-byte aligned)
+    # C_out <= 3: the taps-as-rows kernel (8 x 62 output tiles, chunks of 27 frames)
+    (1, 30, 9, 70, 32, 3),       # two frame chunks, ragged rows and columns
+    (1, 2, 17, 64, 96, 1),       # one output channel, 3 row tiles
+    (2, 3, 8, 62, 48, 2),        # two output channels, exact tiles, batch 2
 ]
 
 
