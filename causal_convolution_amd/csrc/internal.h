@@ -67,9 +67,9 @@ hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
 // Channel GEMM over positions (a pointwise projection) on the conv kernel's
 // 1x1x1 stages: ConvLaunch with gemm = true.
 hipError_t launch_gemm_bf16(const ConvLaunch &a, hipStream_t s);
-// The same product by the dedicated GEMM kernel (128 x 128 tiles, K in stages
-// of 128): y [P][N] = x [P][K] w[N][K]^T + bias (+ res), bf16 channels-last;
-// K and N multiples of 128.
+// The same product by the dedicated GEMM kernel (128 positions resident in
+// LDS, the weight streamed in 128 x 128 stages): y [P][N] = x [P][K] w[N][K]^T
+// + bias (+ res), bf16 channels-last; K in {128, 256, 384}, N a multiple of 128.
 // Compute units of the current device (cached per device).
 hipError_t device_cu_count(int *out);
 bool gemm_bf16_tiled_supported(int K, int N);
