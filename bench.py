@@ -41,12 +41,13 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
-def conv_flops(w):
-    """Algorithmic FLOPs of conv A and conv B (+ the fused 1x1x1 shortcut)."""
+def conv_flops(w, shortcut_in_conv=True):
+    """Algorithmic FLOPs of conv A and conv B (+ the 1x1x1 shortcut when conv
+    B computes it in its own K loop)."""
     P = w.positions
     fa = 2.0 * P * w.cout * 27 * w.cin
     fb = 2.0 * P * w.cout * 27 * w.cout
-    if w.cin != w.cout:
+    if w.cin != w.cout and shortcut_in_conv:
         fb += 2.0 * P * w.cout * w.cin
     return fa, fb
 
@@ -359,10 +360,12 @@ def main():
     conv_kind = wv.KERNEL_CONV_BF16 if w.dtype == wl.BF16 else wv.KERNEL_CONV_F32
     n_conv, conv_ms = wv.timing_read(conv_kind)
     n_norm, norm_ms = wv.timing_read(wv.KERNEL_NORM)
+    # a 1x1x1 shortcut the library ran as a projection GEMM ahead of conv B
+    n_sc, sc_ms = wv.timing_read(wv.KERNEL_GEMM)
     wv.timing_reset()
     print(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms", file=sys.stderr, flush=True)
 
-    fa, fb = conv_flops(w)
+    fa, fb = conv_flops(w, shortcut_in_conv=n_sc == 0)
     conv_avg_ms = conv_ms / n_conv
     # algorithmic work of the timed steps spread over their launches (one conv A
     # and one conv B per step full-T; one of each per chunk when streaming)
@@ -406,6 +409,12 @@ def main():
                  "avg_launch_ms": norm_avg_ms, "launches": n_norm},
         "cpu_baseline": None,
     }
+    if n_sc > 0:
+        sc_flop = 2.0 * w.positions * w.cout * w.cin * args.steps / n_sc
+        out["shortcut"] = {"kernel": "gemm_bf16_kernel (the 1x1x1 shortcut, ahead of conv B)", "bound": "mfma",
+                           "achieved": sc_flop / (sc_ms / n_sc * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "flop_per_launch": sc_flop, "avg_launch_ms": sc_ms / n_sc,
+                           "launches": n_sc}
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20
         src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")

@@ -220,6 +220,39 @@ int plan_block(const wanvae_resblock_params *p, const wanvae_dims *d, Plan *pl) 
     return WANVAE_OK;
 }
 
+// The 1x1x1 shortcut as a separate projection GEMM, S = w_sc x + b_sc, into
+// the conv A output region (free once norm2 has read it), added to conv B as a
+// plain residual.  Taken where the GEMM kernel's tiles fit the channel counts
+// (bf16; in_dim 128, 256 or 384, out_dim a multiple of 64): conv B's fused
+// shortcut stages read x in 64-byte pieces and cost several times their
+// FLOPs.  S is rounded to bf16 once, like the other stored intermediates.
+bool shortcut_as_gemm(const wanvae_resblock_params *p) {
+    return p->dtype == WANVAE_BF16 && p->w_sc != nullptr && wanvae::gemm_bf16_tiled_supported(p->in_dim, p->out_dim);
+}
+
+// conv B's residual: x itself (identity), S computed into `region`, or x with
+// the fused 1x1x1 stages
+int setup_residual(const wanvae_resblock_params *p, const void *x, int64_t P, void *region,
+                   wanvae::ConvLaunch *cb, hipStream_t s) {
+    if (shortcut_as_gemm(p)) {
+        if (int r = timed_launch(WANVAE_KERNEL_GEMM, s, "shortcut projection", [&] {
+                return wanvae::launch_gemm_bf16_tiled(x, p->w_sc, p->b_sc, nullptr, region, P, p->in_dim,
+                                                      p->out_dim, s);
+            }))
+            return r;
+        cb->res = region;
+        cb->cres = p->out_dim;
+        cb->wsc = nullptr;
+        cb->bsc = nullptr;
+        return WANVAE_OK;
+    }
+    cb->res = x;
+    cb->wsc = p->w_sc;
+    cb->bsc = p->b_sc;
+    cb->cres = p->in_dim;
+    return WANVAE_OK;
+}
+
 int check_block_buffers(const wanvae_resblock_params *p, const Plan &pl, const void *x,
                         const void *y, void *ws, size_t ws_bytes) {
     WV_CHECK(x && y, WANVAE_ERR_NULL, "x and y are required");
@@ -462,12 +495,10 @@ int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void
     cb.x = n2;
     cb.w = p->w_b;
     cb.bias = p->b_b;
-    cb.res = x;
-    cb.wsc = p->w_sc;
-    cb.bsc = p->b_sc;
-    cb.cres = p->in_dim;
     cb.y = y;
     cb.cin = p->out_dim;
+    // (bf16: n2 lives in the conv input region, so a's region is free for S)
+    if (int r = setup_residual(p, x, pl.P, a, &cb, s)) return r;
     return run_conv(cb, p->dtype, s);
 }
 
@@ -532,12 +563,9 @@ int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_c
     cb.cache = cache_b;
     cb.w = p->w_b;
     cb.bias = p->b_b;
-    cb.res = x_chunk;
-    cb.wsc = p->w_sc;
-    cb.bsc = p->b_sc;
-    cb.cres = p->in_dim;
     cb.y = y_chunk;
     cb.cin = p->out_dim;
+    if (int r = setup_residual(p, x_chunk, pl.P, a, &cb, s)) return r;
     if (int r = run_conv(cb, p->dtype, s)) return r;
     return timed_launch(WANVAE_KERNEL_ROLL, s, "roll_cache", [&] {
         return wanvae::launch_roll_cache(cache_b, n2, d->n, d->t, (int64_t)slab_b, s);

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;       // channel half, position half
     const int l32 = lane & 31, g = lane >> 5;
-    const int nchunks = N / kBN, kstages = K / kBK;
+    const int nchunks = (N + kBN - 1) / kBN, kstages = K / kBK;   // (the last chunk may be 64 wide)
     const int xrow = 2 * K;                        // bytes of an x row
 
     // ---- this workgroup's position tiles: XCD x (= workgroup index mod 8)
@@ -134,7 +134,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
     }
     auto issue_w = [&](int st) __attribute__((always_inline)) {
         const int nc = st / kstages, kk = (st % kstages) * kBK;
-        const i32x4 r = buffer_rsrc(w + (int64_t)nc * kBN * K + kk, (uint32_t)(kBN * K * 2 - kk * 2));
+        // channels past N (a 64-wide last chunk) fall beyond the buffer's end: zeros
+        const int rows = N - nc * kBN < kBN ? N - nc * kBN : kBN;
+        const i32x4 r = buffer_rsrc(w + (int64_t)nc * kBN * K + kk, (uint32_t)(rows * K * 2 - kk * 2));
         const uint32_t dst = w_base + (uint32_t)((st & 1) * kPart + wave * kWBlocksPerWave * 1024);
 #pragma unroll
         for (int i = 0; i < kWBlocksPerWave; ++i) lds_dma16(r, dst + i * 1024, w_off[i]);
@@ -170,7 +172,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    bv[i][jj] = *reinterpret_cast<const float4 *>(bias + n0 + wm * 64 + 32 * i + 8 * jj + 4 * g);
+                    bv[i][jj] = n0 + wm * 64 < N ? *reinterpret_cast<const float4 *>(bias + n0 + wm * 64 + 32 * i + 8 * jj + 4 * g)
+                                                 : float4{0.0f, 0.0f, 0.0f, 0.0f};
         } else {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -194,7 +197,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    off[jn][i][jj] = pl < rows ? (uint32_t)((pl * N + n0 + wm * 64 + 32 * i + 8 * jj + 4 * g) * 2) : kOOB;
+                    off[jn][i][jj] = pl < rows && n0 + wm * 64 < N
+                                         ? (uint32_t)((pl * N + n0 + wm * 64 + 32 * i + 8 * jj + 4 * g) * 2)
+                                         : kOOB;
         }
         // residual pieces all requested before the first store (a load behind
         // a store would wait for it)
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
 }  // namespace
 
 bool gemm_bf16_tiled_supported(int K, int N) {
-    return K >= kBK && K <= kKMax && K % kBK == 0 && N >= kBN && N % kBN == 0;
+    return K >= kBK && K <= kKMax && K % kBK == 0 && N >= 64 && N % 64 == 0;
 }
 
 hipError_t launch_gemm_bf16_tiled(const void *x, const void *w, const float *bias, const void *res, void *y,

@@ -69,7 +69,7 @@ hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
 hipError_t launch_gemm_bf16(const ConvLaunch &a, hipStream_t s);
 // The same product by the dedicated GEMM kernel (128 positions resident in
 // LDS, the weight streamed in 128 x 128 stages): y [P][N] = x [P][K] w[N][K]^T
-// + bias (+ res), bf16 channels-last; K in {128, 256, 384}, N a multiple of 128.
+// + bias (+ res), bf16 channels-last; K in {128, 256, 384}, N a multiple of 64.
 // Compute units of the current device (cached per device).
 hipError_t device_cu_count(int *out);
 bool gemm_bf16_tiled_supported(int K, int N);

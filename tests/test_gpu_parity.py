@@ -209,6 +209,10 @@ SMALL_BLOCKS = [
     wl.custom("sc96_288", wl.BF16, 1, 3, 13, 36, 96, 288),   # 96-channel tiles, 3 blocks, shortcut
     # a wide odd channel count (norm rows cut raggedly) with norm tiles crossing frames
     wl.custom("sc544_32", wl.BF16, 1, 3, 5, 37, 544, 32),
+    # 1x1x1 shortcuts on the projection GEMM: a 64-wide last channel chunk, a
+    # single 64-wide chunk, and ragged position tiles
+    wl.custom("sc256_320", wl.BF16, 1, 3, 7, 45, 256, 320),
+    wl.custom("sc128_64", wl.BF16, 2, 2, 9, 20, 128, 64),
 ]
 
 
