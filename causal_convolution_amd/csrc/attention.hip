@@ -54,7 +54,8 @@ constexpr int kBufFlags = 0x00020000;   // raw buffer, loads past num_records re
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kBQ = 128;                // queries per workgroup
 constexpr int kBK = 32;                 // keys per block
-constexpr int kWaves = 8;
+constexpr int kGroups = 4;              // query groups of 32 per workgroup
+constexpr int kWaves = 2 * kGroups;     // a producer and a consumer wave per group
 constexpr int kThreads = kWaves * 64;
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -83,20 +84,25 @@ __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
 template <int D>
 struct AttnShape {
-    static constexpr int DH = D / 2;                    // head dims per wave
-    static constexpr int KS = DH / 16;                  // MFMA k-steps of the score product
-    static constexpr int DT = DH / 32;                  // O^T tiles per wave
+    static constexpr int KS = D / 16;                   // MFMA k-steps of the score product
+    static constexpr int DT = D / 32;                   // O^T tiles
     static constexpr int CPR = D / 8;                   // 16-byte chunks per K row
     static constexpr int KSWZ = CPR < 16 ? CPR - 1 : 15;   // chunk swizzle mask of K rows
     static constexpr int K_BYTES = kBK * D * 2;         // one K block
     static constexpr int V_BYTES = D * kBK * 2;         // one V^T block
-    static constexpr int SLOT = K_BYTES + V_BYTES;
-    static constexpr int KB = K_BYTES / 1024;           // 1 KB LDS-DMA blocks of K
-    static constexpr int VB = V_BYTES / 1024;           // and of V^T
-    // partial scores, double-buffered: [2][qg][hf][lane][16] fp32
-    static constexpr int SX_BYTES = 2 * 4 * 2 * 64 * 16 * 4;
+    static constexpr int KB = K_BYTES / 1024;           // 1 KB LDS-DMA blocks of K (and of V^T)
+    // LDS: 2 K slots, 2 V^T slots, then per query group and buffer: P (64
+    // lanes x 32 bytes), the rescale factors (32 floats) and a flag
+    static constexpr int K_OFF = 0, V_OFF = 2 * K_BYTES;
+    static constexpr int P_OFF = V_OFF + 2 * V_BYTES;
+    static constexpr int P_BYTES = 64 * 32;
+    static constexpr int A_OFF = P_OFF + 2 * kGroups * P_BYTES;
+    static constexpr int F_OFF = A_OFF + 2 * kGroups * 32 * 4;
+    static constexpr int L_OFF = F_OFF + 2 * kGroups * 4;
+    static constexpr int LDS = L_OFF + kGroups * 32 * 4;
     static_assert(D % 64 == 0 && D <= 384, "head width a multiple of 64, at most 384");
-    static_assert(2 * SLOT + SX_BYTES <= 160 * 1024, "LDS");
+    static_assert(KB % kGroups == 0, "each producer (consumer) wave issues the same K (V^T) loads");
+    static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // max and sum of v over lanes l and l ^ 32.  v_permlane32_swap on two copies
@@ -117,199 +123,194 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
                                                                    uint16_t *__restrict__ o, int64_t frames,
                                                                    int HW, int HWp, float scale_log2) {
     using S = AttnShape<D>;
-    constexpr int DH = S::DH, KS = S::KS, DT = S::DT;
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[2 * S::SLOT];
-    __shared__ __attribute__((aligned(16))) float sx[S::SX_BYTES / 4];
+    constexpr int KS = S::KS, DT = S::DT;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[S::LDS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qg = wave >> 1, hf = wave & 1;
+    const bool producer = wave < kGroups;          // waves w and w + 4 share SIMD w
+    const int qg = wave & (kGroups - 1);
     const int l32 = lane & 31, g = lane >> 5;
     const int qblocks = (HW + kBQ - 1) / kBQ;
     const int64_t f = blockIdx.x / qblocks;
-    const int q0 = (int)(blockIdx.x % qblocks) * kBQ + qg * 32;   // this wave's first query
+    const int q0 = (int)(blockIdx.x % qblocks) * kBQ + qg * 32;   // this group's first query
     const int row3 = 3 * D;                                        // qkv row stride (elements)
     const uint16_t *qkv_f = qkv + f * (int64_t)HW * row3;
     const uint16_t *vt_f = vt + f * (int64_t)D * HWp;
     const int nblk = (HW + kBK - 1) / kBK;
+    const uint32_t lds_base = lds_address(lds);
 
-    // ---- q fragments of this wave's queries and head half, in registers
-    bf16x8 qf[KS];
-    {
-        const int q = q0 + l32;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u32x4 d = u32x4{0u, 0u, 0u, 0u};
-            if (q < HW)
-                d = *reinterpret_cast<const u32x4 *>(qkv_f + (int64_t)q * row3 + hf * DH + 16 * s + 8 * g);
-            qf[s] = __builtin_bit_cast(bf16x8, d);
-        }
-    }
-
-    // ---- LDS-DMA of key block j into ring slot sl, K and V^T parts apart;
-    // wave w takes the 1 KB blocks w, w + 8, ...  Piece P (16 bytes) of the K
-    // part is K row P / CPR, stored chunk P % CPR = global chunk ^ (row &
-    // KSWZ); piece P of the V^T part is V^T row d = P / 4 (64 bytes, 4
-    // chunks), stored chunk = global chunk ^ ((d >> 2) & 3).
-    const uint32_t ring_base = lds_address(ring);
+    // ---- LDS-DMA.  Producers move K blocks, consumers V^T blocks: each wave
+    // the 1 KB blocks qg, qg + 4, ...  Piece P (16 bytes) of a K block is K row
+    // P / CPR, stored chunk P % CPR = global chunk ^ (row & KSWZ); piece P of a
+    // V^T block is V^T row d = P / 4 (64 bytes, 4 chunks), stored chunk =
+    // global chunk ^ ((d >> 2) & 3).
     const i32x4 rk = buffer_rsrc(qkv_f + D, (uint32_t)((int64_t)HW * row3 * 2 - D * 2));
     const i32x4 rv = buffer_rsrc(vt_f, (uint32_t)((int64_t)D * HWp * 2));
-    auto issue_k = [&](int j, int sl) __attribute__((always_inline)) {
-        for (int b = wave; b < S::KB; b += kWaves) {
+    auto issue_k = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = qg; b < S::KB; b += kGroups) {
             const int P = b * 64 + lane;
             const int row = P / S::CPR, cs = P % S::CPR;
             const int c = cs ^ (row & S::KSWZ);
             const int key = j * kBK + row;
             const uint32_t off = key < HW ? (uint32_t)key * (uint32_t)(row3 * 2) + (uint32_t)c * 16 : kOOB;
-            lds_dma16(rk, ring_base + (uint32_t)(sl * S::SLOT + b * 1024), off);
+            lds_dma16(rk, lds_base + (uint32_t)(S::K_OFF + (j & 1) * S::K_BYTES + b * 1024), off);
         }
     };
-    auto issue_v = [&](int j, int sl) __attribute__((always_inline)) {
-        for (int b = wave; b < S::VB; b += kWaves) {
+    auto issue_v = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = qg; b < S::KB; b += kGroups) {
             const int P = b * 64 + lane;
             const int d = P >> 2, cs = P & 3;
             const int c = cs ^ ((d >> 2) & 3);
             const uint32_t off = (uint32_t)d * (uint32_t)(HWp * 2) + (uint32_t)(j * kBK * 2) + (uint32_t)c * 16;
-            lds_dma16(rv, ring_base + (uint32_t)(sl * S::SLOT + S::K_BYTES + b * 1024), off);
+            lds_dma16(rv, lds_base + (uint32_t)(S::V_OFF + (j & 1) * S::V_BYTES + b * 1024), off);
         }
     };
-
-    // fragment reads
-    auto ldK = [&](const unsigned char *slot, int s) __attribute__((always_inline)) {
-        const int row = l32;                              // key of this lane
-        const int c = (hf * DH / 8 + 2 * s + g) ^ (row & S::KSWZ);
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + (row * S::CPR + c) * 16));
-    };
-    // V^T fragment of tile t, k-step ks: d = hf DH + 32 t + l32, keys 16 ks +
-    // 4 g + {0..3} and 16 ks + 8 + 4 g + {0..3}, stored as 16 contiguous bytes
-    // (logical chunk 2 ks + g of the 64-byte row, swizzled by (d >> 2) & 3)
-    auto ldV = [&](const unsigned char *slot, int t, int ks) __attribute__((always_inline)) {
-        const int d = hf * DH + 32 * t + l32;
-        const unsigned char *row = slot + S::K_BYTES + d * (kBK * 2);
-        const int c = (2 * ks + g) ^ ((d >> 2) & 3);
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + c * 16));
-    };
-
-    floatx16 acc[DT];
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    // this lane's partial scores of buffer sb, and the two halves of its pair
-    auto sx_at = [&](int sb, int half) __attribute__((always_inline)) {
-        return sx + (((sb * 4 + qg) * 2 + half) * 64 + lane) * 16;
-    };
-
-    // One barrier per key block.  Block j: scores from K_j, partials
-    // published, own loads of K_{j+1} and V_j waited for, barrier; then K_{j+2}
-    // goes into K_j's place and V_{j+1} into V_{j-1}'s (both free: every wave
-    // has passed the barrier after its last read of them), and the softmax and
-    // the value product of block j run on data every wave saw land.
-    issue_k(0, 0);
-    issue_v(0, 0);
-    if (nblk > 1) issue_k(1, 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    compiler_fence();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-
-    for (int j = 0; j < nblk; ++j) {
-        const int sl = j & 1;
-        const unsigned char *slot = ring + sl * S::SLOT;
-
-        // partial scores over this wave's head half
-        floatx16 sp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sp[r] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ldK(slot, s), qf[s], sp, 0, 0, 0);
-        float *const mine = sx_at(sl, hf);
-#pragma unroll
-        for (int r = 0; r < 16; r += 4)
-            *reinterpret_cast<float4 *>(mine + r) = float4{sp[r], sp[r + 1], sp[r + 2], sp[r + 3]};
+    // every wave: its loads landed, its LDS accesses done; then the barrier
+    auto sync = [&]() __attribute__((always_inline)) {
         compiler_fence();
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & waitcnt_lgkm0());
         __builtin_amdgcn_s_barrier();
         compiler_fence();
-        if (j + 2 < nblk) issue_k(j + 2, sl);
-        if (j + 1 < nblk) issue_v(j + 1, sl ^ 1);
-        // own partial + the partner's: the same sum in both waves (addition
-        // commutes), so both run the softmax on identical scores
-        float sc[16];
-        const float *const other = sx_at(sl, hf ^ 1);
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-            const float4 b = *reinterpret_cast<const float4 *>(other + r);
-            sc[r] = sp[r] + b.x; sc[r + 1] = sp[r + 1] + b.y; sc[r + 2] = sp[r + 2] + b.z; sc[r + 3] = sp[r + 3] + b.w;
-        }
+    };
+    unsigned char *p_buf = lds + S::P_OFF + qg * S::P_BYTES;        // + (j & 1) * kGroups * P_BYTES
+    float *a_buf = reinterpret_cast<float *>(lds + S::A_OFF) + qg * 32;   // + (j & 1) * kGroups * 32
+    int *f_buf = reinterpret_cast<int *>(lds + S::F_OFF) + qg;             // + (j & 1) * kGroups
+    float *l_buf = reinterpret_cast<float *>(lds + S::L_OFF) + qg * 32;
 
-        // online softmax for this lane's query (column l32), keys 8jj + 4g + i.
-        // The maximum is taken over the raw scores (the scale is positive),
-        // and only the last block can hold keys past HW.
-        if (j * kBK + kBK > HW) {
+    // Phase p (0 .. nblk, one barrier each): the producer of a query group
+    // computes the scores of key block p and their softmax and publishes P_p
+    // (and, when some query's maximum grew, the factors that rescale O); the
+    // consumer adds V_{p-1} P_{p-1} to O.  Loads: K_{p+1} and V^T_p, into the
+    // slots of K_{p-1} and V^T_{p-2}, which the last barrier freed.
+    if (producer) {
+        // ---- producer: q of its 32 queries over the whole head, in registers
+        bf16x8 qf[KS];
+        {
+            const int q = q0 + l32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (j * kBK + 8 * (r >> 2) + 4 * g + (r & 3) >= HW) sc[r] = -INFINITY;
+            for (int s = 0; s < KS; ++s) {
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (q < HW) v = *reinterpret_cast<const u32x4 *>(qkv_f + (int64_t)q * row3 + 16 * s + 8 * g);
+                qf[s] = __builtin_bit_cast(bf16x8, v);
+            }
         }
-        float mx = sc[0];
+        float m_run = -INFINITY, l_run = 0.0f;
+        issue_k(0);
+        sync();
+        for (int p = 0; p <= nblk; ++p) {
+            if (p + 1 < nblk) issue_k(p + 1);
+            if (p < nblk) {
+                const unsigned char *ks = lds + S::K_OFF + (p & 1) * S::K_BYTES;
+                // scores S^T = K q^T: keys as the MFMA rows, this lane's query l32
+                floatx16 sc;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-        mx = halves_max(mx) * scale_log2;
-        // Rescale only when some query's maximum grew: otherwise the factor
-        // is exp2(0) = 1 for every lane, and skipping it changes no bit.
-        if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
+                for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int c = (2 * s + g) ^ (l32 & S::KSWZ);
+                    const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(ks + (l32 * S::CPR + c) * 16));
+                    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc, 0, 0, 0);
+                }
+                // online softmax for the lane's query, keys 8jj + 4g + i; only the
+                // last block can hold keys past HW
+                if (p * kBK + kBK > HW) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (p * kBK + 8 * (r >> 2) + 4 * g + (r & 3) >= HW) sc[r] = -INFINITY;
+                }
+                float mx = sc[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+                mx = halves_max(mx) * scale_log2;
+                // O is rescaled only when some query's maximum grew: otherwise the
+                // factor is exp2(0) = 1 for every lane and skipping it changes no bit
+                const bool grow = __builtin_amdgcn_ballot_w64(mx > m_run) != 0;
+                if (grow) {
+                    const float m_new = fmaxf(m_run, mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= alpha;
+                    m_run = m_new;
+                    if (g == 0) a_buf[(p & 1) * kGroups * 32 + l32] = alpha;
+                }
+                if (lane == 0) f_buf[(p & 1) * kGroups] = grow ? 1 : 0;
+                // P in the consumer's B-operand layout: the lane's keys 16 ks + 4 g +
+                // {0..3, 8..11} are k-step ks; l_run: the lane's share
+                uint32_t w[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * e], scale_log2, -m_run));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * e + 1], scale_log2, -m_run));
+                    l_run += p0 + p1;
+                    w[e] = pack_bf16x2(p0, p1);
+                }
+                u32x4 *pp = reinterpret_cast<u32x4 *>(p_buf + (p & 1) * kGroups * S::P_BYTES + lane * 32);
+                pp[0] = u32x4{w[0], w[1], w[2], w[3]};
+                pp[1] = u32x4{w[4], w[5], w[6], w[7]};
+            }
+            sync();
+        }
+        // the row sums, for the consumer's normalisation
+        l_run = halves_sum(l_run);
+        if (g == 0) l_buf[l32] = l_run;
+        sync();
+    } else {
+        // ---- consumer: O^T (the whole head) for the group's 32 queries
+        floatx16 acc[DT];
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+        sync();
+        for (int p = 0; p <= nblk; ++p) {
+            if (p < nblk) issue_v(p);
+            if (p >= 1) {
+                const int j = p - 1;
+                if (f_buf[(j & 1) * kGroups] != 0) {
+                    const float alpha = a_buf[(j & 1) * kGroups * 32 + l32];
+#pragma unroll
+                    for (int t = 0; t < DT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+                }
+                const u32x4 *pp = reinterpret_cast<const u32x4 *>(p_buf + (j & 1) * kGroups * S::P_BYTES + lane * 32);
+                const bf16x8 pf0 = __builtin_bit_cast(bf16x8, pp[0]);
+                const bf16x8 pf1 = __builtin_bit_cast(bf16x8, pp[1]);
+                // O^T += V^T P^T; V^T fragment of tile t, k-step ks: d = 32 t + l32,
+                // keys 16 ks + 4 g + {0..3, 8..11}: 16 contiguous bytes, logical
+                // chunk 2 ks + g of the 64-byte row, swizzled by (d >> 2) & 3
+                const unsigned char *vs = lds + S::V_OFF + (j & 1) * S::V_BYTES;
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const int d = 32 * t + l32;
+                    const unsigned char *row = vs + d * (kBK * 2);
+                    const int sw = (d >> 2) & 3;
+                    const bf16x8 v0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + ((0 + g) ^ sw) * 16));
+                    const bf16x8 v1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + ((2 + g) ^ sw) * 16));
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pf0, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pf1, acc[t], 0, 0, 0);
+                }
+            }
+            sync();
+        }
+        sync();   // the producer's row sums
+        // ---- o = O / l for this lane's query: d = 32 t + 8 jj + 4 g + i
+        const int q = q0 + l32;
+        if (q < HW) {
+            const float inv = 1.0f / l_buf[l32];
+            uint16_t *orow = o + (f * (int64_t)HW + q) * D;
 #pragma unroll
             for (int t = 0; t < DT; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-            m_run = m_new;
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float v0 = acc[t][4 * jj], v1 = acc[t][4 * jj + 1];
+                    const float v2 = acc[t][4 * jj + 2], v3 = acc[t][4 * jj + 3];
+                    *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * jj + 4 * g) =
+                        u32x2{pack_bf16x2(v0 * inv, v1 * inv), pack_bf16x2(v2 * inv, v3 * inv)};
+                }
         }
-        // l_run: this lane's share (its 16 keys of every block); the two
-        // halves of the wave are added at the end
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            sc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], scale_log2, -m_run));
-            l_run += sc[r];
-        }
-
-        // O^T += V^T P^T over this wave's head half
-        bf16x8 pf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(sc[8 * ks + 2 * e], sc[8 * ks + 2 * e + 1]);
-            pf[ks] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ldV(slot, t, ks), pf[ks], acc[t], 0, 0, 0);
-    }
-
-    // ---- o = O / l for this lane's query: d = hf DH + 32 t + 8 jj + 4 g + i
-    const int q = q0 + l32;
-    l_run = halves_sum(l_run);
-    if (q < HW) {
-        const float inv = 1.0f / l_run;
-        uint16_t *orow = o + (f * (int64_t)HW + q) * D + hf * DH;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float v0 = acc[t][4 * jj], v1 = acc[t][4 * jj + 1];
-                const float v2 = acc[t][4 * jj + 2], v3 = acc[t][4 * jj + 3];
-                u32x2 w;
-                w.x = pack_bf16x2(v0 * inv, v1 * inv);
-                w.y = pack_bf16x2(v2 * inv, v3 * inv);
-                *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * jj + 4 * g) = w;
-            }
     }
 }
 
