@@ -12,27 +12,28 @@
 //
 // Flash-attention form, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and
 // accumulation, the scores never leave the chip.  A workgroup owns 128 queries
-// of one frame and walks the frame's keys in blocks of 32; its 8 waves are 4
-// query groups of 32 x 2 halves of the head width:
-//  - wave (qg, hf) keeps q of its 32 queries, dims [hf D/2, (hf+1) D/2), in
-//    registers (D/32 fragments) and the matching half of O^T;
-//  - per key block it computes the partial scores S^T = K q^T over its half
-//    (keys as the MFMA M rows, queries as N columns), the two halves add
-//    their partials through LDS (half 0 + half 1, in that order, in both
-//    waves, so both hold identical scores), and both run the same online
-//    softmax: row maximum, exp2, running sum, rescale of O;
-//  - then O^T += V^T P^T over its half: P is used straight from the score
-//    registers as the MFMA B operand.  A lane holds the scores of one query
-//    for keys 8j + 4g + i (j, i < 4; g = lane / 32); taking j = 2ks, 2ks + 1
-//    as MFMA k-step ks, the 8 k values of lane group g are keys 16ks + 4g +
-//    {0..3, 8..11}, and the V^T operand is read in that same key order: vt
-//    stores the 4-key groups of every 16 keys as 0, 2, 1, 3, so that order is
-//    16 contiguous bytes (one read per fragment) and P needs no transpose;
-//  - the K and V^T blocks (2 x 24 KB at D = 384) are staged by LDS-DMA
-//    (buffer_load ... lds, 6 instructions per wave and block) into a 2-slot
-//    ring, and the partial scores into a double buffer, which lets one barrier
-//    per key block serve both: K of block j + 2 and V^T of block j + 1 are
-//    requested right after block j's barrier, a full block ahead of use.
+// of one frame and walks the frame's keys in blocks of 32.  Its 8 waves are 4
+// query groups of 32, each a producer and a consumer wave on the same SIMD
+// (waves qg and qg + 4):
+//  - the producer keeps q of its 32 queries over the whole head in registers
+//    and, per key block, computes the scores S^T = K q^T (keys as the MFMA M
+//    rows, queries as N columns) and the online softmax: row maximum (the two
+//    32-lane halves exchange theirs with v_permlane32_swap), exp2, running
+//    sum.  It publishes P in LDS, in the consumer's B-operand layout, and,
+//    when some query's maximum grew, the factors that rescale O;
+//  - the consumer keeps O^T for the whole head (D/32 tiles of 32 x 32) and, one
+//    key block behind, rescales it if told to and adds V^T P^T.  A producer
+//    lane holds the scores of one query for keys 8j + 4g + i (j, i < 4; g =
+//    lane / 32); taking j = 2ks, 2ks + 1 as MFMA k-step ks, the 8 k values of
+//    lane group g are keys 16ks + 4g + {0..3, 8..11}: the consumer lane reads
+//    its P straight from its twin's slot, and the V^T operand is read in that
+//    same key order: vt stores the 4-key groups of every 16 keys as 0, 2, 1,
+//    3, so that order is 16 contiguous bytes (one read per fragment);
+//  - so the two waves of a SIMD overlap: the producer's softmax (VALU) runs
+//    beside the consumer's MFMAs.  One barrier per key block; the K and V^T
+//    blocks (2 x 24 KB at D = 384) are staged by LDS-DMA (buffer_load ...
+//    lds) into 2-slot rings a block ahead of use, the loads issued by the
+//    consumers.
 // LDS: K rows are swizzled in 16-byte chunks (chunk ^ (key & 15)) and V^T rows
 // (64 bytes) by (d >> 2) & 3, so fragment reads spread over the banks.
 // Scores of keys past HW are -inf; queries past HW compute on zero q and are
@@ -140,33 +141,38 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
     const int nblk = (HW + kBK - 1) / kBK;
     const uint32_t lds_base = lds_address(lds);
 
-    // ---- LDS-DMA.  Producers move K blocks, consumers V^T blocks: each wave
-    // the 1 KB blocks qg, qg + 4, ...  Piece P (16 bytes) of a K block is K row
-    // P / CPR, stored chunk P % CPR = global chunk ^ (row & KSWZ); piece P of a
-    // V^T block is V^T row d = P / 4 (64 bytes, 4 chunks), stored chunk =
-    // global chunk ^ ((d >> 2) & 3).
-    const i32x4 rk = buffer_rsrc(qkv_f + D, (uint32_t)((int64_t)HW * row3 * 2 - D * 2));
-    const i32x4 rv = buffer_rsrc(vt_f, (uint32_t)((int64_t)D * HWp * 2));
-    auto issue_k = [&](int j) __attribute__((always_inline)) {
+    // ---- LDS-DMA, issued by the consumers (the producers carry the softmax,
+    // the longer chain): consumer qg moves the 1 KB blocks qg, qg + 4, ... of
+    // each K and V^T block.  Piece P (16 bytes) of a K block is K row P / CPR,
+    // stored chunk P % CPR = global chunk ^ (row & KSWZ); piece P of a V^T
+    // block is V^T row d = P / 4 (64 bytes, 4 chunks), stored chunk = global
+    // chunk ^ ((d >> 2) & 3).
+    // lane offsets within a block do not depend on the block: block j moves
+    // the buffers' bases (scalar), and keys past HW fall beyond the K
+    // buffer's end (zeros)
+    constexpr int NDMA = S::KB / kGroups;
+    uint32_t koff[NDMA], voff[NDMA];
 #pragma unroll
-        for (int b = qg; b < S::KB; b += kGroups) {
-            const int P = b * 64 + lane;
-            const int row = P / S::CPR, cs = P % S::CPR;
-            const int c = cs ^ (row & S::KSWZ);
-            const int key = j * kBK + row;
-            const uint32_t off = key < HW ? (uint32_t)key * (uint32_t)(row3 * 2) + (uint32_t)c * 16 : kOOB;
-            lds_dma16(rk, lds_base + (uint32_t)(S::K_OFF + (j & 1) * S::K_BYTES + b * 1024), off);
-        }
+    for (int i = 0; i < NDMA; ++i) {
+        const int b = qg + i * kGroups;
+        const int P = b * 64 + lane;
+        const int row = P / S::CPR, cs = P % S::CPR;
+        koff[i] = (uint32_t)row * (uint32_t)(row3 * 2) + (uint32_t)((cs ^ (row & S::KSWZ)) * 16);
+        const int d = P >> 2, c4 = P & 3;
+        voff[i] = (uint32_t)d * (uint32_t)(HWp * 2) + (uint32_t)((c4 ^ ((d >> 2) & 3)) * 16);
+    }
+    auto issue_k = [&](int j) __attribute__((always_inline)) {
+        const int64_t k0 = (int64_t)j * kBK;
+        const i32x4 r = buffer_rsrc(qkv_f + k0 * row3 + D, (uint32_t)((HW - k0) * row3 * 2 - D * 2));
+        const uint32_t dst = lds_base + (uint32_t)(S::K_OFF + (j & 1) * S::K_BYTES + qg * 1024);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) lds_dma16(r, dst + (uint32_t)(i * kGroups * 1024), koff[i]);
     };
     auto issue_v = [&](int j) __attribute__((always_inline)) {
+        const i32x4 r = buffer_rsrc(vt_f + j * kBK, (uint32_t)((int64_t)D * HWp * 2 - j * kBK * 2));
+        const uint32_t dst = lds_base + (uint32_t)(S::V_OFF + (j & 1) * S::V_BYTES + qg * 1024);
 #pragma unroll
-        for (int b = qg; b < S::KB; b += kGroups) {
-            const int P = b * 64 + lane;
-            const int d = P >> 2, cs = P & 3;
-            const int c = cs ^ ((d >> 2) & 3);
-            const uint32_t off = (uint32_t)d * (uint32_t)(HWp * 2) + (uint32_t)(j * kBK * 2) + (uint32_t)c * 16;
-            lds_dma16(rv, lds_base + (uint32_t)(S::V_OFF + (j & 1) * S::V_BYTES + b * 1024), off);
-        }
+        for (int i = 0; i < NDMA; ++i) lds_dma16(r, dst + (uint32_t)(i * kGroups * 1024), voff[i]);
     };
     // every wave: its loads landed, its LDS accesses done; then the barrier
     auto sync = [&]() __attribute__((always_inline)) {
@@ -198,10 +204,8 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
             }
         }
         float m_run = -INFINITY, l_run = 0.0f;
-        issue_k(0);
         sync();
         for (int p = 0; p <= nblk; ++p) {
-            if (p + 1 < nblk) issue_k(p + 1);
             if (p < nblk) {
                 const unsigned char *ks = lds + S::K_OFF + (p & 1) * S::K_BYTES;
                 // scores S^T = K q^T: keys as the MFMA rows, this lane's query l32
@@ -263,8 +267,10 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+        issue_k(0);
         sync();
         for (int p = 0; p <= nblk; ++p) {
+            if (p + 1 < nblk) issue_k(p + 1);
             if (p < nblk) issue_v(p);
             if (p >= 1) {
                 const int j = p - 1;
