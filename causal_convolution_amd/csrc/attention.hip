@@ -5,10 +5,11 @@
 // One head of width D = C.
 //
 // Inputs: qkv [F][HW][3D] bf16 (q, k, v of each position side by side, the
-// output of the block's 1x1x1 projection) and vt [F][D][HWp] bf16, v
-// transposed per frame (transpose_v_kernel, keys padded with zeros to HWp, a
-// multiple of 32; within every 16 keys the groups of 4 are stored in the
-// order 0, 2, 1, 3, see below).  Output o [F][HW][D] bf16.
+// output of the block's 1x1x1 projection) and vt [F][HWp/32][D][32] bf16, v
+// transposed per frame and block of 32 keys (transpose_v_kernel, keys padded
+// with zeros to HWp; within every 16 keys the groups of 4 are stored in the
+// order 0, 2, 1, 3, see below), so each key block's V^T is one contiguous
+// run.  Output o [F][HW][D] bf16.
 //
 // Flash-attention form, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 softmax and
 // accumulation, the scores never leave the chip.  A workgroup owns 128 queries
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
     const int q0 = (int)(blockIdx.x % qblocks) * kBQ + qg * 32;   // this group's first query
     const int row3 = 3 * D;                                        // qkv row stride (elements)
     const uint16_t *qkv_f = qkv + f * (int64_t)HW * row3;
-    const uint16_t *vt_f = vt + f * (int64_t)D * HWp;
+    const uint16_t *vt_f = vt + f * (int64_t)D * HWp;   // this frame's key blocks, D * 32 each
     const int nblk = (HW + kBK - 1) / kBK;
     const uint32_t lds_base = lds_address(lds);
 
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         const int row = P / S::CPR, cs = P % S::CPR;
         koff[i] = (uint32_t)row * (uint32_t)(row3 * 2) + (uint32_t)((cs ^ (row & S::KSWZ)) * 16);
         const int d = P >> 2, c4 = P & 3;
-        voff[i] = (uint32_t)d * (uint32_t)(HWp * 2) + (uint32_t)((c4 ^ ((d >> 2) & 3)) * 16);
+        voff[i] = (uint32_t)d * (uint32_t)(kBK * 2) + (uint32_t)((c4 ^ ((d >> 2) & 3)) * 16);
     }
     auto issue_k = [&](int j) __attribute__((always_inline)) {
         const int64_t k0 = (int64_t)j * kBK;
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         for (int i = 0; i < NDMA; ++i) lds_dma16(r, dst + (uint32_t)(i * kGroups * 1024), koff[i]);
     };
     auto issue_v = [&](int j) __attribute__((always_inline)) {
-        const i32x4 r = buffer_rsrc(vt_f + j * kBK, (uint32_t)((int64_t)D * HWp * 2 - j * kBK * 2));
+        const i32x4 r = buffer_rsrc(vt_f + (int64_t)j * D * kBK, (uint32_t)(D * kBK * 2));
         const uint32_t dst = lds_base + (uint32_t)(S::V_OFF + (j & 1) * S::V_BYTES + qg * 1024);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) lds_dma16(r, dst + (uint32_t)(i * kGroups * 1024), voff[i]);
@@ -320,11 +321,12 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
     }
 }
 
-// vt[f][d][s] = v of key key(s) (qkv[f][key][2D + d]) for key < HW, 0 for HW
-// <= key < HWp, where stored position s = 16 m + 4 a + b holds key 16 m +
-// 4 sigma(a) + b, sigma = (0, 2, 1, 3): the 4-key groups of every 16 keys in
-// the order the attention kernel's value product reads them.  64 keys x 64
-// dims per block through LDS: 16-byte reads along d, 16-byte writes along s.
+// vt[f][s / 32][d][s % 32] = v of key key(s) (qkv[f][key][2D + d]) for key <
+// HW, 0 for HW <= key < HWp, where stored position s = 16 m + 4 a + b holds
+// key 16 m + 4 sigma(a) + b, sigma = (0, 2, 1, 3): the 4-key groups of every
+// 16 keys in the order the attention kernel's value product reads them, each
+// block of 32 keys one contiguous [D][32] run.  64 keys x 64 dims per
+// workgroup through LDS: 16-byte reads along d, 16-byte writes along s.
 constexpr int kTT = 64;
 __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *__restrict__ qkv, uint16_t *__restrict__ vt,
                                                           int64_t frames, int HW, int HWp, int D) {
@@ -360,7 +362,10 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t *__rest
             const int key = (kc & ~15) + 4 * (((a & 1) << 1) | (a >> 1)) + (s & 3);
             w[e] = (uint32_t)tile[key][dr] | ((uint32_t)tile[key + 1][dr] << 16);
         }
-        *reinterpret_cast<u32x4 *>(vt + (f * D + d0 + dr) * (int64_t)HWp + k0 + kc) = u32x4{w[0], w[1], w[2], w[3]};
+        // block (k0 + kc) / 32 of the frame, row d, positions (k0 + kc) % 32 ..
+        const int64_t kblk = (k0 + kc) / kBK;
+        *reinterpret_cast<u32x4 *>(vt + ((f * (HWp / kBK) + kblk) * D + d0 + dr) * (int64_t)kBK + (k0 + kc) % kBK) =
+            u32x4{w[0], w[1], w[2], w[3]};
     }
 }
 
