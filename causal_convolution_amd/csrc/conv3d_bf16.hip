@@ -79,8 +79,11 @@
 // position, which the LDS-DMA moves at twice the rate of 32-byte ones.
 //
 // Tile order: batch slowest, then row block, column block, frame, and
-// output-channel block fastest.  Each of the 8 XCDs (workgroup index mod 8)
-// owns a contiguous range of tiles, so the workgroups on one XCD work on
+// output-channel block fastest.  Without a cache the tiles of frames 0 and 1
+// (a third and two thirds of the stages) form one work item, every other tile
+// is an item of its own, so all items carry the same work and the persistent
+// workgroups finish together.  Each of the 8 XCDs (workgroup index mod 8)
+// owns a contiguous range of items, so the workgroups on one XCD work on
 // neighbouring frames of one spatial block, all channel blocks of each side
 // by side: every input frame (and the residual / shortcut input) of the block
 // comes from HBM once and is then shared through the XCD's L2 by the tiles of
@@ -142,7 +145,12 @@ struct Args {
     int cin, cout, cres;
     int cout_p;             // cout rounded up to 32: the packed weight's channel count
     int tiles_w, tiles_h;
-    int64_t tiles;          // total tiles of the launch
+    // work items of the launch: one output tile each, or with pair = 1 (no
+    // cache: frames 0 and 1 skip the stages of the causal pad) the tiles of
+    // frames 0 and 1 of one block together, so every item runs three frames'
+    // worth of stages
+    int64_t items;
+    int pair;
     int x_sliced;           // x and cache frames are [cin/16][h][w][16], not [h][w][cin]
     // 1x1x1 stages (SC kernels): input [n][t][h][w][sc_c] at the output
     // positions and weight wsc [cout][sc_c]: the block's shortcut (sc_in =
@@ -159,11 +167,13 @@ struct Args {
 };
 
 // One output tile: batch item, frame, first row / column / output channel,
-// and its K stages (conv stages from temporal tap kt_begin, then shortcut).
+// and its K stages (conv stages from temporal tap kt_begin, then shortcut);
+// ntiles: the tiles of its work item.
 struct TileInfo {
     int64_t nq, tq;
     int h0, w0, n0;
     int kt_begin, s_conv, s_total;
+    int ntiles;
 };
 
 template <int WM, int WN, int FM, int FN>
@@ -282,25 +292,32 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     auto flag_read = [&](int i) { return __builtin_amdgcn_readfirstlane(__atomic_load_n(&sync[i], __ATOMIC_RELAXED)); };
     auto flag_write = [&](int i, int v) { __atomic_store_n(&sync[i], v, __ATOMIC_RELAXED); };
 
-    // ---- this workgroup's tiles.  XCD x (= workgroup index mod 8) holds wg_x
-    // of the grid's workgroups and owns a contiguous tile range of matching
-    // share, [x_begin, x_begin + x_count); its workgroups take the tiles of
-    // that range round-robin.  (With at least as many tiles as workgroups,
-    // every workgroup gets one or more.)
+    // ---- this workgroup's work items.  XCD x (= workgroup index mod 8) holds
+    // wg_x of the grid's workgroups and owns a contiguous item range of
+    // matching share, [x_begin, x_begin + x_count); its workgroups take the
+    // items of that range round-robin.  (With at least as many items as
+    // workgroups, every workgroup gets one or more.)  Items carry equal work
+    // (pairing frames 0 and 1 when their pad stages are skipped): with a tile
+    // per item, the workgroups that drew no frame-0/1 tiles would run up to
+    // a tenth longer than the mean at the latent resolution.
     const int64_t nwg = gridDim.x, bid = blockIdx.x;
     const int64_t xcd = bid % kXCD, loc = bid / kXCD;
     const int64_t wg_x = nwg / kXCD + (xcd < nwg % kXCD ? 1 : 0);
     const int64_t wg_before = xcd * (nwg / kXCD) + (xcd < nwg % kXCD ? xcd : nwg % kXCD);
-    const int64_t x_begin = a.tiles * wg_before / nwg;
-    const int64_t x_count = a.tiles * (wg_before + wg_x) / nwg - x_begin;
+    const int64_t x_begin = a.items * wg_before / nwg;
+    const int64_t x_count = a.items * (wg_before + wg_x) / nwg - x_begin;
 
     const int ncb = a.cout_p / NB;   // output-channel blocks (the last may be partly padding)
-    auto decode = [&](int64_t tile) __attribute__((always_inline)) {
+    const int64_t ngroups = a.T - a.pair;   // frame groups: {0, 1}, 2, 3, ... when paired
+    // tile `sub` of work item `tile`
+    auto decode = [&](int64_t tile, int sub) __attribute__((always_inline)) {
         TileInfo ti;
         ti.n0 = (int)(tile % ncb) * NB;
         tile /= ncb;
-        ti.tq = tile % a.T;
-        tile /= a.T;
+        const int64_t grp = tile % ngroups;
+        tile /= ngroups;
+        ti.ntiles = a.pair && grp == 0 ? 2 : 1;
+        ti.tq = a.pair ? (grp == 0 ? sub : grp + 1) : grp;
         ti.w0 = (int)(tile % a.tiles_w) * kWB;
         tile /= a.tiles_w;
         ti.h0 = (int)(tile % a.tiles_h) * HB;
@@ -381,13 +398,14 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             return (uint32_t)((ti.n0 + nl) * a.sc_c * 2) + j * kUnit + hf * 16;
         };
 
-        // request cursor: stage si of local tile it (tile x_begin + it), ring slot
+        // request cursor: stage si of tile sub of local item it (item
+        // x_begin + it), ring slot
         TileInfo ti{};
         int64_t it = loc;
-        int si = 0, slot = 0;
+        int si = 0, sub = 0, slot = 0;
         uint32_t l_off[TL::BLOCKS];   // conv-stage offsets of the cursor's tile
         auto start_tile = [&]() __attribute__((always_inline)) {
-            ti = decode(x_begin + it);
+            ti = decode(x_begin + it, sub);
 #pragma unroll
             for (int b = 0; b < TL::BLOCKS; ++b) l_off[b] = block_off(ti, b);
         };
@@ -450,7 +468,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             slot = slot + 1 == NBUF ? 0 : slot + 1;
             if (++si == ti.s_total) {
                 si = 0;
-                it += wg_x;
+                if (++sub == ti.ntiles) {
+                    sub = 0;
+                    it += wg_x;
+                }
                 if (it < x_count) start_tile();
             }
         };
@@ -661,8 +682,13 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         slot = slot + 1 == NBUF ? 0 : slot + 1;
     };
 
-    for (int64_t i = loc; i < x_count; i += wg_x) {
-        const TileInfo ti = decode(x_begin + i);
+    // tile sub of local item i, in the load wave's order
+    for (int64_t i = loc, sub = 0; i < x_count;) {
+        const TileInfo ti = decode(x_begin + i, (int)sub);
+        if (++sub == ti.ntiles) {
+            sub = 0;
+            i += wg_x;
+        }
 
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
@@ -864,14 +890,15 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     if (c.gemm) a.wsc = static_cast<const uint16_t *>(c.w);
     a.tiles_w = (int)((c.w_ + kWB - 1) / kWB);
     a.tiles_h = (int)((c.h + TL::HB - 1) / TL::HB);
-    a.tiles = (int64_t)a.tiles_w * a.tiles_h * c.n * c.t * (a.cout_p / TL::NB);
-    if (a.tiles <= 0) return hipSuccess;
+    a.pair = c.cache == nullptr && !c.up2 && !c.gemm && c.t >= 2 ? 1 : 0;
+    a.items = (int64_t)a.tiles_w * a.tiles_h * c.n * (c.t - a.pair) * (a.cout_p / TL::NB);
+    if (a.items <= 0) return hipSuccess;
     // persistent grid: one workgroup per compute unit (the LDS ring takes most
     // of a CU's 160 KB), each looping over its share of the tiles
     int ncu = 0;
     const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
-    const int64_t grid = a.tiles < (int64_t)ncu * TL::kPerCU ? a.tiles : (int64_t)ncu * TL::kPerCU;
+    const int64_t grid = a.items < (int64_t)ncu * TL::kPerCU ? a.items : (int64_t)ncu * TL::kPerCU;
     conv3d_bf16_kernel<WM, WN, FM, FN, EPI, SC><<<dim3((unsigned)grid), dim3(TL::kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
