@@ -254,6 +254,26 @@ __device__ inline uint32_t lds_address(const unsigned char *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
 }
 
+// Scheduling group of n (<= 9) instructions of class MASK (sched_group_barrier
+// takes constant counts; n is a constant after unrolling).
+template <int MASK>
+__device__ inline void sched_group(int n) {
+    switch (n) {
+        case 1: __builtin_amdgcn_sched_group_barrier(MASK, 1, 0); break;
+        case 2: __builtin_amdgcn_sched_group_barrier(MASK, 2, 0); break;
+        case 3: __builtin_amdgcn_sched_group_barrier(MASK, 3, 0); break;
+        case 4: __builtin_amdgcn_sched_group_barrier(MASK, 4, 0); break;
+        case 5: __builtin_amdgcn_sched_group_barrier(MASK, 5, 0); break;
+        case 6: __builtin_amdgcn_sched_group_barrier(MASK, 6, 0); break;
+        case 7: __builtin_amdgcn_sched_group_barrier(MASK, 7, 0); break;
+        case 8: __builtin_amdgcn_sched_group_barrier(MASK, 8, 0); break;
+        case 9: __builtin_amdgcn_sched_group_barrier(MASK, 9, 0); break;
+        default: break;
+    }
+}
+constexpr int kSchedMfma = 0x008;    // sched_group_barrier class: MFMA
+constexpr int kSchedDsRead = 0x100;  // sched_group_barrier class: LDS read
+
 // compiler-only fence: no memory access moves across it
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -549,21 +569,60 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
     floatx16 acc[FM][FN];
     constexpr int NROW = FM + 2;
-    // One conv stage: 9 taps x FM rows x FN channel blocks of MFMAs.  LDS
-    // reads complete in order, so they are issued in the order of first use:
-    // input row 0 and the kh = 0 weights, then the kh = 1 weights and row 1
-    // (used from row group 1 on), then the kh = 2 weights (row group 2).
-    auto compute_conv = [&](const unsigned char *buf) __attribute__((always_inline)) {
-        bf16x8 fw[9][FN];
-        bf16x8 fx[2][3];
+    // Stage operands, kept across stages: the next stage's first operands
+    // (input row 0 and the kh = 0 weights) are read during this stage's last
+    // two rows, straight into the registers they are used from.  With one
+    // MFMA wave per SIMD nothing else would hide that LDS round trip at every
+    // stage start.  fx is a two-row ring: row r of a stage with parity PAR is
+    // in fx[(r + PAR) & 1], and the next stage's row 0 goes into the buffer
+    // this stage's last row does not use, so with an odd row count the parity
+    // alternates from stage to stage.
+    bf16x8 fw[9][FN];
+    bf16x8 fx[2][3];
+    constexpr bool ALT = NROW % 2 == 1;
+    // row 0 and the kh = 0 weights of the stage in `buf` (parity par)
+    auto load_first = [&](const unsigned char *buf, int par) __attribute__((always_inline)) {
+        if (par) {
 #pragma unroll
-        for (int kw = 0; kw < 3; ++kw) fx[0][kw] = ldA(buf, 0, kw);
+            for (int kw = 0; kw < 3; ++kw) fx[1][kw] = ldA(buf, 0, kw);
+        } else {
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) fx[0][kw] = ldA(buf, 0, kw);
+        }
 #pragma unroll
         for (int tap = 0; tap < 3; ++tap)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = ldB(buf, tap, fn);
+    };
+
+    int consumed = 0, seen = 0, slot = 0;
+    // wait until stage `consumed` has landed
+    auto wait_landed = [&]() __attribute__((always_inline)) {
+        for (int spin = 0; seen <= consumed && spin < kSpinCap; ++spin) {
+            seen = flag_read(0);
+            if (seen <= consumed) __builtin_amdgcn_s_sleep(1);
+        }
+        compiler_fence();   // the stage's reads stay below the flag read
+    };
+
+    // One conv stage: 9 taps x FM rows x FN channel blocks of MFMAs, from row
+    // 0 and the kh = 0 weights already requested.  LDS reads complete in
+    // order, so they are issued in the order of first use: the kh = 1 weights
+    // and row 1 (used from row group 1 on), then the kh = 2 weights (row group
+    // 2).  The following ring slot's first operands are read once this
+    // stage's kh = 0 taps are done (row FM) and during its last row.  Those
+    // reads are unconditional (reading a slot that is still being filled is
+    // harmless, and with no branch around them every LDS wait stays exact);
+    // the result is whether that slot's stage had landed before they were
+    // issued, from a flag read issued early in the stage, so the stage never
+    // blocks on it.
+    auto compute_conv = [&]<int PAR>(const unsigned char *buf, const unsigned char *next)
+                            __attribute__((always_inline)) {
+        bool landed = false;
+        int early = 0;
 #pragma unroll
         for (int qr = 0; qr < NROW; ++qr) {
+            const int cur = (qr + PAR) & 1;
             if (qr + 1 < 3) {
 #pragma unroll
                 for (int tap = 3 * (qr + 1); tap < 3 * (qr + 2); ++tap)
@@ -573,9 +632,23 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             // input row qr feeds output rows fm = qr - kh; the next row is read meanwhile
             if (qr + 1 < NROW) {
 #pragma unroll
-                for (int kw = 0; kw < 3; ++kw) fx[(qr + 1) & 1][kw] = ldA(buf, qr + 1, kw);
+                for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(buf, qr + 1, kw);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            if (qr == 1) early = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
+            if (qr == NROW - 2) {
+                const int f = __builtin_amdgcn_readfirstlane(early);
+                seen = f > seen ? f : seen;
+                landed = seen > consumed + 1;
+#pragma unroll
+                for (int tap = 0; tap < 3; ++tap)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = ldB(next, tap, fn);
+            }
+            if (qr == NROW - 1) {
+#pragma unroll
+                for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(next, 0, kw);
+            }
+            int nm = 0;
 #pragma unroll
             for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
@@ -583,12 +656,28 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     const int fm = qr - kh;
                     if (fm < 0 || fm >= FM) continue;
 #pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
+                    for (int fn = 0; fn < FN; ++fn) {
                         acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            fw[kh * 3 + kw][fn], fx[qr & 1][kw], acc[fm][fn], 0, 0, 0);
+                            fw[kh * 3 + kw][fn], fx[cur][kw], acc[fm][fn], 0, 0, 0);
+                        ++nm;
+                    }
                 }
+            // the row's LDS reads go one after each MFMA (issued as a burst
+            // they leave the matrix core idle for a few cycles each)
+            const int nr = (qr + 1 < 3 ? 3 * FN : 0) + (qr + 1 < NROW ? 3 : 0) + (qr == 1 ? 1 : 0) +
+                           (qr == NROW - 2 ? 3 * FN : 0) + (qr == NROW - 1 ? 3 : 0);
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                if (k < nr && k < nm) {
+                    sched_group<kSchedMfma>(1);
+                    sched_group<kSchedDsRead>(1);
+                }
+            }
+            if (nr > nm) sched_group<kSchedDsRead>(nr - nm);
+            if (nm > nr) sched_group<kSchedMfma>(nm - nr);
             __builtin_amdgcn_sched_barrier(0);
         }
+        return landed;
     };
 
     // The same stage for KH_OUTER tiles: for each kh, the 3 kw x FN weight
@@ -664,15 +753,6 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         }
     };
 
-    int consumed = 0, seen = 0, slot = 0;
-    // wait until stage `consumed` has landed
-    auto wait_landed = [&]() __attribute__((always_inline)) {
-        for (int spin = 0; seen <= consumed && spin < kSpinCap; ++spin) {
-            seen = flag_read(0);
-            if (seen <= consumed) __builtin_amdgcn_s_sleep(1);
-        }
-        compiler_fence();   // the stage's reads stay below the flag read
-    };
     // stage consumed: its reads were issued (and, LDS being in order, execute)
     // before this flag write
     auto release = [&]() __attribute__((always_inline)) {
@@ -697,13 +777,36 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-        for (int s = 0; s < ti.s_conv; ++s) {
-            wait_landed();
-            if constexpr (TL::KH_OUTER)
+        if constexpr (TL::KH_OUTER) {
+            for (int s = 0; s < ti.s_conv; ++s) {
+                wait_landed();
                 compute_conv_kh(smem + slot * TL::STAGE_BYTES);
-            else
-                compute_conv(smem + slot * TL::STAGE_BYTES);
-            release();
+                release();
+            }
+        } else {
+            // Stages run in pairs of parity 0 and 1 (straight-line code, so
+            // both use the same registers), a tile's first stage with parity
+            // 0.  The next stage's operands are kept when it is a conv stage
+            // of this tile and had landed; kernels with shortcut stages read
+            // every stage's first operands at its start.
+            bool preloaded = false;
+            auto stage = [&]<int PAR>(bool more) __attribute__((always_inline)) {
+                const unsigned char *cur = smem + slot * TL::STAGE_BYTES;
+                if (!preloaded) {
+                    wait_landed();
+                    load_first(cur, PAR);
+                }
+                const unsigned char *nxt = smem + (slot + 1 == NBUF ? 0 : slot + 1) * TL::STAGE_BYTES;
+                const bool landed = compute_conv.template operator()<PAR>(cur, nxt);
+                preloaded = !SC && more && landed;
+                release();
+            };
+            int s = 0;
+            for (; s + 2 <= ti.s_conv; s += 2) {
+                stage.template operator()<0>(true);
+                stage.template operator()<ALT ? 1 : 0>(s + 2 < ti.s_conv);
+            }
+            if (s < ti.s_conv) stage.template operator()<0>(false);
         }
         if constexpr (SC) {
             for (int s = ti.s_conv; s < ti.s_total; ++s) {
