@@ -70,9 +70,9 @@
 // zeros and are skipped (uniform per tile); with a cache they read it.
 //
 // Epilogue: each lane owns one output position and 4 consecutive output
-// channels per accumulator quad; bias, then the identity residual or the
-// shortcut bias, are added in fp32 and the result is rounded once to bf16
-// (8-byte stores).  The 1x1x1 shortcut GEMM runs as extra stages of the same
+// channels per accumulator quad.  The accumulators start at the bias (plus
+// the shortcut bias), the identity residual is added in fp32 at the end, and
+// the result is rounded once to bf16 (8-byte stores).  The 1x1x1 shortcut GEMM runs as extra stages of the same
 // accumulators, each holding two 16-channel slices (one when two do not fit a
 // stage buffer) of x at the output positions and of w_sc: every load of such
 // a stage is useful data, and x (channels-last) comes in 64-byte pieces per
@@ -770,12 +770,24 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             i += wg_x;
         }
 
+        // the accumulators start at the bias (+ shortcut bias) of their
+        // channels: accumulator element 4j + q of channel block fn is
+        // channel 8j + 4g + q of the block
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+        for (int fn = 0; fn < FN; ++fn) {
+            floatx16 b0;
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int j = 0; j < 4; ++j) {
+                const float4 bv =
+                    *reinterpret_cast<const float4 *>(bias_lds + ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g);
+                b0[4 * j] = bv.x;
+                b0[4 * j + 1] = bv.y;
+                b0[4 * j + 2] = bv.z;
+                b0[4 * j + 3] = bv.w;
+            }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+            for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = b0;
+        }
 
         if constexpr (TL::KH_OUTER) {
             for (int s = 0; s < ti.s_conv; ++s) {
@@ -827,10 +839,20 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         const int64_t frame = ti.nq * a.T + ti.tq;
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y + frame * HW * a.cout, HW * a.cout * 2);
         const int cbase = ti.n0 + wn * FN * 32 + 4 * g;   // this lane's first channel
+        // Offsets split into a wave-uniform row part (valid or not for the
+        // whole wave) and a per-lane column part fixed for the tile.
         auto pos_off = [&](int fm, int cstride) __attribute__((always_inline)) -> uint32_t {
             const int hh = ti.h0 + wm * FM + fm, ww = ti.w0 + l32;
-            return hh < H && ww < W ? (uint32_t)((hh * W + ww) * cstride + cbase) * 2 : kOOB;
+            return hh < H && ww < W ? (uint32_t)(hh * W * cstride) * 2 + (uint32_t)(ww * cstride + cbase) * 2
+                                    : kOOB;
         };
+        // store pieces: position p = lane / 4 + 16 half, 16-byte quarter lane % 4
+        uint32_t col_off[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int ww = ti.w0 + (lane >> 2) + 16 * half;
+            col_off[half] = ww < W ? (uint32_t)(ww * a.cout + ti.n0 + wn * FN * 32) * 2 + (lane & 3) * 16 : kOOB;
+        }
         // A row of results goes out through this wave's LDS staging buffer:
         // written as the MFMA layout holds it (lane = position, 4 channels per
         // accumulator quad), read back as 16 bytes per lane with 4 lanes per
@@ -855,11 +877,6 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                         float v[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) v[q] = acc[f0 + e][fn][4 * j + q];
-                        {
-                            const float4 bv = *reinterpret_cast<const float4 *>(
-                                bias_lds + ti.n0 + wn * FN * 32 + fn * 32 + 8 * j + 4 * g);
-                            v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
-                        }
                         if (res != nullptr) {
                             const u32x2 r = res[e][fn][j];
                             v[0] += bf16_bits_to_f32(r.x & 0xffffu);
@@ -878,21 +895,16 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                                         (uint32_t)((hh * W + ww) * a.cout + c0 + q) * 2, 0, 0);
                             continue;
                         }
-                        u32x2 o;
-                        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        const u32x2 o = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                         *reinterpret_cast<u32x2 *>(epi + l32 * kEpiStride + j * 16 + g * 8) = o;
                     }
                     if (narrow) continue;
+                    const uint32_t row_off = (uint32_t)(hh * W * a.cout) * 2 + fn * 64;
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const int p = (lane >> 2) + 16 * half, q = lane & 3;
                         const u32x4 d = *reinterpret_cast<const u32x4 *>(epi + p * kEpiStride + q * 16);
-                        const int ww = ti.w0 + p;
-                        const uint32_t off =
-                            hh < H && ww < W
-                                ? (uint32_t)((hh * W + ww) * a.cout + ti.n0 + wn * FN * 32 + fn * 32) * 2 + q * 16
-                                : kOOB;
+                        const uint32_t off = hh < H && col_off[half] != kOOB ? row_off + col_off[half] : kOOB;
                         __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
                     }
                 }
