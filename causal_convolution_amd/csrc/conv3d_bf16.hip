@@ -705,7 +705,6 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 #pragma unroll
                     for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(buf, nr, kw);
                 }
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kw = 0; kw < 3; ++kw) {
 #pragma unroll
@@ -717,6 +716,18 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                         for (int fn = 0; fn < FN; ++fn) fw[kw][fn] = ldB(buf, (kh + 1) * 3 + kw, fn);
                     }
                 }
+                // LDS reads one after each MFMA, as in the row-stationary stage
+                constexpr int nm = 3 * FN;
+                const int nr = (kh == 2 && last_row ? 0 : 3) + (last_row && kh < 2 ? 3 * FN : 0);
+#pragma unroll
+                for (int k = 0; k < 9; ++k) {
+                    if (k < nr && k < nm) {
+                        sched_group<kSchedMfma>(1);
+                        sched_group<kSchedDsRead>(1);
+                    }
+                }
+                if (nr > nm) sched_group<kSchedDsRead>(nr - nm);
+                if (nm > nr) sched_group<kSchedMfma>(nm - nr);
                 __builtin_amdgcn_sched_barrier(0);
             }
     };
