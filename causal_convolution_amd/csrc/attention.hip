@@ -20,8 +20,10 @@
 //    and, per key block, computes the scores S^T = K q^T (keys as the MFMA M
 //    rows, queries as N columns) and the online softmax: row maximum (the two
 //    32-lane halves exchange theirs with v_permlane32_swap), exp2, running
-//    sum.  It publishes P in LDS, in the consumer's B-operand layout, and,
-//    when some query's maximum grew, the factors that rescale O;
+//    sum, with the reference maximum moved only when some query's maximum
+//    passes it by more than 2^8 in the exponential (lazy rescaling; exact).
+//    It publishes P in LDS, in the consumer's B-operand layout, and, when
+//    the reference moved, the factors that rescale O;
 //  - the consumer keeps O^T for the whole head (D/32 tiles of 32 x 32) and, one
 //    key block behind, rescales it if told to and adds V^T P^T.  A producer
 //    lane holds the scores of one query for keys 8j + 4g + i (j, i < 4; g =
@@ -58,6 +60,7 @@ constexpr int kBQ = 128;                // queries per workgroup
 constexpr int kBK = 32;                 // keys per block
 constexpr int kGroups = 4;              // query groups of 32 per workgroup
 constexpr int kWaves = 2 * kGroups;     // a producer and a consumer wave per group
+constexpr float kRescaleLog2 = 8.0f;    // softmax reference moves when a maximum passes it by this (log2)
 constexpr int kThreads = kWaves * 64;
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
 
     // Phase p (0 .. nblk, one barrier each): the producer of a query group
     // computes the scores of key block p and their softmax and publishes P_p
-    // (and, when some query's maximum grew, the factors that rescale O); the
+    // (and, when the reference maximum moved, the factors that rescale O); the
     // consumer adds V_{p-1} P_{p-1} to O.  Loads: K_{p+1} and V^T_p, into the
     // slots of K_{p-1} and V^T_{p-2}, which the last barrier freed.
     if (producer) {
@@ -230,9 +233,14 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
 #pragma unroll
                 for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
                 mx = halves_max(mx) * scale_log2;
-                // O is rescaled only when some query's maximum grew: otherwise the
-                // factor is exp2(0) = 1 for every lane and skipping it changes no bit
-                const bool grow = __builtin_amdgcn_ballot_w64(mx > m_run) != 0;
+                // Lazy rescaling: m_run, the reference the exponentials are taken
+                // against, moves (and O is rescaled) only when some query's
+                // maximum exceeds it by more than kRescaleLog2.  The softmax stays
+                // exact (P, l and O share the reference); P is then at most
+                // 2^kRescaleLog2, well inside bf16 and fp32.  With the reference
+                // tracking every increase, about a quarter of the key blocks of a
+                // 90 x 160 frame rescaled O; now almost only the first does.
+                const bool grow = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0;
                 if (grow) {
                     const float m_new = fmaxf(m_run, mx);
                     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);

@@ -94,6 +94,7 @@
 
 #include "bf16.h"
 #include "internal.h"
+#include "mfma_sched.h"
 
 namespace wanvae {
 namespace {
@@ -253,26 +254,6 @@ __device__ __host__ constexpr int group_rows(int gi) { return FM - gi * EG < EG 
 __device__ inline uint32_t lds_address(const unsigned char *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
 }
-
-// Scheduling group of n (<= 9) instructions of class MASK (sched_group_barrier
-// takes constant counts; n is a constant after unrolling).
-template <int MASK>
-__device__ inline void sched_group(int n) {
-    switch (n) {
-        case 1: __builtin_amdgcn_sched_group_barrier(MASK, 1, 0); break;
-        case 2: __builtin_amdgcn_sched_group_barrier(MASK, 2, 0); break;
-        case 3: __builtin_amdgcn_sched_group_barrier(MASK, 3, 0); break;
-        case 4: __builtin_amdgcn_sched_group_barrier(MASK, 4, 0); break;
-        case 5: __builtin_amdgcn_sched_group_barrier(MASK, 5, 0); break;
-        case 6: __builtin_amdgcn_sched_group_barrier(MASK, 6, 0); break;
-        case 7: __builtin_amdgcn_sched_group_barrier(MASK, 7, 0); break;
-        case 8: __builtin_amdgcn_sched_group_barrier(MASK, 8, 0); break;
-        case 9: __builtin_amdgcn_sched_group_barrier(MASK, 9, 0); break;
-        default: break;
-    }
-}
-constexpr int kSchedMfma = 0x008;    // sched_group_barrier class: MFMA
-constexpr int kSchedDsRead = 0x100;  // sched_group_barrier class: LDS read
 
 // compiler-only fence: no memory access moves across it
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
