@@ -386,6 +386,46 @@ def test_attention_block_small(torch, wv, shape):
     _attn_check(torch, wv, x, p, f"{shape}")
 
 
+def test_attention_block_growing_scores(torch, wv):
+    """Scores that keep growing along the key sequence: the positions of the
+    frame turn from one direction v toward another, u, and the q and k
+    projections are a scaled identity, so a late query scores the later keys
+    ever higher and its running maximum passes the softmax reference by more
+    than 2^8 again and again (the kernel's rescale path, which random inputs
+    reach only at the first key block)."""
+    C, H, W = 128, 16, 40
+    HW = H * W
+    rng = np.random.default_rng(11)
+    a0, a1 = rng.standard_normal(C), rng.standard_normal(C)
+    u = a0 / np.linalg.norm(a0)
+    v = a1 - (a1 @ u) * u
+    v /= np.linalg.norm(v)
+    u, v = u * np.sqrt(C), v * np.sqrt(C)   # unit RMS
+    theta = np.linspace(np.pi / 2, 0.0, HW)
+    x = wl.round_bf16((np.cos(theta)[:, None] * u + np.sin(theta)[:, None] * v).astype(np.float32))
+    x = x.reshape(1, 1, H, W, C)
+    p = wl.make_attention_params(C, seed=11)
+    p["gamma"][:] = 1.0
+    p["beta"][:] = 0.0
+    s = np.sqrt(3.5)
+    eye = wl.round_bf16((s * np.eye(C)).astype(np.float32))
+    p["wqkv"][:C] = eye
+    p["wqkv"][C:2 * C] = eye
+    p["bqkv"][:2 * C] = 0.0
+    # precondition of the data: the last query's running maximum (log2 units,
+    # keys in blocks of 32) passes the reference by more than 8 several times
+    xf = x.reshape(HW, C).astype(np.float64)
+    xn = xf / np.sqrt((xf * xf).mean(axis=1, keepdims=True))
+    sc = (s * s) * (xn @ xn[-1]) / np.sqrt(C) * np.log2(np.e)
+    ref_max, moves = -np.inf, 0
+    for j in range(0, HW, 32):
+        m = sc[j:j + 32].max()
+        if m > ref_max + 8.0:
+            ref_max, moves = m, moves + 1
+    assert moves >= 5, moves
+    _attn_check(torch, wv, x, p, f"growing scores, {moves} reference moves")
+
+
 def test_attention_block_latent_sampled(torch, wv):
     """The latent-resolution mid-block, [1, 21, 90, 160, 384], on sampled
     queries (corners and random positions) of the first, a middle and the
