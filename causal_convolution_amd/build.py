@@ -34,9 +34,12 @@ RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
 
 
 def check_resources(src: str, remarks: str) -> None:
-    """Fails the build if a kernel of `src` spills registers or uses scratch
-    memory: every kernel here is meant to keep its working set in registers
-    and LDS, and scratch traffic in an MFMA loop costs an order of magnitude."""
+    """Fails the build if a kernel of `src` spills vector registers or uses
+    scratch memory: every kernel here is meant to keep its working set in
+    registers and LDS, and scratch traffic in an MFMA loop costs an order of
+    magnitude.  A few scalar-register spills are tolerated (up to 64): they go
+    to lanes of a vector register, not to memory (the scratch size, checked
+    too, stays 0)."""
     bad, name = [], "?"
     for line in remarks.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
@@ -44,7 +47,7 @@ def check_resources(src: str, remarks: str) -> None:
             name = m.group(1)
             continue
         m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
-        if m and int(m.group(2)) > 0 and not (m.group(1) == "SGPRs Spill" and int(m.group(2)) <= 32):
+        if m and int(m.group(2)) > 0 and not (m.group(1) == "SGPRs Spill" and int(m.group(2)) <= 64):
             bad.append(f"{name}: {m.group(1)} = {m.group(2)}")
     if bad:
         raise RuntimeError(f"{src}: kernels spill or use scratch:\n" + "\n".join(bad))

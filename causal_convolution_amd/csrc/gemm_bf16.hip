@@ -5,21 +5,35 @@
 // the 1x1x1 projections around the decoder's mid-block attention (q, k and v
 // from the normed input, C -> 3C, and the output projection with the residual,
 // C -> C; "Closing the gap: Wan 2.2 14B VAE decoder", section 5, and
-// "Sharding of WAN 2.2 VAE", decoder module tree).
+// "Sharding of WAN 2.2 VAE", decoder module tree), and the 1x1x1 shortcut of a
+// channel-changing ResidualBlock.
 //
-// A workgroup owns 128 positions and all N output channels.  Their x rows
-// (K <= 384, up to 96 KB) are loaded into LDS once, by LDS-DMA (buffer_load
-// ... lds, 1 KB per instruction), and stay there while the output channels go
-// by in chunks of 128: the weight (small, L2-resident) streams through a double
-// buffer in stages of 128 channels x 128 k, the next stage loading while the
-// current one computes.  x thus comes from HBM exactly once and only the weight
-// is re-read, from L2.  Four waves, one per SIMD, each own 64 channels x 64
-// positions of a chunk: 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 with the
-// weights as the A operand (channels as M) and x as the B operand (positions
-// as N), so a lane ends up holding 4 consecutive output channels of one
-// position per 4 accumulators and stores them as one 8-byte piece.  Rows are
-// swizzled in 16-byte chunks (chunk ^ (row & 15)) so that fragment reads hit
-// distinct banks.  The grid is persistent, one workgroup per CU.
+// A workgroup owns 256 positions and all N output channels; its four waves
+// (one per SIMD) own 64 positions each and keep their x rows for the whole K
+// (K <= 384) in registers, as MFMA B operands: x comes from HBM exactly once
+// and never passes through LDS.  The weight (small, L2-resident) streams
+// through LDS in stages of 128 output channels x 128 k (32 KB), moved by
+// LDS-DMA (buffer_load ... lds, 1 KB per instruction, each wave a quarter of
+// every stage), in a ring of 4 slots loaded 3 stages ahead; the weight stream
+// does not depend on the positions, so it runs on across tiles.  Per stage a
+// wave runs 4 channel blocks x 2 position blocks x 8 k-steps of
+// v_mfma_f32_32x32x16_bf16 (weights as the A operand, channels as M), each
+// weight fragment read from LDS once for two MFMAs.  A lane ends up holding 4
+// consecutive output channels of one position per 4 accumulators and stores
+// them as one 8-byte piece.  The accumulators start at the bias.  The next
+// tile's x is loaded k-slice by k-slice as the last output-channel chunk of
+// the current tile finishes with each slice.  Weight rows are swizzled in
+// 16-byte chunks (chunk ^ (row & 15)) so that fragment reads hit distinct
+// banks.  The grid is persistent, one workgroup per CU, each XCD a contiguous
+// range of tiles.
+//
+// Waits on the weight stages are exact: vector-memory operations complete in
+// issue order, so "stage s has landed" is "at most the operations issued
+// after its loads are outstanding"; each wave counts what it issues (weight
+// loads, x loads, residual loads, stores) and waits for that count.
+#include <type_traits>
+#include <utility>
+
 #include "bf16.h"
 #include "internal.h"
 
@@ -32,21 +46,29 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;                       // positions per tile
+constexpr int kBM = 256;                       // positions per tile
 constexpr int kBN = 128;                       // output channels per chunk
 constexpr int kBK = 128;                       // K per weight stage
-constexpr int kKMax = 384;                     // the resident x tile holds K <= 384
-constexpr int kXMax = kBM * kKMax * 2;         // 96 KB
+constexpr int kKMax = 384;                     // x of 64 positions in registers: K <= 384
 constexpr int kRowBytes = kBK * 2;             // 256 bytes of a weight row per stage
 constexpr int kPart = kBN * kRowBytes;         // 32 KB: one weight stage
+constexpr int kNBuf = 4;                       // weight ring slots
+constexpr int kNMax = 2048;                    // output channels (the bias is kept in LDS)
+constexpr int kAhead = 3;                      // stages loaded ahead
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kWBlocksPerWave = kPart / 1024 / kWaves;   // 8
 constexpr int kXCD = 8;
-constexpr int kStores = 16;                    // buffer stores per lane in an epilogue
+constexpr int kStores = 2 * 4 * 4;             // stores (and residual loads) per lane in a residual epilogue
+// Without a residual the epilogue goes through LDS: per wave, 32 positions x
+// 64 channels of bf16 at a time (rows kStageRow bytes apart), read back as 8
+// lanes x 16 bytes per position, so a store writes 8 whole 128-byte rows.
+constexpr int kStageRow = 144;
+constexpr int kStagedStores = 2 * 2 * 4;       // stores per lane in such an epilogue
 constexpr int kBufFlags = 0x00020000;          // raw buffer: loads past num_records return zeros
 constexpr uint32_t kOOB = 0x80000000u;
-static_assert(kXMax + 2 * kPart <= 160 * 1024, "LDS");
+static_assert(kNBuf * kPart + kNMax * 4 + kWaves * 32 * kStageRow <= 160 * 1024, "LDS");
+static_assert(kAhead < kNBuf, "a slot is refilled only after the stage it held was consumed");
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
@@ -81,22 +103,49 @@ __device__ inline uint32_t lds_address(const unsigned char *p) {
 
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
-template <bool RES>
+// s_waitcnt for "at most n vector-memory operations outstanding", n known only
+// at run time (the instruction takes an immediate): n is rounded down to a
+// multiple of 8 (at most 56), which only waits longer
+__device__ inline void wait_vm_at_most(int n) {
+    if (n >= 32) {
+        if (n >= 48) {
+            if (n >= 56) __builtin_amdgcn_s_waitcnt(waitcnt_vm(56));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(48));
+        } else {
+            if (n >= 40) __builtin_amdgcn_s_waitcnt(waitcnt_vm(40));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(32));
+        }
+    } else {
+        if (n >= 16) {
+            if (n >= 24) __builtin_amdgcn_s_waitcnt(waitcnt_vm(24));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+        } else {
+            if (n >= 8) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+    }
+}
+
+template <int K, bool RES, bool ONE_CHUNK>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
                                                              const uint16_t *__restrict__ w,
                                                              const float *__restrict__ bias,
                                                              const uint16_t *__restrict__ res,
-                                                             uint16_t *__restrict__ y, int64_t P, int N, int K,
+                                                             uint16_t *__restrict__ y, int64_t P, int N,
                                                              int64_t mtiles) {
-    // LDS: the x tile [128 positions][K] (resident for all output channels),
-    // then two w stages [128 channels][128 k]
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[kXMax + 2 * kPart];
+    constexpr int KS = K / 16;   // MFMA k-steps
+    constexpr int S = K / kBK;   // weight stages per output-channel chunk
+    static_assert(K % kBK == 0 && K <= kKMax, "K");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kNBuf * kPart];
+    // the bias of every output channel, read from LDS: a vector-memory load
+    // of it would make the compiler wait for every load in flight (it does
+    // not see the weight loads, which are inline assembly)
+    __shared__ __attribute__((aligned(16))) float bias_lds[kNMax];
+    __shared__ __attribute__((aligned(16))) unsigned char ostage[kWaves * 32 * kStageRow];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;       // channel half, position half
     const int l32 = lane & 31, g = lane >> 5;
-    const int nchunks = (N + kBN - 1) / kBN, kstages = K / kBK;   // (the last chunk may be 64 wide)
-    const int xrow = 2 * K;                        // bytes of an x row
+    const int nchunks = ONE_CHUNK ? 1 : (N + kBN - 1) / kBN;   // the last may be 64 wide
 
     // ---- this workgroup's position tiles: XCD x (= workgroup index mod 8)
     // owns a contiguous range, its workgroups take them round-robin
@@ -107,189 +156,259 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
     const int64_t x_begin = mtiles * wg_before / nwg;
     const int64_t x_count = mtiles * (wg_before + wg_x) / nwg - x_begin;
     const int64_t my_tiles = x_count > loc ? (x_count - loc + wg_x - 1) / wg_x : 0;
+    if (my_tiles == 0) return;   // uniform over the workgroup: no barrier is left waiting
+    for (int c = tid; c < N; c += kThreads) bias_lds[c] = bias != nullptr ? bias[c] : 0.0f;
+    __syncthreads();
+    const int per_tile = nchunks * S;            // weight stages per tile
+    const int64_t total = my_tiles * per_tile;   // weight stages of this workgroup
+    auto tile_m0 = [&](int64_t it) __attribute__((always_inline)) { return (x_begin + loc + it * wg_x) * kBM; };
 
+    int issued = 0;   // vector-memory operations this wave has issued (they complete in order)
+
+    // ---- weight stage gst (chunk nc, k stage kq, the same for every tile):
+    // 32 blocks of 1 KB, 8 per wave; block b holds rows 4b .. 4b + 3 of the
+    // 128 channels, lane row 4b + l / 16, stored chunk l % 16
     const uint32_t lds_base = lds_address(lds);
-    const uint32_t w_base = lds_base + kXMax;
-    // x tile: K/4 blocks of 1 KB, wave w the blocks w, w + 4, ...; byte o of
-    // the tile is row o / xrow, stored chunk (o % xrow) / 16 = global chunk ^
-    // (row & 15)
-    auto issue_x = [&](int64_t m0) __attribute__((always_inline)) {
-        const int64_t rows = P - m0 < kBM ? P - m0 : kBM;
-        const i32x4 r = buffer_rsrc(x + m0 * K, (uint32_t)(rows * xrow));
-        for (int b = wave; b < K / 4; b += kWaves) {
-            const int o = b * 1024 + lane * 16;
-            const int row = o / xrow, cs = (o % xrow) / 16;
-            const uint32_t off = row < rows ? (uint32_t)(row * xrow + ((cs ^ (row & 15)) * 16)) : kOOB;
-            lds_dma16(r, lds_base + (uint32_t)(b * 1024), off);
-        }
+    // lane offset of block i (computed at each issue: eight live registers
+    // fewer beside the x fragments)
+    auto w_off = [&](int i) __attribute__((always_inline)) {
+        const int row = 4 * (wave * kWBlocksPerWave + i) + (lane >> 4), cs = lane & 15;
+        return (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)((cs ^ (row & 15)) * 16);
     };
-    // w stage (chunk nc, k stage ks): 32 blocks, 8 per wave; block b rows
-    // 4b .. 4b + 3 of the 128 channels, lane row 4b + l / 16, stored chunk l % 16
-    uint32_t w_off[kWBlocksPerWave];
-#pragma unroll
-    for (int i = 0; i < kWBlocksPerWave; ++i) {
-        const int b = wave * kWBlocksPerWave + i;
-        const int row = 4 * b + (lane >> 4), cs = lane & 15;
-        w_off[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)((cs ^ (row & 15)) * 16);
-    }
-    auto issue_w = [&](int st) __attribute__((always_inline)) {
-        const int nc = st / kstages, kk = (st % kstages) * kBK;
+    auto issue_w = [&](int64_t gst) __attribute__((always_inline)) {
+        const int st = (int)(gst % per_tile);
+        const int nc = st / S, kk = (st % S) * kBK;
         // channels past N (a 64-wide last chunk) fall beyond the buffer's end: zeros
         const int rows = N - nc * kBN < kBN ? N - nc * kBN : kBN;
         const i32x4 r = buffer_rsrc(w + (int64_t)nc * kBN * K + kk, (uint32_t)(rows * K * 2 - kk * 2));
-        const uint32_t dst = w_base + (uint32_t)((st & 1) * kPart + wave * kWBlocksPerWave * 1024);
+        const uint32_t dst = lds_base + (uint32_t)((int)(gst % kNBuf) * kPart + wave * kWBlocksPerWave * 1024);
 #pragma unroll
-        for (int i = 0; i < kWBlocksPerWave; ++i) lds_dma16(r, dst + i * 1024, w_off[i]);
-    };
-    // wait for this wave's LDS-DMA (all but the last `after` vector-memory
-    // operations, which counts in issue order) and LDS reads, then barrier
-    auto sync = [&](bool after_stores) __attribute__((always_inline)) {
-        compiler_fence();
-        if (after_stores)
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kStores) & waitcnt_lgkm0());
-        else
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & waitcnt_lgkm0());
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
+        for (int i = 0; i < kWBlocksPerWave; ++i) lds_dma16(r, dst + i * 1024, w_off(i));
+        issued += kWBlocksPerWave;
     };
 
-    // fragments: weight row `row` of a stage, k-step ks (k = 16 ks + 8 g .. +7);
-    // x row `row`, global 16-byte chunk kc
+    // ---- x of this wave's 64 positions: fragment (k-step ks, position block
+    // jn) = x[m0 + 64 wave + 32 jn + l32][16 ks + 8 g .. + 7], one 16-byte
+    // load; positions past P read zeros
+    bf16x8 xf[KS][2];
+    auto load_x = [&](int64_t m0, int ks0, int ks1) __attribute__((always_inline)) {
+        const int64_t rows = P - m0 < kBM ? P - m0 : kBM;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + m0 * K, (uint32_t)(rows * K * 2));
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) {
+            const int pl = wave * 64 + 32 * jn + l32;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks < ks0 || ks >= ks1) continue;
+                const uint32_t off = pl < rows ? (uint32_t)(pl * K * 2 + ks * 32 + g * 16) : kOOB;
+                xf[ks][jn] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+            }
+        }
+        issued += 2 * (ks1 - ks0);
+    };
+
+    floatx16 acc[4][2];
+    // the accumulators start at the bias: element 4 jj + q of channel block i
+    // is channel n0 + 32 i + 8 jj + 4 g + q
+    auto init_acc = [&](int n0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            floatx16 b0;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int c = n0 + 32 * i + 8 * jj + 4 * g;
+                const float4 bv =
+                    c < N ? *reinterpret_cast<const float4 *>(bias_lds + c) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+                b0[4 * jj] = bv.x;
+                b0[4 * jj + 1] = bv.y;
+                b0[4 * jj + 2] = bv.z;
+                b0[4 * jj + 3] = bv.w;
+            }
+            acc[i][0] = b0;
+            acc[i][1] = b0;
+        }
+    };
+    // ---- epilogue of chunk n0.  Accumulator element 4 jj + q of (channel
+    // block i, position block jn) is channel n0 + 32 i + 8 jj + 4 g + q of
+    // position m0 + 64 wave + 32 jn + l32.  The number of vector-memory
+    // operations per lane is fixed whatever the tile: positions past P and
+    // channels past N get an offset beyond the buffer's end (the load returns
+    // zeros, the store is dropped).
+    auto store = [&](int64_t m0, int n0) __attribute__((always_inline)) {
+        const int64_t rows = P - m0 < kBM ? P - m0 : kBM;
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + m0 * N, (uint32_t)(rows * N * 2));
+        if constexpr (!RES) {
+            // through this wave's LDS staging rows, 32 positions x 64 channels
+            // (channel half h of the chunk) at a time.  The lane index is made
+            // opaque here so that the addresses are computed in place instead
+            // of being hoisted out of the stage loop into registers that the
+            // x fragments need.
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int lq = ln & 31, gq = ln >> 5;
+            unsigned char *stg = ostage + wave * 32 * kStageRow;
+#pragma unroll
+            for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const floatx16 &a = acc[2 * h + i2][jn];
+                            *reinterpret_cast<u32x2 *>(stg + lq * kStageRow + (32 * i2 + 8 * jj + 4 * gq) * 2) =
+                                u32x2{pack_bf16x2(a[4 * jj], a[4 * jj + 1]), pack_bf16x2(a[4 * jj + 2], a[4 * jj + 3])};
+                        }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int p = (ln >> 3) + 8 * r, q = ln & 7;
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + p * kStageRow + q * 16);
+                        const int pl = wave * 64 + 32 * jn + p;
+                        const uint32_t off = pl < rows && n0 + 64 * h < N
+                                                 ? (uint32_t)((pl * N + n0 + 64 * h + 8 * q) * 2)
+                                                 : kOOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // one unit's values live at a time
+                }
+            issued += kStagedStores;
+            return;
+        }
+        // with the residual: 8-byte pieces straight from the accumulators,
+        // the residual's pieces all requested before the first store (a load
+        // behind a store would wait for it)
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(RES ? res + m0 * N : y, RES ? (uint32_t)(rows * N * 2) : 0u);
+        // position part per position block (per lane), channel part per
+        // channel block (uniform: a 64-wide last chunk has blocks past N)
+        uint32_t poff[2];
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) {
+            const int pl = wave * 64 + 32 * jn + l32;   // position within the tile
+            poff[jn] = pl < rows ? (uint32_t)((pl * N + n0 + 4 * g) * 2) : kOOB;
+        }
+        auto off = [&](int jn, int i, int jj) __attribute__((always_inline)) -> uint32_t {
+            return poff[jn] != kOOB && n0 + 32 * i < N ? poff[jn] + (uint32_t)((32 * i + 8 * jj) * 2) : kOOB;
+        };
+        u32x2 rv[2][4][4];
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    rv[jn][i][jj] =
+                        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, off(jn, i, jj), 0, 0));
+        issued += kStores;
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    float v0 = acc[i][jn][4 * jj], v1 = acc[i][jn][4 * jj + 1];
+                    float v2 = acc[i][jn][4 * jj + 2], v3 = acc[i][jn][4 * jj + 3];
+                    v0 += bf16_bits_to_f32(rv[jn][i][jj].x & 0xffffu);
+                    v1 += bf16_bits_to_f32(rv[jn][i][jj].x >> 16);
+                    v2 += bf16_bits_to_f32(rv[jn][i][jj].y & 0xffffu);
+                    v3 += bf16_bits_to_f32(rv[jn][i][jj].y >> 16);
+                    const u32x2 d = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, d), ry,
+                        off(jn, i, jj), 0, 0);
+                }
+        issued += kStores;
+    };
+
+    // weight fragment: row `row` of a stage, k-step ks (k = 16 ks + 8 g .. +7)
     auto wfrag = [&](const unsigned char *ws, int row, int ks) __attribute__((always_inline)) {
         const int c = (2 * ks + g) ^ (row & 15);
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(ws + row * kRowBytes + c * 16));
     };
-    auto xfrag = [&](int row, int kc) __attribute__((always_inline)) {
-        const int c = kc ^ (row & 15);
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(lds + row * xrow + c * 16));
-    };
 
-    floatx16 acc[2][2];
-    float4 bv[2][4];   // bias of this lane's channels in the current chunk
-    auto load_bias = [&](int n0) __attribute__((always_inline)) {
-        if (bias) {
+    // ---- prologue: x of the first tile, then the first kAhead weight stages;
+    // mark[d] is the issue count just after the loads of stage gst + d
+    load_x(tile_m0(0), 0, KS);
+    int mark[kAhead];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    bv[i][jj] = n0 + wm * 64 < N ? *reinterpret_cast<const float4 *>(bias + n0 + wm * 64 + 32 * i + 8 * jj + 4 * g)
-                                                 : float4{0.0f, 0.0f, 0.0f, 0.0f};
-        } else {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) bv[i][jj] = float4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-    };
-    // ---- epilogue of chunk n0: channel n0 + 64 wm + 32 i + 8 jj + 4 g + {0..3}
-    // of position m0 + 64 wn + 32 jn + l32: 8 contiguous bytes.  Exactly
-    // kStores buffer stores per lane whatever the tile: positions past P fall
-    // beyond the buffer's end and are dropped (the stage wait counts on it).
-    auto store = [&](int64_t m0, int n0) __attribute__((always_inline)) {
-        const int64_t rows = P - m0 < kBM ? P - m0 : kBM;
-        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + m0 * N, (uint32_t)(rows * N * 2));
-        const __amdgpu_buffer_rsrc_t rr = make_rsrc(RES ? res + m0 * N : y, RES ? (uint32_t)(rows * N * 2) : 0u);
-        uint32_t off[2][2][4];
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn) {
-            const int pl = wn * 64 + 32 * jn + l32;   // position within the tile
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    off[jn][i][jj] = pl < rows && n0 + wm * 64 < N
-                                         ? (uint32_t)((pl * N + n0 + wm * 64 + 32 * i + 8 * jj + 4 * g) * 2)
-                                         : kOOB;
-        }
-        // residual pieces all requested before the first store (a load behind
-        // a store would wait for it)
-        u32x2 rv[2][2][4];
-        if constexpr (RES) {
-#pragma unroll
-            for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        rv[jn][i][jj] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, off[jn][i][jj], 0, 0));
-        }
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float v0 = acc[i][jn][4 * jj] + bv[i][jj].x, v1 = acc[i][jn][4 * jj + 1] + bv[i][jj].y;
-                    float v2 = acc[i][jn][4 * jj + 2] + bv[i][jj].z, v3 = acc[i][jn][4 * jj + 3] + bv[i][jj].w;
-                    if constexpr (RES) {
-                        v0 += bf16_bits_to_f32(rv[jn][i][jj].x & 0xffffu);
-                        v1 += bf16_bits_to_f32(rv[jn][i][jj].x >> 16);
-                        v2 += bf16_bits_to_f32(rv[jn][i][jj].y & 0xffffu);
-                        v3 += bf16_bits_to_f32(rv[jn][i][jj].y >> 16);
-                    }
-                    const u32x2 d = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, d), ry, off[jn][i][jj], 0, 0);
-                }
-    };
-
-    const int wstages = nchunks * kstages;
-    for (int64_t it = 0; it < my_tiles; ++it) {
-        const int64_t m0 = (x_begin + loc + it * wg_x) * kBM;
-        // every wave is done with the previous tile's x and w buffers (LDS
-        // reads only: its stores may still be in flight)
+    for (int d = 0; d < kAhead; ++d) {
+        if (d < total) issue_w(d);
+        mark[d] = issued;
+    }
+    // One weight stage: k stage Q of output-channel chunk nc of tile it.  In
+    // the tile's last chunk (LAST) the k-slice Q of x is used for the last
+    // time, and the next tile's is loaded into its registers.
+    auto stage = [&]<int Q, bool LAST>(int64_t gst, int nc, int64_t it) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);   // nothing moves between stages (register pressure)
+        // stage gst landed (this wave's quarter: at most the operations issued
+        // after it are outstanding; every wave's: the barrier), and every wave
+        // is done with the slot the next load refills (it held stage gst - 1)
         compiler_fence();
-        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+        wait_vm_at_most(issued - mark[0]);
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());   // this wave's LDS reads of stage gst - 1 done
         __builtin_amdgcn_s_barrier();
         compiler_fence();
-        issue_x(m0);
-        issue_w(0);
-        for (int st = 0; st < wstages; ++st) {
-            // stage st (and, first, the x tile) landed; buffer (st + 1) & 1
-            // free.  After an epilogue exactly kStores stores follow the
-            // stage's loads.
-            sync(st > 0 && st % kstages == 0);
-            if (st + 1 < wstages) issue_w(st + 1);
-            const int nc = st / kstages, kq = st % kstages;
-            if (kq == 0) {
-                load_bias(nc * kBN);
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+        for (int d = 0; d + 1 < kAhead; ++d) mark[d] = mark[d + 1];
+        if (gst + kAhead < total) issue_w(gst + kAhead);
+        mark[kAhead - 1] = issued;
+
+        if (Q == 0) init_acc(nc * kBN);
+        const unsigned char *ws = lds + (int)(gst % kNBuf) * kPart;
+        // 8 k-steps; the 4 channel blocks' weight fragments are read one
+        // k-step ahead, each feeds both position blocks
+        bf16x8 fa[2][4];
 #pragma unroll
-                    for (int jn = 0; jn < 2; ++jn)
+        for (int i = 0; i < 4; ++i) fa[0][i] = wfrag(ws, 32 * i + l32, 0);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[i][jn][r] = 0.0f;
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < kBK / 16) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fa[cur ^ 1][i] = wfrag(ws, 32 * i + l32, ks + 1);
             }
-            const unsigned char *ws = lds + kXMax + (st & 1) * kPart;
-            // fragments are read one k-step ahead of their MFMAs
-            bf16x8 fa[2][2], fb[2][2];
-            auto load_frags = [&](int ks, int buf) __attribute__((always_inline)) {
-                const int kc = kq * (kBK / 8) + 2 * ks + g;   // x chunk of this k-step
-                fa[buf][0] = wfrag(ws, wm * 64 + l32, ks);
-                fa[buf][1] = wfrag(ws, wm * 64 + 32 + l32, ks);
-                fb[buf][0] = xfrag(wn * 64 + l32, kc);
-                fb[buf][1] = xfrag(wn * 64 + 32 + l32, kc);
-            };
-            load_frags(0, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < kBK / 16; ++ks) {
-                const int cur = ks & 1;
-                if (ks + 1 < kBK / 16) load_frags(ks + 1, cur ^ 1);
-                __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of these MFMAs
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int jn = 0; jn < 2; ++jn)
-                        acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][jn], acc[i][jn], 0, 0, 0);
-            }
-            if (kq + 1 == kstages) store(m0, nc * kBN);
+                for (int jn = 0; jn < 2; ++jn)
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], xf[Q * 8 + ks][jn],
+                                                                         acc[i][jn], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (Q == S - 1) store(tile_m0(it), nc * kBN);
+        if (LAST && it + 1 < my_tiles) load_x(tile_m0(it + 1), Q * 8, Q * 8 + 8);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto chunk = [&]<bool LAST>(int64_t &gst, int nc, int64_t it) __attribute__((always_inline)) {
+        [&]<int... Q>(std::integer_sequence<int, Q...>) {
+            ((stage.template operator()<Q, LAST>(gst + Q, nc, it)), ...);
+        }(std::make_integer_sequence<int, S>{});
+        gst += S;
+    };
+    // The chunks of a tile as three code paths (one when N <= 128, a separate
+    // instantiation): the first (its stages wait
+    // for the x loads still in flight), the middle ones (in a loop that no x
+    // load enters, so no wait for x is placed in it) and the last (which
+    // loads the next tile's x).  With a single loop over all chunks the
+    // compiler would place the waits for x in every stage, and those waits,
+    // which do not see the inline-assembly weight loads, would drain them and
+    // the stores at every stage.
+    int64_t gst = 0;
+    for (int64_t it = 0; it < my_tiles; ++it) {
+        if constexpr (ONE_CHUNK) {
+            chunk.template operator()<true>(gst, 0, it);
+        } else {
+            chunk.template operator()<false>(gst, 0, it);
+            for (int nc = 1; nc + 1 < nchunks; ++nc) chunk.template operator()<false>(gst, nc, it);
+            chunk.template operator()<true>(gst, nchunks - 1, it);
         }
     }
 }
+
 }  // namespace
 
 bool gemm_bf16_tiled_supported(int K, int N) {
-    return K >= kBK && K <= kKMax && K % kBK == 0 && N >= 64 && N % 64 == 0;
+    return K >= kBK && K <= kKMax && K % kBK == 0 && N >= 64 && N % 64 == 0 && N <= kNMax;
 }
 
 hipError_t launch_gemm_bf16_tiled(const void *x, const void *w, const float *bias, const void *res, void *y,
@@ -305,11 +424,19 @@ hipError_t launch_gemm_bf16_tiled(const void *x, const void *w, const float *bia
     const auto *wp = static_cast<const uint16_t *>(w);
     const auto *rp = static_cast<const uint16_t *>(res);
     auto *yp = static_cast<uint16_t *>(y);
-    if (res)
-        gemm_bf16_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(xp, wp, bias, rp, yp, P, N, K, mtiles);
-    else
-        gemm_bf16_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(xp, wp, bias, rp, yp, P, N, K, mtiles);
-    return hipGetLastError();
+    auto go = [&](auto kernel) {
+        kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(xp, wp, bias, rp, yp, P, N, mtiles);
+        return hipGetLastError();
+    };
+    auto by_k = [&](auto one) {
+        constexpr bool ONE = decltype(one)::value;
+        switch (K) {
+            case 128: return res ? go(gemm_bf16_kernel<128, true, ONE>) : go(gemm_bf16_kernel<128, false, ONE>);
+            case 256: return res ? go(gemm_bf16_kernel<256, true, ONE>) : go(gemm_bf16_kernel<256, false, ONE>);
+            default: return res ? go(gemm_bf16_kernel<384, true, ONE>) : go(gemm_bf16_kernel<384, false, ONE>);
+        }
+    };
+    return N <= kBN ? by_k(std::true_type{}) : by_k(std::false_type{});
 }
 
 }  // namespace wanvae
