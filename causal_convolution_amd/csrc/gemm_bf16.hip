@@ -175,15 +175,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
         const int row = 4 * (wave * kWBlocksPerWave + i) + (lane >> 4), cs = lane & 15;
         return (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)((cs ^ (row & 15)) * 16);
     };
-    auto issue_w = [&](int64_t gst) __attribute__((always_inline)) {
+    // source and LDS destination of stage gst's loads; past the last stage
+    // the buffer is empty (its loads write zeros into a slot already consumed)
+    struct WLoad {
+        i32x4 r;
+        uint32_t dst;
+    };
+    auto w_load = [&](int64_t gst) __attribute__((always_inline)) {
         const int st = (int)(gst % per_tile);
         const int nc = st / S, kk = (st % S) * kBK;
         // channels past N (a 64-wide last chunk) fall beyond the buffer's end: zeros
         const int rows = N - nc * kBN < kBN ? N - nc * kBN : kBN;
-        const i32x4 r = buffer_rsrc(w + (int64_t)nc * kBN * K + kk, (uint32_t)(rows * K * 2 - kk * 2));
-        const uint32_t dst = lds_base + (uint32_t)((int)(gst % kNBuf) * kPart + wave * kWBlocksPerWave * 1024);
+        const uint32_t bytes = gst < total ? (uint32_t)(rows * K * 2 - kk * 2) : 0u;
+        return WLoad{buffer_rsrc(w + (int64_t)nc * kBN * K + kk, bytes),
+                     lds_base + (uint32_t)((int)(gst % kNBuf) * kPart + wave * kWBlocksPerWave * 1024)};
+    };
+    auto issue_w = [&](int64_t gst) __attribute__((always_inline)) {
+        const WLoad l = w_load(gst);
 #pragma unroll
-        for (int i = 0; i < kWBlocksPerWave; ++i) lds_dma16(r, dst + i * 1024, w_off(i));
+        for (int i = 0; i < kWBlocksPerWave; ++i) lds_dma16(l.r, l.dst + i * 1024, w_off(i));
         issued += kWBlocksPerWave;
     };
 
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
     int mark[kAhead];
 #pragma unroll
     for (int d = 0; d < kAhead; ++d) {
-        if (d < total) issue_w(d);
+        issue_w(d);
         mark[d] = issued;
     }
     // One weight stage: k stage Q of output-channel chunk nc of tile it.  In
@@ -349,8 +359,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
         compiler_fence();
 #pragma unroll
         for (int d = 0; d + 1 < kAhead; ++d) mark[d] = mark[d + 1];
-        if (gst + kAhead < total) issue_w(gst + kAhead);
-        mark[kAhead - 1] = issued;
+        // stage gst + kAhead's loads go out one per k-step below (issued as a
+        // burst, the four waves' loads queue behind each other on the CU's
+        // texture path while the matrix cores wait)
+        const WLoad wl = w_load(gst + kAhead);
+        static_assert(kWBlocksPerWave == kBK / 16, "one load per k-step");
 
         if (Q == 0) init_acc(nc * kBN);
         const unsigned char *ws = lds + (int)(gst % kNBuf) * kPart;
@@ -366,6 +379,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
 #pragma unroll
                 for (int i = 0; i < 4; ++i) fa[cur ^ 1][i] = wfrag(ws, 32 * i + l32, ks + 1);
             }
+            lds_dma16(wl.r, wl.dst + ks * 1024, w_off(ks));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -375,6 +389,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
                                                                          acc[i][jn], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        issued += kWBlocksPerWave;
+        mark[kAhead - 1] = issued;
         if (Q == S - 1) store(tile_m0(it), nc * kBN);
         if (LAST && it + 1 < my_tiles) load_x(tile_m0(it + 1), Q * 8, Q * 8 + 8);
         __builtin_amdgcn_sched_barrier(0);
@@ -403,6 +419,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
             chunk.template operator()<true>(gst, nchunks - 1, it);
         }
     }
+    // the loads issued past the last stage (into consumed slots) have landed
+    // before the workgroup ends and its LDS is handed on
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 }  // namespace
