@@ -24,8 +24,11 @@
 //    passes it by more than 2^8 in the exponential (lazy rescaling; exact).
 //    It publishes P in LDS, in the consumer's B-operand layout, and, when
 //    the reference moved, the factors that rescale O;
-//  - the consumer keeps O^T for the whole head (D/32 tiles of 32 x 32) and, one
-//    key block behind, rescales it if told to and adds V^T P^T.  A producer
+//  - the consumer keeps O^T for most of the head (D/32 tiles of 32 x 32, all
+//    but the producer's share) and, one key block behind, rescales it if
+//    told to and adds V^T P^T; the producer does the same for its share of
+//    the tiles (a sixth) from its own P, which its lanes already hold in the
+//    B-operand layout.  A producer
 //    lane holds the scores of one query for keys 8j + 4g + i (j, i < 4; g =
 //    lane / 32); taking j = 2ks, 2ks + 1 as MFMA k-step ks, the 8 k values of
 //    lane group g are keys 16ks + 4g + {0..3, 8..11}: the consumer lane reads
@@ -91,6 +94,10 @@ template <int D>
 struct AttnShape {
     static constexpr int KS = D / 16;                   // MFMA k-steps of the score product
     static constexpr int DT = D / 32;                   // O^T tiles
+    // of them, the producer's (the consumer has the rest): the consumer, which
+    // also issues every load, is the longer chain; 2 of 12 measured best at
+    // D = 384 (1 to 3 within 1%, 4 and more slower)
+    static constexpr int PT = DT / 6;
     static constexpr int CPR = D / 8;                   // 16-byte chunks per K row
     static constexpr int KSWZ = CPR < 16 ? CPR - 1 : 15;   // chunk swizzle mask of K rows
     static constexpr int K_BYTES = kBK * D * 2;         // one K block
@@ -208,8 +215,42 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
             }
         }
         float m_run = -INFINITY, l_run = 0.0f;
+        // O^T tiles 0 .. PT - 1 of the group's queries, one key block behind
+        // like the consumer's, from this wave's own P, factor and flag of the
+        // previous block (P is already in the B-operand layout: the consumer
+        // lane reads its twin's P as it is)
+        floatx16 oacc[S::PT > 0 ? S::PT : 1];
+#pragma unroll
+        for (int t = 0; t < S::PT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[t][r] = 0.0f;
+        u32x4 pw0 = u32x4{0u, 0u, 0u, 0u}, pw1 = pw0;
+        float alpha_prev = 1.0f;
+        bool grow_prev = false;
         sync();
         for (int p = 0; p <= nblk; ++p) {
+            if (S::PT > 0 && p >= 1) {
+                const int j = p - 1;
+                if (grow_prev) {
+#pragma unroll
+                    for (int t = 0; t < S::PT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha_prev;
+                }
+                const bf16x8 pf0 = __builtin_bit_cast(bf16x8, pw0);
+                const bf16x8 pf1 = __builtin_bit_cast(bf16x8, pw1);
+                const unsigned char *vs = lds + S::V_OFF + (j & 1) * S::V_BYTES;
+#pragma unroll
+                for (int t = 0; t < S::PT; ++t) {
+                    const int d = 32 * t + l32;
+                    const unsigned char *row = vs + d * (kBK * 2);
+                    const int sw = (d >> 2) & 3;
+                    const bf16x8 v0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + ((0 + g) ^ sw) * 16));
+                    const bf16x8 v1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + ((2 + g) ^ sw) * 16));
+                    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pf0, oacc[t], 0, 0, 0);
+                    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pf1, oacc[t], 0, 0, 0);
+                }
+            }
             if (p < nblk) {
                 const unsigned char *ks = lds + S::K_OFF + (p & 1) * S::K_BYTES;
                 // scores S^T = K q^T: keys as the MFMA rows, this lane's query l32
@@ -241,11 +282,13 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
                 // tracking every increase, about a quarter of the key blocks of a
                 // 90 x 160 frame rescaled O; now almost only the first does.
                 const bool grow = __builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0;
+                grow_prev = grow;
                 if (grow) {
                     const float m_new = fmaxf(m_run, mx);
                     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                     l_run *= alpha;
                     m_run = m_new;
+                    alpha_prev = alpha;
                     if (g == 0) a_buf[(p & 1) * kGroups * 32 + l32] = alpha;
                 }
                 if (lane == 0) f_buf[(p & 1) * kGroups] = grow ? 1 : 0;
@@ -260,8 +303,10 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
                     w[e] = pack_bf16x2(p0, p1);
                 }
                 u32x4 *pp = reinterpret_cast<u32x4 *>(p_buf + (p & 1) * kGroups * S::P_BYTES + lane * 32);
-                pp[0] = u32x4{w[0], w[1], w[2], w[3]};
-                pp[1] = u32x4{w[4], w[5], w[6], w[7]};
+                pw0 = u32x4{w[0], w[1], w[2], w[3]};
+                pw1 = u32x4{w[4], w[5], w[6], w[7]};
+                pp[0] = pw0;
+                pp[1] = pw1;
             }
             sync();
         }
@@ -269,11 +314,27 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
         l_run = halves_sum(l_run);
         if (g == 0) l_buf[l32] = l_run;
         sync();
-    } else {
-        // ---- consumer: O^T (the whole head) for the group's 32 queries
-        floatx16 acc[DT];
+        // o = O / l for this wave's tiles: d = 32 t + 8 jj + 4 g + i
+        const int q = q0 + l32;
+        if (S::PT > 0 && q < HW) {
+            const float inv = 1.0f / l_run;
+            uint16_t *orow = o + (f * (int64_t)HW + q) * D;
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+            for (int t = 0; t < S::PT; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float v0 = oacc[t][4 * jj], v1 = oacc[t][4 * jj + 1];
+                    const float v2 = oacc[t][4 * jj + 2], v3 = oacc[t][4 * jj + 3];
+                    *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * jj + 4 * g) =
+                        u32x2{pack_bf16x2(v0 * inv, v1 * inv), pack_bf16x2(v2 * inv, v3 * inv)};
+                }
+        }
+    } else {
+        // ---- consumer: O^T tiles PT .. DT - 1 for the group's 32 queries
+        constexpr int CT = DT - S::PT;
+        floatx16 acc[CT];
+#pragma unroll
+        for (int t = 0; t < CT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
         issue_k(0);
@@ -286,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
                 if (f_buf[(j & 1) * kGroups] != 0) {
                     const float alpha = a_buf[(j & 1) * kGroups * 32 + l32];
 #pragma unroll
-                    for (int t = 0; t < DT; ++t)
+                    for (int t = 0; t < CT; ++t)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
                 }
@@ -298,8 +359,8 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
                 // chunk 2 ks + g of the 64-byte row, swizzled by (d >> 2) & 3
                 const unsigned char *vs = lds + S::V_OFF + (j & 1) * S::V_BYTES;
 #pragma unroll
-                for (int t = 0; t < DT; ++t) {
-                    const int d = 32 * t + l32;
+                for (int t = 0; t < CT; ++t) {
+                    const int d = 32 * (S::PT + t) + l32;
                     const unsigned char *row = vs + d * (kBK * 2);
                     const int sw = (d >> 2) & 3;
                     const bf16x8 v0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(row + ((0 + g) ^ sw) * 16));
@@ -317,12 +378,12 @@ __global__ __launch_bounds__(kThreads) void flash_attention_kernel(const uint16_
             const float inv = 1.0f / l_buf[l32];
             uint16_t *orow = o + (f * (int64_t)HW + q) * D;
 #pragma unroll
-            for (int t = 0; t < DT; ++t)
+            for (int t = 0; t < CT; ++t)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const float v0 = acc[t][4 * jj], v1 = acc[t][4 * jj + 1];
                     const float v2 = acc[t][4 * jj + 2], v3 = acc[t][4 * jj + 3];
-                    *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * jj + 4 * g) =
+                    *reinterpret_cast<u32x2 *>(orow + 32 * (S::PT + t) + 8 * jj + 4 * g) =
                         u32x2{pack_bf16x2(v0 * inv, v1 * inv), pack_bf16x2(v2 * inv, v3 * inv)};
                 }
         }
