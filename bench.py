@@ -154,15 +154,22 @@ def head_tail(torch, wv, steps, warmup):
             "steps": steps, "warmup": warmup, "ops": time_ops(torch, wv, ops, steps, warmup)}
 
 
-def time_ops(torch, wv, ops, steps, warmup):
+def time_ops(torch, wv, ops, steps, warmup, min_warm_s=0.05):
     """Per op (name, kernel kind, launch, FLOPs, bytes): `warmup` untimed
-    launches, then the library's hipEvent timing over `steps` launches; the
-    bound is the larger of FLOPs / 2.5 PFLOP/s and bytes / 8 TB/s."""
+    launches, and more until `min_warm_s` seconds of them have run (a launch
+    of about a millisecond right after input generation otherwise meets a
+    clock still ramping up), then the library's hipEvent timing over `steps`
+    launches; the bound is the larger of FLOPs / 2.5 PFLOP/s and bytes /
+    8 TB/s."""
     res = []
     for name, kind, fn, flop, nbytes in ops:
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < min_warm_s:
+            fn()
+            torch.cuda.synchronize()
         wv.timing_reset()
         wv.timing_enable(True)
         for _ in range(steps):
