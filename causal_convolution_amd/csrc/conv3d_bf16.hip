@@ -59,6 +59,10 @@
 // refilled once every MFMA wave has consumed the stage it held.  MFMA waves
 // thus drift apart by up to a few stages, which spreads their LDS read bursts
 // instead of lining them up behind a barrier.  Every wait on a flag is bounded.
+// With one MFMA wave per SIMD nothing hides a stage's first LDS round trip, so
+// each stage reads the next one's first operands during its last rows (when
+// that stage has landed), and every row's fragment reads are issued one per
+// MFMA rather than as a burst.
 //
 // LDS layout: 32-byte units (16 bf16 channels of one position or one weight
 // row), A tile rows 34 units apart.  The two 16-byte halves of a unit are
