@@ -564,7 +564,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // alternates from stage to stage.
     bf16x8 fw[9][FN];
     bf16x8 fx[2][3];
-    constexpr bool ALT = NROW % 2 == 1;
+    constexpr bool ALT = (TL::KH_OUTER ? 3 * FM : NROW) % 2 == 1;   // rows per stage odd
     // row 0 and the kh = 0 weights of the stage in `buf` (parity par)
     auto load_first = [&](const unsigned char *buf, int par) __attribute__((always_inline)) {
         if (par) {
@@ -666,55 +666,64 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     };
 
     // The same stage for KH_OUTER tiles: for each kh, the 3 kw x FN weight
-    // fragments of that kernel row, then each output row fm with input row
-    // fm + kh.  The next input row is read while the current one computes,
-    // and the weights of kh + 1 replace those of kh, kw by kw, during the last
-    // row of kh.
-    auto compute_conv_kh = [&](const unsigned char *buf) __attribute__((always_inline)) {
-        bf16x8 fw[3][FN];
-        bf16x8 fx[2][3];
-#pragma unroll
-        for (int kw = 0; kw < 3; ++kw) fx[0][kw] = ldA(buf, 0, kw);
-#pragma unroll
-        for (int kw = 0; kw < 3; ++kw)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) fw[kw][fn] = ldB(buf, kw, fn);
+    // fragments of that kernel row (in fw[0..2]), then each output row fm
+    // with input row fm + kh.  The next input row is read while the current
+    // one computes, and the weights of kh + 1 replace those of kh, kw by kw,
+    // during the last row of kh.  The last row of kh = 2 reads, in the same
+    // way, the following ring slot's row 0 and kh = 0 weights, unconditionally
+    // as in the row-stationary stage; rows run r = kh * FM + fm, row r in
+    // fx[(r + PAR) & 1].
+    auto compute_conv_kh = [&]<int PAR>(const unsigned char *buf, const unsigned char *next)
+                               __attribute__((always_inline)) {
+        bool landed = false;
+        int early = 0;
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                const int cur = (kh * FM + fm) & 1;
+                const int r = kh * FM + fm;
+                const int cur = (r + PAR) & 1;
                 const bool last_row = fm + 1 == FM;
-                if (!(kh == 2 && last_row)) {
-                    const int nr = last_row ? kh + 1 : fm + 1 + kh;   // next iteration's input row
-#pragma unroll
-                    for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(buf, nr, kw);
+                const bool final_row = kh == 2 && last_row;
+                if (r == 1) early = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
+                if (final_row) {
+                    const int f = __builtin_amdgcn_readfirstlane(early);
+                    seen = f > seen ? f : seen;
+                    landed = seen > consumed + 1;
                 }
+                // next row: input row fm + 1 + kh, the first row of kh + 1, or the next slot's row 0
+                const unsigned char *rb = final_row ? next : buf;
+                const int nr = final_row ? 0 : last_row ? kh + 1 : fm + 1 + kh;
+#pragma unroll
+                for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(rb, nr, kw);
 #pragma unroll
                 for (int kw = 0; kw < 3; ++kw) {
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
                         acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kw][fn], fx[cur][kw],
                                                                               acc[fm][fn], 0, 0, 0);
-                    if (last_row && kh < 2) {
+                    if (last_row) {
+                        const unsigned char *wb = kh < 2 ? buf : next;
+                        const int tap = kh < 2 ? (kh + 1) * 3 + kw : kw;
 #pragma unroll
-                        for (int fn = 0; fn < FN; ++fn) fw[kw][fn] = ldB(buf, (kh + 1) * 3 + kw, fn);
+                        for (int fn = 0; fn < FN; ++fn) fw[kw][fn] = ldB(wb, tap, fn);
                     }
                 }
                 // LDS reads one after each MFMA, as in the row-stationary stage
                 constexpr int nm = 3 * FN;
-                const int nr = (kh == 2 && last_row ? 0 : 3) + (last_row && kh < 2 ? 3 * FN : 0);
+                const int nrd = 3 + (last_row ? 3 * FN : 0) + (r == 1 ? 1 : 0);
 #pragma unroll
                 for (int k = 0; k < 9; ++k) {
-                    if (k < nr && k < nm) {
+                    if (k < nrd && k < nm) {
                         sched_group<kSchedMfma>(1);
                         sched_group<kSchedDsRead>(1);
                     }
                 }
-                if (nr > nm) sched_group<kSchedDsRead>(nr - nm);
-                if (nm > nr) sched_group<kSchedMfma>(nm - nr);
+                if (nrd > nm) sched_group<kSchedDsRead>(nrd - nm);
+                if (nm > nrd) sched_group<kSchedMfma>(nm - nrd);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        return landed;
     };
 
     // One shortcut stage: SCS slices of 16 channels, each x at this wave's
@@ -766,6 +775,21 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             i += wg_x;
         }
 
+        // A tile's first stage reads its own operands: marking the carried
+        // ones undefined here keeps them from being held across the epilogue
+        // (which the KH_OUTER tiles' identity epilogue has no registers for).
+        if constexpr (TL::KH_OUTER) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                fx[0][j] = __builtin_nondeterministic_value(fx[0][j]);
+                fx[1][j] = __builtin_nondeterministic_value(fx[1][j]);
+            }
+#pragma unroll
+            for (int tap = 0; tap < 3; ++tap)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) fw[tap][fn] = __builtin_nondeterministic_value(fw[tap][fn]);
+        }
+
         // the accumulators start at the bias (+ shortcut bias) of their
         // channels: accumulator element 4j + q of channel block fn is
         // channel 8j + 4g + q of the block
@@ -785,13 +809,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = b0;
         }
 
-        if constexpr (TL::KH_OUTER) {
-            for (int s = 0; s < ti.s_conv; ++s) {
-                wait_landed();
-                compute_conv_kh(smem + slot * TL::STAGE_BYTES);
-                release();
-            }
-        } else {
+        {
             // Stages run in pairs of parity 0 and 1 (straight-line code, so
             // both use the same registers), a tile's first stage with parity
             // 0.  The next stage's operands are kept when it is a conv stage
@@ -805,7 +823,11 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     load_first(cur, PAR);
                 }
                 const unsigned char *nxt = smem + (slot + 1 == NBUF ? 0 : slot + 1) * TL::STAGE_BYTES;
-                const bool landed = compute_conv.template operator()<PAR>(cur, nxt);
+                bool landed;
+                if constexpr (TL::KH_OUTER)
+                    landed = compute_conv_kh.template operator()<PAR>(cur, nxt);
+                else
+                    landed = compute_conv.template operator()<PAR>(cur, nxt);
                 preloaded = !SC && more && landed;
                 release();
             };
