@@ -947,10 +947,11 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             load_group(0);
             if (NG > 1) load_group(1);
             // group GI has landed once at most the VMEM operations issued
-            // after its loads are outstanding: the stores of group GI - 1 and
-            // the loads of group GI + 1 (an immediate, hence the template)
+            // after its loads are outstanding: the stores of group GI - 1 (2
+            // per row and channel block) and the loads of group GI + 1 (4 per
+            // row and channel block); an immediate, hence the template
             auto step = [&]<int GI>() __attribute__((always_inline)) {
-                constexpr int kAfter = (GI >= 1 ? group_rows<FM, EG>(GI - 1) * FN * 4 : 0) +
+                constexpr int kAfter = (GI >= 1 ? group_rows<FM, EG>(GI - 1) * FN * 2 : 0) +
                                        (GI + 1 < NG ? group_rows<FM, EG>(GI + 1) * FN * 4 : 0);
                 static_assert(kAfter <= 63, "vmcnt counts to 63");
                 compiler_fence();
