@@ -96,6 +96,8 @@ CONV_SHAPES = [
     # C_out a multiple of 96 but not 64: 12-row tiles of 96 channels
     (1, 2, 13, 40, 96, 288),     # 3 channel blocks, ragged H (13 = 12 + 1) and W
     (1, 3, 24, 32, 32, 96),      # exact tiles, smallest input slice count
+    (1, 3, 14, 40, 48, 96),      # 3 input slices: odd stage counts (9 with a cache) end on a lone stage
+    (2, 4, 13, 33, 112, 288),    # 7 input slices, 3 channel blocks, batch 2, ragged H and W
     # the decoder's head and tail: 16 latent channels in (conv_in), 3 out (conv_out)
     (1, 3, 10, 40, 16, 384),     # one 16-channel stage per temporal tap
     (1, 3, 12, 40, 96, 3),       # C_out padded to one 32-channel block, 2-byte stores
