@@ -852,18 +852,11 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // Branch-free: residual loads and output stores are raw buffer
         // accesses over this frame, and a position outside the image gets an
         // out-of-range offset (its load returns zero, its store is dropped).
-        // The identity residual is fetched two rows at a time, one group ahead
-        // of the stores, with exact vmcnt waits.
+        // The identity residual is fetched in row groups (two rows, or one
+        // with 96-channel tiles), one group ahead of the stores, with exact
+        // vmcnt waits, in the stores' whole-line layout.
         const int64_t frame = ti.nq * a.T + ti.tq;
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y + frame * HW * a.cout, HW * a.cout * 2);
-        const int cbase = ti.n0 + wn * FN * 32 + 4 * g;   // this lane's first channel
-        // Offsets split into a wave-uniform row part (valid or not for the
-        // whole wave) and a per-lane column part fixed for the tile.
-        auto pos_off = [&](int fm, int cstride) __attribute__((always_inline)) -> uint32_t {
-            const int hh = ti.h0 + wm * FM + fm, ww = ti.w0 + l32;
-            return hh < H && ww < W ? (uint32_t)(hh * W * cstride) * 2 + (uint32_t)(ww * cstride + cbase) * 2
-                                    : kOOB;
-        };
         // store pieces: position p = lane / 4 + 16 half, 16-byte quarter lane % 4
         uint32_t col_off[2];
 #pragma unroll
@@ -884,19 +877,29 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // multiples of 64 or 96, the residual epilogues multiples of 32).
         constexpr bool CAN_NARROW = EPI == EPI_BIAS && NB == 32;
         const bool narrow = CAN_NARROW && ((a.cout & 7) != 0 || ti.n0 + NB > a.cout);
-        auto store_rows = [&](int f0, int nrows, const u32x2 (*res)[FN][4]) __attribute__((always_inline)) {
+        // res: the residual of these rows as loaded, in the store layout
+        // (16 bytes per lane, per row, channel block and half); it goes
+        // through the staging buffer into the accumulator layout.
+        auto store_rows = [&](int f0, int nrows, const u32x4 (*res)[FN][2]) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < nrows; ++e) {
                 const int hh = ti.h0 + wm * FM + f0 + e;
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
+                    if (res != nullptr) {
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int p = (lane >> 2) + 16 * half, qq = lane & 3;
+                            *reinterpret_cast<u32x4 *>(epi + p * kEpiStride + qq * 16) = res[e][fn][half];
+                        }
+                    }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         float v[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) v[q] = acc[f0 + e][fn][4 * j + q];
                         if (res != nullptr) {
-                            const u32x2 r = res[e][fn][j];
+                            const u32x2 r = *reinterpret_cast<const u32x2 *>(epi + l32 * kEpiStride + j * 16 + g * 8);
                             v[0] += bf16_bits_to_f32(r.x & 0xffffu);
                             v[1] += bf16_bits_to_f32(r.x >> 16);
                             v[2] += bf16_bits_to_f32(r.y & 0xffffu);
@@ -932,27 +935,39 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             constexpr int EG = FN > 1 ? 1 : 2;             // rows per residual group (registers)
             constexpr int NG = (FM + EG - 1) / EG;
             const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.res + frame * HW * a.cres, HW * a.cres * 2);
-            u32x2 rv[2][EG][FN][4];
+            // residual pieces as the stores write them: position
+            // lane / 4 + 16 half, 16-byte quarter lane % 4 (64 contiguous
+            // bytes per position and channel block)
+            u32x4 rv[2][EG][FN][2];
+            uint32_t rcol[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int ww = ti.w0 + (lane >> 2) + 16 * half;
+                rcol[half] = ww < W ? (uint32_t)(ww * a.cres + ti.n0 + wn * FN * 32) * 2 + (lane & 3) * 16 : kOOB;
+            }
             auto load_group = [&](int gi) __attribute__((always_inline)) {
 #pragma unroll
                 for (int e = 0; e < group_rows<FM, EG>(gi); ++e) {
-                    const uint32_t off = pos_off(gi * EG + e, a.cres);
+                    const int hh = ti.h0 + wm * FM + gi * EG + e;
+                    const uint32_t rrow = (uint32_t)(hh * W * a.cres) * 2;
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            rv[gi & 1][e][fn][j] = __builtin_amdgcn_raw_buffer_load_b64(rr, off + fn * 64 + j * 16, 0, 0);
+                        for (int half = 0; half < 2; ++half) {
+                            const uint32_t off = hh < H && rcol[half] != kOOB ? rrow + fn * 64 + rcol[half] : kOOB;
+                            rv[gi & 1][e][fn][half] = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0);
+                        }
                 }
             };
             load_group(0);
             if (NG > 1) load_group(1);
             // group GI has landed once at most the VMEM operations issued
-            // after its loads are outstanding: the stores of group GI - 1 (2
-            // per row and channel block) and the loads of group GI + 1 (4 per
-            // row and channel block); an immediate, hence the template
+            // after its loads are outstanding: the stores of group GI - 1 and
+            // the loads of group GI + 1 (2 each per row and channel block); an
+            // immediate, hence the template
             auto step = [&]<int GI>() __attribute__((always_inline)) {
                 constexpr int kAfter = (GI >= 1 ? group_rows<FM, EG>(GI - 1) * FN * 2 : 0) +
-                                       (GI + 1 < NG ? group_rows<FM, EG>(GI + 1) * FN * 4 : 0);
+                                       (GI + 1 < NG ? group_rows<FM, EG>(GI + 1) * FN * 2 : 0);
                 static_assert(kAfter <= 63, "vmcnt counts to 63");
                 compiler_fence();
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAfter));
