@@ -59,12 +59,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kWBlocksPerWave = kPart / 1024 / kWaves;   // 8
 constexpr int kXCD = 8;
-constexpr int kStores = 2 * 4 * 4;             // stores (and residual loads) per lane in a residual epilogue
-// Without a residual the epilogue goes through LDS: per wave, 32 positions x
-// 64 channels of bf16 at a time (rows kStageRow bytes apart), read back as 8
-// lanes x 16 bytes per position, so a store writes 8 whole 128-byte rows.
+// The epilogue goes through LDS: per wave, 32 positions x 64 channels of
+// bf16 at a time (rows kStageRow bytes apart), read back as 8 lanes x 16
+// bytes per position, so a store writes 8 whole 128-byte rows (and a residual
+// is loaded the same way).
 constexpr int kStageRow = 144;
-constexpr int kStagedStores = 2 * 2 * 4;       // stores per lane in such an epilogue
+constexpr int kStagedStores = 2 * 2 * 4;       // stores (and residual loads) per lane in an epilogue
 constexpr int kBufFlags = 0x00020000;          // raw buffer: loads past num_records return zeros
 constexpr uint32_t kOOB = 0x80000000u;
 static_assert(kNBuf * kPart + kNMax * 4 + kWaves * 32 * kStageRow <= 160 * 1024, "LDS");
@@ -247,86 +247,70 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const uint16_t *__r
     auto store = [&](int64_t m0, int n0) __attribute__((always_inline)) {
         const int64_t rows = P - m0 < kBM ? P - m0 : kBM;
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + m0 * N, (uint32_t)(rows * N * 2));
-        if constexpr (!RES) {
-            // through this wave's LDS staging rows, 32 positions x 64 channels
-            // (channel half h of the chunk) at a time.  The lane index is made
-            // opaque here so that the addresses are computed in place instead
-            // of being hoisted out of the stage loop into registers that the
-            // x fragments need.
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int lq = ln & 31, gq = ln >> 5;
-            unsigned char *stg = ostage + wave * 32 * kStageRow;
+        // Through this wave's LDS staging rows, 32 positions x 64 channels
+        // (channel half h of the chunk) at a time: written in the
+        // accumulator layout, stored as 16 bytes per lane, 128 contiguous
+        // bytes per position.  A residual is loaded in that store layout,
+        // all of it before the first store (a load behind a store would wait
+        // for it), and reaches the accumulator layout through the same rows,
+        // so the output keeps its single rounding.  The lane index is made
+        // opaque so that the addresses are computed in place instead of being
+        // hoisted out of the stage loop into registers that the x fragments
+        // need.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lq = ln & 31, gq = ln >> 5;
+        unsigned char *stg = ostage + wave * 32 * kStageRow;
+        // piece r of (position block jn, channel half h): position (ln >> 3) + 8 r, 16-byte part ln & 7
+        auto piece_off = [&](int jn, int h, int r) __attribute__((always_inline)) -> uint32_t {
+            const int pl = wave * 64 + 32 * jn + (ln >> 3) + 8 * r;
+            return pl < rows && n0 + 64 * h < N ? (uint32_t)((pl * N + n0 + 64 * h + 8 * (ln & 7)) * 2) : kOOB;
+        };
+        [[maybe_unused]] u32x4 rq[RES ? 2 : 1][2][4];
+        if constexpr (RES) {
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(res + m0 * N, (uint32_t)(rows * N * 2));
 #pragma unroll
             for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i2 = 0; i2 < 2; ++i2)
+                    for (int r = 0; r < 4; ++r)
+                        rq[jn][h][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, piece_off(jn, h, r), 0, 0));
+            issued += kStagedStores;   // as many loads as stores
+        }
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            const floatx16 &a = acc[2 * h + i2][jn];
-                            *reinterpret_cast<u32x2 *>(stg + lq * kStageRow + (32 * i2 + 8 * jj + 4 * gq) * 2) =
-                                u32x2{pack_bf16x2(a[4 * jj], a[4 * jj + 1]), pack_bf16x2(a[4 * jj + 2], a[4 * jj + 3])};
+        for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if constexpr (RES) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        *reinterpret_cast<u32x4 *>(stg + ((ln >> 3) + 8 * r) * kStageRow + (ln & 7) * 16) = rq[jn][h][r];
+                }
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const floatx16 &a = acc[2 * h + i2][jn];
+                        u32x2 *slot = reinterpret_cast<u32x2 *>(stg + lq * kStageRow + (32 * i2 + 8 * jj + 4 * gq) * 2);
+                        float v0 = a[4 * jj], v1 = a[4 * jj + 1], v2 = a[4 * jj + 2], v3 = a[4 * jj + 3];
+                        if constexpr (RES) {
+                            const u32x2 rv = *slot;
+                            v0 += bf16_bits_to_f32(rv.x & 0xffffu);
+                            v1 += bf16_bits_to_f32(rv.x >> 16);
+                            v2 += bf16_bits_to_f32(rv.y & 0xffffu);
+                            v3 += bf16_bits_to_f32(rv.y >> 16);
                         }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int p = (ln >> 3) + 8 * r, q = ln & 7;
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + p * kStageRow + q * 16);
-                        const int pl = wave * 64 + 32 * jn + p;
-                        const uint32_t off = pl < rows && n0 + 64 * h < N
-                                                 ? (uint32_t)((pl * N + n0 + 64 * h + 8 * q) * 2)
-                                                 : kOOB;
-                        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+                        *slot = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
                     }
-                    __builtin_amdgcn_sched_barrier(0);   // one unit's values live at a time
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + ((ln >> 3) + 8 * r) * kStageRow + (ln & 7) * 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, piece_off(jn, h, r), 0, 0);
                 }
-            issued += kStagedStores;
-            return;
-        }
-        // with the residual: 8-byte pieces straight from the accumulators,
-        // the residual's pieces all requested before the first store (a load
-        // behind a store would wait for it)
-        const __amdgpu_buffer_rsrc_t rr = make_rsrc(RES ? res + m0 * N : y, RES ? (uint32_t)(rows * N * 2) : 0u);
-        // position part per position block (per lane), channel part per
-        // channel block (uniform: a 64-wide last chunk has blocks past N)
-        uint32_t poff[2];
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn) {
-            const int pl = wave * 64 + 32 * jn + l32;   // position within the tile
-            poff[jn] = pl < rows ? (uint32_t)((pl * N + n0 + 4 * g) * 2) : kOOB;
-        }
-        auto off = [&](int jn, int i, int jj) __attribute__((always_inline)) -> uint32_t {
-            return poff[jn] != kOOB && n0 + 32 * i < N ? poff[jn] + (uint32_t)((32 * i + 8 * jj) * 2) : kOOB;
-        };
-        u32x2 rv[2][4][4];
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    rv[jn][i][jj] =
-                        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, off(jn, i, jj), 0, 0));
-        issued += kStores;
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float v0 = acc[i][jn][4 * jj], v1 = acc[i][jn][4 * jj + 1];
-                    float v2 = acc[i][jn][4 * jj + 2], v3 = acc[i][jn][4 * jj + 3];
-                    v0 += bf16_bits_to_f32(rv[jn][i][jj].x & 0xffffu);
-                    v1 += bf16_bits_to_f32(rv[jn][i][jj].x >> 16);
-                    v2 += bf16_bits_to_f32(rv[jn][i][jj].y & 0xffffu);
-                    v3 += bf16_bits_to_f32(rv[jn][i][jj].y >> 16);
-                    const u32x2 d = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, d), ry,
-                        off(jn, i, jj), 0, 0);
-                }
-        issued += kStores;
+                __builtin_amdgcn_sched_barrier(0);   // one unit's values live at a time
+            }
+        issued += kStagedStores;
     };
 
     // weight fragment: row `row` of a stage, k-step ks (k = 16 ks + 8 g .. +7)
