@@ -74,6 +74,9 @@ EXPORTS = {
                                              C.c_void_p]),
     "wanvae_packed_conv2d_weight_elems": (C.c_int, [C.c_int32, C.c_int32, C.c_int32,
                                                     C.POINTER(C.c_int64)]),
+    "wanvae_wait_giveups": (C.c_int, [C.POINTER(C.c_uint64)]),
+    "wanvae_wait_giveups_reset": (C.c_int, []),
+    "wanvae_set_wait_bound": (C.c_int, [C.c_int32]),
     "wanvae_last_error": (C.c_char_p, []),
     "wanvae_timing_enable": (C.c_int, [C.c_int]),
     "wanvae_timing_reset": (C.c_int, []),
@@ -447,6 +450,25 @@ class AttentionBlock:
         _check(lib().wanvae_attention_block(C.byref(self.c), _ptr(x), _ptr(y), C.byref(d), _ptr(ws),
                                             ws.numel() * ws.element_size(), _stream(stream)))
         return y
+
+
+def wait_giveups() -> int:
+    """Bounded flag waits of the conv kernels that gave up on the current
+    device since load or the last reset (``wanvae_wait_giveups``; waits for
+    the device to go idle).  Zero when every launch kept its protocol."""
+    n = C.c_uint64(0)
+    _check(lib().wanvae_wait_giveups(C.byref(n)))
+    return n.value
+
+
+def wait_giveups_reset():
+    _check(lib().wanvae_wait_giveups_reset())
+
+
+def set_wait_bound(polls: int):
+    """Polls before a flag wait gives up, for later launches; negative
+    restores the default (``wanvae_set_wait_bound``; a test hook)."""
+    _check(lib().wanvae_set_wait_bound(int(polls)))
 
 
 def timing_enable(on: bool = True):

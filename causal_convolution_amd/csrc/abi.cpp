@@ -78,6 +78,9 @@ std::mutex g_tm_mu;
 bool g_timing = false;
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_pool;
+// Records kept at most: past this many, launches go untimed until the next
+// reset (a caller that enables timing and never resets holds bounded state).
+constexpr size_t kMaxTimingRecs = 1 << 16;
 
 hipEvent_t take_event() {
     if (!g_pool.empty()) {
@@ -96,7 +99,7 @@ int timed_launch(int kind, hipStream_t s, const char *what, F &&launch) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     {
         std::lock_guard<std::mutex> lk(g_tm_mu);
-        if (g_timing) {
+        if (g_timing && g_recs.size() < kMaxTimingRecs) {
             e0 = take_event();
             e1 = take_event();
         }
@@ -267,6 +270,9 @@ int check_block_buffers(const wanvae_resblock_params *p, const Plan &pl, const v
     (void)p;
     return WANVAE_OK;
 }
+
+int forward_planned(const wanvae_resblock_params *p, const Plan &pl, const void *x, void *y,
+                    const wanvae_dims *d, void *workspace, hipStream_t s);
 
 }  // namespace
 
@@ -466,7 +472,36 @@ int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void
     if (int r = plan_block(p, d, &pl)) return r;
     if (pl.P == 0) return WANVAE_OK;
     if (int r = check_block_buffers(p, pl, x, y, workspace, ws_bytes)) return r;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return forward_planned(p, pl, x, y, d, workspace, static_cast<hipStream_t>(stream));
+}
+
+int wanvae_wait_giveups(uint64_t *count) {
+    g_error.clear();
+    WV_CHECK(count != nullptr, WANVAE_ERR_NULL, "count is NULL");
+    const hipError_t e = wanvae::read_wait_giveups(count);
+    if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "reading the wait give-up count: %s", hipGetErrorString(e));
+    return WANVAE_OK;
+}
+
+int wanvae_wait_giveups_reset(void) {
+    g_error.clear();
+    const hipError_t e = wanvae::reset_wait_giveups();
+    if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "resetting the wait give-up count: %s", hipGetErrorString(e));
+    return WANVAE_OK;
+}
+
+int wanvae_set_wait_bound(int32_t polls) {
+    g_error.clear();
+    wanvae::set_wait_bound(polls);
+    return WANVAE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+// The block's four (or five) launches once plan and buffers are checked.
+int forward_planned(const wanvae_resblock_params *p, const Plan &pl, const void *x, void *y,
+                    const wanvae_dims *d, void *workspace, hipStream_t s) {
     char *ws = static_cast<char *>(workspace);
     void *n1 = ws + pl.n_off;
     void *a = ws + pl.a_off;
@@ -501,6 +536,9 @@ int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void
     if (int r = setup_residual(p, x, pl.P, a, &cb, s)) return r;
     return run_conv(cb, p->dtype, s);
 }
+}  // namespace
+
+extern "C" {
 
 int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_chunk,
                                 void *y_chunk, const wanvae_dims *d, void *cache_a, void *cache_b,

@@ -58,7 +58,9 @@
 // landed, each MFMA wave publishes how many it has consumed, and a slot is
 // refilled once every MFMA wave has consumed the stage it held.  MFMA waves
 // thus drift apart by up to a few stages, which spreads their LDS read bursts
-// instead of lining them up behind a barrier.  Every wait on a flag is bounded.
+// instead of lining them up behind a barrier.  Every wait on a flag is bounded;
+// a wait that reaches its bound goes on and is counted (g_wait_giveups), so a
+// stalled protocol shows up as a non-zero count instead of a hang.
 // With one MFMA wave per SIMD nothing hides a stage's first LDS round trip, so
 // each stage reads the next one's first operands during its last rows (when
 // that stage has landed), and every row's fragment reads are issued one per
@@ -125,10 +127,13 @@ constexpr int kSyncBytes = 256;  // LDS for the stage flags
 // writes of 16 lanes over distinct bank groups)
 constexpr int kEpiStride = 80;
 constexpr int kEpiBytes = 32 * kEpiStride;
-// Bound on every flag wait: 2^15 polls ~64 cycles apart (about 2M cycles, far
-// beyond any real wait); past it the wave goes on, so a broken protocol can
-// only give wrong results, never a hung kernel.
-constexpr int kSpinCap = 1 << 15;
+// Default bound on every flag wait: 2^15 polls ~64 cycles apart (about 2M
+// cycles, far beyond any real wait).  Past it the wave goes on rather than
+// hang, and counts the event in g_wait_giveups: the stage it then reads (or
+// the slot it refills) may not be the one the protocol meant, so the launch's
+// output is suspect.  The bound is a kernel argument (set_wait_bound) so that
+// a test can force the give-up path from the host.
+constexpr int kSpinCapDefault = 1 << 15;
 
 // s_waitcnt immediate for "vmcnt <= n" (n <= 63), other counters left alone
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -169,6 +174,8 @@ struct Args {
     // image is x[h/2][w/2]); only the current frame's taps, packed weight
     // [cin/16][9 taps][cout][16]; no cache
     int up2;
+    // polls before a flag wait gives up (and is counted)
+    int spin_cap;
 };
 
 // One output tile: batch item, frame, first row / column / output channel,
@@ -261,6 +268,18 @@ __device__ inline uint32_t lds_address(const unsigned char *p) {
 
 // compiler-only fence: no memory access moves across it
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
+}  // namespace
+
+// Flag waits that reached their bound, per device, since the library was
+// loaded or the count was last reset (a vector atomic by one lane per event).
+__device__ unsigned int g_wait_giveups;
+
+namespace {
+
+__device__ inline void count_giveup(int lane) {
+    if (lane == 0) __hip_atomic_fetch_add(&g_wait_giveups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int WM, int WN, int FM, int FN, int EPI, bool SC>
 __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) {
@@ -520,12 +539,15 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             }
             if (it >= x_count) break;   // everything requested has landed and been published
             // every slot holds a published, unconsumed stage: wait for the slowest wave
-            for (int spin = 0; spin < kSpinCap; ++spin) {
+            for (int spin = 0; spin < a.spin_cap; ++spin) {
                 __builtin_amdgcn_s_sleep(1);
                 done = min_done();
                 if (issued < done + NBUF) break;
             }
-            if (issued >= done + NBUF) done = issued - NBUF + 1;   // bound reached: go on
+            if (issued >= done + NBUF) {   // bound reached: go on, and say so
+                done = issued - NBUF + 1;
+                count_giveup(lane);
+            }
         }
         return;
     }
@@ -583,10 +605,11 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     int consumed = 0, seen = 0, slot = 0;
     // wait until stage `consumed` has landed
     auto wait_landed = [&]() __attribute__((always_inline)) {
-        for (int spin = 0; seen <= consumed && spin < kSpinCap; ++spin) {
+        for (int spin = 0; seen <= consumed && spin < a.spin_cap; ++spin) {
             seen = flag_read(0);
             if (seen <= consumed) __builtin_amdgcn_s_sleep(1);
         }
+        if (seen <= consumed) count_giveup(lane);   // bound reached: go on, and say so
         compiler_fence();   // the stage's reads stay below the flag read
     };
 
@@ -986,6 +1009,28 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
 }  // namespace
 
+namespace {
+std::atomic<int> g_spin_cap{kSpinCapDefault};
+}  // namespace
+
+void set_wait_bound(int polls) { g_spin_cap.store(polls < 0 ? kSpinCapDefault : polls, std::memory_order_relaxed); }
+
+hipError_t read_wait_giveups(uint64_t *count) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    unsigned int v = 0;
+    e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_wait_giveups), sizeof v, 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) *count = v;
+    return e;
+}
+
+hipError_t reset_wait_giveups() {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    const unsigned int zero = 0;
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_wait_giveups), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+}
+
 // Compute units of the current device (cached per device; also used by the
 // other persistent kernels).
 hipError_t device_cu_count(int *out) {
@@ -1034,6 +1079,7 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.x_sliced = c.x_sliced ? 1 : 0;
     a.gemm = c.gemm ? 1 : 0;
     a.up2 = c.up2 ? 1 : 0;
+    a.spin_cap = g_spin_cap.load(std::memory_order_relaxed);
     a.sc_in = static_cast<const uint16_t *>(c.gemm ? c.x : c.res);
     a.sc_c = c.gemm ? c.cin : c.cres;
     if (c.gemm) a.wsc = static_cast<const uint16_t *>(c.w);

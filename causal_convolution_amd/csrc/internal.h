@@ -64,6 +64,13 @@ bool conv3d_narrow_supported(const ConvLaunch &c);
 hipError_t launch_conv3d_narrow(const ConvLaunch &c, hipStream_t s);
 hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
 
+// Bounded flag waits of the bf16 conv: polls per wait before it gives up
+// (negative: the default), and the per-device count of waits that gave up
+// (read and reset wait for the device to go idle first).
+void set_wait_bound(int polls);
+hipError_t read_wait_giveups(uint64_t *count);
+hipError_t reset_wait_giveups();
+
 // Channel GEMM over positions (a pointwise projection) on the conv kernel's
 // 1x1x1 stages: ConvLaunch with gemm = true.
 hipError_t launch_gemm_bf16(const ConvLaunch &a, hipStream_t s);

@@ -28,7 +28,8 @@
  *    are); a misaligned pointer returns WANVAE_ERR_SHAPE.
  *  - Ownership: the caller allocates and owns every buffer (tensors, weights,
  *    caches, workspace).  The library allocates no device memory and keeps no
- *    pointer after a call returns.
+ *    pointer after a call returns.  Its only device memory of its own is
+ *    static, part of its loaded code: the wait give-up counter.
  *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  All
  *    work is enqueued on it; no call synchronizes the device or the stream
  *    (except wanvae_timing_read, which waits for its own events).
@@ -109,26 +110,6 @@ WANVAE_API int wanvae_rmsnorm_silu(const void *x, void *y, int64_t rows, int32_t
                         const float *beta, float eps, int32_t dtype, void *stream);
 
 /*
- * Causal 3x3x3 convolution, stride 1, with bias:
- *   y[n,t,h,w,co] = bias[co] + sum_{kt,kh,kw,ci} w[co,ci,kt,kh,kw] *
- *                   Z[n, t+kt-2, h+kh-1, w+kw-1, ci]
- * ("Sharding of WAN 2.2 VAE", Available Sharding Dimensions, for the conv and
- * its weight; causal in time, zero pad of one pixel in H and W: "Closing the
- * gap", section 2, the padding mask and causal-T-pad).  Z is x inside the
- * tensor and 0 outside it in H and W.  Frames -2 and -1 are cache[:,0] and
- * cache[:,1] when a cache is given (the feat_cache of "Sharding of WAN 2.2
- * VAE", Why depth sharding is not beneficial), else 0 (causal zero pad).
- *   x     : [d.n][d.t][d.h][d.w][cin] of dtype.
- *   cache : [d.n][2][d.h][d.w][cin] of dtype, or NULL.  Only read.
- *   w     : packed weight (wanvae_pack_conv3d_weights, cin x cout, dtype).
- *   bias  : [cout] fp32 or NULL.
- *   y     : [d.n][d.t][d.h][d.w][cout] of dtype; must not overlap x, cache, w.
- *   Channels: bf16 (MFMA implicit GEMM) needs cin a multiple of 16 in
- *   [16, 1024] and cout in [1, 1024] (the decoder's conv_in, 16 latent
- *   channels in, and conv_out, 3 channels out, included); fp32 (direct
- *   kernel) accepts 1..1024 for both.
- */
-/*
  * Packs a 3x3x3 conv weight for wanvae_causal_conv3d and the ResidualBlock
  * calls.  Input: w = [cout][cin][3][3][3] of dtype, the pages' weight layout
  * [C_out, C_in, kD, kH, kW] ("Sharding of WAN 2.2 VAE", Available Sharding
@@ -204,6 +185,26 @@ WANVAE_API int wanvae_pointwise_conv(const void *x, const void *w, const float *
                                      int64_t rows, int32_t cin, int32_t cout, int32_t dtype,
                                      void *stream);
 
+/*
+ * Causal 3x3x3 convolution, stride 1, with bias:
+ *   y[n,t,h,w,co] = bias[co] + sum_{kt,kh,kw,ci} w[co,ci,kt,kh,kw] *
+ *                   Z[n, t+kt-2, h+kh-1, w+kw-1, ci]
+ * ("Sharding of WAN 2.2 VAE", Available Sharding Dimensions, for the conv and
+ * its weight; causal in time, zero pad of one pixel in H and W: "Closing the
+ * gap", section 2, the padding mask and causal-T-pad).  Z is x inside the
+ * tensor and 0 outside it in H and W.  Frames -2 and -1 are cache[:,0] and
+ * cache[:,1] when a cache is given (the feat_cache of "Sharding of WAN 2.2
+ * VAE", Why depth sharding is not beneficial), else 0 (causal zero pad).
+ *   x     : [d.n][d.t][d.h][d.w][cin] of dtype.
+ *   cache : [d.n][2][d.h][d.w][cin] of dtype, or NULL.  Only read.
+ *   w     : packed weight (wanvae_pack_conv3d_weights, cin x cout, dtype).
+ *   bias  : [cout] fp32 or NULL.
+ *   y     : [d.n][d.t][d.h][d.w][cout] of dtype; must not overlap x, cache, w.
+ *   Channels: bf16 (MFMA implicit GEMM) needs cin a multiple of 16 in
+ *   [16, 1024] and cout in [1, 1024] (the decoder's conv_in, 16 latent
+ *   channels in, and conv_out, 3 channels out, included); fp32 (direct
+ *   kernel) accepts 1..1024 for both.
+ */
 WANVAE_API int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const float *bias,
                          void *y, const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
                          void *stream);
@@ -235,8 +236,14 @@ WANVAE_API int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, c
  * shortcut are summed in fp32 and rounded once.
  *   x : [d.n][d.t][d.h][d.w][in_dim];  y : [..][out_dim]; y must not overlap x.
  *   workspace: device buffer of at least wanvae_resblock_workspace_size bytes.
- * Four kernel launches on `stream`: norm1, conv A, norm2 (in place), conv B
- * with the shortcut and residual add in its epilogue.
+ * Kernel launches on `stream`: norm1 (into the conv input region), conv A
+ * (into the region of a), norm2 (a into the conv input region; for fp32, a
+ * normalised in place), then conv B with the residual add in its epilogue.
+ * The 1x1x1 shortcut is added there too: computed inside conv B's K loop, or,
+ * for bf16 with in_dim 128, 256 or 384 and out_dim a multiple of 64, by a
+ * projection GEMM launched ahead of conv B into the region of a (free once
+ * norm2 has read it), S rounded to bf16 and then added like the identity
+ * residual: five launches in that case, four otherwise.
  */
 WANVAE_API int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void *y,
                             const wanvae_dims *d, void *workspace, size_t ws_bytes, void *stream);
@@ -303,6 +310,28 @@ WANVAE_API int wanvae_attention_workspace_size(const wanvae_attention_params *p,
  */
 WANVAE_API int wanvae_attention_block(const wanvae_attention_params *p, const void *x, void *y,
                                       const wanvae_dims *d, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Bounded waits.  The bf16 conv's waves synchronise through flags in LDS
+ * (stage landed / stage consumed), and every wait on a flag is bounded so a
+ * launch can never hang.  A wait that reaches its bound goes on and is
+ * counted: the launch's output is then suspect.
+ *   wanvae_wait_giveups: waits for the current device to go idle, then
+ *     writes the number of waits that gave up on it since the library was
+ *     loaded or the count was last reset.  Zero means no launch on this device
+ *     left its synchronisation protocol.
+ *   wanvae_wait_giveups_reset: waits for the device to go idle, sets the
+ *     count to zero.
+ *   wanvae_set_wait_bound: polls (about 64 cycles apart) before a wait gives
+ *     up, for launches enqueued after the call, process-wide; negative
+ *     restores the default (2^15 polls, about 2M cycles, far beyond any real
+ *     wait).  A test hook: a bound of 0 makes the waits give up at once, so
+ *     that the counting can be checked from the host (the kernels still run
+ *     to completion, their results then meaningless).
+ */
+WANVAE_API int wanvae_wait_giveups(uint64_t *count);
+WANVAE_API int wanvae_wait_giveups_reset(void);
+WANVAE_API int wanvae_set_wait_bound(int32_t polls);
 
 /* Text of this thread's most recent error (library-owned, valid until the
  * thread's next call into the library).  "" when there was none. */

@@ -89,19 +89,34 @@ def sample_boxes(T, H, W, n_random=8, size=4, seed=0):
     return boxes
 
 
+def branch_err(blk_o, x, got, ref):
+    """Parity of the residual branch alone: (y - S(x)) against the oracle's
+    (y - S(x)), relative to the branch's own largest value, with S the
+    oracle's shortcut (x itself, or the 1x1x1 conv) of the exact input
+    values.  The block output is the branch plus S(x) ("return residual +
+    shortcut"), so with an identity shortcut max|y| is about max|x| and an
+    error of the conv branch would otherwise be measured against x."""
+    s = oracle.shortcut(blk_o, np.ascontiguousarray(x, np.float32)).astype(np.float64)
+    return rel_err(np.asarray(got, np.float64) - s, np.asarray(ref, np.float64) - s)
+
+
 def window_compare(blk_o, x_dev, y_dev, boxes):
-    """max rel error of the device output against the oracle on each box,
-    the oracle fed with the exact device input bits of the receptive field."""
+    """(max rel error of the device output against the oracle over the
+    boxes, PCC, max rel error of the residual branch y - S(x)), the oracle fed
+    with the exact device input bits of each box's receptive field."""
     N, T, H, W, _ = x_dev.shape
-    worst, refs, gots = 0.0, [], []
+    refs, gots, brs, bgs = [], [], [], []
     for box in boxes:
         reg = oracle.receptive_region(box, (T, H, W))
         xr = to_host(x_dev[:, reg[0]:reg[1], reg[2]:reg[3], reg[4]:reg[5]])
         ref = oracle.resblock_window(blk_o, xr, reg, (T, H, W), box)
         t0, t1, h0, h1, w0, w1 = box
         got = to_host(y_dev[:, t0:t1, h0:h1, w0:w1])
+        s = oracle.shortcut(blk_o, to_host(x_dev[:, t0:t1, h0:h1, w0:w1])).astype(np.float64)
         refs.append(ref.ravel())
         gots.append(got.ravel())
+        brs.append((ref - s).ravel())
+        bgs.append((got - s).ravel())
     ref = np.concatenate(refs)
     got = np.concatenate(gots)
-    return rel_err(got, ref), pcc(got, ref)
+    return rel_err(got, ref), pcc(got, ref), rel_err(np.concatenate(bgs), np.concatenate(brs))

@@ -34,6 +34,17 @@ def wv(torch):
     return m
 
 
+@pytest.fixture(autouse=True)
+def no_wait_giveups(wv):
+    """Every test leaves the conv's bounded flag waits untouched: a wait that
+    reached its bound means a launch left its synchronisation protocol and
+    its output cannot be trusted, whatever the parity check said."""
+    wv.wait_giveups_reset()
+    yield
+    n = wv.wait_giveups()
+    assert n == 0, f"{n} bounded flag waits gave up during the test"
+
+
 def rnd(rng, shape, scale=1.0, dt=wl.F32):
     a = (rng.standard_normal(shape) * scale).astype(np.float32)
     return wl.round_bf16(a) if dt == wl.BF16 else a
@@ -127,6 +138,31 @@ def test_causal_conv3d_bf16(torch, wv, shape, with_cache):
     err = gu.rel_err(gu.to_host(y), ref)
     gu.report(f"conv bf16 {shape} cache={with_cache}", err, gu.TOL_BF16, f"pcc={gu.pcc(gu.to_host(y), ref):.6f}")
     assert err <= gu.TOL_BF16
+
+
+def test_wait_giveups_are_counted(torch, wv):
+    """A bound of zero polls, set from the host, makes the conv's flag waits
+    give up at once: every launch still runs to completion (its result is
+    then meaningless), and the give-ups are counted.  With the default bound
+    the same conv counts none and matches the oracle."""
+    rng = np.random.default_rng(5)
+    shape = (1, 3, 19, 70, 64, 96)
+    N, T, H, W, Cin, Cout = shape
+    x = rnd(rng, (N, T, H, W, Cin), 1.0, wl.BF16)
+    w = rnd(rng, (Cout, Cin, 3, 3, 3), 1 / math.sqrt(27 * Cin), wl.BF16)
+    xd, pw = gu.to_dev(x, wl.BF16), wv.pack_conv3d_weights(gu.to_dev(w, wl.BF16))
+    wv.set_wait_bound(0)
+    try:
+        wv.causal_conv3d(xd, pw)
+        n = wv.wait_giveups()
+    finally:
+        wv.set_wait_bound(-1)
+    print(f"[giveups] bound 0: {n} waits gave up", flush=True)
+    assert n > 0
+    wv.wait_giveups_reset()
+    y = wv.causal_conv3d(xd, pw)
+    assert wv.wait_giveups() == 0
+    assert gu.rel_err(gu.to_host(y), oracle.causal_conv3d(x, w)) <= gu.TOL_BF16
 
 
 @pytest.mark.parametrize("shape", [(1, 4, 16, 16, 64, 64), (2, 3, 5, 7, 3, 5), (1, 2, 9, 4, 33, 1)])
@@ -230,8 +266,10 @@ def test_block_c1_full(torch, wv):
     ref = oracle.resblock_full(gu.oracle_block(p), x)
     y = blk.forward(gu.to_dev(x, w.dtype))
     err = gu.rel_err(gu.to_host(y), ref)
-    gu.report("block c1 fp32 full", err, gu.TOL_F32)
+    eb = gu.branch_err(gu.oracle_block(p), x, gu.to_host(y), ref)
+    gu.report("block c1 fp32 full", err, gu.TOL_F32, f"branch y-x: {eb:.3e}")
     assert err <= gu.TOL_F32
+    assert eb <= gu.TOL_F32
 
 
 @pytest.mark.parametrize("w", SMALL_BLOCKS, ids=lambda w: w.name)
@@ -242,8 +280,11 @@ def test_block_small_full_and_stream(torch, wv, w):
     xd = gu.to_dev(x, w.dtype)
     y = blk.forward(xd)
     err = gu.rel_err(gu.to_host(y), ref)
-    gu.report(f"block {w.name} full", err, tol(w.dtype), f"pcc={gu.pcc(gu.to_host(y), ref):.6f}")
+    eb = gu.branch_err(gu.oracle_block(p), x, gu.to_host(y), ref)
+    gu.report(f"block {w.name} full", err, tol(w.dtype),
+              f"branch y-S(x): {eb:.3e} pcc={gu.pcc(gu.to_host(y), ref):.6f}")
     assert err <= tol(w.dtype)
+    assert eb <= tol(w.dtype)
     # chunks of 1, 2 and 3 frames (3 leaves a shorter last chunk for T = 4, 5)
     for ts in (1, 2, 3):
         ca, cb = blk.new_caches(w.n, w.h, w.w)
@@ -268,12 +309,43 @@ def test_block_full_size_sampled(torch, wv, name):
     x = wl.make_x_device(w)
     y = blk.forward(x)
     torch.cuda.synchronize()
-    boxes = gu.sample_boxes(w.t, w.h, w.w, n_random=8 if w.cin <= 192 else 4)
-    err, r = gu.window_compare(gu.oracle_block(p), x, y, boxes)
-    gu.report(f"block {name} full-size, {len(boxes)} boxes", err, tol(w.dtype), f"pcc={r:.6f}")
+    # 16 boxes at the corners and edge midpoints of the first and last frames,
+    # 120 at random: 136 boxes of 4 x 4 x 4 outputs
+    boxes = gu.sample_boxes(w.t, w.h, w.w, n_random=120)
+    err, r, eb = gu.window_compare(gu.oracle_block(p), x, y, boxes)
+    gu.report(f"block {name} full-size, {len(boxes)} boxes", err, tol(w.dtype),
+              f"branch y-S(x): {eb:.3e} pcc={r:.6f}")
     assert err <= tol(w.dtype)
+    assert eb <= tol(w.dtype)
     del x, y, blk
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_block_c2_full_output(torch, wv):
+    """The latent-resolution block [1,21,90,160,384] compared over its whole
+    output: the oracle runs the clip in chunks of 3 frames with its caches
+    (its streamed result equals its full-T result bit for bit), printing as
+    it goes."""
+    w = wl.WORKLOADS["c2"]
+    p, blk = _block(wv, w)
+    x = wl.make_x_device(w)
+    y = gu.to_host(blk.forward(x))
+    xh = gu.to_host(x)
+    del x
+    torch.cuda.empty_cache()
+    ob = gu.oracle_block(p)
+    ca = np.zeros((w.n, 2, w.h, w.w, w.cin), np.float32)
+    cb = np.zeros((w.n, 2, w.h, w.w, w.cout), np.float32)
+    ref = np.empty_like(y)
+    for t0 in range(0, w.t, 3):
+        ref[:, t0:t0 + 3] = oracle.resblock_stream_step(ob, np.ascontiguousarray(xh[:, t0:t0 + 3]), ca, cb)
+        print(f"[c2 full] oracle frames {t0}..{min(t0 + 3, w.t) - 1} done", flush=True)
+    err = gu.rel_err(y, ref)
+    eb = gu.branch_err(ob, xh, y, ref)
+    gu.report("block c2 full output", err, gu.TOL_BF16, f"branch y-x: {eb:.3e} pcc={gu.pcc(y, ref):.6f}")
+    assert err <= gu.TOL_BF16
+    assert eb <= gu.TOL_BF16
 
 
 def test_c5_stream_equals_full_t(torch, wv):
@@ -294,9 +366,11 @@ def test_c5_stream_equals_full_t(torch, wv):
     assert diff / scale <= gu.TOL_BF16
     assert same, "c5 streamed frame by frame differs from full-T"
     # and the streamed output against the oracle on sampled boxes
-    boxes = gu.sample_boxes(w.t, w.h, w.w, n_random=2)
-    err, _ = gu.window_compare(gu.oracle_block(p), x, ys, boxes)
+    boxes = gu.sample_boxes(w.t, w.h, w.w, n_random=16)
+    err, _, eb = gu.window_compare(gu.oracle_block(p), x, ys, boxes)
+    gu.report(f"c5 stream vs oracle, {len(boxes)} boxes", err, gu.TOL_BF16, f"branch y-S(x): {eb:.3e}")
     assert err <= gu.TOL_BF16
+    assert eb <= gu.TOL_BF16
     del x, y, ys
     torch.cuda.empty_cache()
 
