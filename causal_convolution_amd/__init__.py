@@ -74,6 +74,8 @@ EXPORTS = {
                                              C.c_void_p]),
     "wanvae_packed_conv2d_weight_elems": (C.c_int, [C.c_int32, C.c_int32, C.c_int32,
                                                     C.POINTER(C.c_int64)]),
+    "wanvae_resblock_forward_noalloc": (C.c_int, [C.POINTER(ResblockParamsC), C.c_void_p, C.c_void_p,
+                                                  C.POINTER(Dims), C.c_void_p]),
     "wanvae_wait_giveups": (C.c_int, [C.POINTER(C.c_uint64)]),
     "wanvae_wait_giveups_reset": (C.c_int, []),
     "wanvae_set_wait_bound": (C.c_int, [C.c_int32]),
@@ -372,6 +374,18 @@ class ResBlock:
                                              _ptr(ws), ws.numel() * ws.element_size(),
                                              _stream(stream)))
         return y
+
+    def forward_noalloc(self, x, out, stream=None):
+        """Full-T block without a workspace (``wanvae_resblock_forward_noalloc``):
+        the library's own 64 MiB device array holds the intermediates; ``out``
+        must be given (nothing is allocated)."""
+        n, t, h, w, ci = x.shape
+        _dev(x, "x", self.dtype, (n, t, h, w, self.in_dim))
+        _dev(out, "out", self.dtype, (n, t, h, w, self.out_dim))
+        d = Dims(n, t, h, w)
+        _check(lib().wanvae_resblock_forward_noalloc(C.byref(self.c), _ptr(x), _ptr(out), C.byref(d),
+                                                     _stream(stream)))
+        return out
 
     def new_caches(self, n, h, w, device="cuda"):
         """Zero caches for a fresh stream, n*2*h*w*in_dim and n*2*h*w*out_dim

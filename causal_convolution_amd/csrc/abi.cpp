@@ -93,11 +93,15 @@ hipEvent_t take_event() {
     return e;
 }
 
+// Launches of a call that must not allocate (the no-workspace entry point)
+// are never timed: a timing event may have to be created.
+thread_local bool g_untimed = false;
+
 // Runs one launch, bracketed by timing events when timing is enabled.
 template <typename F>
 int timed_launch(int kind, hipStream_t s, const char *what, F &&launch) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    {
+    if (!g_untimed) {
         std::lock_guard<std::mutex> lk(g_tm_mu);
         if (g_timing && g_recs.size() < kMaxTimingRecs) {
             e0 = take_event();
@@ -274,6 +278,37 @@ int check_block_buffers(const wanvae_resblock_params *p, const Plan &pl, const v
 int forward_planned(const wanvae_resblock_params *p, const Plan &pl, const void *x, void *y,
                     const wanvae_dims *d, void *workspace, hipStream_t s);
 
+// Workspace of wanvae_resblock_forward_noalloc: a file-scope device array that
+// each GPU the library runs on holds until the process ends.  Its device
+// address is looked up once per device (the name itself is only a host-side
+// stand-in) and kept; calls on one device share it.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+int scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    WV_CHECK(dev >= 0 && dev < kMaxDevices, WANVAE_ERR_HIP, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(WANVAE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return WANVAE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -473,6 +508,25 @@ int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void
     if (pl.P == 0) return WANVAE_OK;
     if (int r = check_block_buffers(p, pl, x, y, workspace, ws_bytes)) return r;
     return forward_planned(p, pl, x, y, d, workspace, static_cast<hipStream_t>(stream));
+}
+
+int wanvae_resblock_forward_noalloc(const wanvae_resblock_params *p, const void *x, void *y,
+                                    const wanvae_dims *d, void *stream) {
+    g_error.clear();
+    Plan pl;
+    if (int r = plan_block(p, d, &pl)) return r;
+    if (pl.P == 0) return WANVAE_OK;
+    WV_CHECK(pl.total <= kScratchBytes, WANVAE_ERR_WORKSPACE,
+             "block of %lld positions needs %zu bytes of workspace; the library's own scratch holds "
+             "%zu (use wanvae_resblock_forward with a caller workspace)",
+             (long long)pl.P, pl.total, kScratchBytes);
+    void *ws = nullptr;
+    if (int r = scratch_address(&ws)) return r;
+    if (int r = check_block_buffers(p, pl, x, y, ws, kScratchBytes)) return r;
+    g_untimed = true;
+    const int r = forward_planned(p, pl, x, y, d, ws, static_cast<hipStream_t>(stream));
+    g_untimed = false;
+    return r;
 }
 
 int wanvae_wait_giveups(uint64_t *count) {

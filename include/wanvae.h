@@ -29,7 +29,8 @@
  *  - Ownership: the caller allocates and owns every buffer (tensors, weights,
  *    caches, workspace).  The library allocates no device memory and keeps no
  *    pointer after a call returns.  Its only device memory of its own is
- *    static, part of its loaded code: the wait give-up counter.
+ *    static, part of its loaded code: the workspace array of
+ *    wanvae_resblock_forward_noalloc and the wait give-up counter.
  *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  All
  *    work is enqueued on it; no call synchronizes the device or the stream
  *    (except wanvae_timing_read, which waits for its own events).
@@ -247,6 +248,24 @@ WANVAE_API int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, c
  */
 WANVAE_API int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void *y,
                             const wanvae_dims *d, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * wanvae_resblock_forward for callers that cannot allocate device memory:
+ * code under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace; the block's intermediates live in a
+ * device array of the library's own (64 MiB, held by each GPU the library
+ * runs on until the process ends), so only blocks whose
+ * wanvae_resblock_workspace_size is at most 64 MiB are accepted (else
+ * WANVAE_ERR_WORKSPACE, nothing enqueued).  The call allocates nothing and
+ * is never timed (wanvae_timing_*); its first call on a device looks the
+ * array's address up once.  Same kernels and results as
+ * wanvae_resblock_forward.  Every call on one device shares that array:
+ * calls that overlap on a device (other streams, other threads) race and
+ * must be ordered by the caller.  Nothing in it needs clearing between calls.
+ * The current device must be the one `stream` belongs to.
+ */
+WANVAE_API int wanvae_resblock_forward_noalloc(const wanvae_resblock_params *p, const void *x, void *y,
+                                               const wanvae_dims *d, void *stream);
 
 /*
  * One streaming step over a chunk of d->t >= 1 frames with the feat_cache

@@ -248,3 +248,20 @@ def test_upsample2d_validation():
     assert L.wanvae_packed_conv2d_weight_elems(192, 96, wv.F32, C.byref(n)) == wv.ERR_DTYPE
     assert L.wanvae_pack_conv2d_weights(p, C.c_void_p((1 << 24) + 4096), 64, 64, wv.BF16, None) == wv.ERR_ALIAS
     assert L.wanvae_pack_conv2d_weights(None, q, 64, 64, wv.BF16, None) == wv.ERR_NULL
+
+
+def test_forward_noalloc_validation():
+    """The allocation-free forward checks its arguments on the host, and
+    rejects a block whose workspace exceeds the library's own 64 MiB array
+    before it looks up or touches any device memory."""
+    L = wv.lib()
+    p = _params()
+    x, y = C.c_void_p(1 << 34), C.c_void_p(1 << 35)
+    big = wv.Dims(1, 21, 90, 160)
+    assert L.wanvae_resblock_forward_noalloc(C.byref(p), x, y, C.byref(big), None) == wv.ERR_WORKSPACE
+    assert "scratch" in wv.last_error()
+    assert L.wanvae_resblock_forward_noalloc(None, x, y, C.byref(big), None) == wv.ERR_NULL
+    p2 = _params(shortcut=False)
+    assert L.wanvae_resblock_forward_noalloc(C.byref(p2), x, y, C.byref(big), None) == wv.ERR_SHAPE
+    empty = wv.Dims(1, 0, 8, 32)
+    assert L.wanvae_resblock_forward_noalloc(C.byref(p), None, None, C.byref(empty), None) == wv.OK
