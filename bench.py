@@ -354,6 +354,68 @@ def attention(torch, wv, wl, steps, warmup):
             "steps": steps, "warmup": warmup, "kernels": ops}
 
 
+def copy_bound(torch, wv, wl, steps, warmup):
+    """The attainable HBM rate for the norm, measured: the library's plain
+    streaming copy (wanvae_stream_copy: read once, write once, 16-byte
+    nontemporal accesses) at the size of one output-resolution activation
+    ([1,81,720,1280,96] bf16, 14.3 GB), over a sweep of pieces in flight and
+    workgroups per CU, beside the runtime's own copy (torch copy_) and the
+    fused RMS_norm + SiLU at the same size in both its output forms (channels
+    -last, and the 16-channel slices the conv reads, as inside the block).
+    GB/s counts the bytes read plus the bytes written."""
+    w = wl.WORKLOADS["c4"]
+    x = wl.make_x_device(w, seed=0)
+    y = torch.empty_like(x)
+    nbytes = x.numel() * x.element_size()
+    g = torch.Generator().manual_seed(0)
+    gam = torch.rand(w.cin, generator=g).add_(0.5).cuda()
+    bet = (torch.randn(w.cin, generator=g) * 0.3).cuda()
+    res = []
+
+    def timed(name, kind, fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        wv.timing_reset()
+        wv.timing_enable(True)
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        wv.timing_enable(False)
+        n, ms = wv.timing_read(kind) if kind is not None else (0, 0.0)
+        wv.timing_reset()
+        return ms / n if n else None
+
+    for unroll in (2, 4, 8):
+        for bpc in (4, 8, 16):
+            avg = timed(None, wv.KERNEL_COPY, lambda: wv.stream_copy(x, y, unroll, bpc))
+            res.append({"op": f"stream copy, unroll {unroll}, {bpc} workgroups/CU", "avg_launch_ms": avg,
+                        "gbs": 2.0 * nbytes / (avg * 1e-3) / 1e9})
+            print(f"[bench] {res[-1]['op']}: {avg:.3f} ms, {res[-1]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    # the runtime's copy kernel, timed with torch events on the stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        y.copy_(x)
+    e0.record()
+    for _ in range(steps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) / steps
+    res.append({"op": "runtime copy (torch copy_)", "avg_launch_ms": avg, "gbs": 2.0 * nbytes / (avg * 1e-3) / 1e9})
+    print(f"[bench] runtime copy: {avg:.3f} ms, {res[-1]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    avg = timed(None, wv.KERNEL_NORM, lambda: wv.rmsnorm_silu(x, gam, bet, out=y))
+    res.append({"op": "RMS_norm + SiLU, channels-last output", "avg_launch_ms": avg,
+                "gbs": 2.0 * nbytes / (avg * 1e-3) / 1e9})
+    best = max(r["gbs"] for r in res if r["op"].startswith("stream copy"))
+    for r in res:
+        r["frac_of_copy"] = r["gbs"] / best
+        r["frac_of_8tbs"] = r["gbs"] / PEAK_HBM_GBS
+    return {"metric": "attainable HBM rate: streaming copy vs the fused norm, 1 GPU", "unit": "GB/s",
+            "bytes_per_launch": 2.0 * nbytes, "best_copy_gbs": best, "steps": steps, "warmup": warmup,
+            "ops": res}
+
+
 def block_pass(torch, wv, step, steps, stream, instrumented):
     """K steps between two events on the launch stream; with `instrumented`,
     the library's hipEvents bracket every launch as well.  Returns the
@@ -407,6 +469,9 @@ def main():
     ap.add_argument("--upsample", action="store_true",
                     help="time the decoder's spatial upsampler conv instead (nearest x2 + 3x3 "
                          "conv) at the three decoder upsampler shapes (one JSON line)")
+    ap.add_argument("--copy-bound", action="store_true",
+                    help="measure the attainable HBM rate instead: the library's streaming copy "
+                         "and the fused norm at one output-resolution activation (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-MiB buffer 3 times (a plain copy "
                          "kernel of known size, to scale HBM byte counters by)")
@@ -439,6 +504,9 @@ def main():
         return
     if args.upsample:
         print(json.dumps(upsample(torch, wv, args.steps, args.warmup)), flush=True)
+        return
+    if args.copy_bound:
+        print(json.dumps(copy_bound(torch, wv, wl, args.steps, args.warmup)), flush=True)
         return
 
     w = wl.WORKLOADS[args.workload]

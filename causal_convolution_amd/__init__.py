@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libwanvae.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP = range(7)
 F32, BF16 = 0, 1
 (KERNEL_NORM, KERNEL_CONV_BF16, KERNEL_CONV_F32, KERNEL_ROLL, KERNEL_POINTWISE, KERNEL_GEMM,
- KERNEL_TRANSPOSE, KERNEL_ATTENTION, KERNEL_UPSAMPLE) = range(9)
+ KERNEL_TRANSPOSE, KERNEL_ATTENTION, KERNEL_UPSAMPLE, KERNEL_COPY) = range(10)
 EPS = 1e-12
 
 
@@ -79,6 +79,11 @@ EXPORTS = {
     "wanvae_wait_giveups": (C.c_int, [C.POINTER(C.c_uint64)]),
     "wanvae_wait_giveups_reset": (C.c_int, []),
     "wanvae_set_wait_bound": (C.c_int, [C.c_int32]),
+    "wanvae_stream_cache_export": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(Dims), C.c_int32, C.c_int32,
+                                             C.c_void_p]),
+    "wanvae_stream_cache_import": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(Dims), C.c_int32, C.c_int32,
+                                             C.c_void_p]),
+    "wanvae_stream_copy": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]),
     "wanvae_last_error": (C.c_char_p, []),
     "wanvae_timing_enable": (C.c_int, [C.c_int]),
     "wanvae_timing_reset": (C.c_int, []),
@@ -388,20 +393,32 @@ class ResBlock:
         return out
 
     def new_caches(self, n, h, w, device="cuda"):
-        """Zero caches for a fresh stream, n*2*h*w*in_dim and n*2*h*w*out_dim
-        elements shaped [n,2,h,w,C].  Their contents are the library's own
-        conv-input frames (16-channel slices for bf16), opaque to callers."""
+        """Zero caches for a fresh stream: flat buffers of n*2*h*w*in_dim and
+        n*2*h*w*out_dim elements.  Their contents are the library's own
+        conv-input frames (16-channel slices for bf16), opaque to callers:
+        ``export_cache`` / ``import_cache`` read and set them channels-last."""
         torch = _torch()
-        return (torch.zeros((n, 2, h, w, self.in_dim), dtype=self.dtype, device=device),
-                torch.zeros((n, 2, h, w, self.out_dim), dtype=self.dtype, device=device))
+        return (torch.zeros((n * 2 * h * w * self.in_dim,), dtype=self.dtype, device=device),
+                torch.zeros((n * 2 * h * w * self.out_dim,), dtype=self.dtype, device=device))
+
+    def export_cache(self, cache, n, h, w, channels, out=None, stream=None):
+        """A cache's frames, channels-last (see ``export_stream_cache``);
+        channels is in_dim for cache_a, out_dim for cache_b."""
+        _dev(cache, "cache", self.dtype)
+        return export_stream_cache(cache, n, h, w, channels, out, stream)
+
+    def import_cache(self, frames, cache, stream=None):
+        """Sets a cache from channels-last frames (see ``import_stream_cache``)."""
+        _dev(cache, "cache", self.dtype)
+        return import_stream_cache(frames, cache, stream)
 
     def stream_step(self, x_chunk, cache_a, cache_b, out=None, workspace=None, stream=None):
         """One streaming step (``wanvae_resblock_stream_step``); caches update in place."""
         torch = _torch()
         n, t, h, w, ci = x_chunk.shape
         _dev(x_chunk, "x_chunk", self.dtype, (n, t, h, w, self.in_dim))
-        _dev(cache_a, "cache_a", self.dtype, (n, 2, h, w, self.in_dim))
-        _dev(cache_b, "cache_b", self.dtype, (n, 2, h, w, self.out_dim))
+        _dev(cache_a, "cache_a", self.dtype, (n * 2 * h * w * self.in_dim,))
+        _dev(cache_b, "cache_b", self.dtype, (n * 2 * h * w * self.out_dim,))
         y = torch.empty((n, t, h, w, self.out_dim), dtype=x_chunk.dtype,
                         device=x_chunk.device) if out is None else out
         _dev(y, "out", self.dtype, (n, t, h, w, self.out_dim))
@@ -412,6 +429,31 @@ class ResBlock:
                                                  _ptr(ws), ws.numel() * ws.element_size(),
                                                  _stream(stream)))
         return y
+
+
+def export_stream_cache(cache, n, h, w, channels, out=None, stream=None):
+    """A stream cache's frames -2, -1 as a channels-last [n, 2, h, w,
+    channels] tensor of the cache's dtype (``wanvae_stream_cache_export``)."""
+    torch = _torch()
+    _dev(cache, "cache", None, (n * 2 * h * w * channels,))
+    y = torch.empty((n, 2, h, w, channels), dtype=cache.dtype, device=cache.device) if out is None else out
+    _dev(y, "out", cache.dtype, (n, 2, h, w, channels))
+    d = Dims(n, 2, h, w)
+    _check(lib().wanvae_stream_cache_export(_ptr(cache), _ptr(y), C.byref(d), int(channels), _dtype_code(cache),
+                                            _stream(stream)))
+    return y
+
+
+def import_stream_cache(frames, cache, stream=None):
+    """Sets a stream cache from channels-last frames [n, 2, h, w, channels]
+    of its dtype (``wanvae_stream_cache_import``)."""
+    n, two, h, w, channels = frames.shape
+    _dev(frames, "frames", cache.dtype, (n, 2, h, w, channels))
+    _dev(cache, "cache", None, (n * 2 * h * w * channels,))
+    d = Dims(n, 2, h, w)
+    _check(lib().wanvae_stream_cache_import(_ptr(frames), _ptr(cache), C.byref(d), int(channels),
+                                            _dtype_code(cache), _stream(stream)))
+    return cache
 
 
 # --------------------------------------------------------------------------- timing
@@ -464,6 +506,19 @@ class AttentionBlock:
         _check(lib().wanvae_attention_block(C.byref(self.c), _ptr(x), _ptr(y), C.byref(d), _ptr(ws),
                                             ws.numel() * ws.element_size(), _stream(stream)))
         return y
+
+
+def stream_copy(src, dst, unroll: int = 4, blocks_per_cu: int = 8, stream=None):
+    """dst = src by the library's plain streaming copy (``wanvae_stream_copy``),
+    the attainable HBM rate of its bandwidth-bound kernels.  Both GPU tensors,
+    contiguous, of equal byte size (a multiple of 16)."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must have the same byte size")
+    _check(lib().wanvae_stream_copy(_ptr(src), _ptr(dst), nb, int(unroll), int(blocks_per_cu), _stream(stream)))
+    return dst
 
 
 def wait_giveups() -> int:

@@ -22,7 +22,7 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwanvae.so")
 SOURCES = ["abi.cpp", "rmsnorm_silu.hip", "conv3d_f32.hip", "conv3d_bf16.hip", "pack_weights.hip",
            "pointwise.hip", "attention.hip", "gemm_bf16.hip",
-           "conv3d_narrow.hip"]
+           "conv3d_narrow.hip", "stream_copy.hip", "cache_io.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -553,41 +553,73 @@ int wanvae_set_wait_bound(int32_t polls) {
 }  // extern "C"
 
 namespace {
-// The block's four (or five) launches once plan and buffers are checked.
-int forward_planned(const wanvae_resblock_params *p, const Plan &pl, const void *x, void *y,
-                    const wanvae_dims *d, void *workspace, hipStream_t s) {
-    char *ws = static_cast<char *>(workspace);
-    void *n1 = ws + pl.n_off;
-    void *a = ws + pl.a_off;
-    const bool sliced = p->dtype == WANVAE_BF16;
-    void *n2 = sliced ? n1 : a;
-    const int64_t hw = d->h * d->w;
+// Where the block's intermediates live in the workspace, and whether conv A
+// computes norm2 + SiLU in its epilogue (bf16 with out_dim 32 or 96: one
+// tile then holds every channel of its positions).  Unfused, n1 and later n2
+// take the conv input region (bf16: n2 sliced from a; fp32: a normalised in
+// place) and S, a GEMM shortcut's output, takes a's region once norm2 has
+// read it.  Fused, conv A writes n2 straight into a's region (n1 is still
+// being read there by other tiles) and S takes the conv input region.
+struct Regions {
+    void *n1, *a, *n2, *s;
+    bool fused;
+};
 
-    if (int r = run_norm_conv_input(x, n1, pl.P, p->in_dim, hw, p->gamma1, p->beta1, p->eps, p->dtype, s))
-        return r;
+Regions block_regions(const wanvae_resblock_params *p, const Plan &pl, void *workspace) {
+    char *ws = static_cast<char *>(workspace);
+    Regions r;
+    r.n1 = ws + pl.n_off;
+    r.a = ws + pl.a_off;
+    r.fused = p->dtype == WANVAE_BF16 && wanvae::conv3d_bf16_norm_supported(p->out_dim);
+    r.n2 = r.fused ? r.a : p->dtype == WANVAE_BF16 ? r.n1 : r.a;
+    r.s = r.fused ? r.n1 : r.a;
+    return r;
+}
+
+// conv A: into a, or with norm2 + SiLU in its epilogue into n2 when fused
+wanvae::ConvLaunch conv_a_launch(const wanvae_resblock_params *p, const wanvae_dims *d, const Regions &g) {
     wanvae::ConvLaunch ca;
-    ca.x = n1;
-    ca.x_sliced = sliced;
+    ca.x = g.n1;
+    ca.x_sliced = p->dtype == WANVAE_BF16;
     ca.w = p->w_a;
     ca.bias = p->b_a;
-    ca.y = a;
+    ca.y = g.fused ? g.n2 : g.a;
     ca.n = d->n;
     ca.t = d->t;
     ca.h = d->h;
     ca.w_ = d->w;
     ca.cin = p->in_dim;
     ca.cout = p->out_dim;
-    if (int r = run_conv(ca, p->dtype, s)) return r;
-    if (int r = run_norm_conv_input(a, n2, pl.P, p->out_dim, hw, p->gamma2, p->beta2, p->eps, p->dtype, s))
+    if (g.fused) {
+        ca.norm_out = true;
+        ca.norm_gamma = p->gamma2;
+        ca.norm_beta = p->beta2;
+        ca.norm_eps = p->eps;
+    }
+    return ca;
+}
+
+// The block's launches once plan and buffers are checked.
+int forward_planned(const wanvae_resblock_params *p, const Plan &pl, const void *x, void *y,
+                    const wanvae_dims *d, void *workspace, hipStream_t s) {
+    const Regions g = block_regions(p, pl, workspace);
+    const int64_t hw = d->h * d->w;
+
+    if (int r = run_norm_conv_input(x, g.n1, pl.P, p->in_dim, hw, p->gamma1, p->beta1, p->eps, p->dtype, s))
         return r;
+    wanvae::ConvLaunch ca = conv_a_launch(p, d, g);
+    if (int r = run_conv(ca, p->dtype, s)) return r;
+    if (!g.fused)
+        if (int r = run_norm_conv_input(g.a, g.n2, pl.P, p->out_dim, hw, p->gamma2, p->beta2, p->eps, p->dtype, s))
+            return r;
     wanvae::ConvLaunch cb = ca;
-    cb.x = n2;
+    cb.norm_out = false;
+    cb.x = g.n2;
     cb.w = p->w_b;
     cb.bias = p->b_b;
     cb.y = y;
     cb.cin = p->out_dim;
-    // (bf16: n2 lives in the conv input region, so a's region is free for S)
-    if (int r = setup_residual(p, x, pl.P, a, &cb, s)) return r;
+    if (int r = setup_residual(p, x, pl.P, g.s, &cb, s)) return r;
     return run_conv(cb, p->dtype, s);
 }
 }  // namespace
@@ -618,49 +650,36 @@ int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_c
                  !overlaps(cache_b, cb_bytes, workspace, pl.total),
              WANVAE_ERR_ALIAS, "caches overlap each other, x, y or the workspace");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    char *ws = static_cast<char *>(workspace);
-    void *n1 = ws + pl.n_off;
-    void *a = ws + pl.a_off;
-    const bool sliced = p->dtype == WANVAE_BF16;
-    void *n2 = sliced ? n1 : a;
+    const Regions g = block_regions(p, pl, workspace);
     const int64_t hw = d->h * d->w;
 
-    if (int r = run_norm_conv_input(x_chunk, n1, pl.P, p->in_dim, hw, p->gamma1, p->beta1, p->eps,
+    if (int r = run_norm_conv_input(x_chunk, g.n1, pl.P, p->in_dim, hw, p->gamma1, p->beta1, p->eps,
                                     p->dtype, s))
         return r;
-    wanvae::ConvLaunch ca;
-    ca.x = n1;
-    ca.x_sliced = sliced;
+    wanvae::ConvLaunch ca = conv_a_launch(p, d, g);
     ca.cache = cache_a;
-    ca.w = p->w_a;
-    ca.bias = p->b_a;
-    ca.y = a;
-    ca.n = d->n;
-    ca.t = d->t;
-    ca.h = d->h;
-    ca.w_ = d->w;
-    ca.cin = p->in_dim;
-    ca.cout = p->out_dim;
     if (int r = run_conv(ca, p->dtype, s)) return r;
     if (int r = timed_launch(WANVAE_KERNEL_ROLL, s, "roll_cache", [&] {
-            return wanvae::launch_roll_cache(cache_a, n1, d->n, d->t, (int64_t)slab_a, s);
+            return wanvae::launch_roll_cache(cache_a, g.n1, d->n, d->t, (int64_t)slab_a, s);
         }))
         return r;
-    // n2 may take n1's place: the roll above has been enqueued before it
-    if (int r = run_norm_conv_input(a, n2, pl.P, p->out_dim, hw, p->gamma2, p->beta2, p->eps,
-                                    p->dtype, s))
-        return r;
+    // n2 (or S) may take n1's place: the roll above has been enqueued before it
+    if (!g.fused)
+        if (int r = run_norm_conv_input(g.a, g.n2, pl.P, p->out_dim, hw, p->gamma2, p->beta2, p->eps,
+                                        p->dtype, s))
+            return r;
     wanvae::ConvLaunch cb = ca;
-    cb.x = n2;
+    cb.norm_out = false;
+    cb.x = g.n2;
     cb.cache = cache_b;
     cb.w = p->w_b;
     cb.bias = p->b_b;
     cb.y = y_chunk;
     cb.cin = p->out_dim;
-    if (int r = setup_residual(p, x_chunk, pl.P, a, &cb, s)) return r;
+    if (int r = setup_residual(p, x_chunk, pl.P, g.s, &cb, s)) return r;
     if (int r = run_conv(cb, p->dtype, s)) return r;
     return timed_launch(WANVAE_KERNEL_ROLL, s, "roll_cache", [&] {
-        return wanvae::launch_roll_cache(cache_b, n2, d->n, d->t, (int64_t)slab_b, s);
+        return wanvae::launch_roll_cache(cache_b, g.n2, d->n, d->t, (int64_t)slab_b, s);
     });
 }
 
@@ -767,6 +786,61 @@ int wanvae_attention_block(const wanvae_attention_params *p, const void *x, void
     go.y = y;
     go.cout = C;
     return timed_launch(WANVAE_KERNEL_GEMM, s, "output projection", [&] { return project(go); });
+}
+
+namespace {
+int cache_io(const void *src, void *dst, const wanvae_dims *d, int32_t C, int32_t dtype, bool to_sliced,
+             void *stream) {
+    g_error.clear();
+    WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
+    WV_CHECK(d != nullptr, WANVAE_ERR_NULL, "dims is NULL");
+    wanvae_dims fd = *d;
+    fd.t = 2;   // the cache's two frames per batch item
+    int64_t P = 0;
+    if (int r = positions(&fd, &P)) return r;
+    WV_CHECK(C >= 1 && C <= 1024 && (dtype != WANVAE_BF16 || C % 16 == 0), WANVAE_ERR_SHAPE,
+             "cache channels must be in [1, 1024] (a multiple of 16 for bf16; got %d)", C);
+    if (P == 0) return WANVAE_OK;
+    WV_CHECK(src && dst, WANVAE_ERR_NULL, "both buffers are required");
+    WV_CHECK(aligned16(src) && aligned16(dst), WANVAE_ERR_SHAPE, "pointers must be 16-byte aligned");
+    const size_t bytes = (size_t)P * C * esize(dtype);
+    WV_CHECK(!overlaps(src, bytes, dst, bytes), WANVAE_ERR_ALIAS, "the two buffers overlap");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == WANVAE_BF16)
+        e = wanvae::launch_cache_layout(src, dst, d->n * 2, d->h * d->w, C, to_sliced, s);
+    else   // fp32 caches are channels-last already
+        e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(WANVAE_ERR_HIP, "cache layout copy failed: %s", hipGetErrorString(e));
+    return WANVAE_OK;
+}
+}  // namespace
+
+int wanvae_stream_cache_export(const void *cache, void *out, const wanvae_dims *d, int32_t C, int32_t dtype,
+                               void *stream) {
+    return cache_io(cache, out, d, C, dtype, false, stream);
+}
+
+int wanvae_stream_cache_import(const void *in, void *cache, const wanvae_dims *d, int32_t C, int32_t dtype,
+                               void *stream) {
+    return cache_io(in, cache, d, C, dtype, true, stream);
+}
+
+int wanvae_stream_copy(const void *src, void *dst, int64_t bytes, int32_t unroll, int32_t blocks_per_cu,
+                       void *stream) {
+    g_error.clear();
+    WV_CHECK(bytes >= 0 && bytes % 16 == 0, WANVAE_ERR_SHAPE, "bytes must be a non-negative multiple of 16");
+    WV_CHECK(unroll == 1 || unroll == 2 || unroll == 4 || unroll == 8, WANVAE_ERR_SHAPE,
+             "unroll must be 1, 2, 4 or 8 (got %d)", unroll);
+    WV_CHECK(blocks_per_cu >= 1 && blocks_per_cu <= 64, WANVAE_ERR_SHAPE, "blocks_per_cu must be in [1, 64]");
+    if (bytes == 0) return WANVAE_OK;
+    WV_CHECK(src && dst, WANVAE_ERR_NULL, "src and dst are required");
+    WV_CHECK(aligned16(src) && aligned16(dst), WANVAE_ERR_SHAPE, "pointers must be 16-byte aligned");
+    WV_CHECK(!overlaps(src, (size_t)bytes, dst, (size_t)bytes), WANVAE_ERR_ALIAS, "dst overlaps src");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return timed_launch(WANVAE_KERNEL_COPY, s, "stream copy", [&] {
+        return wanvae::launch_stream_copy(src, dst, bytes, unroll, blocks_per_cu, s);
+    });
 }
 
 int wanvae_timing_enable(int on) {

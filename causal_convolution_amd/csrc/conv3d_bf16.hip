@@ -84,6 +84,13 @@
 // a stage is useful data, and x (channels-last) comes in 64-byte pieces per
 // position, which the LDS-DMA moves at twice the rate of 32-byte ones.
 //
+// Conv A of a ResidualBlock whose out_dim is one tile's channel block (96 or
+// 32) computes norm2 + SiLU in its epilogue (EPI_NORM): each wave holds every
+// channel of its output positions, so the sum of squares is one exchange
+// between a lane and its partner lane ^ 32, and n2 is written straight into
+// the 16-channel-slice layout conv B reads (a is never stored, nor read back
+// by a norm kernel).
+//
 // Tile order: batch slowest, then row block, column block, frame, and
 // output-channel block fastest.  Without a cache the tiles of frames 0 and 1
 // (a third and two thirds of the stages) form one work item, every other tile
@@ -140,7 +147,21 @@ constexpr int kSpinCapDefault = 1 << 15;
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitVm0 = waitcnt_vm(0);
 
-enum Epilogue { EPI_BIAS = 0, EPI_IDENTITY = 1, EPI_SHORTCUT = 2 };
+// EPI_NORM: conv A of the ResidualBlock with norm2 + SiLU in its epilogue,
+// for tiles whose waves hold every output channel of their positions (one
+// channel block per tile, WN = 1): y is then n2, in the 16-channel-slice
+// layout conv B reads, instead of a.
+enum Epilogue { EPI_BIAS = 0, EPI_IDENTITY = 1, EPI_SHORTCUT = 2, EPI_NORM = 3 };
+
+// u / (1 + exp(-u)); exp(-u) = inf for very negative u gives -0
+__device__ inline float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
+
+// sum of v over lanes l and l ^ 32: v_permlane32_swap on two copies of v
+// leaves each lane its own value and its partner's, one in each result
+__device__ inline float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct Args {
     const uint16_t *x;      // conv input [n][t][h][w][cin]
@@ -150,7 +171,10 @@ struct Args {
     const uint16_t *res;    // [n][t][h][w][cres] or null
     const uint16_t *wsc;    // [cout][cres] or null
     const float *bsc;       // [cout] or null
-    uint16_t *y;            // [n][t][h][w][cout]
+    uint16_t *y;            // [n][t][h][w][cout], or for EPI_NORM [n][t][cout/16][h][w][16]
+    // EPI_NORM: norm2 scale and shift ([cout] fp32, shift may be null) and eps
+    const float *ngamma, *nbeta;
+    float neps;
     int64_t N, T, H, W;
     int cin, cout, cres;
     int cout_p;             // cout rounded up to 32: the packed weight's channel count
@@ -308,7 +332,14 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         if constexpr (SC)
             if (a.bsc && c < a.cout) b += a.bsc[c];
         bias_lds[c] = b;
+        if constexpr (EPI == EPI_NORM) {
+            // gamma * sqrt(C) and beta after the bias
+            bias_lds[a.cout_p + c] = a.ngamma[c] * sqrtf((float)a.cout);
+            bias_lds[2 * a.cout_p + c] = a.nbeta ? a.nbeta[c] : 0.0f;
+        }
     }
+    static_assert(EPI != EPI_NORM || (WN == 1 && 3 * NB <= TL::kBiasBytes / 4),
+                  "the norm epilogue needs every channel of a position in one wave");
     __syncthreads();
     // flag accesses: relaxed atomics on the LDS array itself, so they stay
     // ds_read / ds_write (through a generic pointer they would become FLAT
@@ -1001,6 +1032,55 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             [&]<int... GI>(std::integer_sequence<int, GI...>) {
                 (step.template operator()<GI>(), ...);
             }(std::make_integer_sequence<int, NG>{});
+        } else if constexpr (EPI == EPI_NORM) {
+            // norm2 + SiLU of each output position from the fp32 accumulators
+            // (bias included): the lane holds 16 of every 32-channel block's
+            // channels (8j + 4g + q), its partner lane ^ 32 the other 16, so
+            // the sum of squares takes one exchange.  n2 goes out in the
+            // 16-channel-slice layout: through the staging buffer, each slice
+            // of a row is one 1 KB run (32 positions x 32 bytes), a lane
+            // storing half of one position's unit.
+            const float *gs = bias_lds + a.cout_p;        // gamma * sqrt(C)
+            const float *gb = bias_lds + 2 * a.cout_p;    // beta
+            const int p2 = lane >> 1, h2 = lane & 1;     // read-back: position, half unit
+            const int ww2 = ti.w0 + p2;
+#pragma unroll
+            for (int e = 0; e < FM; ++e) {
+                const int hh = ti.h0 + wm * FM + e;
+                float ss = 0.0f;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) ss = fmaf(acc[e][fn][k], acc[e][fn][k], ss);
+                ss = halves_sum(ss);
+                const float inv = 1.0f / fmaxf(sqrtf(ss), a.neps);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c0 = fn * 32 + 8 * j + 4 * g;
+                        const float4 gv = *reinterpret_cast<const float4 *>(gs + c0);
+                        const float4 bv = *reinterpret_cast<const float4 *>(gb + c0);
+                        const float v0 = silu(fmaf(acc[e][fn][4 * j] * inv, gv.x, bv.x));
+                        const float v1 = silu(fmaf(acc[e][fn][4 * j + 1] * inv, gv.y, bv.y));
+                        const float v2 = silu(fmaf(acc[e][fn][4 * j + 2] * inv, gv.z, bv.z));
+                        const float v3 = silu(fmaf(acc[e][fn][4 * j + 3] * inv, gv.w, bv.w));
+                        *reinterpret_cast<u32x2 *>(epi + l32 * kEpiStride + j * 16 + g * 8) =
+                            u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                    }
+                    // slice (2 fn + sl) of this row: position p2, bytes 16 h2 .. + 15
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) {
+                        const u32x4 d = *reinterpret_cast<const u32x4 *>(epi + p2 * kEpiStride + sl * 32 + h2 * 16);
+                        const uint32_t off = hh < H && ww2 < W
+                            ? (uint32_t)(((int64_t)(2 * fn + sl) * HW + hh * W + ww2) * kUnit) + h2 * 16
+                            : kOOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
+                    }
+                    // one channel block's scales in registers at a time
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         } else {
             store_rows(0, FM, nullptr);
         }
@@ -1080,6 +1160,9 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.gemm = c.gemm ? 1 : 0;
     a.up2 = c.up2 ? 1 : 0;
     a.spin_cap = g_spin_cap.load(std::memory_order_relaxed);
+    a.ngamma = c.norm_gamma;
+    a.nbeta = c.norm_beta;
+    a.neps = c.norm_eps;
     a.sc_in = static_cast<const uint16_t *>(c.gemm ? c.x : c.res);
     a.sc_c = c.gemm ? c.cin : c.cres;
     if (c.gemm) a.wsc = static_cast<const uint16_t *>(c.w);
@@ -1111,6 +1194,10 @@ bool conv3d_bf16_supported(int cin, int cout) {
     return cin >= 16 && cin <= 1024 && cin % 16 == 0 && cout >= 1 && cout <= 1024;
 }
 
+// The norm epilogue needs one channel block per tile (WN = 1): the
+// 96-channel kh-outer tile or the 32-channel one.
+bool conv3d_bf16_norm_supported(int cout) { return cout == 96 || cout == 32; }
+
 // Rows a tile height computes for an image height (the last tile is padded).
 int64_t rows_computed(int64_t h, int hb) { return (h + hb - 1) / hb * hb; }
 
@@ -1126,6 +1213,14 @@ int64_t rows_computed(int64_t h, int hb) { return (h + hb - 1) / hb * hb; }
 //    block padded with zero weights (the decoder's 3-channel conv_out).
 hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
     if (c.cout < 1 || c.cout > 1024) return hipErrorInvalidValue;
+    if (c.norm_out) {
+        // one channel block per tile: the 96-channel kh-outer tile, or the
+        // 32-channel one
+        if (c.res != nullptr || c.norm_gamma == nullptr || c.up2 || c.gemm) return hipErrorInvalidValue;
+        if (c.cout == 96) return launch_cfg<4, 1, 3, 3, EPI_NORM>(c, s);
+        if (c.cout == 32) return launch_cfg<4, 1, 4, 1, EPI_NORM>(c, s);
+        return hipErrorInvalidValue;
+    }
     const bool tall = rows_computed(c.h, 18) <= rows_computed(c.h, 16);
     if (c.res != nullptr && c.wsc != nullptr) {
         if (c.cout % 64 == 0)

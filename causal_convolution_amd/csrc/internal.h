@@ -34,6 +34,13 @@ struct ConvLaunch {
     // (h/2) x (w/2) read by nearest neighbour, w packed by
     // launch_pack_conv2d_weights; no cache, no residual
     bool up2 = false;
+    // bf16 only, conv3d_bf16_norm_supported(cout): y is silu(RMS_norm(conv)),
+    // the ResidualBlock's n2, with scale norm_gamma, shift norm_beta (or
+    // null) and clamp norm_eps, written in the 16-channel-slice layout
+    // [n][t][cout/16][h][w][16]; no residual
+    bool norm_out = false;
+    const float *norm_gamma = nullptr, *norm_beta = nullptr;
+    float norm_eps = 0.0f;
 };
 
 // Fused RMS_norm + SiLU over rows of C channels (C % 32 == 0, 32..1024).
@@ -57,6 +64,9 @@ hipError_t launch_rmsnorm_silu_f32(const void *x, void *y, int64_t rows, int C, 
 // multiple of 32 in the packed weight); cres (the block's shortcut input) a
 // multiple of 32.
 bool conv3d_bf16_supported(int cin, int cout);
+// C_out for which the conv can compute norm2 + SiLU in its epilogue (a tile
+// holds every channel of its positions): 32 and 96.
+bool conv3d_bf16_norm_supported(int cout);
 // The bf16 causal conv for C_out <= 3 (the taps on the MFMA M dimension, then
 // a tap sum per output): channels-last x and cache, 16 <= C_in <= 96, C_in a
 // multiple of 16; no residual or shortcut.
@@ -107,6 +117,18 @@ hipError_t launch_pack_conv3d_weights(const void *w, void *out, int cin, int cou
 // x, w, y of one dtype, fp32 accumulation; cin, cout in [1, 64]; y must not overlap x.
 hipError_t launch_pointwise_conv(const void *x, const void *w, const float *bias, void *y,
                                  int64_t rows, int cin, int cout, bool bf16, hipStream_t s);
+
+// Streaming copy of `bytes` (a multiple of 16) with `unroll` 16-byte pieces
+// per lane in flight (1, 2, 4 or 8) and at most blocks_per_cu workgroups of
+// 256 lanes per compute unit.
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, int unroll, int blocks_per_cu,
+                              hipStream_t s);
+
+// frames x hw positions x C channels (C % 16 == 0, bf16) between the
+// 16-channel-slice layout [frame][C/16][hw][16] and channels-last
+// [frame][hw][C]; to_sliced picks the direction.  src and dst must not overlap.
+hipError_t launch_cache_layout(const void *src, void *dst, int64_t frames, int64_t hw, int C, bool to_sliced,
+                               hipStream_t s);
 
 // fp32 direct conv, any channel counts.
 hipError_t launch_conv3d_f32(const ConvLaunch &a, hipStream_t s);

@@ -214,6 +214,19 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_silu_kernel(
             for (int q = 0; q < G; ++q) {
                 // all 64 lanes take part: the xor masks stay inside each 16-lane group
                 float t = ss[q];
+                // Row q's first piece sits at lane (q * RB / 16) % 16 of the
+                // group; rotating the partial sums so that it comes to lane 0
+                // makes the order of the sum below (and so its rounding) the
+                // same wherever a row falls in its group.  A position then
+                // gets the same norm whether it is normalised with its whole
+                // clip or in a chunk of frames (rows shift by the frames
+                // before it, h * w rows each, which need not be a multiple
+                // of G).
+                constexpr int kRowPieces = S::RB / 16;
+                if (G > 1 && (q * kRowPieces) % kGroupLanes != 0) {
+                    const int wl = threadIdx.x & 63;
+                    t = __shfl(t, (wl & ~(kGroupLanes - 1)) | ((wl + q * kRowPieces) & (kGroupLanes - 1)));
+                }
                 t += __shfl_xor(t, 1);
                 t += __shfl_xor(t, 2);
                 t += __shfl_xor(t, 4);

@@ -278,14 +278,32 @@ WANVAE_API int wanvae_resblock_forward_noalloc(const wanvae_resblock_params *p, 
  * the cache holds the last two frames of [cache, this chunk's conv input].
  * The frames are stored as the library stores conv inputs: [n][2][h][w][C]
  * for fp32, [n][2][C/16][h][w][16] (16-channel slices) for bf16; callers
- * treat the caches as opaque state.  A fresh stream starts from zero-filled
- * caches (zero is the causal pad in either layout), so running a clip chunk
- * by chunk gives the full-T result.  Caches must not overlap each other, x,
- * y or the workspace.
+ * treat the caches as opaque buffers of that many elements and read or set
+ * their frames channels-last with wanvae_stream_cache_export / _import.  A
+ * fresh stream starts from zero-filled caches (zero is the causal pad in
+ * either layout), so running a clip chunk by chunk gives the full-T result.
+ * Caches must not overlap each other, x, y or the workspace.
  */
 WANVAE_API int wanvae_resblock_stream_step(const wanvae_resblock_params *p, const void *x_chunk,
                                 void *y_chunk, const wanvae_dims *d, void *cache_a, void *cache_b,
                                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * A stream cache's frames, channels-last.  The feat_cache is the streaming
+ * decoder's only state ("Sharding of WAN 2.2 VAE", Why depth sharding is not
+ * beneficial: the last frames of every CausalConv3d's input); these calls let
+ * a caller save it and resume later, or seed it from frames of its own.
+ *   export: out = the cache's frames -2, -1 as [d.n][2][d.h][d.w][C];
+ *   import: the cache set from in = [d.n][2][d.h][d.w][C].
+ * C is in_dim for cache_a and out_dim for cache_b (a multiple of 16 for
+ * bf16); d.t is ignored.  For bf16 a permutation kernel on `stream` (bit for
+ * bit); for fp32, whose caches are channels-last already, a device copy on
+ * `stream`.  Device pointers, 16-byte aligned, not overlapping; asynchronous.
+ */
+WANVAE_API int wanvae_stream_cache_export(const void *cache, void *out, const wanvae_dims *d, int32_t C,
+                                          int32_t dtype, void *stream);
+WANVAE_API int wanvae_stream_cache_import(const void *in, void *cache, const wanvae_dims *d, int32_t C,
+                                          int32_t dtype, void *stream);
 
 /* Parameters of the decoder mid-block attention block (bf16).  All pointers
  * are device pointers. */
@@ -352,6 +370,20 @@ WANVAE_API int wanvae_wait_giveups(uint64_t *count);
 WANVAE_API int wanvae_wait_giveups_reset(void);
 WANVAE_API int wanvae_set_wait_bound(int32_t polls);
 
+/*
+ * A plain streaming copy, for measurement: dst = src over `bytes` bytes, each
+ * read once and written once, as the fused RMS_norm + SiLU reads its input
+ * and writes its output.  Its rate is the attainable HBM rate that the
+ * library's bandwidth-bound kernels are compared with (the 8 TB/s of the HBM
+ * specification is not reached by any copy).  16-byte nontemporal accesses
+ * per lane, `unroll` (1, 2, 4 or 8) of them in flight, at most blocks_per_cu
+ * (1..64) workgroups of 256 lanes per compute unit, striding over the buffer.
+ *   src, dst: device pointers, 16-byte aligned, not overlapping; bytes a
+ *   multiple of 16.  Asynchronous on `stream`; timed as WANVAE_KERNEL_COPY.
+ */
+WANVAE_API int wanvae_stream_copy(const void *src, void *dst, int64_t bytes, int32_t unroll,
+                                  int32_t blocks_per_cu, void *stream);
+
 /* Text of this thread's most recent error (library-owned, valid until the
  * thread's next call into the library).  "" when there was none. */
 WANVAE_API const char *wanvae_last_error(void);
@@ -363,14 +395,15 @@ WANVAE_API const char *wanvae_last_error(void);
  * one kernel kind, the number of launches and their summed duration in ms.
  * Kinds: 0 = fused RMS_norm+SiLU, 1 = bf16 MFMA conv, 2 = fp32 conv,
  * 3 = cache roll, 4 = pointwise conv, 5 = attention projection GEMM,
- * 6 = v transpose, 7 = flash attention.  wanvae_timing_reset forgets all
- * records.  Timing state is process-wide; enable it only while one thread
+ * 6 = v transpose, 7 = flash attention, 8 = upsampler conv, 9 = stream copy.
+ * wanvae_timing_reset forgets all records; at most 65536 launches are
+ * recorded between resets (later ones go untimed).  Timing state is process-wide; enable it only while one thread
  * drives the library.
  */
 enum { WANVAE_KERNEL_NORM = 0, WANVAE_KERNEL_CONV_BF16 = 1, WANVAE_KERNEL_CONV_F32 = 2,
        WANVAE_KERNEL_ROLL = 3, WANVAE_KERNEL_POINTWISE = 4, WANVAE_KERNEL_GEMM = 5,
        WANVAE_KERNEL_TRANSPOSE = 6, WANVAE_KERNEL_ATTENTION = 7, WANVAE_KERNEL_UPSAMPLE = 8,
-       WANVAE_KERNEL_KINDS = 9 };
+       WANVAE_KERNEL_COPY = 9, WANVAE_KERNEL_KINDS = 10 };
 WANVAE_API int wanvae_timing_enable(int on);
 WANVAE_API int wanvae_timing_reset(void);
 WANVAE_API int wanvae_timing_read(int32_t kind, int64_t *launches, double *total_ms);

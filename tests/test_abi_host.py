@@ -265,3 +265,19 @@ def test_forward_noalloc_validation():
     assert L.wanvae_resblock_forward_noalloc(C.byref(p2), x, y, C.byref(big), None) == wv.ERR_SHAPE
     empty = wv.Dims(1, 0, 8, 32)
     assert L.wanvae_resblock_forward_noalloc(C.byref(p), None, None, C.byref(empty), None) == wv.OK
+
+
+def test_stream_cache_io_validation():
+    L = wv.lib()
+    p, q = C.c_void_p(1 << 24), C.c_void_p(1 << 34)
+    d = _dims(1, 1, 4, 8)
+    for f in (L.wanvae_stream_cache_export, L.wanvae_stream_cache_import):
+        assert f(p, q, C.byref(d), 24, wv.BF16, None) == wv.ERR_SHAPE     # bf16 needs C % 16
+        assert f(p, q, C.byref(d), 0, wv.F32, None) == wv.ERR_SHAPE
+        assert f(p, q, C.byref(d), 64, 9, None) == wv.ERR_DTYPE
+        assert f(None, q, C.byref(d), 64, wv.BF16, None) == wv.ERR_NULL
+        assert f(p, q, None, 64, wv.BF16, None) == wv.ERR_NULL
+        assert f(p, C.c_void_p((1 << 24) + 64), C.byref(d), 64, wv.BF16, None) == wv.ERR_ALIAS
+        assert f(p, C.c_void_p((1 << 34) + 8), C.byref(d), 64, wv.BF16, None) == wv.ERR_SHAPE
+        empty = _dims(0, 1, 4, 8)
+        assert f(None, None, C.byref(empty), 64, wv.BF16, None) == wv.OK

@@ -251,6 +251,14 @@ SMALL_BLOCKS = [
     # single 64-wide chunk, and ragged position tiles
     wl.custom("sc256_320", wl.BF16, 1, 3, 7, 45, 256, 320),
     wl.custom("sc128_64", wl.BF16, 2, 2, 9, 20, 128, 64),
+    # conv A with norm2 + SiLU in its epilogue (out_dim 96 or 32): ragged rows
+    # and columns, batch 2, and with the fused 1x1x1 shortcut
+    wl.custom("id96_b2", wl.BF16, 2, 5, 13, 37, 96, 96),
+    wl.custom("id32", wl.BF16, 1, 4, 17, 45, 32, 32),
+    wl.custom("sc64_96", wl.BF16, 1, 3, 12, 40, 64, 96),
+    # the identity residual through the ring with 32-channel tiles over
+    # several channel blocks (160 = 5 x 32)
+    wl.custom("id160", wl.BF16, 1, 3, 10, 40, 160, 160),
 ]
 
 
@@ -401,8 +409,11 @@ def test_output_guard_bands(torch, wv):
     assert torch.equal(y, blk.forward(xd))
 
 
-def test_timing_counts_launches(torch, wv):
-    w = wl.custom("timing", wl.BF16, 1, 2, 8, 32, 96, 96)
+@pytest.mark.parametrize("cout,norms", [(192, 2), (96, 1)])
+def test_timing_counts_launches(torch, wv, cout, norms):
+    """Launches per forward: norm1, conv A, norm2, conv B; with 96 (or 32)
+    output channels conv A computes norm2 in its epilogue, one norm less."""
+    w = wl.custom("timing", wl.BF16, 1, 2, 8, 32, cout, cout)
     p, blk = _block(wv, w)
     xd = gu.to_dev(wl.make_x_host(w), w.dtype)
     wv.timing_reset()
@@ -413,7 +424,7 @@ def test_timing_counts_launches(torch, wv):
     n_norm, ms_norm = wv.timing_read(wv.KERNEL_NORM)
     n_conv, ms_conv = wv.timing_read(wv.KERNEL_CONV_BF16)
     wv.timing_reset()
-    assert n_norm == 4 and n_conv == 4
+    assert n_norm == 2 * norms and n_conv == 4
     assert ms_norm > 0 and ms_conv > 0
 
 
@@ -572,3 +583,71 @@ def test_upsample2d_decoder_sampled(torch, wv, shape, cout):
     _upsample_check(torch, wv, xd, x_host, w, b, f"{shape} -> {cout} sampled", frames=frames, rows=rows)
     del xd
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- reference copy
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000, (1 << 22) + 48])
+def test_stream_copy(torch, wv, nbytes):
+    """The measurement copy moves every byte and nothing past the end."""
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    for unroll in (1, 2, 4, 8):
+        buf = torch.full((nbytes + 4096,), 7, dtype=torch.uint8, device="cuda")
+        wv.stream_copy(src, buf[:nbytes], unroll, 4)
+        torch.cuda.synchronize()
+        assert torch.equal(buf[:nbytes], src)
+        assert bool((buf[nbytes:] == 7).all())
+
+
+# --------------------------------------------------------------------------- stream state
+@pytest.mark.parametrize("C", [16, 96, 384])
+def test_stream_cache_layout(torch, wv, C):
+    """export / import convert between the cache's 16-channel slices,
+    [n][2][C/16][h][w][16], and channels-last [n][2][h][w][C], bit for bit."""
+    n, h, w = 2, 5, 7
+    g = torch.Generator(device="cuda").manual_seed(C)
+    frames = torch.randn((n, 2, h, w, C), device="cuda", generator=g).to(torch.bfloat16)
+    sliced = frames.view(n, 2, h, w, C // 16, 16).permute(0, 1, 4, 2, 3, 5).contiguous().view(-1)
+    got = wv.export_stream_cache(sliced, n, h, w, C)
+    assert torch.equal(got, frames)
+    back = torch.zeros_like(sliced)
+    wv.import_stream_cache(frames, back)
+    assert torch.equal(back, sliced)
+
+
+@pytest.mark.parametrize("w", [wl.custom("ckpt_sc", wl.BF16, 1, 6, 12, 40, 384, 192),
+                               wl.custom("ckpt_id96", wl.BF16, 2, 6, 13, 37, 96, 96),
+                               wl.custom("ckpt_f32", wl.F32, 1, 6, 6, 10, 64, 32)],
+                         ids=lambda w: w.name)
+def test_stream_checkpoint_resume(torch, wv, w):
+    """Save the stream state mid-clip and resume from it: after 3 frames the
+    caches go to the host channels-last, the device caches are discarded, new
+    ones are set from the saved frames, and the last 3 frames stream on.  The
+    result equals full-T bit for bit, and the saved frames equal the oracle's
+    caches after the same 3 frames (n1 and n2 of frames 1 and 2) within the
+    bar."""
+    p, blk = _block(wv, w, seed=31)
+    x = wl.make_x_host(w, seed=31)
+    xd = gu.to_dev(x, w.dtype)
+    full = blk.forward(xd)
+    ca, cb = blk.new_caches(w.n, w.h, w.w)
+    ys = [blk.stream_step(xd[:, t:t + 1].contiguous(), ca, cb) for t in range(3)]
+    saved_a = blk.export_cache(ca, w.n, w.h, w.w, w.cin).cpu()
+    saved_b = blk.export_cache(cb, w.n, w.h, w.w, w.cout).cpu()
+    del ca, cb
+    ca, cb = blk.new_caches(w.n, w.h, w.w)
+    blk.import_cache(saved_a.to("cuda"), ca)
+    blk.import_cache(saved_b.to("cuda"), cb)
+    ys += [blk.stream_step(xd[:, t:t + 1].contiguous(), ca, cb) for t in range(3, w.t)]
+    ys = torch.cat(ys, 1)
+    assert torch.equal(ys, full), "resumed stream differs from full-T"
+    # the saved state against the oracle's caches after the same frames
+    ob = gu.oracle_block(p)
+    oa = np.zeros((w.n, 2, w.h, w.w, w.cin), np.float32)
+    obb = np.zeros((w.n, 2, w.h, w.w, w.cout), np.float32)
+    oracle.resblock_stream_step(ob, np.ascontiguousarray(x[:, :3]), oa, obb)
+    ea = gu.rel_err(saved_a.float().numpy(), oa)
+    eb = gu.rel_err(saved_b.float().numpy(), obb)
+    gu.report(f"checkpoint {w.name}: saved cache_a / cache_b vs oracle", max(ea, eb), tol(w.dtype),
+              f"a {ea:.3e} b {eb:.3e}")
+    assert ea <= tol(w.dtype) and eb <= tol(w.dtype)
