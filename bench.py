@@ -103,21 +103,18 @@ def measured_traffic(workload, kernel):
     return None if e is None else e["read_bytes"] + e["write_bytes"]
 
 
-def _counter_means(run_dir, counter):
-    """Per kernel name: the mean per-dispatch value of `counter` in the
-    rocprofv3 counter CSV(s) under run_dir."""
+def _counter_values(run_dir, counter):
+    """Per kernel name: the per-dispatch values of `counter` in the rocprofv3
+    counter CSV(s) under run_dir."""
     import csv
     import glob
-    sums = {}
+    vals = {}
     for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
             for row in csv.DictReader(f):
-                if row.get("Counter_Name") != counter:
-                    continue
-                k = row["Kernel_Name"]
-                s_, n_ = sums.get(k, (0.0, 0))
-                sums[k] = (s_ + float(row["Counter_Value"]), n_ + 1)
-    return {k: s_ / n_ for k, (s_, n_) in sums.items()}
+                if row.get("Counter_Name") == counter:
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return vals
 
 
 def record_traffic(workload, fetch_dir, write_dir, copy_bytes):
@@ -126,17 +123,26 @@ def record_traffic(workload, fetch_dir, write_dir, copy_bytes):
     ``bench.py --workload W --copy-calibration MIB`` (KiB per dispatch), each
     scaled by what the same counter reads for the run's plain copy of
     copy_bytes (read once, written once)."""
-    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
-    write = _counter_means(write_dir, "WRITE_SIZE")
+    fetch = _counter_values(fetch_dir, "FETCH_SIZE")
+    write = _counter_values(write_dir, "WRITE_SIZE")
 
     def pick(d, key):
-        ks = [k for k in d if key in k]
-        if not ks:
+        v = [x for k in d if key in k for x in d[k]]
+        if not v:
             raise SystemExit(f"no dispatch of a kernel named like {key!r} in the counters")
-        return sum(d[k] for k in ks) / len(ks)
+        return sum(v) / len(v)
 
-    ff = copy_bytes / (pick(fetch, "copyBuffer") * 1024)
-    wf = copy_bytes / (pick(write, "copyBuffer") * 1024)
+    def calib(d):
+        # the calibration copies: the largest runtime-copy dispatches (the
+        # run's small set-up copies go through the same kernel)
+        v = [x for k in d if "copyBuffer" in k for x in d[k]]
+        if not v:
+            raise SystemExit("no runtime copy in the counters (run with --copy-calibration)")
+        big = [x for x in v if x >= 0.5 * max(v)]
+        return sum(big) / len(big)
+
+    ff = copy_bytes / (calib(fetch) * 1024)
+    wf = copy_bytes / (calib(write) * 1024)
     entry = {"calibration": {"fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}}
     for name, key in (("conv", "conv3d_bf16_kernel"), ("norm", "rmsnorm_silu_kernel")):
         if any(key in k for k in fetch):

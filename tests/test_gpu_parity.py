@@ -651,3 +651,28 @@ def test_stream_checkpoint_resume(torch, wv, w):
     gu.report(f"checkpoint {w.name}: saved cache_a / cache_b vs oracle", max(ea, eb), tol(w.dtype),
               f"a {ea:.3e} b {eb:.3e}")
     assert ea <= tol(w.dtype) and eb <= tol(w.dtype)
+
+
+@pytest.mark.parametrize("cout", [96, 192])
+def test_block_zero_conv_a(torch, wv, cout):
+    """Conv A's weight and bias all zero: every a vector is zero, the norm's
+    clamp takes over and n2 = silu(beta2) at every position (in conv A's
+    epilogue at 96 channels, in the norm kernel at 192); the pad positions
+    conv B reads stay 0.  Against the oracle, with the residual branch gated
+    on its own."""
+    w = wl.custom(f"zero_a_{cout}", wl.BF16, 1, 3, 13, 37, cout, cout)
+    p = wl.make_params(w, seed=41)
+    p["wa"][:] = 0.0
+    p["ba"][:] = 0.0
+    blk = wv.ResBlock.from_host(p, torch.bfloat16)
+    # the branch is small here (conv B of one constant vector), so x is scaled
+    # by 2^-5 (exactly, in bf16) to keep y's own rounding, which grows with
+    # |y| ~ |x|, small next to the branch
+    x = wl.make_x_host(w, seed=41) * np.float32(2.0 ** -5)
+    y = gu.to_host(blk.forward(gu.to_dev(x, w.dtype)))
+    ob = gu.oracle_block(p)
+    ref = oracle.resblock_full(ob, x)
+    err = gu.rel_err(y, ref)
+    eb = gu.branch_err(ob, x, y, ref)
+    gu.report(f"block zero conv A, {cout} channels", err, gu.TOL_BF16, f"branch y-x: {eb:.3e}")
+    assert err <= gu.TOL_BF16 and eb <= gu.TOL_BF16
