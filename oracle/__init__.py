@@ -88,6 +88,9 @@ def lib():
         L.oracle_upsample2d_conv.argtypes = [_f32p, _i64, _i64, _i64, C.c_int, C.c_int, _f32p, _f32p,
                                              _i64, _i64, _f32p]
         L.oracle_upsample2d_conv.restype = None
+        L.oracle_upsample3d_conv.argtypes = [_f32p, _i64, _i64, _i64, _i64, C.c_int, C.c_int, _f32p, _f32p,
+                                             _f32p]
+        L.oracle_upsample3d_conv.restype = None
         for f in ("oracle_norm_silu", "oracle_rms_norm", "oracle_causal_conv3d", "oracle_shortcut",
                   "oracle_resblock_full", "oracle_resblock_stream_step",
                   "oracle_resblock_stream", "oracle_resblock_window"):
@@ -333,3 +336,20 @@ def upsample2d_conv(x, w, bias=None, frames=None, rows=None):
     y = np.empty((nf, r1 - r0, 2 * W, cout), np.float32)
     lib().oracle_upsample2d_conv(_ptr(xs), nf, H, W, cin, cout, _ptr(w), _ptr(bias), r0, r1, _ptr(y))
     return y.reshape(N, T, r1 - r0, 2 * W, cout) if frames is None else y
+
+
+def upsample3d_conv(x, w, bias=None):
+    """The decoder's upsample3d (readings in oracle.c, oracle_upsample3d_conv):
+    T frames to 2T - 1, output frame t' being input frame (t' + 1) // 2, then
+    each frame through upsample2d_conv.  x [N,T,H,W,Cin] (T >= 1); w
+    [Cout,Cin,3,3]; bias [Cout] or None.  Returns [N,2T-1,2H,2W,Cout]."""
+    x = _f32(x)
+    w = _f32(w)
+    N, T, H, W, cin = x.shape
+    assert T >= 1
+    cout = w.shape[0]
+    assert w.shape == (cout, cin, 3, 3)
+    bias = None if bias is None else _f32(bias)
+    y = np.empty((N, 2 * T - 1, 2 * H, 2 * W, cout), np.float32)
+    lib().oracle_upsample3d_conv(_ptr(x), N, T, H, W, cin, cout, _ptr(w), _ptr(bias), _ptr(y))
+    return y

@@ -556,3 +556,33 @@ void oracle_upsample2d_conv(const float *x, int64_t nf, int64_t H, int64_t W, in
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* The decoder's upsample3d: the frames doubled in time, then each frame     */
+/* through the spatial upsampler above.  "Sharding of WAN 2.2 VAE", decoder  */
+/* module tree: up_blocks[0] and up_blocks[1] end in upsample3d, and the     */
+/* decoder takes the 21 latent frames to 81 output frames ("Optimize         */
+/* attention ... WAN 2.2 Training on TPU 7x", inference validation workload:  */
+/* 81 frames; the mid-resolution block runs 41): each upsample3d takes T     */
+/* frames to 2T - 1.  How the frames are made is not on the pages; the       */
+/* reading used is the plainest causal one that gives 2T - 1, nearest        */
+/* neighbour in time with the first frame kept once:                          */
+/*   output frame 0 = input frame 0;                                          */
+/*   output frames 2k - 1 and 2k = input frame k   (k = 1 .. T - 1),          */
+/* i.e. output frame t' takes input frame (t' + 1) / 2 (integer division),    */
+/* so an output frame depends on no later input frame.                        */
+/* x: [N][T][H][W][cin]; w: [cout][cin][3][3]; b: [cout] or NULL;             */
+/* y: [N][2T - 1][2H][2W][cout].                                              */
+/* ------------------------------------------------------------------------ */
+void oracle_upsample3d_conv(const float *x, int64_t N, int64_t T, int64_t H, int64_t W, int cin, int cout,
+                            const float *w, const float *b, float *y)
+{
+    const int64_t To = 2 * T - 1;
+    const int64_t in_frame = H * W * (int64_t)cin, out_frame = 4 * H * W * (int64_t)cout;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t t = 0; t < To; ++t) {
+            const int64_t src = (t + 1) / 2;
+            oracle_upsample2d_conv(x + (n * T + src) * in_frame, 1, H, W, cin, cout, w, b, 0, 2 * H,
+                                   y + (n * To + t) * out_frame);
+        }
+}

@@ -49,6 +49,8 @@ MUTANTS = {
     "upsample_kh_kw_transposed": ("* cin + ci) * 3 + kh) * 3 + kw]", "* cin + ci) * 3 + kw) * 3 + kh]"),
     "upsample_dropped_bias": ("if (b) acc += (double)b[co];", "if (b) acc += 0.0;"),
     "upsample_row_stride": ("xf + ((uh / 2) * W + uw / 2)", "xf + ((uh / 2) * 2 * W / 2 + uw / 2 + uh % 2)"),
+    "upsample3d_frames_anti_causal": ("const int64_t src = (t + 1) / 2;", "const int64_t src = t / 2;"),
+    "upsample3d_resize_nearest": ("const int64_t src = (t + 1) / 2;", "const int64_t src = t * T / To;"),
 }
 
 

@@ -603,3 +603,86 @@ def test_upsample2d_rows_and_frames_equal_full(orc):
     part = orc.upsample2d_conv(x, w, b, frames=[(1, 2), (0, 0)], rows=(3, 8))
     assert np.array_equal(part[0], full[1, 2, 3:8])
     assert np.array_equal(part[1], full[0, 0, 3:8])
+
+
+# --------------------------------------------------------------------------- upsample3d
+def _frames_doubled_after_first(x):
+    """Frame 0 once, then every later frame twice, built with numpy's repeat:
+    the frame sequence the temporal reading gives (T -> 2T - 1)."""
+    return np.concatenate([x[:, :1], np.repeat(x[:, 1:], 2, axis=1)], axis=1)
+
+
+@pytest.mark.parametrize("shape,cout", [((1, 3, 3, 5, 8), 4), ((2, 2, 4, 4, 16), 8), ((1, 1, 2, 3, 4), 3)])
+def test_upsample3d_matches_library_routines(orc, shape, cout):
+    """torch fp64: the frames doubled after the first (torch
+    repeat_interleave), then F.interpolate(nearest, x2 in H and W) and
+    F.conv2d(padding=1) per frame."""
+    import torch
+    rng = np.random.default_rng(sum(shape) + 3 * cout)
+    x = rng.standard_normal(shape).astype(np.float32)
+    w, b = _up_params(rng, shape[-1], cout)
+    y = orc.upsample3d_conv(x, w, b)
+    N, T, H, W, C = shape
+    X = torch.from_numpy(x).double()
+    X = torch.cat([X[:, :1], torch.repeat_interleave(X[:, 1:], 2, dim=1)], dim=1)   # [N, 2T-1, H, W, C]
+    To = 2 * T - 1
+    U = torch.nn.functional.interpolate(X.reshape(N * To, H, W, C).permute(0, 3, 1, 2), scale_factor=2,
+                                        mode="nearest")
+    R = torch.nn.functional.conv2d(U, torch.from_numpy(w).double(), torch.from_numpy(b).double(), padding=1)
+    ref = R.permute(0, 2, 3, 1).reshape(N, To, 2 * H, 2 * W, cout).numpy()
+    assert y.shape == ref.shape == (N, To, 2 * H, 2 * W, cout)
+    assert np.abs(y - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_upsample3d_brute_force(orc):
+    """Pure-Python loops: for output frame t', the input frame is looked up in
+    an explicit list [0, 1, 1, 2, 2, ...]; bounds checked per tap."""
+    rng = np.random.default_rng(12)
+    T, H, W, cin, cout = 3, 2, 2, 2, 3
+    x = rng.standard_normal((1, T, H, W, cin)).astype(np.float32)
+    w, b = _up_params(rng, cin, cout)
+    y = orc.upsample3d_conv(x, w, b)
+    src = [0]
+    for k in range(1, T):
+        src += [k, k]
+    assert y.shape[1] == len(src) == 5
+    for tt, s in enumerate(src):
+        for h in range(2 * H):
+            for c in range(2 * W):
+                for co in range(cout):
+                    acc = float(b[co])
+                    for kh in range(3):
+                        for kw in range(3):
+                            uh, uw = h + kh - 1, c + kw - 1
+                            if 0 <= uh < 2 * H and 0 <= uw < 2 * W:
+                                for ci in range(cin):
+                                    acc += float(w[co, ci, kh, kw]) * float(x[0, s, uh // 2, uw // 2, ci])
+                    assert abs(y[0, tt, h, c, co] - acc) <= 1e-6 * (1 + abs(acc))
+
+
+def test_upsample3d_equals_upsample2d_of_doubled_frames(orc):
+    """Bitwise equal to the pinned spatial upsampler on the frame sequence
+    built by numpy's repeat; one frame in gives that frame's upsample2d."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((2, 4, 3, 5, 16)).astype(np.float32)
+    w, b = _up_params(rng, 16, 8)
+    assert np.array_equal(orc.upsample3d_conv(x, w, b), orc.upsample2d_conv(_frames_doubled_after_first(x), w, b))
+    assert np.array_equal(orc.upsample3d_conv(x[:, :1], w, b), orc.upsample2d_conv(x[:, :1], w, b))
+
+
+def test_upsample3d_is_causal(orc):
+    """A clip's first k + 1 frames give the first 2k + 1 output frames
+    (bitwise), and changing input frame k changes output frames 2k - 1 and
+    2k only (frame 0 for k = 0)."""
+    rng = np.random.default_rng(14)
+    T = 5
+    x = rng.standard_normal((1, T, 3, 4, 16)).astype(np.float32)
+    w, b = _up_params(rng, 16, 8)
+    full = orc.upsample3d_conv(x, w, b)
+    for k in range(T):
+        assert np.array_equal(orc.upsample3d_conv(x[:, :k + 1], w, b), full[:, :2 * k + 1])
+        xk = x.copy()
+        xk[:, k] += 1.0
+        yk = orc.upsample3d_conv(xk, w, b)
+        changed = [t for t in range(2 * T - 1) if not np.array_equal(yk[:, t], full[:, t])]
+        assert changed == ([0] if k == 0 else [2 * k - 1, 2 * k])
