@@ -272,30 +272,36 @@ def time_ops(torch, wv, ops, steps, warmup, min_warm_s=0.05):
 
 
 def upsample(torch, wv, steps, warmup):
-    """The decoder's spatial upsamplers (wanvae_upsample2d_conv: nearest x2,
-    then the 3x3 conv halving the channels) at the Wan 2.2 720p decoder
-    shapes, with the frame counts of the blocks around them: 384 -> 192 from
-    90 x 160 (21 frames) and from 180 x 320 (41 frames), 192 -> 96 from
-    360 x 640 (81 frames).  Seeded synthetic bf16 values."""
+    """The decoder's upsamplers in the order the Wan 2.2 720p decoder runs
+    them: upsample3d 384 -> 192 from [1,21,90,160] (to 41 frames of
+    180 x 320), upsample3d 384 -> 192 from [1,41,180,320] (to 81 frames of
+    360 x 640), and upsample2d 192 -> 96 from [1,81,360,640] (to 720 x 1280)
+    (wanvae_upsample3d_conv / wanvae_upsample2d_conv: frames doubled after the
+    first for the 3D ones, nearest x2 in H and W, then the 3x3 conv halving
+    the channels).  Seeded synthetic bf16 values."""
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
     res = []
-    for (t, h, w, cin, cout) in [(21, 90, 160, 384, 192), (41, 180, 320, 384, 192), (81, 360, 640, 192, 96)]:
+    for (t, h, w, cin, cout, temporal) in [(21, 90, 160, 384, 192, True), (41, 180, 320, 384, 192, True),
+                                           (81, 360, 640, 192, 96, False)]:
         x = torch.empty((1, t, h, w, cin), dtype=torch.bfloat16, device="cuda")
         for i in range(t):
             x[0, i].copy_(torch.randn((h, w, cin), device="cuda", generator=g))
         wp = wv.pack_conv2d_weights((torch.randn((cout, cin, 3, 3), device="cuda", generator=g)
                                      * (1.0 / (9 * cin)) ** 0.5).to(torch.bfloat16))
         b = torch.randn(cout, device="cuda", generator=g) * 0.1
-        y = torch.empty((1, t, 2 * h, 2 * w, cout), dtype=torch.bfloat16, device="cuda")
-        P_in, P_out = t * h * w, t * 4 * h * w
-        ops = [(f"upsample2d {cin}->{cout}, [1,{t},{h},{w},{cin}] -> [1,{t},{2 * h},{2 * w},{cout}]",
-                wv.KERNEL_UPSAMPLE, lambda: wv.upsample2d_conv(x, wp, b, out=y),
+        to = 2 * t - 1 if temporal else t
+        y = torch.empty((1, to, 2 * h, 2 * w, cout), dtype=torch.bfloat16, device="cuda")
+        P_in, P_out = t * h * w, to * 4 * h * w
+        fn = wv.upsample3d_conv if temporal else wv.upsample2d_conv
+        name = "upsample3d" if temporal else "upsample2d"
+        ops = [(f"{name} {cin}->{cout}, [1,{t},{h},{w},{cin}] -> [1,{to},{2 * h},{2 * w},{cout}]",
+                wv.KERNEL_UPSAMPLE, lambda: fn(x, wp, b, out=y),
                 2.0 * P_out * cout * 9 * cin, 2.0 * (P_in * cin + P_out * cout))]
         res += time_ops(torch, wv, ops, steps, warmup)
         del x, y
         torch.cuda.empty_cache()
-    return {"metric": "decoder spatial upsampler conv, average launch time (1 GPU)", "unit": "ms",
+    return {"metric": "decoder upsampler convs, average launch time (1 GPU)", "unit": "ms",
             "higher_is_better": False, "dtype": "bf16", "data": "synthetic (seeded)",
             "steps": steps, "warmup": warmup, "ops": res}
 
@@ -473,8 +479,8 @@ def main():
                     help="time the decoder mid-block attention block instead, at the latent "
                          "shape [1,21,90,160,384] (one JSON line)")
     ap.add_argument("--upsample", action="store_true",
-                    help="time the decoder's spatial upsampler conv instead (nearest x2 + 3x3 "
-                         "conv) at the three decoder upsampler shapes (one JSON line)")
+                    help="time the decoder's upsamplers instead (two upsample3d, one upsample2d, "
+                         "at the decoder's shapes; one JSON line)")
     ap.add_argument("--copy-bound", action="store_true",
                     help="measure the attainable HBM rate instead: the library's streaming copy "
                          "and the fused norm at one output-resolution activation (one JSON line)")

@@ -70,6 +70,8 @@ EXPORTS = {
                                          C.c_void_p, C.c_size_t, C.c_void_p]),
     "wanvae_upsample2d_conv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(Dims),
                                          C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
+    "wanvae_upsample3d_conv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(Dims),
+                                         C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
     "wanvae_pack_conv2d_weights": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                              C.c_void_p]),
     "wanvae_packed_conv2d_weight_elems": (C.c_int, [C.c_int32, C.c_int32, C.c_int32,
@@ -297,6 +299,30 @@ def upsample2d_conv(x, w, bias=None, out=None, stream=None):
     _dev(y, "out", x.dtype, shape)
     d = Dims(n, t, h, wd)
     _check(lib().wanvae_upsample2d_conv(_ptr(x), _ptr(w.data), _ptr(bias), _ptr(y), C.byref(d), cin, cout,
+                                        BF16, _stream(stream)))
+    return y
+
+
+def upsample3d_conv(x, w, bias=None, out=None, stream=None):
+    """The decoder's upsample3d (``wanvae_upsample3d_conv``): x [n,t,h,w,Cin]
+    bf16, w a PackedWeight2d (Cin -> Cout), bias [Cout] fp32 or None ->
+    [n,2t-1,2h,2w,Cout]: output frame t' is input frame (t'+1)//2, doubled
+    in H and W by nearest neighbour, then the 3x3 conv."""
+    torch = _torch()
+    n, t, h, wd, cin = x.shape
+    if not isinstance(w, PackedWeight2d):
+        raise TypeError("w must be a PackedWeight2d (see pack_conv2d_weights)")
+    if w.cin != cin:
+        raise ValueError(f"w is {w.cin}->{w.cout}, x has {cin} channels")
+    cout = w.cout
+    _dev(x, "x", torch.bfloat16)
+    _dev(w.data, "w", torch.bfloat16, (packed_conv2d_weight_elems(cin, cout),))
+    _dev(bias, "bias", torch.float32, (cout,))
+    shape = (n, max(2 * t - 1, 0), 2 * h, 2 * wd, cout)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    _dev(y, "out", x.dtype, shape)
+    d = Dims(n, t, h, wd)
+    _check(lib().wanvae_upsample3d_conv(_ptr(x), _ptr(w.data), _ptr(bias), _ptr(y), C.byref(d), cin, cout,
                                         BF16, _stream(stream)))
     return y
 

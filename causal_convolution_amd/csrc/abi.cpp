@@ -426,18 +426,21 @@ int wanvae_pack_conv2d_weights(const void *w, void *packed, int32_t cin, int32_t
     return WANVAE_OK;
 }
 
-int wanvae_upsample2d_conv(const void *x, const void *w, const float *bias, void *y, const wanvae_dims *d,
-                           int32_t cin, int32_t cout, int32_t dtype, void *stream) {
+namespace {
+// upsample2d (temporal = false) and upsample3d (temporal: 2t - 1 output frames)
+int upsample_conv(const void *x, const void *w, const float *bias, void *y, const wanvae_dims *d, int32_t cin,
+                  int32_t cout, int32_t dtype, bool temporal, void *stream) {
     g_error.clear();
     WV_CHECK(valid_dtype(dtype), WANVAE_ERR_DTYPE, "unknown dtype %d", dtype);
     WV_CHECK(dtype == WANVAE_BF16, WANVAE_ERR_DTYPE, "the upsampler conv is bf16 only");
     int64_t P = 0;
     if (int r = positions(d, &P)) return r;
     if (int r = check_conv_channels(cin, cout, dtype)) return r;
-    // the output frame is 2h x 2w
+    // the output frame is 2h x 2w; upsample3d makes 2t - 1 frames of t
     wanvae_dims od = *d;
     od.h = 2 * d->h;
     od.w = 2 * d->w;
+    if (temporal) od.t = d->t > 0 ? 2 * d->t - 1 : 0;
     int64_t Po = 0;
     if (int r = positions(&od, &Po)) return r;
     if (int r = check_conv_slab(d, cin, dtype)) return r;
@@ -462,9 +465,21 @@ int wanvae_upsample2d_conv(const void *x, const void *w, const float *bias, void
     c.cin = cin;
     c.cout = cout;
     c.up2 = true;
+    c.up_t = temporal;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return timed_launch(WANVAE_KERNEL_UPSAMPLE, s, "upsample2d conv",
+    return timed_launch(WANVAE_KERNEL_UPSAMPLE, s, temporal ? "upsample3d conv" : "upsample2d conv",
                         [&] { return wanvae::launch_conv3d_bf16(c, s); });
+}
+}  // namespace
+
+int wanvae_upsample2d_conv(const void *x, const void *w, const float *bias, void *y, const wanvae_dims *d,
+                           int32_t cin, int32_t cout, int32_t dtype, void *stream) {
+    return upsample_conv(x, w, bias, y, d, cin, cout, dtype, false, stream);
+}
+
+int wanvae_upsample3d_conv(const void *x, const void *w, const float *bias, void *y, const wanvae_dims *d,
+                           int32_t cin, int32_t cout, int32_t dtype, void *stream) {
+    return upsample_conv(x, w, bias, y, d, cin, cout, dtype, true, stream);
 }
 
 int wanvae_pointwise_conv(const void *x, const void *w, const float *bias, void *y, int64_t rows,

@@ -198,6 +198,11 @@ struct Args {
     // image is x[h/2][w/2]); only the current frame's taps, packed weight
     // [cin/16][9 taps][cout][16]; no cache
     int up2;
+    // with up2: the frames doubled in time as well (upsample3d): x holds
+    // xT = (T + 1) / 2 frames per batch item and output frame t reads input
+    // frame (t + 1) / 2; otherwise xT = T and frame t reads frame t
+    int up_t;
+    int64_t xT;
     // polls before a flag wait gives up (and is counted)
     int spin_cap;
 };
@@ -489,8 +494,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     kt = ti.kt_begin + cs / ck;
                     cc = cs % ck;
                 }
-                const int64_t ts = ti.tq + kt - 2;
-                abase = (ts >= 0 ? a.x + ((ti.nq * a.T + ts) * HWi) * a.cin
+                // (the temporal upsampler reads input frame (t + 1) / 2 for
+                // output frame t; it has only the current-frame tap)
+                const int64_t ts = a.up_t ? (ti.tq + 1) >> 1 : ti.tq + kt - 2;
+                abase = (ts >= 0 ? a.x + ((ti.nq * a.xT + ts) * HWi) * a.cin
                                  : a.cache + ((ti.nq * 2 + (ts + 2)) * HWi) * a.cin) +
                         cc * slice_elems;
                 abytes = (uint32_t)(HWi * a.cin * 2 - cc * slice_elems * 2);
@@ -1159,6 +1166,8 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.x_sliced = c.x_sliced ? 1 : 0;
     a.gemm = c.gemm ? 1 : 0;
     a.up2 = c.up2 ? 1 : 0;
+    a.up_t = c.up2 && c.up_t ? 1 : 0;
+    a.xT = a.up_t ? (c.t + 1) / 2 : c.t;
     a.spin_cap = g_spin_cap.load(std::memory_order_relaxed);
     a.ngamma = c.norm_gamma;
     a.nbeta = c.norm_beta;

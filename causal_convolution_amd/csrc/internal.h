@@ -34,6 +34,10 @@ struct ConvLaunch {
     // (h/2) x (w/2) read by nearest neighbour, w packed by
     // launch_pack_conv2d_weights; no cache, no residual
     bool up2 = false;
+    // with up2: the frames doubled in time too (upsample3d): t is the
+    // output's 2 t_in - 1 frames, x has t_in = (t + 1) / 2 frames per batch
+    // item, and output frame t' reads input frame (t' + 1) / 2
+    bool up_t = false;
     // bf16 only, conv3d_bf16_norm_supported(cout): y is silu(RMS_norm(conv)),
     // the ResidualBlock's n2, with scale norm_gamma, shift norm_beta (or
     // null) and clamp norm_eps, written in the 16-channel-slice layout

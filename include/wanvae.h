@@ -146,8 +146,8 @@ WANVAE_API int wanvae_packed_conv3d_weight_elems(int32_t cin, int32_t cout, int3
  * with the terms outside the 2h x 2w image left out.  The doubled image is
  * never stored: the conv reads each input position for the output positions
  * it covers.  bf16 only (other dtypes: WANVAE_ERR_DTYPE); fp32 accumulation,
- * bias added in fp32, one RNE rounding.  The temporal half of upsample3d is
- * not described on the pages and is not provided.
+ * bias added in fp32, one RNE rounding.  wanvae_upsample3d_conv adds the
+ * temporal doubling of upsample3d.
  *   x     : [n][t][h][w][cin] bf16, channels-last (d gives this extent).
  *   w     : packed by wanvae_pack_conv2d_weights (cin x cout).
  *   bias  : [cout] fp32 or NULL.
@@ -156,6 +156,30 @@ WANVAE_API int wanvae_packed_conv3d_weight_elems(int32_t cin, int32_t cout, int3
  *   y below 2 GiB.  Asynchronous on `stream`; allocates nothing.
  */
 WANVAE_API int wanvae_upsample2d_conv(const void *x, const void *w, const float *bias, void *y,
+                                      const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
+                                      void *stream);
+
+/*
+ * Decoder upsampler with the frames doubled in time (upsample3d): T frames
+ * become 2T - 1, then each frame goes through wanvae_upsample2d_conv's
+ * spatial doubling and 3x3 conv.  The pages fix only the frame counts (up
+ * blocks 0 and 1 of "Sharding of WAN 2.2 VAE"'s decoder module tree end in
+ * upsample3d; 21 latent frames, "Closing the gap", gap #1, become the 81 of
+ * the decoded video, "Optimize attention ... WAN 2.2 Training on TPU 7x",
+ * inference validation table); the frames are made by nearest neighbour in
+ * time with the first kept once:
+ *   output frame 0 = input frame 0, output frames 2k - 1 and 2k = input frame k
+ * (output frame t' reads input frame (t' + 1) / 2, no later frame), so
+ *   y[n][t'][h][w][co] = bias[co] + sum_{kh,kw,ci} w[co][ci][kh][kw] *
+ *                        x[n][(t'+1)/2][(h+kh-1)/2][(w+kw-1)/2][ci]
+ * with the terms outside the 2h x 2w image left out.  bf16 only; fp32
+ * accumulation, one RNE rounding.
+ *   x : [n][t][h][w][cin] bf16, channels-last (d gives this extent).
+ *   w : packed by wanvae_pack_conv2d_weights; bias: [cout] fp32 or NULL.
+ *   y : [n][2t - 1][2h][2w][cout] bf16; must not overlap x or w.
+ *   Same channel and frame-size limits as wanvae_upsample2d_conv.
+ */
+WANVAE_API int wanvae_upsample3d_conv(const void *x, const void *w, const float *bias, void *y,
                                       const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
                                       void *stream);
 

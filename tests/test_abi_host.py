@@ -281,3 +281,17 @@ def test_stream_cache_io_validation():
         assert f(p, C.c_void_p((1 << 34) + 8), C.byref(d), 64, wv.BF16, None) == wv.ERR_SHAPE
         empty = _dims(0, 1, 4, 8)
         assert f(None, None, C.byref(empty), 64, wv.BF16, None) == wv.OK
+
+
+def test_upsample3d_validation():
+    L = wv.lib()
+    p, q = C.c_void_p(1 << 24), C.c_void_p(1 << 34)
+    d = _dims()
+    up = L.wanvae_upsample3d_conv
+    assert up(p, p, None, q, C.byref(d), 64, 32, wv.F32, None) == wv.ERR_DTYPE     # bf16 only
+    assert up(p, p, None, q, C.byref(d), 24, 32, wv.BF16, None) == wv.ERR_SHAPE    # cin % 16
+    assert up(None, p, None, q, C.byref(d), 64, 32, wv.BF16, None) == wv.ERR_NULL
+    # y (2t - 1 frames of 2h x 2w) may not overlap x
+    assert up(p, q, None, C.c_void_p((1 << 24) + 1024), C.byref(d), 64, 32, wv.BF16, None) == wv.ERR_ALIAS
+    empty = _dims(1, 0, 3, 4)
+    assert up(None, None, None, None, C.byref(empty), 64, 32, wv.BF16, None) == wv.OK

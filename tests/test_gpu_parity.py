@@ -676,3 +676,60 @@ def test_block_zero_conv_a(torch, wv, cout):
     eb = gu.branch_err(ob, x, y, ref)
     gu.report(f"block zero conv A, {cout} channels", err, gu.TOL_BF16, f"branch y-x: {eb:.3e}")
     assert err <= gu.TOL_BF16 and eb <= gu.TOL_BF16
+
+
+# --------------------------------------------------------------------------- upsample3d
+@pytest.mark.parametrize("shape,cout", [
+    ((1, 3, 5, 17, 16), 32),     # 5 output frames, ragged row and column tiles
+    ((2, 2, 9, 16, 64), 64),     # batch 2, 18-row tiles
+    ((1, 4, 6, 12, 192), 96),    # 96-channel (kh-outer) tiles, 7 output frames
+    ((1, 1, 2, 3, 32), 3),       # one input frame: one output frame, 3 output channels
+    ((1, 3, 4, 9, 96), 40),      # a padded channel block
+])
+def test_upsample3d_small(torch, wv, shape, cout):
+    """The whole output against the oracle; and bitwise equal to upsample2d
+    of the frames doubled after the first (the same kernel on the same
+    values, the frame read remapped)."""
+    rng = np.random.default_rng(sum(shape) + 2 * cout)
+    x = wl.round_bf16(rng.standard_normal(shape).astype(np.float32))
+    w, b = wl.make_upsample_params(shape[-1], cout, seed=sum(shape) + 1)
+    wp = wv.pack_conv2d_weights(torch.from_numpy(w).to("cuda").to(torch.bfloat16))
+    bd = torch.from_numpy(b).to("cuda")
+    xd = gu.to_dev(x, wl.BF16)
+    y = wv.upsample3d_conv(xd, wp, bd)
+    ref = oracle.upsample3d_conv(x, w, b)
+    got = gu.to_host(y)
+    err = gu.rel_err(got, ref)
+    gu.report(f"upsample3d {shape} -> {cout}", err, gu.TOL_BF16, f"pcc={gu.pcc(got, ref):.6f}")
+    assert got.shape == ref.shape and err <= gu.TOL_BF16
+    idx = torch.tensor([0] + [k for k in range(1, shape[1]) for _ in range(2)], device="cuda")
+    y2 = wv.upsample2d_conv(xd.index_select(1, idx).contiguous(), wp, bd)
+    assert torch.equal(y, y2)
+
+
+def test_upsample3d_decoder_sampled(torch, wv):
+    """up_blocks[0]'s upsample3d at the decoder's shape, [1,21,90,160,384] ->
+    [1,41,180,320,192]: output frames 0..4 against the oracle on input frames
+    0..2 and output frames 37..40 against it on input frames 18..20 (an
+    output frame reads no later input frame, and frames 2k - 1, 2k only input
+    frame k), rows at the top, middle and bottom."""
+    w_ = wl.custom("up3", wl.BF16, 1, 21, 90, 160, 384, 192)
+    xd = wl.make_x_device(w_, seed=7)
+    w, b = wl.make_upsample_params(384, 192, seed=7)
+    wp = wv.pack_conv2d_weights(torch.from_numpy(w).to("cuda").to(torch.bfloat16))
+    y = wv.upsample3d_conv(xd, wp, torch.from_numpy(b).to("cuda"))
+    torch.cuda.synchronize()
+    rows = [(0, 3), (89, 92), (177, 180)]
+    errs = []
+    for (i0, i1, o0) in [(0, 3, 0), (18, 21, 36)]:
+        ref = oracle.upsample3d_conv(gu.to_host(xd[:, i0:i1]), w, b)      # 5 output frames
+        # a clip starting at input frame i0 reproduces output frames 2 i0 + 1 .. (not 2 i0 - 1, 2 i0)
+        first = 0 if i0 == 0 else 1
+        for (r0, r1) in rows:
+            got = gu.to_host(y[:, o0 + first:o0 + 5, r0:r1])
+            errs.append(gu.rel_err(got, ref[:, first:, r0:r1]))
+    err = max(errs)
+    gu.report("upsample3d [1,21,90,160,384] -> 192 sampled", err, gu.TOL_BF16)
+    assert err <= gu.TOL_BF16
+    del xd, y
+    torch.cuda.empty_cache()
