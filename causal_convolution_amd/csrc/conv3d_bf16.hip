@@ -371,17 +371,22 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int64_t ngroups = a.T - a.pair;   // frame groups: {0, 1}, 2, 3, ... when paired
     // tile `sub` of work item `tile`
     auto decode = [&](int64_t tile, int sub) __attribute__((always_inline)) {
+        // the divisors are made opaque here, so the divisions' reciprocals are
+        // formed per call (once per tile) instead of being held in vector
+        // registers across the whole kernel
+        int64_t d_cb = ncb, d_g = ngroups, d_w = a.tiles_w, d_h = a.tiles_h;
+        asm volatile("" : "+s"(d_cb), "+s"(d_g), "+s"(d_w), "+s"(d_h));
         TileInfo ti;
-        ti.n0 = (int)(tile % ncb) * NB;
-        tile /= ncb;
-        const int64_t grp = tile % ngroups;
-        tile /= ngroups;
+        ti.n0 = (int)(tile % d_cb) * NB;
+        tile /= d_cb;
+        const int64_t grp = tile % d_g;
+        tile /= d_g;
         ti.ntiles = a.pair && grp == 0 ? 2 : 1;
         ti.tq = a.pair ? (grp == 0 ? sub : grp + 1) : grp;
-        ti.w0 = (int)(tile % a.tiles_w) * kWB;
-        tile /= a.tiles_w;
-        ti.h0 = (int)(tile % a.tiles_h) * HB;
-        tile /= a.tiles_h;
+        ti.w0 = (int)(tile % d_w) * kWB;
+        tile /= d_w;
+        ti.h0 = (int)(tile % d_h) * HB;
+        tile /= d_h;
         ti.nq = tile;
         // without a cache the stages of frames before 0 only add zeros: skipped
         const int kt_begin = a.up2 ? 2 : (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
@@ -624,10 +629,16 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // alternates from stage to stage.
     bf16x8 fw[9][FN];
     bf16x8 fx[2][3];
-    constexpr bool ALT = (TL::KH_OUTER ? 3 * FM : NROW) % 2 == 1;   // rows per stage odd
+    // KH_OUTER tiles keep input rows across kernel rows instead: input row i
+    // of a stage (0 .. FM + 1) in fk[i % 3], the next stage's row 0 in fk[0]
+    bf16x8 fk[3][3];
+    constexpr bool ALT = !TL::KH_OUTER && NROW % 2 == 1;   // rows per stage odd
     // row 0 and the kh = 0 weights of the stage in `buf` (parity par)
     auto load_first = [&](const unsigned char *buf, int par) __attribute__((always_inline)) {
-        if (par) {
+        if constexpr (TL::KH_OUTER) {
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) fk[0][kw] = ldA(buf, 0, kw);
+        } else if (par) {
 #pragma unroll
             for (int kw = 0; kw < 3; ++kw) fx[1][kw] = ldA(buf, 0, kw);
         } else {
@@ -728,14 +739,19 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
     // The same stage for KH_OUTER tiles: for each kh, the 3 kw x FN weight
     // fragments of that kernel row (in fw[0..2]), then each output row fm
-    // with input row fm + kh.  The next input row is read while the current
-    // one computes, and the weights of kh + 1 replace those of kh, kw by kw,
-    // during the last row of kh.  The last row of kh = 2 reads, in the same
-    // way, the following ring slot's row 0 and kh = 0 weights, unconditionally
-    // as in the row-stationary stage; rows run r = kh * FM + fm, row r in
-    // fx[(r + PAR) & 1].
+    // with input row fm + kh.  An input row's fragments are read once per
+    // stage and kept while a later kernel row still uses them (rows 1 .. FM
+    // serve two or three kh): 3 (FM + 2) input reads per stage instead of
+    // 9 FM.  With FM = 3 at most three rows are live, so row i sits in
+    // fk[i % 3]: row 1 and 2 are read during the rows before their first
+    // use, row 3 (into row 0's registers) during kh = 1's first row, row 4
+    // during its second, and the following ring slot's row 0 during the
+    // stage's last row, which also reads that slot's kh = 0 weights
+    // (unconditionally, as in the row-stationary stage).  The weights of
+    // kh + 1 replace those of kh, kw by kw, during the last row of kh.
     auto compute_conv_kh = [&]<int PAR>(const unsigned char *buf, const unsigned char *next)
                                __attribute__((always_inline)) {
+        static_assert(FM == 3, "three live input rows hold exactly the rows a kernel-row change keeps");
         bool landed = false;
         int early = 0;
 #pragma unroll
@@ -743,7 +759,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int r = kh * FM + fm;
-                const int cur = (r + PAR) & 1;
+                const int row = fm + kh;
                 const bool last_row = fm + 1 == FM;
                 const bool final_row = kh == 2 && last_row;
                 if (r == 1) early = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
@@ -752,16 +768,18 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                     seen = f > seen ? f : seen;
                     landed = seen > consumed + 1;
                 }
-                // next row: input row fm + 1 + kh, the first row of kh + 1, or the next slot's row 0
-                const unsigned char *rb = final_row ? next : buf;
-                const int nr = final_row ? 0 : last_row ? kh + 1 : fm + 1 + kh;
+                // input row read during this row: rows 1 and 2 (kh = 0), 3 and 4 (kh = 1), the next slot's row 0
+                const int nr = kh == 0 && fm < 2 ? fm + 1 : kh == 1 && fm < 2 ? fm + 3 : final_row ? 0 : -1;
+                if (nr >= 0) {
+                    const unsigned char *rb = final_row ? next : buf;
 #pragma unroll
-                for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(rb, nr, kw);
+                    for (int kw = 0; kw < 3; ++kw) fk[nr % 3][kw] = ldA(rb, nr, kw);
+                }
 #pragma unroll
                 for (int kw = 0; kw < 3; ++kw) {
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kw][fn], fx[cur][kw],
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kw][fn], fk[row % 3][kw],
                                                                               acc[fm][fn], 0, 0, 0);
                     if (last_row) {
                         const unsigned char *wb = kh < 2 ? buf : next;
@@ -772,7 +790,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                 }
                 // LDS reads one after each MFMA, as in the row-stationary stage
                 constexpr int nm = 3 * FN;
-                const int nrd = 3 + (last_row ? 3 * FN : 0) + (r == 1 ? 1 : 0);
+                const int nrd = (nr >= 0 ? 3 : 0) + (last_row ? 3 * FN : 0) + (r == 1 ? 1 : 0);
 #pragma unroll
                 for (int k = 0; k < 9; ++k) {
                     if (k < nrd && k < nm) {
@@ -842,8 +860,9 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         if constexpr (TL::KH_OUTER) {
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
-                fx[0][j] = __builtin_nondeterministic_value(fx[0][j]);
-                fx[1][j] = __builtin_nondeterministic_value(fx[1][j]);
+                fk[0][j] = __builtin_nondeterministic_value(fk[0][j]);
+                fk[1][j] = __builtin_nondeterministic_value(fk[1][j]);
+                fk[2][j] = __builtin_nondeterministic_value(fk[2][j]);
             }
 #pragma unroll
             for (int tap = 0; tap < 3; ++tap)
