@@ -190,7 +190,10 @@ def head_tail(torch, wv, steps, warmup):
     720p decoder shapes: conv_in on the 16-channel latent [1,21,90,160,16] to
     384 channels, post_quant_conv (1x1x1, 16 -> 16) on the latent, and
     norm_out (RMS_norm + SiLU, 96 channels) + conv_out (96 -> 3) on the
-    output-resolution activation [1,81,720,1280,96].  Seeded synthetic bf16
+    output-resolution activation [1,81,720,1280,96], as two launches and as
+    the one fused launch (the norm applied as the conv reads its input: x read
+    once with the tiles' halos, y written; its FLOPs are the conv's, its bytes
+    x and y).  Seeded synthetic bf16
     values.  Per op: average launch time over `steps` launches, algorithmic
     FLOPs and HBM bytes (read inputs once, write outputs once), and the
     fraction of the bound that limits it (the larger of FLOPs / 2.5 PFLOP/s
@@ -228,6 +231,9 @@ def head_tail(torch, wv, steps, warmup):
          0.0, 2.0 * P_out * 96 * 2),
         ("conv_out 96->3, causal 3x3x3, [1,81,720,1280,96]", wv.KERNEL_CONV_BF16,
          lambda: wv.causal_conv3d(n_out, w_out, b3, out=y_out),
+         2.0 * P_out * 3 * 27 * 96, 2.0 * P_out * (96 + 3)),
+        ("norm_out + conv_out fused, [1,81,720,1280,96] -> 3", wv.KERNEL_CONV_BF16,
+         lambda: wv.rmsnorm_silu_conv_out(act, gam, bet, wv.EPS, w_out, b3, out=y_out),
          2.0 * P_out * 3 * 27 * 96, 2.0 * P_out * (96 + 3)),
     ]
     return {"metric": "decoder head/tail ops, average launch time (1 GPU)", "unit": "ms",

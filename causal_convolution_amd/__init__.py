@@ -54,6 +54,9 @@ EXPORTS = {
     "wanvae_causal_conv3d": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32,
                                        C.c_void_p]),
+    "wanvae_rmsnorm_silu_conv_out": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_float,
+                                               C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(Dims),
+                                               C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
     "wanvae_resblock_workspace_size": (C.c_int, [C.POINTER(ResblockParamsC), C.POINTER(Dims),
                                                  C.POINTER(C.c_size_t)]),
     "wanvae_resblock_forward": (C.c_int, [C.POINTER(ResblockParamsC), C.c_void_p, C.c_void_p,
@@ -248,6 +251,29 @@ def causal_conv3d(x, w, bias=None, cache=None, out=None, stream=None):
     d = Dims(n, t, h, wd)
     _check(lib().wanvae_causal_conv3d(_ptr(x), _ptr(cache), _ptr(w.data), _ptr(bias), _ptr(y),
                                       C.byref(d), cin, cout, _dtype_code(x), _stream(stream)))
+    return y
+
+
+def rmsnorm_silu_conv_out(x, gamma, beta, eps, w, bias=None, cache=None, out=None, stream=None):
+    """The decoder's norm_out -> SiLU -> conv_out in one pass
+    (``wanvae_rmsnorm_silu_conv_out``, bf16): x [n,t,h,w,Cin] the norm's
+    input, gamma/beta [Cin] fp32, w a PackedWeight (Cin -> Cout <= 3), cache
+    [n,2,h,w,Cin] of the norm's input or None -> [n,t,h,w,Cout]."""
+    torch = _torch()
+    n, t, h, wd, cin = x.shape
+    cout = w.cout
+    _dev(x, "x", torch.bfloat16)
+    _packed(w, "w", x.dtype, cin, cout)
+    _dev(gamma, "gamma", torch.float32, (cin,))
+    _dev(beta, "beta", torch.float32, (cin,))
+    _dev(bias, "bias", torch.float32, (cout,))
+    _dev(cache, "cache", x.dtype, (n, 2, h, wd, cin))
+    y = torch.empty((n, t, h, wd, cout), dtype=x.dtype, device=x.device) if out is None else out
+    _dev(y, "out", x.dtype, (n, t, h, wd, cout))
+    d = Dims(n, t, h, wd)
+    _check(lib().wanvae_rmsnorm_silu_conv_out(_ptr(x), _ptr(cache), _ptr(gamma), _ptr(beta), float(eps),
+                                              _ptr(w.data), _ptr(bias), _ptr(y), C.byref(d), cin, cout,
+                                              _dtype_code(x), _stream(stream)))
     return y
 
 

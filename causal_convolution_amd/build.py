@@ -32,6 +32,13 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 
 RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
 
+# Per-source device flags.  conv3d_narrow.hip: the narrow conv's row loop
+# (10 input rows per tile) must unroll fully so its accumulators stay in
+# registers (their row index is the loop's); with the fused input norm the
+# body outgrows the default limit for a requested full unroll, and the
+# accumulators would go to scratch (which check_resources rejects).
+EXTRA = {"conv3d_narrow.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
+
 
 def check_resources(src: str, remarks: str) -> None:
     """Fails the build if a kernel of `src` spills vector registers or uses
@@ -56,7 +63,7 @@ def check_resources(src: str, remarks: str) -> None:
 def _compile(src: str, verbose: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(OBJDIR, src + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE + [RESOURCE_REMARKS, "-c", path, "-o", obj]
+    cmd = [HIPCC] + COMMON + DEVICE + EXTRA.get(src, []) + [RESOURCE_REMARKS, "-c", path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON + ["-x", "hip"] + DEVICE + ["-c", path, "-o", obj]
     if verbose:

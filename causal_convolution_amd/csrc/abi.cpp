@@ -368,6 +368,47 @@ int wanvae_causal_conv3d(const void *x, const void *cache, const void *w, const 
     return run_conv(c, dtype, static_cast<hipStream_t>(stream));
 }
 
+int wanvae_rmsnorm_silu_conv_out(const void *x, const void *cache, const float *gamma, const float *beta,
+                                 float eps, const void *w, const float *bias, void *y, const wanvae_dims *d,
+                                 int32_t cin, int32_t cout, int32_t dtype, void *stream) {
+    g_error.clear();
+    WV_CHECK(dtype == WANVAE_BF16, WANVAE_ERR_DTYPE, "the fused norm + conv_out is bf16 only (got dtype %d)",
+             dtype);
+    WV_CHECK(cin >= 16 && cin <= 96 && cin % 16 == 0 && cout >= 1 && cout <= 3, WANVAE_ERR_SHAPE,
+             "the fused norm + conv_out needs cin a multiple of 16 in [16, 96] and cout in [1, 3] "
+             "(got %d, %d)", cin, cout);
+    WV_CHECK(std::isfinite(eps) && eps >= 0.0f, WANVAE_ERR_SHAPE, "eps must be finite and >= 0");
+    int64_t P = 0;
+    if (int r = positions(d, &P)) return r;
+    if (int r = check_conv_slab(d, cin, dtype)) return r;
+    if (P == 0) return WANVAE_OK;
+    WV_CHECK(x && w && y && gamma, WANVAE_ERR_NULL, "x, w, y and gamma are required");
+    WV_CHECK(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(cache) && aligned16(bias) &&
+                 aligned16(gamma) && aligned16(beta),
+             WANVAE_ERR_SHAPE, "pointers must be 16-byte aligned");
+    const size_t xb = (size_t)P * cin * 2, yb = (size_t)P * cout * 2;
+    const size_t cb = (size_t)d->n * 2 * d->h * d->w * cin * 2;
+    const size_t wb = (size_t)wanvae::packed_conv3d_weight_elems(cin, cout, true) * 2;
+    WV_CHECK(!overlaps(y, yb, x, xb) && !overlaps(y, yb, cache, cb) && !overlaps(y, yb, w, wb),
+             WANVAE_ERR_ALIAS, "y overlaps x, cache or w");
+    wanvae::ConvLaunch c;
+    c.x = x;
+    c.cache = cache;
+    c.w = w;
+    c.bias = bias;
+    c.y = y;
+    c.n = d->n;
+    c.t = d->t;
+    c.h = d->h;
+    c.w_ = d->w;
+    c.cin = cin;
+    c.cout = cout;
+    c.in_norm_gamma = gamma;
+    c.in_norm_beta = beta;
+    c.in_norm_eps = eps;
+    return run_conv(c, dtype, static_cast<hipStream_t>(stream));
+}
+
 int wanvae_pack_conv3d_weights(const void *w, void *packed, int32_t cin, int32_t cout, int32_t dtype,
                                void *stream) {
     g_error.clear();

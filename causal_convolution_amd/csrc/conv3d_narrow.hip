@@ -25,6 +25,18 @@
 // complete and stored; so each input frame's Z is computed once.  A chunk of
 // frames starts 2 frames early (from the cache, or skipped before frame 0) to
 // rebuild its accumulators.
+//
+// NORM: the decoder's tail norm_out -> SiLU -> conv_out in one pass.  The
+// kernel then reads the norm's input and normalises each input position as
+// its row arrives, before the MFMAs: the RMS_norm + SiLU of "Closing the gap",
+// section 4 (d = max(sqrt(sum_c v_c^2), eps), u_c = v_c sqrt(C) / d gamma_c +
+// beta_c, silu(u_c)), rounded to bf16 as a separate norm's output would be.
+// Lane (l32, g) holds 8 of every 16 channels of its position and lane ^ 32
+// the other 8, so the sum of squares takes one exchange.  Positions outside
+// the frame stay 0 (the conv's zero pad applies to the norm's output), and a
+// cache holds the norm's input frames, normalised on the way in like x.  The
+// activation's round trip through memory (the norm writing it, the conv
+// reading it back) is gone: x is read once, with the tiles' halos.
 #include "bf16.h"
 #include "internal.h"
 
@@ -41,17 +53,35 @@ constexpr int kChunk = 27;             // frames per work item
 constexpr int kMT = 3;                 // 32-row MFMA tiles over the 27 C_out (tap, co) rows
 constexpr int kZS = 64;                // LDS row stride of Z (transposed: [row][position]) in floats
 
-template <int KS, int COUT>
+__device__ inline float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
+
+// the norm of NORM kernels: scale gamma (sqrt(C) applied here), shift beta
+// (or null), clamp eps
+struct InNorm {
+    const float *gamma = nullptr, *beta = nullptr;
+    float eps = 0.0f, sqrt_c = 0.0f;
+};
+
+template <int KS, int COUT, bool NORM>
 __global__ __launch_bounds__(64) void conv3d_narrow_kernel(const uint16_t *__restrict__ x,
                                                            const uint16_t *__restrict__ cache,
                                                            const uint16_t *__restrict__ wp,
                                                            const float *__restrict__ bias,
                                                            uint16_t *__restrict__ y, int T, int H, int W,
-                                                           int tiles_h, int tiles_w, int chunks) {
+                                                           int tiles_h, int tiles_w, int chunks, InNorm nm) {
     constexpr int CIN = 16 * KS;
     __shared__ __attribute__((aligned(16))) float zl[96 * kZS];
+    // NORM: gamma * sqrt(C) of each input channel, then beta
+    __shared__ __attribute__((aligned(16))) float nrm[NORM ? 2 * CIN : 4];
     const int lane = threadIdx.x;
     const int l32 = lane & 31, g = lane >> 5;
+    if constexpr (NORM) {
+        for (int c = lane; c < CIN; c += 64) {
+            nrm[c] = nm.gamma[c] * nm.sqrt_c;
+            nrm[CIN + c] = nm.beta ? nm.beta[c] : 0.0f;
+        }
+        __syncthreads();
+    }
 
     int64_t item = blockIdx.x;
     const int chunk = (int)(item % chunks);
@@ -108,15 +138,52 @@ __global__ __launch_bounds__(64) void conv3d_narrow_kernel(const uint16_t *__res
             // row ir - 1 run (from LDS) while they load, then the MFMAs turn
             // them into Z of row ir.
             u32x4 bfr[2][KS];
+            uint32_t in_mask[2];   // all ones where the position is inside the frame
             auto load_row = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int wc = w0 - 1 + 32 * nt + l32;
                     const bool inside = wc >= 0 && wc < W;
+                    in_mask[nt] = inside ? ~0u : 0u;
                     const uint16_t *px = src + ((int64_t)h * W + (inside ? wc : 0)) * CIN + 8 * g;
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
                         bfr[nt][s] = inside ? *reinterpret_cast<const u32x4 *>(px + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+                }
+            };
+            // NORM: the loaded row in place, channel 16 s + 8 g + 2 k (+1) in
+            // bfr[nt][s][k]; sum of squares in that order, then lane ^ 32's
+            auto normalize_row = [&]() __attribute__((always_inline)) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    float ss = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const float lo = bf16_bits_to_f32(bfr[nt][s][k] & 0xffffu);
+                            const float hi = bf16_bits_to_f32(bfr[nt][s][k] >> 16);
+                            ss = fmaf(lo, lo, ss);
+                            ss = fmaf(hi, hi, ss);
+                        }
+                    ss += __shfl_xor(ss, 32);
+                    const float inv = 1.0f / fmaxf(sqrtf(ss), nm.eps);
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        const int c0 = 16 * s + 8 * g;
+                        const u32x4 q = bfr[nt][s];
+                        uint32_t o[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const float2 gv = *reinterpret_cast<const float2 *>(nrm + c0 + 2 * k);
+                            const float2 bv = *reinterpret_cast<const float2 *>(nrm + CIN + c0 + 2 * k);
+                            const float lo = bf16_bits_to_f32(q[k] & 0xffffu);
+                            const float hi = bf16_bits_to_f32(q[k] >> 16);
+                            o[k] = pack_bf16x2(silu(fmaf(lo * inv, gv.x, bv.x)), silu(fmaf(hi * inv, gv.y, bv.y))) &
+                                   in_mask[nt];
+                        }
+                        bfr[nt][s] = u32x4{o[0], o[1], o[2], o[3]};
+                    }
                 }
             };
             // Z is stored transposed, zl[row][position]: the tap sums read 64
@@ -177,6 +244,8 @@ __global__ __launch_bounds__(64) void conv3d_narrow_kernel(const uint16_t *__res
                 // (one wave: its LDS accesses are served in order; the fences
                 // keep the compiler from moving them across each other)
                 asm volatile("" ::: "memory");
+                if constexpr (NORM)
+                    if (valid) normalize_row();
                 if (valid) compute_row();
                 asm volatile("" ::: "memory");
                 prev = valid;
@@ -210,28 +279,45 @@ __global__ __launch_bounds__(64) void conv3d_narrow_kernel(const uint16_t *__res
     }
 }
 
-template <int KS, int COUT>
+template <int KS, int COUT, bool NORM>
 hipError_t launch_ks(const ConvLaunch &c, hipStream_t s) {
     const int tiles_h = (int)((c.h + kRows - 1) / kRows), tiles_w = (int)((c.w_ + kCols - 1) / kCols);
     const int chunks = (int)((c.t + kChunk - 1) / kChunk);
     const int64_t items = c.n * tiles_h * tiles_w * chunks;
     if (items == 0) return hipSuccess;
-    conv3d_narrow_kernel<KS, COUT><<<dim3((unsigned)items), dim3(64), 0, s>>>(
+    InNorm nm;
+    if (NORM) {
+        nm.gamma = c.in_norm_gamma;
+        nm.beta = c.in_norm_beta;
+        nm.eps = c.in_norm_eps;
+        nm.sqrt_c = sqrtf((float)c.cin);
+    }
+    conv3d_narrow_kernel<KS, COUT, NORM><<<dim3((unsigned)items), dim3(64), 0, s>>>(
         static_cast<const uint16_t *>(c.x), static_cast<const uint16_t *>(c.cache),
         static_cast<const uint16_t *>(c.w), c.bias, static_cast<uint16_t *>(c.y), (int)c.t, (int)c.h, (int)c.w_,
-        tiles_h, tiles_w, chunks);
+        tiles_h, tiles_w, chunks, nm);
     return hipGetLastError();
 }
 
-template <int COUT>
+template <int COUT, bool NORM>
 hipError_t launch_cout(const ConvLaunch &c, hipStream_t s) {
     switch (c.cin / 16) {
-        case 1: return launch_ks<1, COUT>(c, s);
-        case 2: return launch_ks<2, COUT>(c, s);
-        case 3: return launch_ks<3, COUT>(c, s);
-        case 4: return launch_ks<4, COUT>(c, s);
-        case 5: return launch_ks<5, COUT>(c, s);
-        case 6: return launch_ks<6, COUT>(c, s);
+        case 1: return launch_ks<1, COUT, NORM>(c, s);
+        case 2: return launch_ks<2, COUT, NORM>(c, s);
+        case 3: return launch_ks<3, COUT, NORM>(c, s);
+        case 4: return launch_ks<4, COUT, NORM>(c, s);
+        case 5: return launch_ks<5, COUT, NORM>(c, s);
+        case 6: return launch_ks<6, COUT, NORM>(c, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool NORM>
+hipError_t launch_norm(const ConvLaunch &c, hipStream_t s) {
+    switch (c.cout) {
+        case 1: return launch_cout<1, NORM>(c, s);
+        case 2: return launch_cout<2, NORM>(c, s);
+        case 3: return launch_cout<3, NORM>(c, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -245,12 +331,8 @@ bool conv3d_narrow_supported(const ConvLaunch &c) {
 
 hipError_t launch_conv3d_narrow(const ConvLaunch &c, hipStream_t s) {
     if (!conv3d_narrow_supported(c)) return hipErrorInvalidValue;
-    switch (c.cout) {
-        case 1: return launch_cout<1>(c, s);
-        case 2: return launch_cout<2>(c, s);
-        case 3: return launch_cout<3>(c, s);
-        default: return hipErrorInvalidValue;
-    }
+    if (c.in_norm_gamma != nullptr) return launch_norm<true>(c, s);
+    return launch_norm<false>(c, s);
 }
 
 }  // namespace wanvae

@@ -45,6 +45,12 @@ struct ConvLaunch {
     bool norm_out = false;
     const float *norm_gamma = nullptr, *norm_beta = nullptr;
     float norm_eps = 0.0f;
+    // bf16 narrow conv only (conv3d_narrow_supported): x and cache hold the
+    // input of an RMS_norm + SiLU (scale in_norm_gamma, shift in_norm_beta or
+    // null, clamp in_norm_eps) that the conv applies to each position as it
+    // reads it (the decoder's norm_out -> SiLU -> conv_out); null: no norm
+    const float *in_norm_gamma = nullptr, *in_norm_beta = nullptr;
+    float in_norm_eps = 0.0f;
 };
 
 // Fused RMS_norm + SiLU over rows of C channels (C % 32 == 0, 32..1024).

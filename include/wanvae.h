@@ -235,6 +235,33 @@ WANVAE_API int wanvae_causal_conv3d(const void *x, const void *cache, const void
                          void *stream);
 
 /*
+ * The decoder's tail, norm_out -> SiLU -> conv_out, in one pass ("Sharding of
+ * WAN 2.2 VAE", decoder module tree; the norm and SiLU as in "Closing the gap:
+ * Wan 2.2 14B VAE decoder", section 4):
+ *   n = silu(x / max(||x||_2, eps) * sqrt(cin) * gamma + beta)   per position
+ *   y = causal_conv3d(n; w, bias)   (as wanvae_causal_conv3d)
+ * The conv reads x and normalises each position as it loads it, so n never
+ * goes through memory; n is rounded to bf16 before the products, as the
+ * separate wanvae_rmsnorm_silu + wanvae_causal_conv3d would store it.  The
+ * conv's zero padding (H, W, and frames before 0 without a cache) applies to
+ * n.  bf16 only.
+ *   x     : [d.n][d.t][d.h][d.w][cin], the norm's input.
+ *   cache : [d.n][2][d.h][d.w][cin], the norm's INPUT for frames -2 and -1
+ *           (normalised on the way in like x), or NULL.
+ *   gamma : [cin] fp32 (required); beta: [cin] fp32 or NULL; eps >= 0.
+ *   w     : packed by wanvae_pack_conv3d_weights(cin, cout, bf16).
+ *   bias  : [cout] fp32 or NULL.   y : [..][cout], must not overlap x, cache or w.
+ *   cin a multiple of 16 in [16, 96]; cout in [1, 3] (the decoder: 96 -> 3).
+ * Asynchronous on `stream`; timed as WANVAE_KERNEL_CONV_BF16.  Errors:
+ * WANVAE_ERR_DTYPE (not bf16), WANVAE_ERR_SHAPE, WANVAE_ERR_NULL,
+ * WANVAE_ERR_ALIAS; nothing is launched then.
+ */
+WANVAE_API int wanvae_rmsnorm_silu_conv_out(const void *x, const void *cache, const float *gamma,
+                                            const float *beta, float eps, const void *w, const float *bias,
+                                            void *y, const wanvae_dims *d, int32_t cin, int32_t cout,
+                                            int32_t dtype, void *stream);
+
+/*
  * Workspace bytes that wanvae_resblock_forward / wanvae_resblock_stream_step
  * need for extent *d (for the stream step, d->t is the chunk length), with
  * P = n*t*h*w, two 256-byte aligned regions:

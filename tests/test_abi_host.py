@@ -295,3 +295,20 @@ def test_upsample3d_validation():
     assert up(p, q, None, C.c_void_p((1 << 24) + 1024), C.byref(d), 64, 32, wv.BF16, None) == wv.ERR_ALIAS
     empty = _dims(1, 0, 3, 4)
     assert up(None, None, None, None, C.byref(empty), 64, 32, wv.BF16, None) == wv.OK
+
+
+def test_rmsnorm_silu_conv_out_validation():
+    L = wv.lib()
+    p, g, q = C.c_void_p(1 << 24), C.c_void_p(1 << 30), C.c_void_p(1 << 34)
+    d = _dims()
+    f = L.wanvae_rmsnorm_silu_conv_out
+    assert f(p, None, g, None, 1e-6, p, None, q, C.byref(d), 96, 3, wv.F32, None) == wv.ERR_DTYPE  # bf16 only
+    assert f(p, None, g, None, 1e-6, p, None, q, C.byref(d), 112, 3, wv.BF16, None) == wv.ERR_SHAPE  # cin <= 96
+    assert f(p, None, g, None, 1e-6, p, None, q, C.byref(d), 24, 3, wv.BF16, None) == wv.ERR_SHAPE   # cin % 16
+    assert f(p, None, g, None, 1e-6, p, None, q, C.byref(d), 96, 4, wv.BF16, None) == wv.ERR_SHAPE   # cout <= 3
+    assert f(p, None, g, None, -1.0, p, None, q, C.byref(d), 96, 3, wv.BF16, None) == wv.ERR_SHAPE   # eps >= 0
+    assert f(p, None, None, None, 1e-6, p, None, q, C.byref(d), 96, 3, wv.BF16, None) == wv.ERR_NULL  # gamma
+    assert f(p, None, g, None, 1e-6, p, None, C.c_void_p((1 << 24) + 1024), C.byref(d), 96, 3, wv.BF16,
+             None) == wv.ERR_ALIAS                                                                  # y overlaps x
+    empty = _dims(1, 0, 3, 4)
+    assert f(None, None, None, None, 1e-6, None, None, None, C.byref(empty), 96, 3, wv.BF16, None) == wv.OK

@@ -733,3 +733,101 @@ def test_upsample3d_decoder_sampled(torch, wv):
     assert err <= gu.TOL_BF16
     del xd, y
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- decoder tail, fused
+TAIL_SHAPES = [
+    (1, 3, 12, 40, 96, 3),       # the decoder's 96 -> 3, ragged W
+    (2, 2, 9, 33, 16, 3),        # one 16-channel slice, batch 2
+    (1, 30, 9, 70, 32, 3),       # two frame chunks, ragged rows and columns
+    (1, 2, 17, 64, 96, 1),       # one output channel, 3 row tiles
+    (2, 3, 8, 62, 48, 2),        # two output channels, exact tiles, batch 2
+    (1, 1, 1, 1, 96, 3),         # one position
+]
+
+
+# fused against separate launches: the two differ where the sum of squares'
+# order flips a bf16 rounding of n, which can move an output by one of its
+# own bf16 ulps (2^-8 of it, 3.9e-3 of max|y| at the largest outputs)
+TAIL_SEP_BAR = 1e-2
+
+
+def _tail_inputs(rng, Cin, Cout):
+    g = (1.0 + 0.2 * rng.standard_normal(Cin)).astype(np.float32)
+    be = (0.5 * rng.standard_normal(Cin)).astype(np.float32)
+    w = rnd(rng, (Cout, Cin, 3, 3, 3), 1 / math.sqrt(27 * Cin), wl.BF16)
+    b = rnd(rng, (Cout,), 0.1)
+    return g, be, w, b
+
+
+@pytest.mark.parametrize("shape", TAIL_SHAPES)
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_rmsnorm_silu_conv_out(torch, wv, shape, with_cache):
+    """norm_out -> SiLU -> conv_out in one launch against the oracle's
+    norm_silu then causal_conv3d (fp64 sums, n not rounded), and, where the
+    norm kernel takes the channel count (C % 32 == 0), against the library's
+    two separate launches (n through memory in bf16).  beta is far from 0, so
+    a pad position normalised (silu(beta)) instead of left at zero would
+    show; the cache holds the norm's input."""
+    N, T, H, W, Cin, Cout = shape
+    rng = np.random.default_rng(sum(shape) + 7 * with_cache)
+    x = rnd(rng, (N, T, H, W, Cin), 2.0, wl.BF16)
+    g, be, w, b = _tail_inputs(rng, Cin, Cout)
+    cache = rnd(rng, (N, 2, H, W, Cin), 2.0, wl.BF16) if with_cache else None
+    ref = oracle.causal_conv3d(oracle.norm_silu(x, g, be), w, b,
+                               None if cache is None else oracle.norm_silu(cache, g, be))
+    wp = wv.pack_conv3d_weights(gu.to_dev(w, wl.BF16))
+    xd, gd, bed, bd = gu.to_dev(x, wl.BF16), gu.to_dev(g, wl.F32), gu.to_dev(be, wl.F32), gu.to_dev(b, wl.F32)
+    cd = None if cache is None else gu.to_dev(cache, wl.BF16)
+    y = wv.rmsnorm_silu_conv_out(xd, gd, bed, oracle.EPS, wp, bd, cd)
+    got = gu.to_host(y)
+    err = gu.rel_err(got, ref)
+    extra = f"pcc={gu.pcc(got, ref):.6f}"
+    sep = 0.0
+    if Cin % 32 == 0:
+        n = wv.rmsnorm_silu(xd, gd, bed, oracle.EPS)
+        nc = None if cd is None else wv.rmsnorm_silu(cd, gd, bed, oracle.EPS)
+        sep = gu.rel_err(got, gu.to_host(wv.causal_conv3d(n, wp, bd, nc)))
+        extra += f" vs separate launches {sep:.3e}"
+    gu.report(f"norm + conv_out {shape} cache={with_cache}", err, gu.TOL_BF16, extra)
+    assert got.shape == ref.shape and err <= gu.TOL_BF16
+    assert sep <= TAIL_SEP_BAR
+
+
+def test_rmsnorm_silu_conv_out_decoder_sampled(torch, wv):
+    """The decoder's tail at the output resolution, [1,81,720,1280,96] -> 3,
+    in the launch the benchmark times: against the library's separate norm
+    and conv launches over the whole output, and against the oracle on
+    row bands (top, middle, bottom; full width) of the first and last
+    frames, each band's oracle run on its input rows and frames (a band's
+    first row and frames whose neighbourhood it does not hold are not
+    compared)."""
+    w_ = wl.custom("tail", wl.BF16, 1, 81, 720, 1280, 96, 3)
+    xd = wl.make_x_device(w_, seed=11)
+    rng = np.random.default_rng(11)
+    g, be, w, b = _tail_inputs(rng, 96, 3)
+    wp = wv.pack_conv3d_weights(gu.to_dev(w, wl.BF16))
+    gd, bed, bd = gu.to_dev(g, wl.F32), gu.to_dev(be, wl.F32), gu.to_dev(b, wl.F32)
+    y = wv.rmsnorm_silu_conv_out(xd, gd, bed, oracle.EPS, wp, bd)
+    n = wv.rmsnorm_silu(xd, gd, bed, oracle.EPS)
+    y2 = wv.causal_conv3d(n, wp, bd)
+    del n
+    torch.cuda.synchronize()
+    sep = (y.float() - y2.float()).abs().max().item() / y2.float().abs().max().item()
+    del y2
+    errs = []
+    H = 720
+    for (f0, f1) in [(0, 3), (78, 81)]:
+        i0 = max(f0 - 2, 0)
+        for (r0, r1) in [(0, 6), (357, 363), (714, 720)]:
+            a0, a1 = max(r0 - 1, 0), min(r1 + 1, H)
+            xc = gu.to_host(xd[:, i0:f1, a0:a1])
+            ref = oracle.causal_conv3d(oracle.norm_silu(xc, g, be), w, b)
+            got = gu.to_host(y[:, f0:f1, r0:r1])
+            errs.append(gu.rel_err(got, ref[:, f0 - i0:, r0 - a0:r1 - a0]))
+    err = max(errs)
+    gu.report("norm + conv_out [1,81,720,1280,96] -> 3 sampled", err, gu.TOL_BF16,
+              f"whole output vs separate launches {sep:.3e}")
+    assert err <= gu.TOL_BF16 and sep <= TAIL_SEP_BAR
+    del xd, y
+    torch.cuda.empty_cache()
