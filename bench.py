@@ -284,7 +284,11 @@ def upsample(torch, wv, steps, warmup):
     360 x 640), and upsample2d 192 -> 96 from [1,81,360,640] (to 720 x 1280)
     (wanvae_upsample3d_conv / wanvae_upsample2d_conv: frames doubled after the
     first for the 3D ones, nearest x2 in H and W, then the 3x3 conv halving
-    the channels).  Seeded synthetic bf16 values."""
+    the channels).  Seeded synthetic bf16 values.  With C_out a multiple of 96
+    (all three) the library runs the conv by output phase, 4 merged taps per
+    output instead of 9: the MFMA work counted is those 4 taps, and each op
+    also reports the 9-tap direct form's FLOPs (``flop_direct``) and the rate
+    they would correspond to."""
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
     res = []
@@ -301,10 +305,16 @@ def upsample(torch, wv, steps, warmup):
         P_in, P_out = t * h * w, to * 4 * h * w
         fn = wv.upsample3d_conv if temporal else wv.upsample2d_conv
         name = "upsample3d" if temporal else "upsample2d"
+        taps = 4 if cout % 96 == 0 else 9
         ops = [(f"{name} {cin}->{cout}, [1,{t},{h},{w},{cin}] -> [1,{to},{2 * h},{2 * w},{cout}]",
                 wv.KERNEL_UPSAMPLE, lambda: fn(x, wp, b, out=y),
-                2.0 * P_out * cout * 9 * cin, 2.0 * (P_in * cin + P_out * cout))]
-        res += time_ops(torch, wv, ops, steps, warmup)
+                2.0 * P_out * cout * taps * cin, 2.0 * (P_in * cin + P_out * cout))]
+        r = time_ops(torch, wv, ops, steps, warmup)
+        for e in r:
+            e["taps_per_output"] = taps
+            e["flop_direct"] = 2.0 * P_out * cout * 9 * cin
+            e["tflops_direct_equivalent"] = e["flop_direct"] / (e["avg_launch_ms"] * 1e-3) / 1e12
+        res += r
         del x, y
         torch.cuda.empty_cache()
     return {"metric": "decoder upsampler convs, average launch time (1 GPU)", "unit": "ms",

@@ -215,23 +215,27 @@ struct TileInfo {
     int h0, w0, n0;
     int kt_begin, s_conv, s_total;
     int ntiles;
+    int ph;   // PH kernels: output phase 2 py + px (output row 2 i + py, column 2 j + px)
 };
 
-template <int WM, int WN, int FM, int FN>
+// PH: the upsampler conv by output phase (see the kernel's comment): rows
+// and columns are the input's (half-resolution) ones, a stage holds the 4
+// merged taps of one phase, and the A tile needs one halo row, not two.
+template <int WM, int WN, int FM, int FN, bool PH = false>
 struct Tile {
     static constexpr int NWAVE = WM * WN;                    // MFMA waves
     static constexpr int kThreads = (NWAVE + 1) * 64;        // + one load wave
     static constexpr int HB = WM * FM;                       // output rows
     static constexpr int NB = WN * FN * 32;                  // output channels
-    static constexpr int AR = HB + 2;                        // A tile rows (H halo)
+    static constexpr int AR = HB + (PH ? 1 : 2);             // A tile rows (H halo)
     static constexpr int A_BLOCKS = (AR * kAS + 31) / 32;    // 1 KB blocks = 32 units
-    static constexpr int B_BLOCKS = 9 * NB / 32;
+    static constexpr int B_BLOCKS = (PH ? 4 : 9) * NB / 32;
     static constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;       // load instructions per stage
     static constexpr int STAGE_BYTES = BLOCKS * 1024;
     // FN > 1: each wave owns several channel blocks and walks the taps kh by kh
     // (9 FN weight fragments in registers would not fit beside the
     // accumulators).  The bias of every tile sits in LDS, not in registers.
-    static constexpr bool KH_OUTER = FN > 1;
+    static constexpr bool KH_OUTER = FN > 1 && !PH;
     static constexpr int kBiasBytes = 8 * 1024;   // bias in LDS: [cout_p] fp32, cout <= 2048
     static constexpr int kLds = 160 * 1024 - kSyncBytes - NWAVE * kEpiBytes - kBiasBytes;
     static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
@@ -310,9 +314,11 @@ __device__ inline void count_giveup(int lane) {
     if (lane == 0) __hip_atomic_fetch_add(&g_wait_giveups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int WM, int WN, int FM, int FN, int EPI, bool SC>
+template <int WM, int WN, int FM, int FN, int EPI, bool SC, bool PH>
 __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) {
-    using TL = Tile<WM, WN, FM, FN>;
+    using TL = Tile<WM, WN, FM, FN, PH>;
+    static_assert(!PH || (WM == 4 && WN == 1 && FM == 3 && EPI == EPI_BIAS && !SC),
+                  "the phase upsampler runs on the 96-channel tile with a bias epilogue");
     constexpr int HB = TL::HB;
     constexpr int NB = TL::NB;
     constexpr int NBUF = TL::NBUF;
@@ -379,6 +385,12 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         TileInfo ti;
         ti.n0 = (int)(tile % d_cb) * NB;
         tile /= d_cb;
+        ti.ph = 0;
+        if constexpr (PH) {
+            // the four phases of a block side by side (they read the same input)
+            ti.ph = (int)(tile & 3);
+            tile >>= 2;
+        }
         const int64_t grp = tile % d_g;
         tile /= d_g;
         ti.ntiles = a.pair && grp == 0 ? 2 : 1;
@@ -419,6 +431,13 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                 const int u = b * 32 + (lane >> 1);
                 const int r = u / kAS, c = u % kAS;
                 const int hf = (lane & 1) ^ ((c >> 3) & 1);
+                if constexpr (PH) {
+                    // input rows h0 + py - 1 .. and columns w0 + px - 1 .. of
+                    // the half-resolution frame
+                    const int hh = ti.h0 + (ti.ph >> 1) - 1 + r, ww = ti.w0 + (ti.ph & 1) - 1 + c;
+                    const bool inside = r < TL::AR && hh >= 0 && hh < (H >> 1) && ww >= 0 && ww < Wi;
+                    return inside ? (uint32_t)(hh * Wi + ww) * cs2 + hf * 16 : kOOB;
+                }
                 const int hh = ti.h0 - 1 + r, ww = ti.w0 - 1 + c;
                 const bool inside = r < TL::AR && hh >= 0 && hh < H && ww >= 0 && ww < W;
                 return inside ? (uint32_t)((hh >> up) * Wi + (ww >> up)) * cs2 + hf * 16 : kOOB;
@@ -507,11 +526,13 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                         cc * slice_elems;
                 abytes = (uint32_t)(HWi * a.cin * 2 - cc * slice_elems * 2);
                 // elements of the packed weight before stage (kt, cc); an
-                // upsampler's weight holds the current frame's taps only
+                // upsampler's weight holds the current frame's taps only, and
+                // by phase its 4 merged taps of each phase
                 const int wkt = up ? kt - 2 : kt;
-                const int64_t wskip = (int64_t)(wkt * ck + cc) * 9 * a.cout_p * kKC;
+                const int64_t wskip = PH ? (int64_t)(cc * 4 + ti.ph) * 4 * a.cout_p * kKC
+                                         : (int64_t)(wkt * ck + cc) * 9 * a.cout_p * kKC;
                 bbase = a.w + wskip;
-                bbytes = (uint32_t)(((int64_t)(up ? 9 : 27) * a.cin * a.cout_p - wskip) * 2);
+                bbytes = (uint32_t)(((int64_t)(PH ? 16 : up ? 9 : 27) * a.cin * a.cout_p - wskip) * 2);
             } else {
                 // first 16-channel slice of this shortcut stage
                 const int cc = (si - ti.s_conv) * TL::SCS;
@@ -632,10 +653,22 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // KH_OUTER tiles keep input rows across kernel rows instead: input row i
     // of a stage (0 .. FM + 1) in fk[i % 3], the next stage's row 0 in fk[0]
     bf16x8 fk[3][3];
-    constexpr bool ALT = !TL::KH_OUTER && NROW % 2 == 1;   // rows per stage odd
+    // PH tiles: the merged weights of row tap a and column tap b (pw[a][b]),
+    // input rows 0 .. FM of the wave (pr[r][b]: columns l32 + b)
+    bf16x8 pw[2][2][FN];
+    bf16x8 pr[FM + 1][2];
+    constexpr bool ALT = !TL::KH_OUTER && !PH && NROW % 2 == 1;   // rows per stage odd
     // row 0 and the kh = 0 weights of the stage in `buf` (parity par)
     auto load_first = [&](const unsigned char *buf, int par) __attribute__((always_inline)) {
-        if constexpr (TL::KH_OUTER) {
+        if constexpr (PH) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) pr[0][b] = ldA(buf, 0, b);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) pw[0][b][fn] = ldB(buf, b, fn);
+            return;
+        } else if constexpr (TL::KH_OUTER) {
 #pragma unroll
             for (int kw = 0; kw < 3; ++kw) fk[0][kw] = ldA(buf, 0, kw);
         } else if (par) {
@@ -805,6 +838,69 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         return landed;
     };
 
+    // The upsampler stage by phase (PH): output row fm of the wave (input row
+    // i = wm FM + fm of the tile) takes row tap a from A row fm + a and
+    // column tap b from column l32 + b, with the 4 merged weights of the
+    // tile's phase.  Row tap 0 runs first with rows 0 .. FM - 1, while the
+    // row tap 1 weights and rows 1 .. FM are read; row tap 1 then reads the
+    // following ring slot's tap 0 weights and row 0 (unconditionally, kept
+    // if that stage had landed, as in the other stages).
+    auto compute_conv_ph = [&]<int PAR>(const unsigned char *buf, const unsigned char *next)
+                               __attribute__((always_inline)) {
+        bool landed = false;
+        int early = 0;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                int nrd = 0;
+                if (a == 0) {
+                    // the next input row first (needed soonest), then the tap 1 weights
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) pr[fm + 1][b] = ldA(buf, fm + 1, b);
+                    nrd += 2;
+                    if (fm == 0) {
+                        early = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+#pragma unroll
+                            for (int fn = 0; fn < FN; ++fn) pw[1][b][fn] = ldB(buf, 2 + b, fn);
+                        nrd += 1 + 2 * FN;
+                    }
+                } else if (fm == 0) {
+                    const int f = __builtin_amdgcn_readfirstlane(early);
+                    seen = f > seen ? f : seen;
+                    landed = seen > consumed + 1;
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) pr[0][b] = ldA(next, 0, b);
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn) pw[0][b][fn] = ldB(next, b, fn);
+                    nrd += 2 + 2 * FN;
+                }
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pw[a][b][fn], pr[fm + a][b],
+                                                                              acc[fm][fn], 0, 0, 0);
+                // LDS reads after the row's first MFMAs, two per MFMA while
+                // more are left than MFMAs to follow, then one
+                constexpr int nm = 2 * FN;
+                int left = nrd;
+#pragma unroll
+                for (int k = 0; k < nm; ++k) {
+                    const int per = left > nm - k - 1 ? (left >= 2 ? 2 : left) : left > 0 ? 1 : 0;
+                    sched_group<kSchedMfma>(1);
+                    sched_group<kSchedDsRead>(per);
+                    left -= per;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        return landed;
+    };
+
     // One shortcut stage: SCS slices of 16 channels, each x at this wave's
     // output rows times that slice of w_sc.
     auto ldU = [&](const unsigned char *buf, int u) __attribute__((always_inline)) {
@@ -857,6 +953,14 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         // A tile's first stage reads its own operands: marking the carried
         // ones undefined here keeps them from being held across the epilogue
         // (which the KH_OUTER tiles' identity epilogue has no registers for).
+        if constexpr (PH) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                pr[0][b] = __builtin_nondeterministic_value(pr[0][b]);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) pw[0][b][fn] = __builtin_nondeterministic_value(pw[0][b][fn]);
+            }
+        }
         if constexpr (TL::KH_OUTER) {
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
@@ -904,7 +1008,9 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                 }
                 const unsigned char *nxt = smem + (slot + 1 == NBUF ? 0 : slot + 1) * TL::STAGE_BYTES;
                 bool landed;
-                if constexpr (TL::KH_OUTER)
+                if constexpr (PH)
+                    landed = compute_conv_ph.template operator()<PAR>(cur, nxt);
+                else if constexpr (TL::KH_OUTER)
                     landed = compute_conv_kh.template operator()<PAR>(cur, nxt);
                 else
                     landed = compute_conv.template operator()<PAR>(cur, nxt);
@@ -938,11 +1044,15 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
         const int64_t frame = ti.nq * a.T + ti.tq;
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y + frame * HW * a.cout, HW * a.cout * 2);
         // store pieces: position p = lane / 4 + 16 half, 16-byte quarter lane % 4
+        // (PH: tile positions are the input's; output column 2 w + px, row 2 h + py)
         uint32_t col_off[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int ww = ti.w0 + (lane >> 2) + 16 * half;
-            col_off[half] = ww < W ? (uint32_t)(ww * a.cout + ti.n0 + wn * FN * 32) * 2 + (lane & 3) * 16 : kOOB;
+            const int wo = PH ? 2 * ww + (ti.ph & 1) : ww;
+            col_off[half] = ww < (PH ? W >> 1 : W)
+                                ? (uint32_t)(wo * a.cout + ti.n0 + wn * FN * 32) * 2 + (lane & 3) * 16
+                                : kOOB;
         }
         // A row of results goes out through this wave's LDS staging buffer:
         // written as the MFMA layout holds it (lane = position, 4 channels per
@@ -1000,12 +1110,14 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                         *reinterpret_cast<u32x2 *>(epi + l32 * kEpiStride + j * 16 + g * 8) = o;
                     }
                     if (narrow) continue;
-                    const uint32_t row_off = (uint32_t)(hh * W * a.cout) * 2 + fn * 64;
+                    const int ho = PH ? 2 * hh + (ti.ph >> 1) : hh;
+                    const bool row_in = hh < (PH ? H >> 1 : H);
+                    const uint32_t row_off = (uint32_t)(ho * W * a.cout) * 2 + fn * 64;
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const int p = (lane >> 2) + 16 * half, q = lane & 3;
                         const u32x4 d = *reinterpret_cast<const u32x4 *>(epi + p * kEpiStride + q * 16);
-                        const uint32_t off = hh < H && col_off[half] != kOOB ? row_off + col_off[half] : kOOB;
+                        const uint32_t off = row_in && col_off[half] != kOOB ? row_off + col_off[half] : kOOB;
                         __builtin_amdgcn_raw_buffer_store_b128(d, ry, off, 0, 0);
                     }
                 }
@@ -1162,9 +1274,9 @@ hipError_t device_cu_count(int *out) {
 
 namespace {
 
-template <int WM, int WN, int FM, int FN, int EPI, bool SC = EPI == EPI_SHORTCUT>
+template <int WM, int WN, int FM, int FN, int EPI, bool SC = EPI == EPI_SHORTCUT, bool PH = false>
 hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
-    using TL = Tile<WM, WN, FM, FN>;
+    using TL = Tile<WM, WN, FM, FN, PH>;
     Args a;
     a.x = static_cast<const uint16_t *>(c.x);
     a.cache = static_cast<const uint16_t *>(c.cache);
@@ -1194,10 +1306,12 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.sc_in = static_cast<const uint16_t *>(c.gemm ? c.x : c.res);
     a.sc_c = c.gemm ? c.cin : c.cres;
     if (c.gemm) a.wsc = static_cast<const uint16_t *>(c.w);
-    a.tiles_w = (int)((c.w_ + kWB - 1) / kWB);
-    a.tiles_h = (int)((c.h + TL::HB - 1) / TL::HB);
+    // (PH: tiles over the half-resolution input, four phases each)
+    const int64_t th = PH ? c.h / 2 : c.h, tw = PH ? c.w_ / 2 : c.w_;
+    a.tiles_w = (int)((tw + kWB - 1) / kWB);
+    a.tiles_h = (int)((th + TL::HB - 1) / TL::HB);
     a.pair = c.cache == nullptr && !c.up2 && !c.gemm && c.t >= 2 ? 1 : 0;
-    a.items = (int64_t)a.tiles_w * a.tiles_h * c.n * (c.t - a.pair) * (a.cout_p / TL::NB);
+    a.items = (int64_t)a.tiles_w * a.tiles_h * c.n * (c.t - a.pair) * (a.cout_p / TL::NB) * (PH ? 4 : 1);
     if (a.items <= 0) return hipSuccess;
     // persistent grid: one workgroup per compute unit (the LDS ring takes most
     // of a CU's 160 KB), each looping over its share of the tiles
@@ -1205,7 +1319,7 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
     const int64_t grid = a.items < (int64_t)ncu * TL::kPerCU ? a.items : (int64_t)ncu * TL::kPerCU;
-    conv3d_bf16_kernel<WM, WN, FM, FN, EPI, SC><<<dim3((unsigned)grid), dim3(TL::kThreads), 0, s>>>(a);
+    conv3d_bf16_kernel<WM, WN, FM, FN, EPI, SC, PH><<<dim3((unsigned)grid), dim3(TL::kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -1248,6 +1362,10 @@ hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
         if (c.cout == 96) return launch_cfg<4, 1, 3, 3, EPI_NORM>(c, s);
         if (c.cout == 32) return launch_cfg<4, 1, 4, 1, EPI_NORM>(c, s);
         return hipErrorInvalidValue;
+    }
+    if (c.up2 && upsample_by_phase(c.cout)) {
+        if (c.res != nullptr || c.cache != nullptr || (c.h | c.w_) & 1) return hipErrorInvalidValue;
+        return launch_cfg<4, 1, 3, 3, EPI_BIAS, false, true>(c, s);
     }
     const bool tall = rows_computed(c.h, 18) <= rows_computed(c.h, 16);
     if (c.res != nullptr && c.wsc != nullptr) {

@@ -81,6 +81,11 @@ bool conv3d_bf16_norm_supported(int cout);
 // a tap sum per output): channels-last x and cache, 16 <= C_in <= 96, C_in a
 // multiple of 16; no residual or shortcut.
 bool conv3d_narrow_supported(const ConvLaunch &c);
+// The upsampler conv by output phase (C_out a multiple of 96): its weight is
+// packed as the 4 merged 2 x 2 taps of each of the 4 output phases, and the
+// conv runs on the half-resolution input (launch_pack_conv2d_weights and the
+// up2 launches agree through this test).
+inline bool upsample_by_phase(int cout) { return cout % 96 == 0; }
 hipError_t launch_conv3d_narrow(const ConvLaunch &c, hipStream_t s);
 hipError_t launch_conv3d_bf16(const ConvLaunch &a, hipStream_t s);
 

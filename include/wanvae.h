@@ -145,9 +145,11 @@ WANVAE_API int wanvae_packed_conv3d_weight_elems(int32_t cin, int32_t cout, int3
  *                       x[n][t][(h+kh-1)/2][(w+kw-1)/2][ci]
  * with the terms outside the 2h x 2w image left out.  The doubled image is
  * never stored: the conv reads each input position for the output positions
- * it covers.  bf16 only (other dtypes: WANVAE_ERR_DTYPE); fp32 accumulation,
- * bias added in fp32, one RNE rounding.  wanvae_upsample3d_conv adds the
- * temporal doubling of upsample3d.
+ * it covers; for cout a multiple of 96 it runs by output phase, 4 merged taps
+ * of the input per output (the weights as wanvae_pack_conv2d_weights merges
+ * them, rounded to bf16 once).  bf16 only (other dtypes: WANVAE_ERR_DTYPE);
+ * fp32 accumulation, bias added in fp32, one RNE rounding.
+ * wanvae_upsample3d_conv adds the temporal doubling of upsample3d.
  *   x     : [n][t][h][w][cin] bf16, channels-last (d gives this extent).
  *   w     : packed by wanvae_pack_conv2d_weights (cin x cout).
  *   bias  : [cout] fp32 or NULL.
@@ -183,14 +185,21 @@ WANVAE_API int wanvae_upsample3d_conv(const void *x, const void *w, const float 
                                       const wanvae_dims *d, int32_t cin, int32_t cout, int32_t dtype,
                                       void *stream);
 
-/* Packs a 2D 3x3 conv weight [cout][cin][3][3] (bf16) for
- * wanvae_upsample2d_conv into [cin/16][kh][kw][cout_p][16] (cout_p = cout
- * rounded up to 32, zero padding): the bf16 conv layout with one temporal
- * tap.  Same rules as wanvae_pack_conv3d_weights; bf16 only. */
+/* Packs a 2D 3x3 conv weight [cout][cin][3][3] (bf16) for the upsampler
+ * convs.  cout a multiple of 96 (every decoder upsampler): by output phase,
+ * [cin/16][phase][a][b][cout_p][16], phase = 2 py + px and (a, b) the 2 x 2
+ * taps on the half-resolution input, each the fp32 sum of the 3x3 taps that
+ * land on that input position after the nearest x2 doubling (output row
+ * 2i + py reads input rows i + py - 1 + a: kernel rows {-1} and {0, +1} for
+ * py = 0, {-1, 0} and {+1} for py = 1; columns alike), rounded to bf16 once.
+ * Other cout: [cin/16][kh][kw][cout_p][16], the bf16 conv layout with one
+ * temporal tap.  cout_p = cout rounded up to 32, zero padding.  Same rules as
+ * wanvae_pack_conv3d_weights; bf16 only. */
 WANVAE_API int wanvae_pack_conv2d_weights(const void *w, void *packed, int32_t cin, int32_t cout,
                                           int32_t dtype, void *stream);
 
-/* Elements of a packed 2D conv weight (9*cin*cout_p).  Host only. */
+/* Elements of a packed 2D conv weight: 16*cin*cout_p by phase (cout a
+ * multiple of 96), else 9*cin*cout_p.  Host only. */
 WANVAE_API int wanvae_packed_conv2d_weight_elems(int32_t cin, int32_t cout, int32_t dtype,
                                                  int64_t *elems);
 

@@ -241,8 +241,11 @@ def test_upsample2d_validation():
     empty = _dims(0, 2, 3, 4)
     assert up(None, None, None, None, C.byref(empty), 64, 32, wv.BF16, None) == wv.OK
     n = C.c_int64(0)
+    # C_out a multiple of 96: 4 output phases x 4 merged taps; otherwise the 9 taps
     assert L.wanvae_packed_conv2d_weight_elems(384, 192, wv.BF16, C.byref(n)) == wv.OK
-    assert n.value == 9 * 384 * 192
+    assert n.value == 16 * 384 * 192
+    assert L.wanvae_packed_conv2d_weight_elems(64, 128, wv.BF16, C.byref(n)) == wv.OK
+    assert n.value == 9 * 64 * 128
     assert L.wanvae_packed_conv2d_weight_elems(192, 3, wv.BF16, C.byref(n)) == wv.OK
     assert n.value == 9 * 192 * 32
     assert L.wanvae_packed_conv2d_weight_elems(192, 96, wv.F32, C.byref(n)) == wv.ERR_DTYPE

@@ -555,7 +555,11 @@ def _upsample_check(torch, wv, xd, x_host, w, b, label, frames=None, rows=None):
     ((1, 2, 5, 17, 16), 32),     # 10 x 34 out: ragged row and column tiles, one 32-channel block
     ((1, 3, 9, 16, 64), 64),     # 18-row tiles
     ((2, 1, 7, 20, 384), 192),   # the decoder's 384 -> 192, batch 2
-    ((1, 2, 6, 12, 192), 96),    # 96-channel (kh-outer) tiles
+    ((1, 2, 6, 12, 192), 96),    # C_out a multiple of 96: by output phase
+    ((1, 2, 13, 33, 96), 96),    # by phase: 13 input rows (12-row tiles + 1), 33 columns (32 + 1)
+    ((2, 1, 12, 32, 192), 192),  # by phase: exact tiles, two channel blocks, batch 2
+    ((1, 3, 25, 70, 48), 96),    # by phase: 3 input slices (a lone last stage), ragged rows and columns
+    ((1, 1, 1, 1, 96), 96),      # by phase: one input position, a 2 x 2 output
     ((1, 2, 4, 9, 96), 40),      # a padded channel block
     ((1, 1, 1, 1, 32), 3),       # one input position, 3 output channels (2-byte stores)
 ])
