@@ -224,7 +224,11 @@ struct TileInfo {
 template <int WM, int WN, int FM, int FN, bool PH = false>
 struct Tile {
     static constexpr int NWAVE = WM * WN;                    // MFMA waves
-    static constexpr int kThreads = (NWAVE + 1) * 64;        // + one load wave
+    // load waves: one; two for PH, whose short stages (36 MFMAs a wave) need
+    // more DMA in flight than one wave's 63 outstanding loads cover: the first
+    // moves each stage's A blocks, the second its B blocks
+    static constexpr int NLW = PH ? 2 : 1;
+    static constexpr int kThreads = (NWAVE + NLW) * 64;
     static constexpr int HB = WM * FM;                       // output rows
     static constexpr int NB = WN * FN * 32;                  // output channels
     static constexpr int AR = HB + (PH ? 1 : 2);             // A tile rows (H halo)
@@ -238,7 +242,10 @@ struct Tile {
     static constexpr bool KH_OUTER = FN > 1 && !PH;
     static constexpr int kBiasBytes = 8 * 1024;   // bias in LDS: [cout_p] fp32, cout <= 2048
     static constexpr int kLds = 160 * 1024 - kSyncBytes - NWAVE * kEpiBytes - kBiasBytes;
-    static constexpr int NBUF = 4 * STAGE_BYTES <= kLds ? 4 : 3 * STAGE_BYTES <= kLds ? 3 : 2;
+    static constexpr int NBUF = 5 * STAGE_BYTES <= kLds   ? 5
+                                : 4 * STAGE_BYTES <= kLds ? 4
+                                : 3 * STAGE_BYTES <= kLds ? 3
+                                                          : 2;
     static_assert(NBUF * STAGE_BYTES <= kLds, "tile does not fit the 160 KB LDS");
     static_assert(NWAVE + 1 <= kSyncBytes / 4, "one flag per wave");
     static constexpr int kPerCU =
@@ -315,7 +322,7 @@ __device__ inline void count_giveup(int lane) {
 }
 
 template <int WM, int WN, int FM, int FN, int EPI, bool SC, bool PH>
-__global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) {
+__global__ __launch_bounds__((WM *WN + (PH ? 2 : 1)) * 64) void conv3d_bf16_kernel(Args a) {
     using TL = Tile<WM, WN, FM, FN, PH>;
     static_assert(!PH || (WM == 4 && WN == 1 && FM == 3 && EPI == EPI_BIAS && !SC),
                   "the phase upsampler runs on the 96-channel tile with a bias epilogue");
@@ -324,7 +331,8 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     constexpr int NBUF = TL::NBUF;
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * TL::STAGE_BYTES];
-    // sync[0]: stages landed (load wave); sync[1 + w]: stages consumed by MFMA wave w
+    // sync[0]: stages landed (load wave); sync[1 + w]: stages consumed by MFMA
+    // wave w; sync[1 + NWAVE]: stages landed, second load wave (NLW = 2)
     __shared__ int sync[kSyncBytes / 4];
     __shared__ __attribute__((aligned(16))) unsigned char epi_stage[TL::NWAVE * kEpiBytes];
     // bias (+ shortcut bias) of every output channel
@@ -337,7 +345,9 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     const int64_t HW = (int64_t)H * W;
     const int ck = a.cin / kKC;
 
-    if (tid <= TL::NWAVE) sync[tid] = 0;
+    static_assert(TL::NLW == 1 || !SC, "two load waves split conv stages only");
+    static_assert(TL::NWAVE + 2 <= kSyncBytes / 4, "flags");
+    if (tid <= TL::NWAVE + 1) sync[tid] = 0;
     for (int c = tid; c < a.cout_p; c += TL::kThreads) {
         float b = a.bias && c < a.cout ? a.bias[c] : 0.0f;
         if constexpr (SC)
@@ -357,6 +367,16 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // accesses, which the compiler must also wait for with vmcnt)
     auto flag_read = [&](int i) { return __builtin_amdgcn_readfirstlane(__atomic_load_n(&sync[i], __ATOMIC_RELAXED)); };
     auto flag_write = [&](int i, int v) { __atomic_store_n(&sync[i], v, __ATOMIC_RELAXED); };
+    // stages landed (both load waves' parts, with two): a VGPR value, made
+    // uniform where it is used
+    auto landed_count = [&]() __attribute__((always_inline)) {
+        const int l0 = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
+        if constexpr (TL::NLW == 2) {
+            const int l1 = __atomic_load_n(&sync[1 + TL::NWAVE], __ATOMIC_RELAXED);
+            return l0 < l1 ? l0 : l1;
+        }
+        return l0;
+    };
 
     // ---- this workgroup's work items.  XCD x (= workgroup index mod 8) holds
     // wg_x of the grid's workgroups and owns a contiguous item range of
@@ -410,7 +430,10 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 
     const uint32_t smem_base = lds_address(smem);
 
-    if (wave == TL::NWAVE) {
+    if (wave >= TL::NWAVE) {
+        // load wave lw: everything (one load wave), or with two the A (lw = 0)
+        // or B (lw = 1) blocks of every stage
+        const int lw = wave - TL::NWAVE;
         // ================= load wave: all global -> LDS traffic of every tile.
         // Block b of a stage: lane l writes physical half (l & 1) of unit
         // 32 * b' + l / 2 (b' relative to the A or B region), so it fetches the
@@ -545,13 +568,23 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             const i32x4 ar = buffer_rsrc(abase, abytes);
             const i32x4 br = buffer_rsrc(bbase, bbytes);
             const uint32_t base = smem_base + (uint32_t)slot * TL::STAGE_BYTES;
+            if constexpr (TL::NLW == 2) {
+                if (lw == 0) {
 #pragma unroll
-            for (int b = 0; b < TL::BLOCKS; ++b) {
-                uint32_t off = l_off[b];
-                bool from_b = b >= TL::A_BLOCKS;
-                if constexpr (SC)
-                    if (sc) off = sc_block_off(ti, b, from_b);
-                lds_dma16(from_b ? br : ar, base + b * 1024, off);
+                    for (int b = 0; b < TL::A_BLOCKS; ++b) lds_dma16(ar, base + b * 1024, l_off[b]);
+                } else {
+#pragma unroll
+                    for (int b = TL::A_BLOCKS; b < TL::BLOCKS; ++b) lds_dma16(br, base + b * 1024, l_off[b]);
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < TL::BLOCKS; ++b) {
+                    uint32_t off = l_off[b];
+                    bool from_b = b >= TL::A_BLOCKS;
+                    if constexpr (SC)
+                        if (sc) off = sc_block_off(ti, b, from_b);
+                    lds_dma16(from_b ? br : ar, base + b * 1024, off);
+                }
             }
             slot = slot + 1 == NBUF ? 0 : slot + 1;
             if (++si == ti.s_total) {
@@ -587,16 +620,27 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             if (landed < issued) {
                 // the oldest requested stage has landed once at most the loads
                 // requested after it are outstanding (vmcnt counts to 63 at most,
-                // and at most 63 loads are ever in flight)
-                switch (issued - landed - 1) {
-                    case 0: __builtin_amdgcn_s_waitcnt(kWaitVm0); break;
-                    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(TL::BLOCKS < 63 ? TL::BLOCKS : 63)); break;
-                    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * TL::BLOCKS < 63 ? 2 * TL::BLOCKS : 63)); break;
-                    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * TL::BLOCKS < 63 ? 3 * TL::BLOCKS : 63)); break;
+                // and at most 63 loads are ever in flight); B: this wave's
+                // loads per stage
+                auto wait_oldest = [&]<int B>() __attribute__((always_inline)) {
+                    switch (issued - landed - 1) {
+                        case 0: __builtin_amdgcn_s_waitcnt(kWaitVm0); break;
+                        case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(B < 63 ? B : 63)); break;
+                        case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * B < 63 ? 2 * B : 63)); break;
+                        default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * B < 63 ? 3 * B : 63)); break;
+                    }
+                };
+                if constexpr (TL::NLW == 2) {
+                    if (lw == 0)
+                        wait_oldest.template operator()<TL::A_BLOCKS>();
+                    else
+                        wait_oldest.template operator()<TL::BLOCKS - TL::A_BLOCKS>();
+                } else {
+                    wait_oldest.template operator()<TL::BLOCKS>();
                 }
                 compiler_fence();
                 ++landed;
-                if (lane == 0) flag_write(0, landed);
+                if (lane == 0) flag_write(lw == 0 ? 0 : 1 + TL::NWAVE, landed);
                 compiler_fence();
                 done = min_done();
                 continue;
@@ -688,7 +732,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
     // wait until stage `consumed` has landed
     auto wait_landed = [&]() __attribute__((always_inline)) {
         for (int spin = 0; seen <= consumed && spin < a.spin_cap; ++spin) {
-            seen = flag_read(0);
+            seen = __builtin_amdgcn_readfirstlane(landed_count());
             if (seen <= consumed) __builtin_amdgcn_s_sleep(1);
         }
         if (seen <= consumed) count_giveup(lane);   // bound reached: go on, and say so
@@ -724,7 +768,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
 #pragma unroll
                 for (int kw = 0; kw < 3; ++kw) fx[cur ^ 1][kw] = ldA(buf, qr + 1, kw);
             }
-            if (qr == 1) early = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
+            if (qr == 1) early = landed_count();
             if (qr == NROW - 2) {
                 const int f = __builtin_amdgcn_readfirstlane(early);
                 seen = f > seen ? f : seen;
@@ -795,7 +839,7 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
                 const int row = fm + kh;
                 const bool last_row = fm + 1 == FM;
                 const bool final_row = kh == 2 && last_row;
-                if (r == 1) early = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
+                if (r == 1) early = landed_count();
                 if (final_row) {
                     const int f = __builtin_amdgcn_readfirstlane(early);
                     seen = f > seen ? f : seen;
@@ -855,17 +899,23 @@ __global__ __launch_bounds__((WM *WN + 1) * 64) void conv3d_bf16_kernel(Args a) 
             for (int fm = 0; fm < FM; ++fm) {
                 int nrd = 0;
                 if (a == 0) {
-                    // the next input row first (needed soonest), then the tap 1 weights
-#pragma unroll
-                    for (int b = 0; b < 2; ++b) pr[fm + 1][b] = ldA(buf, fm + 1, b);
-                    nrd += 2;
                     if (fm == 0) {
-                        early = __atomic_load_n(&sync[0], __ATOMIC_RELAXED);
+                        // every input row of the stage, in the order of use, then the tap 1 weights
+#pragma unroll
+                        for (int r = 1; r <= FM; ++r)
+#pragma unroll
+                            for (int b = 0; b < 2; ++b) pr[r][b] = ldA(buf, r, b);
 #pragma unroll
                         for (int b = 0; b < 2; ++b)
 #pragma unroll
                             for (int fn = 0; fn < FN; ++fn) pw[1][b][fn] = ldB(buf, 2 + b, fn);
-                        nrd += 1 + 2 * FN;
+                        nrd += 2 * FM + 2 * FN;
+                    }
+                    if (fm == FM - 1) {
+                        // the landed count as late as its read still returns
+                        // before the next slot's operands are requested
+                        early = landed_count();
+                        nrd += TL::NLW;
                     }
                 } else if (fm == 0) {
                     const int f = __builtin_amdgcn_readfirstlane(early);
