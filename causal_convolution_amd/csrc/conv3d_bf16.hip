@@ -1393,6 +1393,30 @@ bool conv3d_bf16_norm_supported(int cout) { return cout == 96 || cout == 32; }
 // Rows a tile height computes for an image height (the last tile is padded).
 int64_t rows_computed(int64_t h, int hb) { return (h + hb - 1) / hb * hb; }
 
+// A launch too small for the large tiles to fill the chip evenly (a one-frame
+// stream step: 300 tiles of 18 x 32 x 64 on 256 compute units run as two
+// rounds, the second a sixth full) runs on the 32-channel tile instead when
+// its rounds cost less: the large tiles' rounds times their outputs, against
+// the small ones' times theirs and the small tile's higher cost per output
+// (measured 1.4x: more weight reads per MFMA).  Full-T launches have many
+// rounds and keep the large tiles.
+bool prefer_small_tiles(const ConvLaunch &c, bool tall) {
+    if (c.res != nullptr && c.wsc != nullptr) return false;   // the shortcut stages are sized per tile
+    int ncu = 0;
+    if (device_cu_count(&ncu) != hipSuccess || ncu <= 0) return false;
+    const bool pair = c.cache == nullptr && c.t >= 2;
+    const int64_t frames = c.n * (c.t - (pair ? 1 : 0));
+    const int64_t tw = (c.w_ + kWB - 1) / kWB;
+    auto rounds = [&](int hb, int nb) {
+        const int64_t items = tw * ((c.h + hb - 1) / hb) * frames * (((c.cout + 31) / 32 * 32) / nb);
+        return (items + ncu - 1) / ncu;
+    };
+    const int hb = c.cout % 64 == 0 ? (tall ? 18 : 16) : 12, nb = c.cout % 64 == 0 ? 64 : 96;
+    const double big = (double)rounds(hb, nb) * hb * nb;
+    const double small = 1.4 * (double)rounds(16, 32) * 16 * 32;
+    return small < big;
+}
+
 // Tile choice (measured on the workload shapes):
 //  - C_out a multiple of 64: a 2 x 2 grid of MFMA waves, each 8 or 9 rows x 32
 //    columns x 32 channels (128 or 144 accumulators), plus the load wave.  The
@@ -1424,6 +1448,7 @@ hipError_t launch_conv3d_bf16(const ConvLaunch &c, hipStream_t s) {
         if (c.cout % 96 == 0) return launch_cfg<4, 1, 3, 3, EPI_SHORTCUT>(c, s);
         return launch_cfg<4, 1, 4, 1, EPI_SHORTCUT>(c, s);
     }
+    if ((c.cout % 64 == 0 || c.cout % 96 == 0) && prefer_small_tiles(c, tall)) return launch_plain<4, 1, 4, 1>(c, s);
     if (c.cout % 64 == 0) return tall ? launch_plain<2, 2, 9, 1>(c, s) : launch_plain<2, 2, 8, 1>(c, s);
     if (c.cout % 96 == 0) return launch_plain<4, 1, 3, 3>(c, s);
     return launch_plain<4, 1, 4, 1>(c, s);
