@@ -66,6 +66,17 @@
 // that stage has landed), and every row's fragment reads are issued one per
 // MFMA rather than as a burst.
 //
+// The decoder's upsampler conv (up2: nearest x2 in H and W, then a 3x3 conv
+// with one temporal tap) runs by output phase where C_out is a multiple of 96
+// (PH kernels): output row 2i + py reads input rows i + py - 1 and i + py
+// only (likewise columns), so each phase (py, px) is a 2x2 conv of the
+// half-resolution input with merged weights (packed that way by
+// launch_pack_conv2d_weights).  A PH tile is 12 input rows x 32 columns x 96
+// channels of one phase; a stage holds that phase's 4 taps, 36 MFMAs per wave,
+// and two load waves share its DMA (A and B blocks).  Other C_out read the
+// doubled image through the loader (output position (h, w) from input
+// (h/2, w/2)) and run the 9 taps.
+//
 // LDS layout: 32-byte units (16 bf16 channels of one position or one weight
 // row), A tile rows 34 units apart.  The two 16-byte halves of a unit are
 // swapped when bit 3 of its column (A) or unit index (B) is set: 16 lanes
@@ -166,7 +177,7 @@ __device__ inline float halves_sum(float v) {
 struct Args {
     const uint16_t *x;      // conv input [n][t][h][w][cin]
     const uint16_t *cache;  // [n][2][h][w][cin] or null
-    const uint16_t *w;      // packed: [3 kt][cin/16][9 taps][cout][16]
+    const uint16_t *w;      // packed: [3 kt][cin/16][9 taps][cout][16] (upsampler: 1 kt; PH: [cin/16][4 phases][4 taps][cout][16])
     const float *bias;      // [cout] or null
     const uint16_t *res;    // [n][t][h][w][cres] or null
     const uint16_t *wsc;    // [cout][cres] or null
