@@ -560,6 +560,8 @@ def _upsample_check(torch, wv, xd, x_host, w, b, label, frames=None, rows=None):
     ((2, 1, 12, 32, 192), 192),  # by phase: exact tiles, two channel blocks, batch 2
     ((1, 3, 25, 70, 48), 96),    # by phase: 3 input slices (a lone last stage), ragged rows and columns
     ((1, 1, 1, 1, 96), 96),      # by phase: one input position, a 2 x 2 output
+    ((1, 2, 5, 9, 64), 288),     # by phase: three 96-channel blocks
+    ((2, 1, 7, 40, 16), 96),     # by phase: one input slice (a lone stage per tile), batch 2
     ((1, 2, 4, 9, 96), 40),      # a padded channel block
     ((1, 1, 1, 1, 32), 3),       # one input position, 3 output channels (2-byte stores)
 ])
