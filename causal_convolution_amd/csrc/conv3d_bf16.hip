@@ -174,6 +174,33 @@ __device__ inline float halves_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Division of a work-item index by a launch constant d (1 <= d < 2^31) as a
+// multiply and a shift, q = (n m) >> (31 + s) with s = ceil(log2 d) and
+// m = ceil(2^(31+s) / d) (a 32-bit value): m / 2^(31+s) exceeds 1/d by less
+// than 2^-(31+s), so for 0 <= n < 2^31 the product exceeds n/d by less than
+// 2^-s <= 1/d and never reaches the next integer (the fraction of n/d is at
+// most (d-1)/d).  A tile decode then costs a few scalar instructions instead
+// of four 64-bit divisions by kernel arguments.
+// The launch holds the four multipliers and the four shifts 31 + s packed
+// into one word (a byte each), to spare scalar registers.
+struct FastDiv {
+    uint32_t m[4];
+    uint32_t shifts;
+};
+
+inline void set_fastdiv(FastDiv &f, int k, uint32_t d) {
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.m[k] = (uint32_t)(((1ull << (31 + s)) + d - 1) / d);
+    f.shifts = (f.shifts & ~(0xffu << (8 * k))) | ((31 + s) << (8 * k));
+}
+
+// the quotient n / d_k, for 0 <= n < 2^31
+template <int K>
+__device__ inline uint32_t fdiv(uint32_t n, const FastDiv &f) {
+    return (uint32_t)(((uint64_t)n * f.m[K]) >> ((f.shifts >> (8 * K)) & 0xff));
+}
+
 struct Args {
     const uint16_t *x;      // conv input [n][t][h][w][cin]
     const uint16_t *cache;  // [n][2][h][w][cin] or null
@@ -190,7 +217,10 @@ struct Args {
     int cin, cout, cres;
     int cout_p;             // cout rounded up to 32: the packed weight's channel count
     int tiles_w, tiles_h;
-    // work items of the launch: one output tile each, or with pair = 1 (no
+    // the tile decode's divisors: output-channel blocks (0), frame groups
+    // (1), column blocks (2) and row blocks (3)
+    FastDiv div;
+    // work items of the launch (fewer than 2^31): one output tile each, or with pair = 1 (no
     // cache: frames 0 and 1 skip the stages of the causal pad) the tiles of
     // frames 0 and 1 of one block together, so every item runs three frames'
     // worth of stages
@@ -406,31 +436,31 @@ __global__ __launch_bounds__((WM *WN + (PH ? 2 : 1)) * 64) void conv3d_bf16_kern
 
     const int ncb = a.cout_p / NB;   // output-channel blocks (the last may be partly padding)
     const int64_t ngroups = a.T - a.pair;   // frame groups: {0, 1}, 2, 3, ... when paired
-    // tile `sub` of work item `tile`
-    auto decode = [&](int64_t tile, int sub) __attribute__((always_inline)) {
-        // the divisors are made opaque here, so the divisions' reciprocals are
-        // formed per call (once per tile) instead of being held in vector
-        // registers across the whole kernel
-        int64_t d_cb = ncb, d_g = ngroups, d_w = a.tiles_w, d_h = a.tiles_h;
-        asm volatile("" : "+s"(d_cb), "+s"(d_g), "+s"(d_w), "+s"(d_h));
+    // tile `sub` of work item `item` (a scalar decode: multiply-shift
+    // divisions by the launch's precomputed divisors)
+    auto decode = [&](int64_t item, int sub) __attribute__((always_inline)) {
+        uint32_t tile = (uint32_t)item, q;
         TileInfo ti;
-        ti.n0 = (int)(tile % d_cb) * NB;
-        tile /= d_cb;
+        q = fdiv<0>(tile, a.div);
+        ti.n0 = (int)(tile - q * (uint32_t)ncb) * NB;
+        tile = q;
         ti.ph = 0;
         if constexpr (PH) {
             // the four phases of a block side by side (they read the same input)
             ti.ph = (int)(tile & 3);
             tile >>= 2;
         }
-        const int64_t grp = tile % d_g;
-        tile /= d_g;
+        q = fdiv<1>(tile, a.div);
+        const int64_t grp = tile - q * (uint32_t)ngroups;
+        tile = q;
         ti.ntiles = a.pair && grp == 0 ? 2 : 1;
         ti.tq = a.pair ? (grp == 0 ? sub : grp + 1) : grp;
-        ti.w0 = (int)(tile % d_w) * kWB;
-        tile /= d_w;
-        ti.h0 = (int)(tile % d_h) * HB;
-        tile /= d_h;
-        ti.nq = tile;
+        q = fdiv<2>(tile, a.div);
+        ti.w0 = (int)(tile - q * (uint32_t)a.tiles_w) * kWB;
+        tile = q;
+        q = fdiv<3>(tile, a.div);
+        ti.h0 = (int)(tile - q * (uint32_t)a.tiles_h) * HB;
+        ti.nq = q;
         // without a cache the stages of frames before 0 only add zeros: skipped
         const int kt_begin = a.up2 ? 2 : (a.cache != nullptr || ti.tq >= 2) ? 0 : (int)(2 - ti.tq);
         ti.kt_begin = kt_begin;
@@ -1374,6 +1404,12 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.pair = c.cache == nullptr && !c.up2 && !c.gemm && c.t >= 2 ? 1 : 0;
     a.items = (int64_t)a.tiles_w * a.tiles_h * c.n * (c.t - a.pair) * (a.cout_p / TL::NB) * (PH ? 4 : 1);
     if (a.items <= 0) return hipSuccess;
+    if (a.items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // the decode's 31-bit item indices
+    a.div.shifts = 0;
+    set_fastdiv(a.div, 0, (uint32_t)(a.cout_p / TL::NB));
+    set_fastdiv(a.div, 1, (uint32_t)(c.t - a.pair));
+    set_fastdiv(a.div, 2, (uint32_t)a.tiles_w);
+    set_fastdiv(a.div, 3, (uint32_t)a.tiles_h);
     // persistent grid: one workgroup per compute unit (the LDS ring takes most
     // of a CU's 160 KB), each looping over its share of the tiles
     int ncu = 0;

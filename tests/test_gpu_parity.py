@@ -259,6 +259,9 @@ SMALL_BLOCKS = [
     # the identity residual through the ring with 32-channel tiles over
     # several channel blocks (160 = 5 x 32)
     wl.custom("id160", wl.BF16, 1, 3, 10, 40, 160, 160),
+    # the identity residual with 96-channel tiles over three channel blocks,
+    # ragged rows and columns
+    wl.custom("id288", wl.BF16, 1, 3, 13, 36, 288, 288),
 ]
 
 

@@ -1,0 +1,40 @@
+"""The conv kernel's tile decode divides 31-bit work-item indices by launch
+constants with a multiply and a shift (s = ceil(log2 d), m = ceil(2^(31+s)/d),
+q = (n m) >> (31 + s)).  The claim that this is exact for 0 <= n < 2^31 and
+1 <= d < 2^31, and that m fits 32 bits, checked here on the CPU over every
+divisor up to 4096 and the edges above."""
+import numpy as np
+
+
+def magic(d):
+    s = 0
+    while (1 << s) < d:
+        s += 1
+    return ((1 << (31 + s)) + d - 1) // d, s
+
+
+def check(d, ns):
+    m, s = magic(d)
+    assert 0 < m < (1 << 32), (d, m)
+    for n in ns:
+        assert (n * m) >> (31 + s) == n // d, (n, d)
+
+
+def test_every_small_divisor():
+    top = (1 << 31) - 1
+    for d in range(1, 4097):
+        # around each multiple of d near 0 and near the top of the range, and
+        # the largest index
+        k = top // d
+        ns = {0, 1, d - 1, d, d + 1, 2 * d - 1, top, k * d, k * d - 1, (k - 1) * d + d - 1}
+        check(d, [n for n in ns if 0 <= n <= top])
+
+
+def test_large_divisors_random_indices():
+    rng = np.random.default_rng(0)
+    top = (1 << 31) - 1
+    ds = [4097, 65535, 65536, 65537, 194400, (1 << 30) - 1, 1 << 30, (1 << 30) + 1, top]
+    ds += [int(v) for v in rng.integers(1, top, 200)]
+    for d in ds:
+        ns = [int(v) for v in rng.integers(0, top, 200)] + [top, d - 1, d, top - top % d, top - top % d - 1]
+        check(d, [n for n in ns if 0 <= n <= top])
