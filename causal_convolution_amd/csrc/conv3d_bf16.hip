@@ -132,7 +132,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // Buffer resource word 3 for raw (unformatted, stride 0) buffers on gfx9-family
 // GPUs; loads past num_records return zero.
 constexpr int kBufFlags = 0x00020000;
-constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer: the load returns zeros
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kSuperBlock = 20;   // frame groups per super-block of the tile order (launch_cfg)  // beyond every buffer: the load returns zeros
 
 constexpr int kKC = 16;          // input channels per stage = one MFMA k-step
 constexpr int kUnit = 32;        // bytes per LDS unit (16 bf16)
@@ -181,24 +182,25 @@ __device__ inline float halves_sum(float v) {
 // 2^-s <= 1/d and never reaches the next integer (the fraction of n/d is at
 // most (d-1)/d).  A tile decode then costs a few scalar instructions instead
 // of four 64-bit divisions by kernel arguments.
-// The launch holds the four multipliers and the four shifts 31 + s packed
-// into one word (a byte each), to spare scalar registers.
+// The launch holds six multipliers and their shifts 31 + s, packed four to a
+// word (a byte each), to spare scalar registers.
 struct FastDiv {
-    uint32_t m[4];
-    uint32_t shifts;
+    uint32_t m[6];
+    uint32_t shifts[2];
 };
 
 inline void set_fastdiv(FastDiv &f, int k, uint32_t d) {
     uint32_t s = 0;
     while ((1ull << s) < d) ++s;
     f.m[k] = (uint32_t)(((1ull << (31 + s)) + d - 1) / d);
-    f.shifts = (f.shifts & ~(0xffu << (8 * k))) | ((31 + s) << (8 * k));
+    uint32_t &w = f.shifts[k / 4];
+    w = (w & ~(0xffu << (8 * (k % 4)))) | ((31 + s) << (8 * (k % 4)));
 }
 
 // the quotient n / d_k, for 0 <= n < 2^31
 template <int K>
 __device__ inline uint32_t fdiv(uint32_t n, const FastDiv &f) {
-    return (uint32_t)(((uint64_t)n * f.m[K]) >> ((f.shifts >> (8 * K)) & 0xff));
+    return (uint32_t)(((uint64_t)n * f.m[K]) >> ((f.shifts[K / 4] >> (8 * (K % 4))) & 0xff));
 }
 
 struct Args {
@@ -217,9 +219,18 @@ struct Args {
     int cin, cout, cres;
     int cout_p;             // cout rounded up to 32: the packed weight's channel count
     int tiles_w, tiles_h;
-    // the tile decode's divisors: output-channel blocks (0), frame groups
-    // (1), column blocks (2) and row blocks (3)
+    // Tile order within one (batch item, row block): frame groups in
+    // super-blocks of sbg, and within a super-block the frame group fastest,
+    // then the column block (the last super-block holds sb_r groups).  The
+    // decode's divisors: output-channel blocks (0), the items of one (batch
+    // item, row block) (1), of one full super-block (2), row blocks (3),
+    // sbg (4) and sb_r (5).
     FastDiv div;
+    int region;     // frame groups x column blocks
+    int sbg, sb_gw; // frame groups per super-block, and times the column blocks
+    int sb_full;    // items of the full super-blocks: (super-blocks - 1) sb_gw
+    int sb_last0;   // first frame group of the last super-block
+    int sb_r;       // its frame groups
     // work items of the launch (fewer than 2^31): one output tile each, or with pair = 1 (no
     // cache: frames 0 and 1 skip the stages of the causal pad) the tiles of
     // frames 0 and 1 of one block together, so every item runs three frames'
@@ -435,7 +446,6 @@ __global__ __launch_bounds__((WM *WN + (PH ? 2 : 1)) * 64) void conv3d_bf16_kern
     const int64_t x_count = a.items * (wg_before + wg_x) / nwg - x_begin;
 
     const int ncb = a.cout_p / NB;   // output-channel blocks (the last may be partly padding)
-    const int64_t ngroups = a.T - a.pair;   // frame groups: {0, 1}, 2, 3, ... when paired
     // tile `sub` of work item `item` (a scalar decode: multiply-shift
     // divisions by the launch's precomputed divisors)
     auto decode = [&](int64_t item, int sub) __attribute__((always_inline)) {
@@ -450,14 +460,27 @@ __global__ __launch_bounds__((WM *WN + (PH ? 2 : 1)) * 64) void conv3d_bf16_kern
             ti.ph = (int)(tile & 3);
             tile >>= 2;
         }
+        // frame groups ({0, 1}, 2, 3, ... when paired) and column blocks of
+        // one (batch item, row block), by super-block
         q = fdiv<1>(tile, a.div);
-        const int64_t grp = tile - q * (uint32_t)ngroups;
+        uint32_t idx = tile - q * (uint32_t)a.region, wb, g0, gl;
         tile = q;
+        if (idx < (uint32_t)a.sb_full) {
+            q = fdiv<2>(idx, a.div);
+            g0 = q * (uint32_t)a.sbg;
+            idx -= q * (uint32_t)a.sb_gw;
+            wb = fdiv<4>(idx, a.div);
+            gl = idx - wb * (uint32_t)a.sbg;
+        } else {
+            idx -= (uint32_t)a.sb_full;
+            g0 = (uint32_t)a.sb_last0;
+            wb = fdiv<5>(idx, a.div);
+            gl = idx - wb * (uint32_t)a.sb_r;
+        }
+        const int64_t grp = g0 + gl;
         ti.ntiles = a.pair && grp == 0 ? 2 : 1;
         ti.tq = a.pair ? (grp == 0 ? sub : grp + 1) : grp;
-        q = fdiv<2>(tile, a.div);
-        ti.w0 = (int)(tile - q * (uint32_t)a.tiles_w) * kWB;
-        tile = q;
+        ti.w0 = (int)wb * kWB;
         q = fdiv<3>(tile, a.div);
         ti.h0 = (int)(tile - q * (uint32_t)a.tiles_h) * HB;
         ti.nq = q;
@@ -1405,11 +1428,28 @@ hipError_t launch_cfg(const ConvLaunch &c, hipStream_t s) {
     a.items = (int64_t)a.tiles_w * a.tiles_h * c.n * (c.t - a.pair) * (a.cout_p / TL::NB) * (PH ? 4 : 1);
     if (a.items <= 0) return hipSuccess;
     if (a.items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // the decode's 31-bit item indices
-    a.div.shifts = 0;
-    set_fastdiv(a.div, 0, (uint32_t)(a.cout_p / TL::NB));
-    set_fastdiv(a.div, 1, (uint32_t)(c.t - a.pair));
-    set_fastdiv(a.div, 2, (uint32_t)a.tiles_w);
+    // Super-blocks of 20 frame groups where one channel block spans every
+    // output channel (c4's 96-channel tiles): an XCD's 32 workgroups then run
+    // neighbouring column blocks of the same frames together as well as
+    // neighbouring frames, and the tiles' column halos are read from L2.
+    // Where several channel blocks share a frame (C_out 192, 384), and for
+    // the upsampler by phase (four phase tiles per block already), the frame
+    // groups stay undivided: measured neutral to slightly slower there.
+    const int ngroups = (int)(c.t - a.pair), ncb = a.cout_p / TL::NB;
+    a.sbg = ncb == 1 && !PH ? (ngroups < kSuperBlock ? ngroups : kSuperBlock) : ngroups;
+    const int nsb = (ngroups + a.sbg - 1) / a.sbg;
+    a.region = ngroups * a.tiles_w;
+    a.sb_gw = a.sbg * a.tiles_w;
+    a.sb_full = (nsb - 1) * a.sb_gw;
+    a.sb_last0 = (nsb - 1) * a.sbg;
+    a.sb_r = ngroups - a.sb_last0;
+    a.div.shifts[0] = a.div.shifts[1] = 0;
+    set_fastdiv(a.div, 0, (uint32_t)ncb);
+    set_fastdiv(a.div, 1, (uint32_t)a.region);
+    set_fastdiv(a.div, 2, (uint32_t)a.sb_gw);
     set_fastdiv(a.div, 3, (uint32_t)a.tiles_h);
+    set_fastdiv(a.div, 4, (uint32_t)a.sbg);
+    set_fastdiv(a.div, 5, (uint32_t)a.sb_r);
     // persistent grid: one workgroup per compute unit (the LDS ring takes most
     // of a CU's 160 KB), each looping over its share of the tiles
     int ncu = 0;
