@@ -262,6 +262,9 @@ SMALL_BLOCKS = [
     # the identity residual with 96-channel tiles over three channel blocks,
     # ragged rows and columns
     wl.custom("id288", wl.BF16, 1, 3, 13, 36, 288, 288),
+    # 24 frames, 96 channels: the convs' tiles go in frame super-blocks of 20
+    # groups, the last one ragged (23 groups: 20 + 3)
+    wl.custom("id96_t24", wl.BF16, 1, 24, 13, 40, 96, 96),
 ]
 
 
