@@ -181,7 +181,7 @@ __device__ inline float halves_sum(float v) {
 // than 2^-(31+s), so for 0 <= n < 2^31 the product exceeds n/d by less than
 // 2^-s <= 1/d and never reaches the next integer (the fraction of n/d is at
 // most (d-1)/d).  A tile decode then costs a few scalar instructions instead
-// of four 64-bit divisions by kernel arguments.
+// of 64-bit divisions by kernel arguments.
 // The launch holds six multipliers and their shifts 31 + s, packed four to a
 // word (a byte each), to spare scalar registers.
 struct FastDiv {

@@ -300,11 +300,13 @@ WANVAE_API int wanvae_resblock_workspace_size(const wanvae_resblock_params *p, c
  * Kernel launches on `stream`: norm1 (into the conv input region), conv A
  * (into the region of a), norm2 (a into the conv input region; for fp32, a
  * normalised in place), then conv B with the residual add in its epilogue.
- * The 1x1x1 shortcut is added there too: computed inside conv B's K loop, or,
- * for bf16 with in_dim 128, 256 or 384 and out_dim a multiple of 64, by a
- * projection GEMM launched ahead of conv B into the region of a (free once
- * norm2 has read it), S rounded to bf16 and then added like the identity
- * residual: five launches in that case, four otherwise.
+ * For bf16 with out_dim 96 or 32 conv A computes norm2 + SiLU in its own
+ * epilogue and writes conv B's input directly (a is never stored, no norm2
+ * launch).  The 1x1x1 shortcut is added in conv B's epilogue too: computed
+ * inside conv B's K loop, or, for bf16 with in_dim 128, 256 or 384 and
+ * out_dim a multiple of 64, by a projection GEMM launched ahead of conv B
+ * into the region of a (free once norm2 has read it), S rounded to bf16 and
+ * then added like the identity residual.  Three to five launches in all.
  */
 WANVAE_API int wanvae_resblock_forward(const wanvae_resblock_params *p, const void *x, void *y,
                             const wanvae_dims *d, void *workspace, size_t ws_bytes, void *stream);
