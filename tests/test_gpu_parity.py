@@ -265,6 +265,10 @@ SMALL_BLOCKS = [
     # 24 frames, 96 channels: the convs' tiles go in frame super-blocks of 20
     # groups, the last one ragged (23 groups: 20 + 3)
     wl.custom("id96_t24", wl.BF16, 1, 24, 13, 40, 96, 96),
+    # the same on the 32-channel tiles (norm2 in conv A's epilogue), and with
+    # the fused 1x1x1 shortcut stages on the 96-channel tiles (21 groups)
+    wl.custom("id32_t24", wl.BF16, 1, 24, 9, 40, 32, 32),
+    wl.custom("sc64_96_t22", wl.BF16, 1, 22, 12, 40, 64, 96),
 ]
 
 
